@@ -1,0 +1,343 @@
+"""Pins of the CPU oracle against what the paper and the mathematics fix.
+
+Each test checks the oracle against something other than itself: a hand-worked example, a
+closed form, an invariant the paper states, a brute-force computation on tiny inputs, or a
+library routine that a special case reduces to. Runs on the CPU only.
+"""
+import json
+import math
+import os
+from fractions import Fraction
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import hhr_oracle as orc
+from long_context_decode_gkr_amd import synth
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+
+
+def _orth(seed, d):
+    a = np.random.default_rng(seed).standard_normal((d, d))
+    q, r = np.linalg.qr(a)
+    return (q * np.sign(np.diag(r))[None, :]).astype(np.float32)
+
+
+# ---------------------------------------------------------------------------------------------
+# Hand-worked example (§3.3.1 Eq.3-4, §3.1 Eq.1-2)
+# ---------------------------------------------------------------------------------------------
+def test_tiny_worked_example():
+    g = json.load(open(os.path.join(GOLDEN, "tiny_worked_example.json")))
+    i, e = g["inputs"], g["expected"]
+    K = np.array(i["keys"], np.float32)
+    V = np.array(i["values"], np.float32)
+    q = np.array(i["q"], np.float32)
+    R = np.array(i["R"], np.float32)
+    W = np.array(i["W"], np.float32)
+    S, L = i["S"], i["L"]
+
+    assert np.array_equal(orc.rotate(q[None], R)[0], e["q_rot"])
+    assert np.array_equal(orc.rotate(K, R), e["keys_rot"])
+    lo, hi, kc = orc.build_head(K, L, R, W, S)
+    assert np.array_equal(lo, e["page_lo"]) and np.array_equal(hi, e["page_hi"])
+    assert kc[:, 0].tolist() == e["key_codes"]
+
+    for k, sel_key in ((1, "sel_k1"), (2, "sel_k2")):
+        r = orc.decode_head(q, K, V, L, lo, hi, kc, R, W, S, i["rho"], k, i["scale"])
+        assert r["U"].tolist() == e["U"]
+        assert r["n_keep"] == e["n_keep"]
+        assert r["pages"].tolist() == e["pages"]
+        assert int(r["q_code"][0]) == e["q_code"]
+        assert r["cand"].tolist() == e["candidates"]
+        assert r["D"].tolist() == e["D"]
+        assert r["sel"].tolist() == e[sel_key]
+        if k == 1:
+            assert np.array_equal(r["out"], e["out_k1"])
+        else:
+            t = math.exp(0.75)
+            np.testing.assert_allclose(r["out"], [1.0 / (1.0 + t), t / (1.0 + t)], rtol=1e-14)
+    # Eq. (3) bounds the true page maxima; page 1's bound is tight.
+    assert all(u >= m for u, m in zip(e["U"], e["true_page_max_logit"]))
+
+
+# ---------------------------------------------------------------------------------------------
+# Rotation (§3.3.1 Eq.4): row-vector convention and logit preservation
+# ---------------------------------------------------------------------------------------------
+def test_rotation_row_vector_convention():
+    # A permutation matrix with R[i, pi(i)] = 1 sends coordinate i of x to coordinate pi(i).
+    d = 8
+    pi = np.array([3, 0, 7, 1, 6, 2, 5, 4])
+    R = np.zeros((d, d), np.float32)
+    R[np.arange(d), pi] = 1.0
+    x = np.arange(1, d + 1, dtype=np.float32)
+    y = orc.rotate(x[None], R)[0]
+    assert all(y[pi[i]] == x[i] for i in range(d))
+
+
+def test_rotation_preserves_logits():
+    d = 128
+    R = _orth(1, d)
+    assert np.abs(R.astype(np.float64) @ R.T.astype(np.float64) - np.eye(d)).max() < 1e-6
+    rng = np.random.default_rng(2)
+    q = rng.standard_normal(d).astype(np.float32)
+    K = rng.standard_normal((500, d)).astype(np.float32)
+    K[:, :4] *= 10
+    qt = orc.rotate(q[None], R)[0].astype(np.float64)
+    kt = orc.rotate(K, R).astype(np.float64)
+    exact = K.astype(np.float64) @ q.astype(np.float64)
+    tol = 1e-6 * np.linalg.norm(q) * np.linalg.norm(K, axis=1)
+    assert np.all(np.abs(kt @ qt - exact) <= tol)
+
+
+# ---------------------------------------------------------------------------------------------
+# Page bound (§3.3.1 Eq.3): validity, page size 1, identity rotation
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("rotated", [False, True])
+@pytest.mark.parametrize("S", [1, 3, 16])
+def test_bound_is_valid_upper_bound(rotated, S):
+    d, L = 64, 203
+    rng = np.random.default_rng(S + 10 * rotated)
+    K = rng.standard_normal((L, d)).astype(np.float32)
+    K[:, 5] *= 10
+    q = rng.standard_normal(d).astype(np.float32)
+    R = _orth(3, d) if rotated else np.eye(d, dtype=np.float32)
+    W = rng.standard_normal((d, 32)).astype(np.float32)
+    lo, hi, _ = orc.build_head(K, L, R, W, S)
+    qt = orc.rotate(q[None], R)[0]
+    U = orc.page_bounds(qt, lo, hi)
+    logits = K.astype(np.float64) @ q.astype(np.float64)
+    for p in range(orc.num_pages(L, S)):
+        rows = logits[p * S:min(L, p * S + S)]
+        scale = np.abs(qt.astype(np.float64)) @ np.maximum(np.abs(lo[p]), np.abs(hi[p]))
+        assert U[p] >= rows.max() - 1e-5 * scale
+        if S == 1:
+            # one key per page: l = u = k~, so U is that key's (rotated) logit
+            assert U[p] == pytest.approx(float(qt.astype(np.float64) @ lo[p].astype(np.float64)), rel=1e-13, abs=1e-13)
+            assert abs(U[p] - rows[0]) <= 1e-5 * scale
+
+
+def test_bound_identity_rotation_is_plain_min_max_bound():
+    # With R = I the bound is sum_j max(q_j min_t k_tj, q_j max_t k_tj) over the raw keys.
+    rng = np.random.default_rng(4)
+    d, S = 16, 4
+    K = rng.standard_normal((S, d)).astype(np.float32)
+    q = rng.standard_normal(d).astype(np.float32)
+    lo, hi, _ = orc.build_head(K, S, np.eye(d, dtype=np.float32), np.eye(d, dtype=np.float32), S)
+    want = 0.0
+    for j in range(d):
+        col = [float(K[t, j]) for t in range(S)]
+        want += max(float(q[j]) * min(col), float(q[j]) * max(col))
+    assert orc.page_bounds(q, lo, hi)[0] == pytest.approx(want, rel=1e-15)
+
+
+def test_partial_last_page_covers_only_valid_rows():
+    K = np.array([[1, 1], [2, -5], [9, 9], [100, 100]], np.float32)
+    lo, hi = orc.page_extrema(K, 3, 2)
+    assert lo.tolist() == [[1, -5], [9, 9]] and hi.tolist() == [[2, 1], [9, 9]]
+
+
+# ---------------------------------------------------------------------------------------------
+# Codes (§3.1 Eq.1, §3.3.2 Eq.10 with c = sign(z))
+# ---------------------------------------------------------------------------------------------
+def test_codes_identity_projection_and_bit_order():
+    d = 128
+    W = np.eye(d, dtype=np.float32)
+    for c in (0, 1, 31, 32, 33, 63, 64, 100, 127):
+        x = np.zeros(d, np.float32)
+        x[c] = 0.25
+        words = orc.codes(x[None], W)[0]
+        expect = [0, 0, 0, 0]
+        expect[c // 32] = 1 << (c % 32)
+        assert words.tolist() == expect
+    rng = np.random.default_rng(5)
+    x = rng.standard_normal((20, d)).astype(np.float32)
+    x[0, :7] = 0.0
+    bits = orc.sign_bits(x, W)
+    assert np.array_equal(bits, x > 0)          # sign(0) gives bit 0
+
+
+def test_codes_of_negated_input_are_complements():
+    rng = np.random.default_rng(6)
+    x = rng.standard_normal((50, 128)).astype(np.float32)
+    W = rng.standard_normal((128, 256)).astype(np.float32)
+    a, b = orc.codes(x, W), orc.codes(-x, W)
+    assert np.array_equal(a ^ b, np.full_like(a, 0xFFFFFFFF))
+    assert np.all(orc.hamming(a[0], a) == orc.hamming(a[0], a))
+    assert np.all(orc.hamming(a[3], b[3:4]) == 256) and orc.hamming(a[3], a[3:4])[0] == 0
+
+
+def _brute_sign(x_row, w_col):
+    # exact sum of products with integers: every float is m * 2**e with integer m
+    terms = []
+    for a, b in zip(x_row, w_col):
+        na, da = float(a).as_integer_ratio()
+        nb, db = float(b).as_integer_ratio()
+        terms.append((na * nb, da * db))
+    den = 1
+    for _, dd in terms:
+        den = den * dd // math.gcd(den, dd)
+    num = sum(n * (den // dd) for n, dd in terms)
+    return num > 0
+
+
+def test_codes_exact_sign_where_fp64_sum_cancels():
+    # z = 2^100 + 2^-100 - 2^100 = 2^-100 > 0, but a left-to-right fp64 sum gives 0.
+    big, small = 2.0 ** 100, 2.0 ** -100
+    x = np.ones((6, 3), np.float32)
+    cols = [[big, small, -big], [-big, small, big], [big, -small, -big], [small, big, -big],
+            [big, -big, 0.0], [1.0, -1.0, 2.0 ** -24]]
+    W = np.array(cols, np.float32).T
+    bits = orc.sign_bits(x, W)[0]
+    assert bits.tolist() == [True, True, False, True, False, True]
+    for c in range(W.shape[1]):
+        assert bits[c] == _brute_sign(x[0], W[:, c])
+
+
+def test_codes_match_brute_force_on_tiny_inputs():
+    rng = np.random.default_rng(7)
+    for trial in range(30):
+        d, nb = int(rng.integers(1, 9)), int(rng.integers(1, 70))
+        x = rng.integers(-3, 4, size=(5, d)).astype(np.float32) * np.float32(0.5)
+        W = rng.integers(-3, 4, size=(d, nb)).astype(np.float32)
+        bits = orc.sign_bits(x, W)
+        for i in range(5):
+            for c in range(nb):
+                assert bits[i, c] == _brute_sign(x[i], W[:, c])
+        words = orc.pack_bits(bits)
+        for i in range(5):
+            for c in range(nb):
+                assert ((int(words[i, c // 32]) >> (c % 32)) & 1) == int(bits[i, c])
+
+
+# ---------------------------------------------------------------------------------------------
+# Hamming distance (§3.1 Eq.2): brute force per-bit loop
+# ---------------------------------------------------------------------------------------------
+def test_hamming_matches_per_bit_loop():
+    rng = np.random.default_rng(8)
+    for nw in (1, 4, 8):
+        qc = rng.integers(0, 2 ** 32, size=nw, dtype=np.uint64).astype(np.uint32)
+        kc = rng.integers(0, 2 ** 32, size=(40, nw), dtype=np.uint64).astype(np.uint32)
+        D = orc.hamming(qc, kc)
+        for t in range(40):
+            n = 0
+            for c in range(32 * nw):
+                n += ((int(qc[c // 32]) >> (c % 32)) & 1) != ((int(kc[t, c // 32]) >> (c % 32)) & 1)
+            assert D[t] == n
+
+
+# ---------------------------------------------------------------------------------------------
+# Selections: properties that define "top n by key, ties to the lower index"
+# ---------------------------------------------------------------------------------------------
+def test_keep_count():
+    assert orc.keep_count(10, 0.3) == 3           # 0.3 * 10 rounds to exactly 3.0 in IEEE double
+    assert orc.keep_count(8192, 1 / 16) == 512
+    assert orc.keep_count(5, 1e-9) == 1
+    assert orc.keep_count(7, 1.0) == 7
+    assert orc.keep_count(3, 0.34) == 2
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_select_pages_is_top_n_with_lower_index_ties(seed):
+    rng = np.random.default_rng(seed)
+    P = int(rng.integers(1, 300))
+    U = rng.integers(-5, 5, size=P).astype(np.float64)   # many exact ties
+    U[rng.integers(0, P)] = -0.0
+    n = int(rng.integers(1, P + 1))
+    sel = orc.select_pages(U, n)
+    assert len(sel) == n and np.all(np.diff(sel) > 0)
+    s = set(sel.tolist())
+    for a in s:
+        for b in range(P):
+            if b not in s:
+                assert U[a] > U[b] or (U[a] == U[b] and a < b)
+
+
+@pytest.mark.parametrize("seed", range(5))
+def test_select_tokens_is_top_k_smallest_distance_lower_index_ties(seed):
+    rng = np.random.default_rng(seed + 100)
+    n = int(rng.integers(1, 400))
+    cand = np.sort(rng.choice(10 * n, n, replace=False))
+    D = rng.integers(0, 12, size=n)
+    k = int(rng.integers(1, n + 20))
+    sel = orc.select_tokens(cand, D, k)
+    assert len(sel) == min(k, n) and np.all(np.diff(sel) > 0)
+    dmap = dict(zip(cand.tolist(), D.tolist()))
+    s = set(sel.tolist())
+    for a in s:
+        for b in cand.tolist():
+            if b not in s:
+                assert dmap[a] < dmap[b] or (dmap[a] == dmap[b] and a < b)
+
+
+# ---------------------------------------------------------------------------------------------
+# Attention: full budget equals dense attention; k = 1 returns one value row
+# ---------------------------------------------------------------------------------------------
+def test_full_budget_equals_dense_attention():
+    cfg = synth.CONFIGS[2].scaled(seq_len=301, n_plant=4)
+    lay = synth.make_layer(cfg)
+    idx = orc.build_layer(lay["K"], lay["seq_lens"], lay["R"], lay["W"], cfg.page_size)
+    L = int(lay["seq_lens"][0])
+    heads = [(0, 0), (0, 5), (0, 31)]
+    res = orc.decode_layer(lay["q"], lay["K"], lay["V"], lay["seq_lens"], idx, lay["R"], lay["W"],
+                           cfg.page_size, rho=1.0, k=L, heads=heads)
+    for (b, h), r in res.items():
+        g = h // cfg.group
+        assert r["sel"].tolist() == list(range(L))
+        qt = torch.tensor(lay["q"][b, h], dtype=torch.float64)[None, None, None]
+        kt = torch.tensor(lay["K"][b, g, :L], dtype=torch.float64)[None, None]
+        vt = torch.tensor(lay["V"][b, g, :L], dtype=torch.float64)[None, None]
+        dense = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, scale=orc.default_scale(cfg.head_dim))[0, 0, 0].numpy()
+        np.testing.assert_allclose(r["out"], dense, rtol=1e-12, atol=1e-13)
+
+
+def test_budget_one_returns_a_value_row():
+    cfg = synth.CONFIGS[1].scaled(seq_len=200, n_plant=2)
+    lay = synth.make_layer(cfg)
+    idx = orc.build_layer(lay["K"], lay["seq_lens"], lay["R"], lay["W"], cfg.page_size)
+    r = orc.decode_layer(lay["q"], lay["K"], lay["V"], lay["seq_lens"], idx, lay["R"], lay["W"],
+                         cfg.page_size, rho=0.25, k=1)[(0, 0)]
+    assert len(r["sel"]) == 1
+    assert np.array_equal(r["out"], lay["V"][0, 0, r["sel"][0]].astype(np.float64))
+
+
+# ---------------------------------------------------------------------------------------------
+# Append: build(L) followed by n appends equals build(L + n)
+# ---------------------------------------------------------------------------------------------
+def test_append_equals_build():
+    rng = np.random.default_rng(9)
+    d, nb, S, L0, n = 32, 64, 4, 9, 11
+    K = rng.standard_normal((L0 + n, d)).astype(np.float32)
+    V = rng.standard_normal((L0 + n, d)).astype(np.float32)
+    R, W = _orth(10, d), rng.standard_normal((d, nb)).astype(np.float32)
+    lo, hi, kc = orc.build_head(K, L0, R, W, S)
+    Pmax = orc.num_pages(L0 + n, S)
+    st = dict(K=np.zeros_like(K), V=np.zeros_like(V), lo=np.zeros((Pmax, d), np.float32),
+              hi=np.zeros((Pmax, d), np.float32), codes=np.zeros((L0 + n, nb // 32), np.uint32), L=L0)
+    st["K"][:L0], st["V"][:L0] = K[:L0], V[:L0]
+    st["lo"][:len(lo)], st["hi"][:len(hi)], st["codes"][:L0] = lo, hi, kc
+    for t in range(L0, L0 + n):
+        orc.append_head(st, K[t], V[t], R, W, S)
+    lo2, hi2, kc2 = orc.build_head(K, L0 + n, R, W, S)
+    assert st["L"] == L0 + n
+    assert np.array_equal(st["lo"], lo2) and np.array_equal(st["hi"], hi2)
+    assert np.array_equal(st["codes"], kc2)
+    assert np.array_equal(st["K"], K) and np.array_equal(st["V"], V)
+
+
+# ---------------------------------------------------------------------------------------------
+# Planted keys (input recipe): each planted key's logit is mean + 4 std of its head's logits
+# ---------------------------------------------------------------------------------------------
+def test_generator_planted_keys_are_selected_at_full_budget_ratio():
+    cfg = synth.CONFIGS[1].scaled(seq_len=1024, n_plant=8)
+    lay = synth.make_layer(cfg)
+    logits = lay["K"][0, 0, :1024].astype(np.float64) @ lay["q"][0, 0].astype(np.float64)
+    top = np.sort(logits)[-8:]
+    assert top.min() > logits.mean() + 3.0 * logits.std()
+
+
+def test_candidates_drop_positions_past_the_sequence_end():
+    assert orc.candidates(np.array([0, 2]), 10, 4).tolist() == [0, 1, 2, 3, 8, 9]
+    assert orc.candidates(np.array([1]), 10, 4).tolist() == [4, 5, 6, 7]
