@@ -1,0 +1,178 @@
+/*
+ * hhr.h -- C ABI of the HHR (Hierarchical Hash Retrieval) sparse-attention decode library for
+ * AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one of "HHR: Hierarchical Hash Retrieval for Efficient LLM Generation"
+ * (arXiv 2610.01230). One decode step, for every sequence b and query head h, runs
+ *   coarse stage (GKR, §3.3.1): rotate the query, q~ = q R (Eq. 4); bound every page p of the
+ *     head's rotated keys by U = sum_j max(q~_j l_j, q~_j u_j) (Eq. 3), where l, u are the
+ *     page's per-dimension minimum and maximum of the rotated keys; keep the best pages;
+ *   fine stage (LHP, §3.3.2): hash the query, c = sign(q W) (Eq. 1, Eq. 10), take the Hamming
+ *     distance (Eq. 2) to the stored code of every key in the kept pages and keep the closest
+ *     keys;
+ *   attention: exact softmax attention of q over the kept keys (§1).
+ *
+ * Conventions shared by every entry point
+ *   - All array arguments are DEVICE pointers owned by the caller. The library allocates no
+ *     memory, keeps no state between calls, never synchronises the host, and enqueues all work
+ *     on `stream` (a hipStream_t; NULL means the null stream). Calls on different streams that
+ *     touch disjoint caches and workspaces may run concurrently.
+ *   - Arguments are validated on the host before anything is enqueued; an invalid call
+ *     returns an error status and enqueues nothing. Values that live in device memory
+ *     (seq_lens) cannot be checked on the host: kernels clamp them to [0, max_seq_len].
+ *   - A failed kernel launch returns HHR_ERR_HIP. Faults inside a kernel surface at the
+ *     caller's next synchronisation.
+ *   - Head dimension d is 128. Query head h reads KV head g = h / (Hq / Hkv) (grouped-query
+ *     attention); the rotation R_g and projection W_g belong to the KV head.
+ *   - Rows are row vectors: q~ = q R_g, z = x W_g.
+ *   - Inputs must be finite.
+ *
+ * Layouts (row-major, innermost last; Pmax = max_seq_len / page_size, nw = hash_bits / 32)
+ *   K, V       [B][Hkv][max_seq_len][128]   kv_dtype
+ *   page_min   [B][Hkv][128][Pmax]          fp32, channel-major ("SoA"): entry [b][g][j][p] is
+ *   page_max   [B][Hkv][128][Pmax]          the min / max over the page's valid tokens of
+ *                                            dimension j of the rotated key k~ = k R_g
+ *   codes      [B][Hkv][max_seq_len][nw]    uint32; bit c of a key's code sits in word c / 32
+ *                                            at bit position c % 32; bit c = 1 iff the exact
+ *                                            real value of (k W_g)_c is > 0
+ *   seq_lens   [B]                          int32, number of valid tokens per sequence
+ *   R          [Hkv][128][128]              fp32, orthogonal (caller-supplied)
+ *   W          [Hkv][128][hash_bits]        fp32 (caller-supplied)
+ *   q          [B][Hq][128]                 q_dtype
+ *   out        [B][Hq][128]                 fp32
+ */
+#ifndef HHR_H
+#define HHR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* hhr_stream_t; /* the same type as hipStream_t */
+
+typedef enum {
+  HHR_OK = 0,
+  HHR_ERR_INVALID_ARG = 1,  /* null pointer, non-positive size, malformed value          */
+  HHR_ERR_UNSUPPORTED = 2,  /* well-formed but outside what the kernels implement         */
+  HHR_ERR_CAPACITY = 3,     /* a size exceeds a documented maximum                        */
+  HHR_ERR_WORKSPACE = 4,    /* workspace too small or misaligned                          */
+  HHR_ERR_HIP = 5           /* a HIP launch or runtime call failed                        */
+} hhr_status;
+
+typedef enum { HHR_F32 = 0, HHR_BF16 = 1 } hhr_dtype;
+
+/* Shapes. Supported: head_dim = 128; num_q_heads = G * num_kv_heads with G in {1, 2, 4, 8};
+ * page_size in {16, 32}; hash_bits in {128, 256}; max_seq_len a multiple of 4 * page_size with
+ * max_seq_len / page_size <= HHR_MAX_PAGES; kv_dtype and q_dtype in {HHR_F32, HHR_BF16}. */
+typedef struct {
+  int32_t batch;
+  int32_t num_q_heads;
+  int32_t num_kv_heads;
+  int32_t head_dim;
+  int32_t page_size;
+  int32_t hash_bits;
+  int32_t max_seq_len;
+  int32_t kv_dtype;     /* hhr_dtype of K and V (and k_new, v_new) */
+  int32_t q_dtype;      /* hhr_dtype of q */
+} hhr_dims;
+
+#define HHR_MAX_PAGES 16384
+
+/* Budgets of one decode step.
+ * page_keep_ratio rho in (0, 1]: a sequence with L tokens has P = ceil(L / page_size) pages and
+ *   keeps n_keep = min(P, max(1, ceil(rho * P))) of them, rho * P being one IEEE double multiply
+ *   (the threshold c_h of §3.3.1, read as "keep the n_keep largest bounds"; the paper's default
+ *   candidate budget is 30 %, Appendix A). Ties in U go to the lower page index.
+ * token_budget k >= 1: the min(k, #candidates) candidates of smallest (Hamming distance,
+ *   token position) are attended to (§3.3.2; the paper's default is 1.5 % of the context).
+ * softmax_scale: logits are scale * q.k; a value <= 0 selects 1/sqrt(128) rounded to fp32. */
+typedef struct {
+  double page_keep_ratio;
+  int32_t token_budget;
+  float softmax_scale;
+} hhr_params;
+
+/* The KV cache and its derived index (page extrema and key codes). All device pointers.
+ * append_ticket is a [B] int32 array that must be zero when the cache is created; every call
+ * leaves it zero again. */
+typedef struct {
+  void* K;
+  void* V;
+  float* page_min;
+  float* page_max;
+  uint32_t* codes;
+  int32_t* seq_lens;
+  int32_t* append_ticket;
+} hhr_cache;
+
+/* Optional intermediate outputs of hhr_decode, for testing. Every pointer may be NULL.
+ *   q_rot       [B][Hq][128]        fp32  q~ = q R_g (Eq. 4)
+ *   q_code      [B][Hq][nw]         query code (Eq. 1 / Eq. 10)
+ *   bounds      [B][Hq][Pmax]       U of every page p < P_b (Eq. 3); other entries untouched
+ *   page_ids    [B][Hq][Pmax]       the kept pages, ascending, in the first n_keep entries
+ *   page_count  [B][Hq]             n_keep
+ *   dist        [B][Hq][max_seq_len] Hamming distance of candidate slot i, i.e. of token
+ *                                   page_ids[i / S] * S + i % S, for i < n_keep * S; 0xFFFF
+ *                                   for a slot past the end of the sequence
+ *   token_idx   [B][Hq][k]          the selected token positions, ascending
+ *   token_count [B][Hq]             how many were selected */
+typedef struct {
+  float* q_rot;
+  uint32_t* q_code;
+  float* bounds;
+  int32_t* page_ids;
+  int32_t* page_count;
+  uint16_t* dist;
+  int32_t* token_idx;
+  int32_t* token_count;
+} hhr_debug;
+
+/* Index build (prefill; §3.3.1 paging and page extrema, §3.3.2 key codes).
+ * For every sequence b and KV head g, over tokens t < seq_lens[b] of K: computes k~ = k R_g,
+ * writes page_min / page_max of every page p < ceil(seq_lens[b] / page_size) (a partial last
+ * page covers only its valid tokens) and the code of every token t < seq_lens[b]. Entries past
+ * the end are left untouched, and so are V and seq_lens. Sets append_ticket to zero.
+ * bf16 keys go through matrix-core (MFMA) GEMMs of K against [R_g | W_g]; fp32 keys through
+ * the fp64 vector path of hhr_build_pages_fp64. Codes are exact in both (see `codes` above);
+ * page extrema are within a few fp32 ulps of the correctly rounded rotated keys. */
+hhr_status hhr_build_pages(const hhr_dims* dims, const hhr_cache* cache, const float* R,
+                           const float* W, hhr_stream_t stream);
+
+/* The same index build on the fp64 vector units for any kv_dtype: rotated keys are the fp64
+ * dot products rounded once to fp32; codes are certified from fp64 sums of exact products and
+ * recomputed exactly where the fp64 sum is too close to zero. */
+hhr_status hhr_build_pages_fp64(const hhr_dims* dims, const hhr_cache* cache, const float* R,
+                                const float* W, hhr_stream_t stream);
+
+/* Append one token per (sequence, KV head). k_new, v_new: [B][Hkv][128] in kv_dtype.
+ * For each b with t = seq_lens[b] < max_seq_len: writes K[b][g][t] and V[b][g][t]; folds
+ * k~ = k R_g into page t / page_size (a new page when t % page_size == 0: min = max = k~);
+ * writes the code of k; then sets seq_lens[b] = t + 1. A sequence already at max_seq_len is
+ * left unchanged. The index maintenance an appended token needs is implied by the paper (every
+ * key has a page summary and a code), which does not describe it. */
+hhr_status hhr_append(const hhr_dims* dims, const hhr_cache* cache, const void* k_new,
+                      const void* v_new, const float* R, const float* W, hhr_stream_t stream);
+
+/* Bytes of workspace hhr_decode needs for these shapes and budgets (0 if they are invalid). */
+size_t hhr_decode_workspace_bytes(const hhr_dims* dims, const hhr_params* params);
+
+/* One decode step (both stages and the attention) for every (b, h), over the seq_lens[b]
+ * tokens of the cache. ws: device workspace of at least hhr_decode_workspace_bytes bytes,
+ * 256-byte aligned, caller-owned, needing no initialisation; it must not be shared by calls
+ * that may run concurrently. out: [B][Hq][128] fp32. dbg: NULL or optional side outputs.
+ * A sequence with no tokens gets a zero output. */
+hhr_status hhr_decode(const hhr_dims* dims, const hhr_params* params, const hhr_cache* cache,
+                      const void* q, const float* R, const float* W, void* ws, size_t ws_bytes,
+                      float* out, const hhr_debug* dbg, hhr_stream_t stream);
+
+/* Static text for a status code. */
+const char* hhr_status_string(hhr_status status);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HHR_H */

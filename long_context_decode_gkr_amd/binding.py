@@ -1,0 +1,211 @@
+"""ctypes binding of libhhr.so (the C ABI in include/hhr.h).
+
+Only argument marshalling lives here: every step of the method runs in the library's HIP
+kernels. PyTorch supplies device memory and the stream. Loading fails loudly when the library
+has not been built (`python -m long_context_decode_gkr_amd.build`).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+from typing import Optional
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libhhr.so")
+
+HHR_F32, HHR_BF16 = 0, 1
+HHR_MAX_PAGES = 16384
+STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or type",
+          3: "size exceeds a documented maximum", 4: "workspace too small or misaligned",
+          5: "HIP launch or runtime error"}
+
+# Every exported symbol of include/hhr.h.
+EXPORTS = ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode_workspace_bytes",
+           "hhr_decode", "hhr_status_string")
+
+
+class Dims(ctypes.Structure):
+    _fields_ = [("batch", ctypes.c_int32), ("num_q_heads", ctypes.c_int32),
+                ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
+                ("page_size", ctypes.c_int32), ("hash_bits", ctypes.c_int32),
+                ("max_seq_len", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
+                ("q_dtype", ctypes.c_int32)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [("page_keep_ratio", ctypes.c_double), ("token_budget", ctypes.c_int32),
+                ("softmax_scale", ctypes.c_float)]
+
+
+class CacheStruct(ctypes.Structure):
+    _fields_ = [("K", ctypes.c_void_p), ("V", ctypes.c_void_p), ("page_min", ctypes.c_void_p),
+                ("page_max", ctypes.c_void_p), ("codes", ctypes.c_void_p),
+                ("seq_lens", ctypes.c_void_p), ("append_ticket", ctypes.c_void_p)]
+
+
+class DebugStruct(ctypes.Structure):
+    _fields_ = [("q_rot", ctypes.c_void_p), ("q_code", ctypes.c_void_p),
+                ("bounds", ctypes.c_void_p), ("page_ids", ctypes.c_void_p),
+                ("page_count", ctypes.c_void_p), ("dist", ctypes.c_void_p),
+                ("token_idx", ctypes.c_void_p), ("token_count", ctypes.c_void_p)]
+
+
+class HHRError(RuntimeError):
+    def __init__(self, fn: str, status: int):
+        super().__init__(f"{fn} returned {status} ({STATUS.get(status, 'unknown')})")
+        self.status = status
+
+
+_lib: Optional[ctypes.CDLL] = None
+
+
+def load() -> ctypes.CDLL:
+    """Load libhhr.so; raises if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError(f"{LIB_PATH} is missing: build it with "
+                           "`python -m long_context_decode_gkr_amd.build`")
+    lib = ctypes.CDLL(LIB_PATH)
+    P = ctypes.POINTER
+    vp = ctypes.c_void_p
+    lib.hhr_build_pages.argtypes = [P(Dims), P(CacheStruct), vp, vp, vp]
+    lib.hhr_build_pages_fp64.argtypes = [P(Dims), P(CacheStruct), vp, vp, vp]
+    lib.hhr_append.argtypes = [P(Dims), P(CacheStruct), vp, vp, vp, vp, vp]
+    lib.hhr_decode_workspace_bytes.argtypes = [P(Dims), P(Params)]
+    lib.hhr_decode_workspace_bytes.restype = ctypes.c_size_t
+    lib.hhr_decode.argtypes = [P(Dims), P(Params), P(CacheStruct), vp, vp, vp, vp, ctypes.c_size_t,
+                               vp, P(DebugStruct), vp]
+    lib.hhr_status_string.argtypes = [ctypes.c_int]
+    lib.hhr_status_string.restype = ctypes.c_char_p
+    for fn in ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode"):
+        getattr(lib, fn).restype = ctypes.c_int
+    _lib = lib
+    return lib
+
+
+def _check(fn: str, status: int) -> None:
+    if status != 0:
+        raise HHRError(fn, status)
+
+
+# ---- raw entry points (pointers as ints; None = NULL) -----------------------------------------
+def hhr_build_pages(dims: Dims, cache: CacheStruct, R: int, W: int, stream: int = 0,
+                    method: str = "auto") -> None:
+    fn = "hhr_build_pages" if method == "auto" else "hhr_build_pages_fp64"
+    _check(fn, getattr(load(), fn)(ctypes.byref(dims), ctypes.byref(cache), R, W, stream))
+
+
+def hhr_append(dims: Dims, cache: CacheStruct, k_new: int, v_new: int, R: int, W: int,
+               stream: int = 0) -> None:
+    _check("hhr_append", load().hhr_append(ctypes.byref(dims), ctypes.byref(cache), k_new, v_new,
+                                           R, W, stream))
+
+
+def hhr_decode_workspace_bytes(dims: Dims, params: Params) -> int:
+    return int(load().hhr_decode_workspace_bytes(ctypes.byref(dims), ctypes.byref(params)))
+
+
+def hhr_decode(dims: Dims, params: Params, cache: CacheStruct, q: int, R: int, W: int, ws: int,
+               ws_bytes: int, out: int, dbg: Optional[DebugStruct] = None, stream: int = 0) -> None:
+    _check("hhr_decode", load().hhr_decode(
+        ctypes.byref(dims), ctypes.byref(params), ctypes.byref(cache), q, R, W, ws, ws_bytes, out,
+        ctypes.byref(dbg) if dbg is not None else None, stream))
+
+
+def hhr_status_string(status: int) -> str:
+    return load().hhr_status_string(status).decode()
+
+
+# ---- torch-owned buffers ----------------------------------------------------------------------
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def make_dims(batch, num_q_heads, num_kv_heads, page_size, hash_bits, max_seq_len,
+              kv_dtype=HHR_BF16, q_dtype=None, head_dim=128) -> Dims:
+    return Dims(batch, num_q_heads, num_kv_heads, head_dim, page_size, hash_bits, max_seq_len,
+                kv_dtype, kv_dtype if q_dtype is None else q_dtype)
+
+
+class Cache:
+    """Device buffers of one layer's KV cache and its index, allocated through torch."""
+
+    def __init__(self, dims: Dims, device="cuda"):
+        import torch
+        self.dims = dims
+        B, Hkv, L, d = dims.batch, dims.num_kv_heads, dims.max_seq_len, dims.head_dim
+        P = L // dims.page_size
+        kvt = torch.bfloat16 if dims.kv_dtype == HHR_BF16 else torch.float32
+        self.K = torch.zeros((B, Hkv, L, d), dtype=kvt, device=device)
+        self.V = torch.zeros((B, Hkv, L, d), dtype=kvt, device=device)
+        self.page_min = torch.zeros((B, Hkv, d, P), dtype=torch.float32, device=device)
+        self.page_max = torch.zeros((B, Hkv, d, P), dtype=torch.float32, device=device)
+        self.codes = torch.zeros((B, Hkv, L, dims.hash_bits // 32), dtype=torch.int32, device=device)
+        self.seq_lens = torch.zeros((B,), dtype=torch.int32, device=device)
+        self.append_ticket = torch.zeros((B,), dtype=torch.int32, device=device)
+
+    def struct(self) -> CacheStruct:
+        return CacheStruct(_ptr(self.K), _ptr(self.V), _ptr(self.page_min), _ptr(self.page_max),
+                           _ptr(self.codes), _ptr(self.seq_lens), _ptr(self.append_ticket))
+
+
+class Debug:
+    """Optional side outputs of hhr_decode (all allocated)."""
+
+    def __init__(self, dims: Dims, token_budget: int, device="cuda"):
+        import torch
+        B, H, d = dims.batch, dims.num_q_heads, dims.head_dim
+        P = dims.max_seq_len // dims.page_size
+        k = min(token_budget, dims.max_seq_len)
+        i32 = torch.int32
+        self.q_rot = torch.zeros((B, H, d), dtype=torch.float32, device=device)
+        self.q_code = torch.zeros((B, H, dims.hash_bits // 32), dtype=i32, device=device)
+        self.bounds = torch.zeros((B, H, P), dtype=torch.float32, device=device)
+        self.page_ids = torch.full((B, H, P), -1, dtype=i32, device=device)
+        self.page_count = torch.zeros((B, H), dtype=i32, device=device)
+        self.dist = torch.zeros((B, H, dims.max_seq_len), dtype=torch.int16, device=device)
+        self.token_idx = torch.full((B, H, k), -1, dtype=i32, device=device)
+        self.token_count = torch.zeros((B, H), dtype=i32, device=device)
+
+    def struct(self) -> DebugStruct:
+        return DebugStruct(_ptr(self.q_rot), _ptr(self.q_code), _ptr(self.bounds),
+                           _ptr(self.page_ids), _ptr(self.page_count), _ptr(self.dist),
+                           _ptr(self.token_idx), _ptr(self.token_count))
+
+
+def current_stream() -> int:
+    import torch
+    return torch.cuda.current_stream().cuda_stream
+
+
+class Decoder:
+    """Holds the workspace for hhr_decode at fixed shapes and budgets."""
+
+    def __init__(self, dims: Dims, keep_ratio: float, token_budget: int, softmax_scale: float = 0.0,
+                 device="cuda"):
+        import torch
+        self.dims = dims
+        self.params = Params(keep_ratio, token_budget, softmax_scale)
+        self.ws_bytes = hhr_decode_workspace_bytes(dims, self.params)
+        if self.ws_bytes == 0:
+            raise HHRError("hhr_decode_workspace_bytes", 1)
+        self.ws = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=device)
+
+    def __call__(self, cache: Cache, q, R, W, out, dbg: Optional[Debug] = None,
+                 stream: Optional[int] = None) -> None:
+        hhr_decode(self.dims, self.params, cache.struct(), _ptr(q), _ptr(R), _ptr(W),
+                   _ptr(self.ws), self.ws_bytes, _ptr(out),
+                   dbg.struct() if dbg is not None else None,
+                   current_stream() if stream is None else stream)
+
+
+def build_pages(cache: Cache, R, W, method: str = "auto", stream: Optional[int] = None) -> None:
+    hhr_build_pages(cache.dims, cache.struct(), _ptr(R), _ptr(W),
+                    current_stream() if stream is None else stream, method)
+
+
+def append(cache: Cache, k_new, v_new, R, W, stream: Optional[int] = None) -> None:
+    hhr_append(cache.dims, cache.struct(), _ptr(k_new), _ptr(v_new), _ptr(R), _ptr(W),
+               current_stream() if stream is None else stream)

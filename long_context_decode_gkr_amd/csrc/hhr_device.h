@@ -1,0 +1,141 @@
+// Device-side helpers shared by the HHR kernels (gfx950, wave64).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hhr {
+
+constexpr int kD = 128;         // head dimension
+constexpr int kWave = 64;
+
+// ---------------------------------------------------------------------------------------------
+// Element loads: K, V, q are fp32 or bf16; everything is computed in fp32 / fp64.
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+__device__ __forceinline__ float load_elem(const void* base, size_t i, int is_bf16) {
+  if (is_bf16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
+  return reinterpret_cast<const float*>(base)[i];
+}
+
+// ---------------------------------------------------------------------------------------------
+// Exact sign of a dot product of finite fp32 values (the code bit of §3.1 Eq. 1 is defined on
+// the exact real value of z = x . w).
+//
+// Every finite fp32 value is m * 2^(e - 150) with an integer m < 2^24 and e in [1, 254]
+// (subnormals: e = 1). A product is then a 48-bit integer times 2^(ea + eb - 300), i.e. the
+// integer placed at bit ea + eb - 2 >= 0 of a fixed-point number whose unit is 2^-298. The
+// accumulator keeps that number in 18 signed 64-bit limbs of 32 bits each (576 bits, enough
+// for 128 products of at most 2^555 plus a sign); carries are resolved once at the end.
+// ---------------------------------------------------------------------------------------------
+struct LongAcc {
+  int64_t limb[18];
+  __device__ __forceinline__ void clear() {
+#pragma unroll
+    for (int i = 0; i < 18; ++i) limb[i] = 0;
+  }
+  __device__ __forceinline__ void add_product(float a, float b) {
+    uint32_t ua = __float_as_uint(a), ub = __float_as_uint(b);
+    uint32_t ea = (ua >> 23) & 0xFFu, eb = (ub >> 23) & 0xFFu;
+    uint64_t ma = ua & 0x7FFFFFu, mb = ub & 0x7FFFFFu;
+    if (ea) ma |= 0x800000u; else ea = 1;
+    if (eb) mb |= 0x800000u; else eb = 1;
+    uint64_t m = ma * mb;
+    if (m == 0) return;
+    int sh = int(ea + eb) - 2;
+    int li = sh >> 5, bs = sh & 31;
+    uint64_t t0 = (m & 0xFFFFFFFFull) << bs;
+    uint64_t t1 = (m >> 32) << bs;
+    int64_t c0 = int64_t(t0 & 0xFFFFFFFFull);
+    int64_t c1 = int64_t((t0 >> 32) + (t1 & 0xFFFFFFFFull));
+    int64_t c2 = int64_t(t1 >> 32);
+    if ((ua ^ ub) >> 31) { c0 = -c0; c1 = -c1; c2 = -c2; }
+    limb[li] += c0;
+    limb[li + 1] += c1;
+    limb[li + 2] += c2;
+  }
+  // +1, 0 or -1.
+  __device__ __forceinline__ int sign() {
+    for (int i = 0; i < 17; ++i) {
+      int64_t carry = limb[i] >> 32;  // floor division by 2^32
+      limb[i] -= carry * 4294967296ll;
+      limb[i + 1] += carry;
+    }
+    if (limb[17] > 0) return 1;
+    if (limb[17] < 0) return -1;
+    for (int i = 16; i >= 0; --i)
+      if (limb[i] != 0) return 1;
+    return 0;
+  }
+};
+
+// Certainty test for a code bit from an fp64 sum z of exact products and the fp64 sum s of
+// their magnitudes (n <= 128 terms, any summation order): |z - exact| <= gamma_n * sum|p|, so
+// the sign of z is the exact sign when |z| > 4 * 128 * 2^-53 * s (the factor also covers the
+// rounding of s). Returns 1 or 0 when certain, -1 when the exact path must decide.
+__device__ __forceinline__ int certain_bit(double z, double s) {
+  const double tau = s * (double(kD) * 0x1p-51);
+  if (z > tau) return 1;
+  if (z < -tau || s == 0.0) return 0;
+  return -1;
+}
+
+// Exact code bit [sum_j x[j] * w[j * w_stride] > 0] (j < 128); x: fp32 values through any
+// indexable accessor, w: fp32 in global memory.
+template <typename XPtr>
+__device__ __noinline__ uint32_t exact_bit(XPtr xs, const float* __restrict__ w, int w_stride) {
+  LongAcc acc;
+  acc.clear();
+  for (int j = 0; j < kD; ++j) acc.add_product(float(xs[j]), w[size_t(j) * w_stride]);
+  return acc.sign() > 0 ? 1u : 0u;
+}
+
+// Code bit of z = x . w computed in fp64 (exact products), certified, exact where needed.
+template <typename XPtr>
+__device__ __forceinline__ uint32_t certified_bit(XPtr xs, const float* __restrict__ w,
+                                                  int w_stride) {
+  double z = 0.0, s = 0.0;
+#pragma unroll 8
+  for (int j = 0; j < kD; ++j) {
+    double p = double(xs[j]) * double(w[size_t(j) * w_stride]);
+    z += p;
+    s += fabs(p);
+  }
+  int c = certain_bit(z, s);
+  if (c >= 0) return uint32_t(c);
+  return exact_bit(xs, w, w_stride);
+}
+
+// Strided view of fp32 values (e.g. one column of a transposed tile in LDS).
+struct Strided {
+  const float* p;
+  int stride;
+  __device__ __forceinline__ float operator[](int j) const { return p[j * stride]; }
+};
+
+// ---------------------------------------------------------------------------------------------
+// Wave-level helpers
+// ---------------------------------------------------------------------------------------------
+__device__ __forceinline__ int lane_id() { return __lane_id(); }
+__device__ __forceinline__ int wave_id() {
+  return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
+}
+
+// Number of set bits of `mask` in lanes below this one.
+__device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
+  return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+
+}  // namespace hhr

@@ -1,0 +1,58 @@
+// Internal launch interface between the C-ABI host layer and the kernel translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+namespace hhr {
+
+struct Shape {
+  int B, Hq, Hkv, G, S, NB, NW, Lmax, Pmax;
+  int kv_bf16, q_bf16;
+};
+
+struct CacheView {
+  void* K;
+  void* V;
+  float* pmin;
+  float* pmax;
+  uint32_t* codes;
+  int32_t* seq_lens;
+  int32_t* ticket;
+};
+
+struct DebugView {
+  float* q_rot;
+  uint32_t* q_code;
+  float* bounds;
+  int32_t* page_ids;
+  int32_t* page_count;
+  uint16_t* dist;
+  int32_t* token_idx;
+  int32_t* token_count;
+};
+
+// Workspace carve-up of one decode call (byte offsets from the workspace base).
+struct DecodePlan {
+  int kcap;        // token budget clamped to max_seq_len
+  int chunk;       // tokens per attention workgroup
+  int nsplit;      // attention workgroups per (b, h)
+  double rho;
+  float scale;
+  size_t off_U, off_idx, off_cnt, off_ticket, off_part, total;
+};
+
+DecodePlan plan_decode(const Shape& s, double rho, int k, float scale);
+
+hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R, const float* W,
+                             hipStream_t st);
+hipError_t launch_build_mfma(const Shape& s, const CacheView& c, const float* R, const float* W,
+                             hipStream_t st);
+hipError_t launch_append(const Shape& s, const CacheView& c, const void* k_new,
+                         const void* v_new, const float* R, const float* W, hipStream_t st);
+hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c, const void* q,
+                         const float* R, const float* W, void* ws, float* out,
+                         const DebugView& dbg, hipStream_t st);
+
+}  // namespace hhr

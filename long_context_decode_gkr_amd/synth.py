@@ -146,7 +146,7 @@ def make_layer(cfg: Config, max_seq_len: Optional[int] = None, layer: int = 0,
     lens = list(lens) if lens is not None else _lengths(cfg)
     S = cfg.page_size
     Lmax = max_seq_len or max(lens)
-    Lmax = -(-Lmax // S) * S
+    Lmax = -(-Lmax // (4 * S)) * (4 * S)   # capacity in whole groups of four pages
     assert max(lens) <= Lmax
     K = np.zeros((B, Hkv, Lmax, d), np.float32)
     V = np.zeros((B, Hkv, Lmax, d), np.float32)

@@ -1,0 +1,115 @@
+"""The C-ABI library on the CPU: it loads, exports every symbol the header declares, and rejects
+invalid calls with the documented status before touching the device. No kernel is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+from long_context_decode_gkr_amd import binding as hb
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hhr.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(hb.LIB_PATH), reason="libhhr.so not built")
+
+FAKE = 0x1000  # never dereferenced: every call below fails validation first
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:hhr_status|size_t|const char\*)\s+(hhr_\w+)\s*\(", text,
+                                 re.M)))
+
+
+def test_library_exports_every_declared_symbol():
+    lib = hb.load()
+    names = declared_functions()
+    assert set(names) == set(hb.EXPORTS)
+    for n in names:
+        assert hasattr(lib, n), n
+
+
+def test_status_strings():
+    for code, text in hb.STATUS.items():
+        assert hb.hhr_status_string(code) == text
+
+
+def good_dims(**kw):
+    d = dict(batch=1, num_q_heads=32, num_kv_heads=8, page_size=16, hash_bits=128,
+             max_seq_len=4096, kv_dtype=hb.HHR_BF16)
+    d.update(kw)
+    return hb.make_dims(**d)
+
+
+def fake_cache(**kw):
+    c = hb.CacheStruct(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE)
+    for k, v in kw.items():
+        setattr(c, k, v)
+    return c
+
+
+def decode_status(dims=None, params=None, cache=None, ws=FAKE * 256, ws_bytes=1 << 40, q=FAKE,
+                  out=FAKE):
+    lib = hb.load()
+    dims = dims or good_dims()
+    params = params or hb.Params(0.125, 2048, 0.0)
+    cache = cache or fake_cache()
+    return lib.hhr_decode(ctypes.byref(dims), ctypes.byref(params), ctypes.byref(cache), q, FAKE,
+                          FAKE, ws, ws_bytes, out, None, None)
+
+
+@pytest.mark.parametrize("field,value,status", [
+    ("head_dim", 64, 2), ("page_size", 8, 2), ("hash_bits", 64, 2), ("num_q_heads", 12, 1),
+    ("num_q_heads", 48, 2), ("batch", 0, 1), ("max_seq_len", 4104, 2), ("kv_dtype", 7, 1),
+    ("q_dtype", -1, 1), ("max_seq_len", 16 * 16384 + 64, 3), ("max_seq_len", -64, 1),
+])
+def test_invalid_dims(field, value, status):
+    d = good_dims()
+    setattr(d, field, value)
+    assert decode_status(dims=d) == status
+    lib = hb.load()
+    assert lib.hhr_build_pages(ctypes.byref(d), ctypes.byref(fake_cache()), FAKE, FAKE, None) == status
+    assert lib.hhr_append(ctypes.byref(d), ctypes.byref(fake_cache()), FAKE, FAKE, FAKE, FAKE, None) == status
+
+
+@pytest.mark.parametrize("rho,k,scale", [(0.0, 10, 0.0), (1.5, 10, 0.0), (float("nan"), 10, 0.0),
+                                         (0.5, 0, 0.0), (0.5, -3, 0.0), (0.5, 4, float("inf"))])
+def test_invalid_params(rho, k, scale):
+    assert decode_status(params=hb.Params(rho, k, scale)) == 1
+    assert hb.hhr_decode_workspace_bytes(good_dims(), hb.Params(rho, k, scale)) == 0
+
+
+@pytest.mark.parametrize("field", ["K", "V", "page_min", "page_max", "codes", "seq_lens"])
+def test_null_cache_pointer(field):
+    assert decode_status(cache=fake_cache(**{field: None})) == 1
+
+
+def test_null_ticket_only_matters_for_append():
+    lib = hb.load()
+    c = fake_cache(append_ticket=None)
+    d = good_dims()
+    assert lib.hhr_append(ctypes.byref(d), ctypes.byref(c), FAKE, FAKE, FAKE, FAKE, None) == 1
+
+
+def test_null_io_pointers():
+    assert decode_status(q=None) == 1
+    assert decode_status(out=None) == 1
+
+
+def test_workspace_checks():
+    need = hb.hhr_decode_workspace_bytes(good_dims(), hb.Params(0.125, 2048, 0.0))
+    assert need > 0
+    assert decode_status(ws_bytes=need - 1) == 4
+    assert decode_status(ws=FAKE * 256 + 64, ws_bytes=need) == 4
+    assert decode_status(ws=None, ws_bytes=need) == 4
+
+
+def test_workspace_size_grows_with_shapes():
+    p = hb.Params(0.125, 2048, 0.0)
+    a = hb.hhr_decode_workspace_bytes(good_dims(max_seq_len=4096), p)
+    b = hb.hhr_decode_workspace_bytes(good_dims(max_seq_len=131072), p)
+    c = hb.hhr_decode_workspace_bytes(good_dims(batch=4, max_seq_len=131072), p)
+    assert 0 < a < b < c
+    # U + indices + counters + split partials: at least the bounds and the token indices
+    assert b >= 32 * (131072 // 16) * 4 + 32 * 2048 * 4

@@ -1,0 +1,189 @@
+"""GPU parity: the HIP library (through its C ABI) against the CPU oracle on seeded inputs.
+
+Sizes span several kernel tiles and a ragged tail while the oracle still finishes in seconds;
+the full-size workloads are checked on sampled heads in test_gpu_fullsize.py.
+"""
+import numpy as np
+import pytest
+
+from long_context_decode_gkr_amd import binding as hb
+from long_context_decode_gkr_amd import synth
+from oracle import hhr_oracle as orc
+
+import hhr_case as hc
+
+pytestmark = pytest.mark.gpu
+
+
+def _torch():
+    import torch
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    return torch
+
+
+def _cfg(i, L, **kw):
+    return synth.CONFIGS[i].scaled(seq_len=L, **kw)
+
+
+# ---------------------------------------------------------------------------------------------
+# Index build (fp64 vector path): codes bit-exact, extrema within a few ulps
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg_id,L,batch", [(1, 4096, None), (1, 1000, None), (2, 3001, None),
+                                            (5, 2085, 2)])
+def test_build_fp64_matches_oracle(cfg_id, L, batch):
+    _torch()
+    cfg = _cfg(cfg_id, L, batch=batch, n_plant=8)
+    lay = hc.GpuLayer(cfg, max_seq_len=L + 4 * cfg.page_size * 2)
+    lay.build(method="fp64")
+    hc.check_index(lay, hc.oracle_index(lay))
+
+
+# ---------------------------------------------------------------------------------------------
+# Decode step per workload shape (scaled-down contexts)
+# ---------------------------------------------------------------------------------------------
+DECODE_CASES = [
+    # cfg, L, batch, lens, rho, k
+    (1, 4096, None, None, 0.25, 256),        # workload 1 at full size
+    (1, 1111, None, None, 0.25, 100),        # ragged tail, G = 1, fp32
+    (2, 5003, None, None, 1 / 8, 300),       # Llama shape, bf16, ragged
+    (3, 8192, None, None, 1 / 16, 256),      # 128K-workload budgets at 8K
+    (4, 6000, 3, [5000, 6000, 2001], 0.30, 200),   # varlen batch
+    (5, 4096, 2, None, 1 / 8, 257),          # page 32, 256-bit codes, lognormal keys
+]
+
+
+@pytest.mark.parametrize("cfg_id,L,batch,lens,rho,k", DECODE_CASES)
+def test_decode_matches_oracle(cfg_id, L, batch, lens, rho, k):
+    _torch()
+    cfg = _cfg(cfg_id, L, batch=batch, lens=lens, n_plant=16)
+    lay = hc.GpuLayer(cfg, max_seq_len=L + 64)
+    lay.build(method="fp64")
+    ref = hc.oracle_index(lay)
+    hc.check_index(lay, ref)
+    out, dbg = lay.decode(rho, k)
+    st = hc.check_decode(lay, out, dbg, rho, k, ref_index=ref)
+    print(f"cfg{cfg_id} L={L}: max out rel err {st['max_out_rel']:.2e}, page swaps {st['swaps']}")
+
+
+def test_decode_full_budget_is_dense_attention():
+    torch = _torch()
+    cfg = _cfg(2, 777, n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=1024)
+    lay.build(method="fp64")
+    out, dbg = lay.decode(1.0, 777)
+    assert np.all(dbg.token_count.cpu().numpy() == 777)
+    d = lay.data
+    for h in (0, 13, 31):
+        g = h // cfg.group
+        qt = torch.tensor(d["q"][0, h], dtype=torch.float64)[None, None, None]
+        kt = torch.tensor(d["K"][0, g, :777], dtype=torch.float64)[None, None]
+        vt = torch.tensor(d["V"][0, g, :777], dtype=torch.float64)[None, None]
+        dense = torch.nn.functional.scaled_dot_product_attention(
+            qt, kt, vt, scale=orc.default_scale(128))[0, 0, 0].numpy()
+        rel = np.abs(out[0, h].cpu().numpy() - dense).max() / np.abs(dense).max()
+        assert rel <= hc.OUT_RTOL
+
+
+@pytest.mark.parametrize("k", [1, 5000])
+def test_decode_budget_extremes(k):
+    _torch()
+    cfg = _cfg(2, 2048 + 7, n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=2048 + 64)
+    lay.build(method="fp64")
+    out, dbg = lay.decode(0.2, k)
+    hc.check_decode(lay, out, dbg, 0.2, k)
+
+
+def test_decode_short_and_empty_sequences():
+    _torch()
+    cfg = _cfg(4, 64, batch=4, lens=[0, 1, 15, 17], n_plant=0)
+    lay = hc.GpuLayer(cfg, max_seq_len=64)
+    lay.build(method="fp64")
+    out, dbg = lay.decode(0.3, 8)
+    hc.check_decode(lay, out, dbg, 0.3, 8)
+    assert np.all(out[0].cpu().numpy() == 0.0)
+
+
+def test_decode_many_candidates_recompute_path():
+    # more than 32768 candidate slots: distances are recomputed instead of cached in LDS
+    _torch()
+    cfg = _cfg(1, 40000, n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=40064)
+    lay.build(method="fp64")
+    heads = [(0, 0)]
+    out, dbg = lay.decode(1.0, 3000)
+    hc.check_decode(lay, out, dbg, 1.0, 3000, heads=heads)
+
+
+def test_decode_ties_all_bounds_equal():
+    # identical keys: every page bound and every distance ties; lower indices must win
+    torch = _torch()
+    cfg = _cfg(2, 1024, n_plant=0)
+    data = synth.make_layer(cfg)
+    data["K"][:, :, :1024] = data["K"][:, :, :1][:, :, :1]
+    lay = hc.GpuLayer(cfg, data=data)
+    lay.build(method="fp64")
+    out, dbg = lay.decode(0.25, 50)
+    hc.check_decode(lay, out, dbg, 0.25, 50)
+    pid = dbg.page_ids.cpu().numpy()[0, 0, :16]
+    assert pid.tolist() == list(range(16))
+    assert dbg.token_idx.cpu().numpy()[0, 0].tolist() == list(range(50))
+    del torch
+
+
+def test_decode_is_deterministic():
+    torch = _torch()
+    cfg = _cfg(2, 6000, n_plant=16)
+    lay = hc.GpuLayer(cfg, max_seq_len=6016)
+    lay.build(method="fp64")
+    o1, d1 = lay.decode(0.125, 512)
+    o2, d2 = lay.decode(0.125, 512)
+    assert torch.equal(o1, o2)
+    assert torch.equal(d1.token_idx, d2.token_idx) and torch.equal(d1.bounds, d2.bounds)
+
+
+# ---------------------------------------------------------------------------------------------
+# Append: one token per step; equals a rebuild; decode sees the new token
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("cfg_id", [1, 3, 5])
+def test_append_matches_oracle_and_rebuild(cfg_id):
+    torch = _torch()
+    base = synth.CONFIGS[cfg_id]
+    S = base.page_size
+    L0, n = 3 * S - 5, 2 * S + 9          # crosses two page boundaries
+    cfg = base.scaled(seq_len=L0, batch=min(base.batch, 2), n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=L0 + n + 4 * S)
+    lay.build(method="fp64")
+    kn, vn = synth.append_tokens(cfg, n)
+    for i in range(n):
+        hb.append(lay.cache, hc.to_dev(kn[i], lay.tdt), hc.to_dev(vn[i], lay.tdt), lay.R, lay.W)
+    torch.cuda.synchronize()
+    lens = lay.cache.seq_lens.cpu().numpy()
+    assert np.all(lens == L0 + n)
+    # oracle: the same appends on the host
+    d = lay.data
+    for b in range(cfg.batch):
+        d["K"][b, :, L0:L0 + n] = kn[:, b].transpose(1, 0, 2)
+        d["V"][b, :, L0:L0 + n] = vn[:, b].transpose(1, 0, 2)
+    d["seq_lens"][:] = L0 + n
+    ref = hc.oracle_index(lay)
+    hc.check_index(lay, ref)
+    np.testing.assert_array_equal(lay.cache.K.float().cpu().numpy(), d["K"])
+    np.testing.assert_array_equal(lay.cache.V.float().cpu().numpy(), d["V"])
+    assert np.all(lay.cache.append_ticket.cpu().numpy() == 0)
+    out, dbg = lay.decode(cfg.keep_ratio, 40)
+    hc.check_decode(lay, out, dbg, cfg.keep_ratio, 40, ref_index=ref)
+
+
+def test_append_at_capacity_is_a_no_op():
+    torch = _torch()
+    cfg = _cfg(2, 64, n_plant=0)
+    lay = hc.GpuLayer(cfg, max_seq_len=64)
+    lay.build(method="fp64")
+    before = lay.cache.codes.clone()
+    kn, vn = synth.append_tokens(cfg, 1)
+    hb.append(lay.cache, hc.to_dev(kn[0], lay.tdt), hc.to_dev(vn[0], lay.tdt), lay.R, lay.W)
+    torch.cuda.synchronize()
+    assert int(lay.cache.seq_lens[0]) == 64
+    assert torch.equal(before, lay.cache.codes)
