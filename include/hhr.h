@@ -52,6 +52,7 @@ extern "C" {
 #endif
 
 typedef struct ihipStream_t* hhr_stream_t; /* the same type as hipStream_t */
+typedef struct ihipEvent_t* hhr_event_t;   /* the same type as hipEvent_t */
 
 typedef enum {
   HHR_OK = 0,
@@ -118,7 +119,10 @@ typedef struct {
  *                                   page_ids[i / S] * S + i % S, for i < n_keep * S; 0xFFFF
  *                                   for a slot past the end of the sequence
  *   token_idx   [B][Hq][k]          the selected token positions, ascending
- *   token_count [B][Hq]             how many were selected */
+ *   token_count [B][Hq]             how many were selected
+ *   kernel_events  NULL or 4 caller-created events, recorded on the stream before the page-bound
+ *                  kernel, between the bound and selection kernels, between the selection and
+ *                  attention kernels, and after the attention kernel (per-kernel timing) */
 typedef struct {
   float* q_rot;
   uint32_t* q_code;
@@ -128,13 +132,14 @@ typedef struct {
   uint16_t* dist;
   int32_t* token_idx;
   int32_t* token_count;
+  hhr_event_t* kernel_events;
 } hhr_debug;
 
 /* Index build (prefill; §3.3.1 paging and page extrema, §3.3.2 key codes).
  * For every sequence b and KV head g, over tokens t < seq_lens[b] of K: computes k~ = k R_g,
  * writes page_min / page_max of every page p < ceil(seq_lens[b] / page_size) (a partial last
  * page covers only its valid tokens) and the code of every token t < seq_lens[b]. Entries past
- * the end are left untouched, and so are V and seq_lens. Sets append_ticket to zero.
+ * the end are left untouched, and so are V, seq_lens and append_ticket.
  * bf16 keys go through matrix-core (MFMA) GEMMs of K against [R_g | W_g]; fp32 keys through
  * the fp64 vector path of hhr_build_pages_fp64. Codes are exact in both (see `codes` above);
  * page extrema are within a few fp32 ulps of the correctly rounded rotated keys. */

@@ -47,7 +47,8 @@ class DebugStruct(ctypes.Structure):
     _fields_ = [("q_rot", ctypes.c_void_p), ("q_code", ctypes.c_void_p),
                 ("bounds", ctypes.c_void_p), ("page_ids", ctypes.c_void_p),
                 ("page_count", ctypes.c_void_p), ("dist", ctypes.c_void_p),
-                ("token_idx", ctypes.c_void_p), ("token_count", ctypes.c_void_p)]
+                ("token_idx", ctypes.c_void_p), ("token_count", ctypes.c_void_p),
+                ("kernel_events", ctypes.c_void_p)]
 
 
 class HHRError(RuntimeError):
@@ -67,6 +68,9 @@ def load() -> ctypes.CDLL:
     if not os.path.exists(LIB_PATH):
         raise RuntimeError(f"{LIB_PATH} is missing: build it with "
                            "`python -m long_context_decode_gkr_amd.build`")
+    # torch first: the library then binds to the HIP runtime torch already loaded (same
+    # SONAME), so device pointers and streams are shared by a single runtime.
+    import torch  # noqa: F401
     lib = ctypes.CDLL(LIB_PATH)
     P = ctypes.POINTER
     vp = ctypes.c_void_p
@@ -172,7 +176,7 @@ class Debug:
     def struct(self) -> DebugStruct:
         return DebugStruct(_ptr(self.q_rot), _ptr(self.q_code), _ptr(self.bounds),
                            _ptr(self.page_ids), _ptr(self.page_count), _ptr(self.dist),
-                           _ptr(self.token_idx), _ptr(self.token_count))
+                           _ptr(self.token_idx), _ptr(self.token_count), None)
 
 
 def current_stream() -> int:
@@ -209,3 +213,41 @@ def build_pages(cache: Cache, R, W, method: str = "auto", stream: Optional[int] 
 def append(cache: Cache, k_new, v_new, R, W, stream: Optional[int] = None) -> None:
     hhr_append(cache.dims, cache.struct(), _ptr(k_new), _ptr(v_new), _ptr(R), _ptr(W),
                current_stream() if stream is None else stream)
+
+
+# ---- raw HIP events (the runtime torch loaded) ------------------------------------------------
+class HipEvents:
+    """A pool of hipEvent_t handles for per-kernel timing on the decode stream."""
+
+    def __init__(self, n: int):
+        import torch  # noqa: F401  (loads the runtime)
+        self.rt = ctypes.CDLL("libamdhip64.so.7")
+        self.rt.hipEventCreate.argtypes = [ctypes.POINTER(ctypes.c_void_p)]
+        self.rt.hipEventRecord.argtypes = [ctypes.c_void_p, ctypes.c_void_p]
+        self.rt.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), ctypes.c_void_p,
+                                                ctypes.c_void_p]
+        self.rt.hipEventDestroy.argtypes = [ctypes.c_void_p]
+        self.handles = (ctypes.c_void_p * n)()
+        for i in range(n):
+            h = ctypes.c_void_p()
+            if self.rt.hipEventCreate(ctypes.byref(h)) != 0:
+                raise RuntimeError("hipEventCreate failed")
+            self.handles[i] = h.value
+
+    def address(self, i: int) -> int:
+        """Address of handles[i] (a hipEvent_t* for hhr_debug.kernel_events)."""
+        return ctypes.addressof(self.handles) + i * ctypes.sizeof(ctypes.c_void_p)
+
+    def record(self, i: int, stream: int) -> None:
+        if self.rt.hipEventRecord(self.handles[i], stream) != 0:
+            raise RuntimeError("hipEventRecord failed")
+
+    def elapsed_ms(self, i: int, j: int) -> float:
+        ms = ctypes.c_float()
+        if self.rt.hipEventElapsedTime(ctypes.byref(ms), self.handles[i], self.handles[j]) != 0:
+            raise RuntimeError("hipEventElapsedTime failed")
+        return ms.value
+
+    def close(self) -> None:
+        for h in self.handles:
+            self.rt.hipEventDestroy(h)

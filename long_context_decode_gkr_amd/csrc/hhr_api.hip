@@ -129,7 +129,8 @@ hhr_status hhr_decode(const hhr_dims* dims, const hhr_params* params, const hhr_
     return HHR_ERR_WORKSPACE;
   DebugView dv{};
   if (dbg) dv = DebugView{dbg->q_rot, dbg->q_code, dbg->bounds, dbg->page_ids,
-                          dbg->page_count, dbg->dist, dbg->token_idx, dbg->token_count};
+                          dbg->page_count, dbg->dist, dbg->token_idx, dbg->token_count,
+                          reinterpret_cast<hipEvent_t*>(dbg->kernel_events)};
   return hip_status(launch_decode(s, p, c, q, R, W, ws, out, dv,
                                   reinterpret_cast<hipStream_t>(stream)));
 }

@@ -685,20 +685,24 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
   uint32_t* tick = reinterpret_cast<uint32_t*>(base + p.off_ticket);
   float* part = reinterpret_cast<float*>(base + p.off_part);
 
+  hipError_t e = hipSuccess;
+  if (dbg.events && (e = hipEventRecord(dbg.events[0], st)) != hipSuccess) return e;
   switch (s.G) {
     case 1: launch_bound_t<1>(s, c, q, R, U, dbg, st); break;
     case 2: launch_bound_t<2>(s, c, q, R, U, dbg, st); break;
     case 4: launch_bound_t<4>(s, c, q, R, U, dbg, st); break;
     default: launch_bound_t<8>(s, c, q, R, U, dbg, st); break;
   }
-  hipError_t e = hipGetLastError();
+  e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (dbg.events && (e = hipEventRecord(dbg.events[1], st)) != hipSuccess) return e;
 
   SelectArgs sa{U, idx, cnt, tick, p.rho, p.kcap};
   if (s.NB == 128) launch_select_nb<128>(s, c, q, W, sa, dbg, st);
   else launch_select_nb<256>(s, c, q, W, sa, dbg, st);
   e = hipGetLastError();
   if (e != hipSuccess) return e;
+  if (dbg.events && (e = hipEventRecord(dbg.events[2], st)) != hipSuccess) return e;
 
   AttnArgs aa{idx, cnt, part, tick, p.kcap, p.nsplit, p.scale * 1.4426950408889634f};
   dim3 grid(p.nsplit, s.Hq, s.B);
@@ -706,7 +710,10 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
     hipLaunchKernelGGL((attn_kernel<1>), grid, dim3(256), 0, st, s, c.K, c.V, q, aa, out);
   else
     hipLaunchKernelGGL((attn_kernel<0>), grid, dim3(256), 0, st, s, c.K, c.V, q, aa, out);
-  return hipGetLastError();
+  e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (dbg.events) e = hipEventRecord(dbg.events[3], st);
+  return e;
 }
 
 }  // namespace hhr

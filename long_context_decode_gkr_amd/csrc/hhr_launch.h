@@ -31,6 +31,7 @@ struct DebugView {
   uint16_t* dist;
   int32_t* token_idx;
   int32_t* token_count;
+  hipEvent_t* events;  // NULL or 4 events around the three decode kernels
 };
 
 // Workspace carve-up of one decode call (byte offsets from the workspace base).
