@@ -6,11 +6,13 @@ Workload (synthetic, seeded): 32 query heads, 8 KV heads, d = 128, bf16 K/V, bat
 N(0,1) with 4 outlier channels x10 per KV head and 32 planted high-logit keys per query head;
 one new token appended per step (the index is updated), then the decode step runs.
 
-A "step" is hhr_append followed by hhr_decode on one layer. The benchmark cycles over
---layers distinct layer instances (separate K/V, index and sequence state in HBM) so the
-~256 MB Infinity Cache cannot serve a step from the previous visit. Timing: W warm-up steps,
-then exactly K steps bracketed by torch.cuda.synchronize(); per-kernel durations come from HIP
-events recorded on the decode stream inside the timed region.
+A "step" is hhr_append_decode (append one token, then decode) on one layer. The benchmark
+cycles over --layers distinct layer instances (separate K/V, index and sequence state in HBM) so
+the ~256 MB Infinity Cache cannot serve a step from the previous visit. Two passes, each W
+warm-up steps then exactly K timed steps bracketed by torch.cuda.synchronize():
+  1. eager launches with HIP events recorded by the library around each of its five kernels on
+     the decode stream: per-kernel durations, the roofline figure, and eager_us_per_step;
+  2. replay of one captured HIP graph per layer instance: the headline us/step/layer.
 
 Prints ONE JSON line. Options: --gpus (must be 1), --steps, --warmup, --layers,
 --no-cpu-baseline, --quiet.
@@ -30,7 +32,7 @@ sys.path.insert(0, ROOT)
 
 CTX = 131072
 HBM_PEAK_GBS = 8000.0
-KERNELS = ("hhr_append", "page_bound", "select", "sparse_attn")
+KERNELS = ("prep", "page_bound", "select", "sparse_attn", "combine")
 
 
 def log(msg, quiet):
@@ -46,8 +48,10 @@ def algorithmic_bytes(cfg, L):
     select:     U read, the codes of the kept pages' tokens (16 B per candidate and query head),
                 W read, the selected indices written.
     sparse_attn: K and V rows of the selected tokens (2 x 256 B per token and query head),
-                indices read, output written.
-    hhr_append: one K and V row, the page extrema column pair and the code per KV head, R and W.
+                indices and q read, one (o, m, l) partial per 256 tokens written.
+    combine:    the partials read, the output written.
+    prep:       the appended token (one K and V row, the page extrema column pair and the code
+                per KV head), q read, R and W read, q~ and the query codes written.
     """
     d, S, nb = cfg.head_dim, cfg.page_size, cfg.hash_bits
     Hq, Hkv = cfg.num_q_heads, cfg.num_kv_heads
@@ -59,8 +63,11 @@ def algorithmic_bytes(cfg, L):
     return {
         "page_bound": Hkv * P * d * 8 + Hq * P * 4 + Hq * d * esz + Hkv * d * d * 4,
         "select": Hq * P * 4 + Hq * n_keep * S * (nb // 8) + Hkv * d * nb * 4 + Hq * k * 4,
-        "sparse_attn": Hq * k * 2 * d * esz + Hq * k * 4 + Hq * d * (esz + 4),
-        "hhr_append": Hkv * (2 * d * esz + 2 * d * 4 * 2 + nb // 8) + rw,
+        "sparse_attn": Hq * k * 2 * d * esz + Hq * k * 4 + Hq * d * esz
+        + Hq * -(-k // 256) * (d + 2) * 4,
+        "combine": Hq * -(-k // 256) * (d + 2) * 4 + Hq * d * 4,
+        "prep": Hkv * (2 * d * esz + 2 * d * 4 * 2 + nb // 8) + rw + Hq * d * esz
+                + Hq * (d * 4 + nb // 8),
     }
 
 
@@ -158,7 +165,7 @@ def main():
     hb.load()
     cfg = synth.CONFIGS[3]
     NL, K, Wm = args.layers, args.steps, args.warmup
-    visits = -(-(K + Wm) // NL)
+    visits = -(-(2 * (K + Wm)) // NL)     # appends per layer over both passes
     L0 = CTX - visits                      # every layer ends at <= 128K tokens
     log(f"generating the 128K layer (L0={L0})", q)
     t0 = time.time()
@@ -188,46 +195,57 @@ def main():
     vnd = torch.from_numpy(vn).to(dev).to(bf)
     dec = hb.Decoder(dims, cfg.keep_ratio, cfg.token_budget)
     out = torch.empty((1, 32, 128), dtype=torch.float32, device=dev)
-    stream = hb.current_stream()
-
-    ev = hb.HipEvents(5 * K)
-    dbg_structs = []
-    for i in range(K):
-        dbg_structs.append(hb.DebugStruct(None, None, None, None, None, None, None, None,
-                                          ev.address(5 * i + 1)))
     cache_structs = [c.struct() for c in layers]
-    ptrs = dict(q=qd.data_ptr(), R=Rd.data_ptr(), W=Wd.data_ptr(), ws=dec.ws.data_ptr(),
-                out=out.data_ptr())
+    P = dict(q=qd.data_ptr(), R=Rd.data_ptr(), W=Wd.data_ptr(), ws=dec.ws.data_ptr(),
+             out=out.data_ptr())
 
-    def step(i, timed):
+    def step(i, dbg, stream, visit=None):
         li = i % NL
-        v = i // NL
-        if timed:
-            ev.record(5 * (i - Wm), stream)
-        hb.hhr_append(dims, cache_structs[li], knd[v].data_ptr(), vnd[v].data_ptr(), ptrs["R"],
-                      ptrs["W"], stream)
-        hb.hhr_decode(dims, dec.params, cache_structs[li], ptrs["q"], ptrs["R"], ptrs["W"],
-                      ptrs["ws"], dec.ws_bytes, ptrs["out"],
-                      dbg_structs[i - Wm] if timed else None, stream)
+        v = i // NL if visit is None else visit
+        hb.hhr_append_decode(dims, dec.params, cache_structs[li], knd[v].data_ptr(),
+                             vnd[v].data_ptr(), P["q"], P["R"], P["W"], P["ws"], dec.ws_bytes,
+                             P["out"], dbg, stream)
 
-    log(f"warm-up {Wm} steps, timed {K} steps over {NL} layer instances", q)
+    # ---- pass 1 (eager launches): per-kernel durations from HIP events on the decode stream
+    stream = hb.current_stream()
+    NE = len(KERNELS) + 1
+    ev = hb.HipEvents(NE * K)
+    dbgs = [hb.DebugStruct(None, None, None, None, None, None, None, None, ev.address(NE * i))
+            for i in range(K)]
+    log(f"eager pass: warm-up {Wm}, timed {K} steps over {NL} layer instances", q)
     for i in range(Wm):
-        step(i, False)
+        step(i, None, stream)
     torch.cuda.synchronize()
     t_start = time.perf_counter()
-    for i in range(Wm, Wm + K):
-        step(i, True)
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    ms_step = wall * 1e3 / K
-    # per-kernel durations from the events: [5i] before append, [5i+1] before bound,
-    # [5i+2] before select, [5i+3] before attention, [5i+4] after attention
-    per = {n: [] for n in KERNELS}
     for i in range(K):
-        b = 5 * i
-        for j, n in enumerate(KERNELS):
-            per[n].append(ev.elapsed_ms(b + j, b + j + 1))
+        step(Wm + i, dbgs[i], stream)
+    torch.cuda.synchronize()
+    eager_ms = (time.perf_counter() - t_start) * 1e3 / K
+    # events [NE i + j] precede kernel j of step i; [NE i + NE - 1] follows the last one
+    per = {n: [ev.elapsed_ms(NE * i + j, NE * i + j + 1) for i in range(K)]
+           for j, n in enumerate(KERNELS)}
     ev.close()
+
+    # ---- pass 2 (graph replay): the timed K steps; one captured step per layer instance
+    graphs = []
+    gstream = torch.cuda.Stream()
+    with torch.cuda.stream(gstream):
+        for li in range(NL):
+            gr = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(gr, stream=gstream):
+                step(li, None, hb.current_stream(), visit=(li % visits))
+            graphs.append(gr)
+    torch.cuda.synchronize()
+    log(f"graph pass: warm-up {Wm}, timed {K} steps", q)
+    for i in range(Wm):
+        graphs[i % NL].replay()
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        graphs[(Wm + i) % NL].replay()
+    torch.cuda.synchronize()
+    graph_ms = (time.perf_counter() - t_start) * 1e3 / K
+    ms_step = graph_ms
     avg_ms = {n: float(np.mean(v)) for n, v in per.items()}
     Lavg = L0 + visits // 2
     alg = algorithmic_bytes(cfg, Lavg)
@@ -250,6 +268,7 @@ def main():
         "steps": K,
         "warmup": Wm,
         "ms_per_step": round(ms_step, 5),
+        "eager_us_per_step": round(eager_ms * 1e3, 2),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,

@@ -120,9 +120,11 @@ typedef struct {
  *                                   for a slot past the end of the sequence
  *   token_idx   [B][Hq][k]          the selected token positions, ascending
  *   token_count [B][Hq]             how many were selected
- *   kernel_events  NULL or 4 caller-created events, recorded on the stream before the page-bound
- *                  kernel, between the bound and selection kernels, between the selection and
- *                  attention kernels, and after the attention kernel (per-kernel timing) */
+ *   kernel_events  NULL or 6 caller-created events recorded on the stream around the five
+ *                  kernels of a decode step (per-kernel timing): before the preparation kernel
+ *                  (query rotation and code, and the append of hhr_append_decode), before the
+ *                  page-bound kernel, before the selection kernel, before the attention kernel,
+ *                  before the kernel that merges the attention partials, and after it */
 typedef struct {
   float* q_rot;
   uint32_t* q_code;
@@ -172,6 +174,16 @@ size_t hhr_decode_workspace_bytes(const hhr_dims* dims, const hhr_params* params
 hhr_status hhr_decode(const hhr_dims* dims, const hhr_params* params, const hhr_cache* cache,
                       const void* q, const float* R, const float* W, void* ws, size_t ws_bytes,
                       float* out, const hhr_debug* dbg, hhr_stream_t stream);
+
+/* hhr_append followed by hhr_decode in one call (the query attends over the new token too).
+ * The append is folded into the decode's first kernel, so a generation step costs one launch
+ * less than the two calls. Same arguments and rules as the two calls; append_ticket is
+ * required. */
+hhr_status hhr_append_decode(const hhr_dims* dims, const hhr_params* params,
+                             const hhr_cache* cache, const void* k_new, const void* v_new,
+                             const void* q, const float* R, const float* W, void* ws,
+                             size_t ws_bytes, float* out, const hhr_debug* dbg,
+                             hhr_stream_t stream);
 
 /* Static text for a status code. */
 const char* hhr_status_string(hhr_status status);

@@ -21,7 +21,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or type",
 
 # Every exported symbol of include/hhr.h.
 EXPORTS = ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode_workspace_bytes",
-           "hhr_decode", "hhr_status_string")
+           "hhr_decode", "hhr_append_decode", "hhr_status_string")
 
 
 class Dims(ctypes.Structure):
@@ -81,9 +81,12 @@ def load() -> ctypes.CDLL:
     lib.hhr_decode_workspace_bytes.restype = ctypes.c_size_t
     lib.hhr_decode.argtypes = [P(Dims), P(Params), P(CacheStruct), vp, vp, vp, vp, ctypes.c_size_t,
                                vp, P(DebugStruct), vp]
+    lib.hhr_append_decode.argtypes = [P(Dims), P(Params), P(CacheStruct), vp, vp, vp, vp, vp, vp,
+                                      ctypes.c_size_t, vp, P(DebugStruct), vp]
     lib.hhr_status_string.argtypes = [ctypes.c_int]
     lib.hhr_status_string.restype = ctypes.c_char_p
-    for fn in ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode"):
+    for fn in ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode",
+               "hhr_append_decode"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -116,6 +119,14 @@ def hhr_decode(dims: Dims, params: Params, cache: CacheStruct, q: int, R: int, W
     _check("hhr_decode", load().hhr_decode(
         ctypes.byref(dims), ctypes.byref(params), ctypes.byref(cache), q, R, W, ws, ws_bytes, out,
         ctypes.byref(dbg) if dbg is not None else None, stream))
+
+
+def hhr_append_decode(dims: Dims, params: Params, cache: CacheStruct, k_new: int, v_new: int,
+                      q: int, R: int, W: int, ws: int, ws_bytes: int, out: int,
+                      dbg: Optional[DebugStruct] = None, stream: int = 0) -> None:
+    _check("hhr_append_decode", load().hhr_append_decode(
+        ctypes.byref(dims), ctypes.byref(params), ctypes.byref(cache), k_new, v_new, q, R, W, ws,
+        ws_bytes, out, ctypes.byref(dbg) if dbg is not None else None, stream))
 
 
 def hhr_status_string(status: int) -> str:
@@ -198,11 +209,17 @@ class Decoder:
         self.ws = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=device)
 
     def __call__(self, cache: Cache, q, R, W, out, dbg: Optional[Debug] = None,
-                 stream: Optional[int] = None) -> None:
-        hhr_decode(self.dims, self.params, cache.struct(), _ptr(q), _ptr(R), _ptr(W),
-                   _ptr(self.ws), self.ws_bytes, _ptr(out),
-                   dbg.struct() if dbg is not None else None,
-                   current_stream() if stream is None else stream)
+                 stream: Optional[int] = None, k_new=None, v_new=None) -> None:
+        """hhr_decode, or hhr_append_decode when k_new / v_new are given."""
+        st = current_stream() if stream is None else stream
+        d = dbg.struct() if dbg is not None else None
+        if k_new is None:
+            hhr_decode(self.dims, self.params, cache.struct(), _ptr(q), _ptr(R), _ptr(W),
+                       _ptr(self.ws), self.ws_bytes, _ptr(out), d, st)
+        else:
+            hhr_append_decode(self.dims, self.params, cache.struct(), _ptr(k_new), _ptr(v_new),
+                              _ptr(q), _ptr(R), _ptr(W), _ptr(self.ws), self.ws_bytes, _ptr(out),
+                              d, st)
 
 
 def build_pages(cache: Cache, R, W, method: str = "auto", stream: Optional[int] = None) -> None:

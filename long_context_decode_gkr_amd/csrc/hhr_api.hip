@@ -103,7 +103,8 @@ hhr_status hhr_append(const hhr_dims* dims, const hhr_cache* cache, const void* 
   if (st != HHR_OK) return st;
   if ((st = check_cache(cache, true, &c)) != HHR_OK) return st;
   if (!k_new || !v_new || !R || !W) return HHR_ERR_INVALID_ARG;
-  return hip_status(launch_append(s, c, k_new, v_new, R, W, reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(launch_prep(s, c, k_new, v_new, nullptr, R, W, nullptr, nullptr, nullptr,
+                                nullptr, reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t hhr_decode_workspace_bytes(const hhr_dims* dims, const hhr_params* params) {
@@ -114,25 +115,44 @@ size_t hhr_decode_workspace_bytes(const hhr_dims* dims, const hhr_params* params
   return p.total;
 }
 
-hhr_status hhr_decode(const hhr_dims* dims, const hhr_params* params, const hhr_cache* cache,
-                      const void* q, const float* R, const float* W, void* ws, size_t ws_bytes,
-                      float* out, const hhr_debug* dbg, hhr_stream_t stream) {
+static hhr_status decode_common(const hhr_dims* dims, const hhr_params* params,
+                                const hhr_cache* cache, const void* k_new, const void* v_new,
+                                bool append, const void* q, const float* R, const float* W,
+                                void* ws, size_t ws_bytes, float* out, const hhr_debug* dbg,
+                                hhr_stream_t stream) {
   Shape s;
   CacheView c;
   DecodePlan p;
   hhr_status st = check_dims(dims, &s);
   if (st != HHR_OK) return st;
-  if ((st = check_cache(cache, false, &c)) != HHR_OK) return st;
+  if ((st = check_cache(cache, append, &c)) != HHR_OK) return st;
   if ((st = check_params(params, s, &p)) != HHR_OK) return st;
   if (!q || !R || !W || !out) return HHR_ERR_INVALID_ARG;
+  if (append && (!k_new || !v_new)) return HHR_ERR_INVALID_ARG;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < p.total)
     return HHR_ERR_WORKSPACE;
   DebugView dv{};
   if (dbg) dv = DebugView{dbg->q_rot, dbg->q_code, dbg->bounds, dbg->page_ids,
                           dbg->page_count, dbg->dist, dbg->token_idx, dbg->token_count,
                           reinterpret_cast<hipEvent_t*>(dbg->kernel_events)};
-  return hip_status(launch_decode(s, p, c, q, R, W, ws, out, dv,
-                                  reinterpret_cast<hipStream_t>(stream)));
+  return hip_status(launch_decode(s, p, c, append ? k_new : nullptr, append ? v_new : nullptr, q,
+                                  R, W, ws, out, dv, reinterpret_cast<hipStream_t>(stream)));
+}
+
+hhr_status hhr_decode(const hhr_dims* dims, const hhr_params* params, const hhr_cache* cache,
+                      const void* q, const float* R, const float* W, void* ws, size_t ws_bytes,
+                      float* out, const hhr_debug* dbg, hhr_stream_t stream) {
+  return decode_common(dims, params, cache, nullptr, nullptr, false, q, R, W, ws, ws_bytes, out,
+                       dbg, stream);
+}
+
+hhr_status hhr_append_decode(const hhr_dims* dims, const hhr_params* params,
+                             const hhr_cache* cache, const void* k_new, const void* v_new,
+                             const void* q, const float* R, const float* W, void* ws,
+                             size_t ws_bytes, float* out, const hhr_debug* dbg,
+                             hhr_stream_t stream) {
+  return decode_common(dims, params, cache, k_new, v_new, true, q, R, W, ws, ws_bytes, out, dbg,
+                       stream);
 }
 
 const char* hhr_status_string(hhr_status status) {

@@ -3,6 +3,8 @@
 // Method: "HHR: Hierarchical Hash Retrieval for Efficient LLM Generation", §3.3.1 (pages,
 // per-dimension extrema of the rotated keys k~ = k R, Eq. 4) and §3.1 Eq. 1 / §3.3.2 Eq. 10
 // (key code = sign of z = k W at inference).
+#include <type_traits>
+
 #include "hhr_device.h"
 #include "hhr_launch.h"
 
@@ -131,84 +133,198 @@ hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Append: one workgroup per (KV head, sequence). Writes the token's K and V rows, folds its
-// rotated key into page t / S, writes its code; the last workgroup of a sequence to finish
-// advances seq_lens[b] (a per-sequence ticket counts the finished KV heads and is left at 0).
+// Step preparation, grid (4 column slices, KV head g, sequence b). Each workgroup
+//   * appends the new token when k_new is given: writes its slice of the K and V rows, folds its
+//     32 channels of k~ = k R_g into page t / S (opens the page when t % S == 0) and writes its
+//     code words; the last workgroup of the sequence to finish advances seq_lens[b] (a
+//     per-sequence ticket, left at 0);
+//   * prepares the G queries of the group when q is given: its 32 channels of q~ = q R_g (Eq. 4)
+//     and its code words of sign(q W_g) (Eq. 1, Eq. 10), written to the decode workspace.
+// The new key and the G queries are the "vectors" v = 0 .. nvec-1; each R_g / W_g column of
+// the slice is read once and multiplied into all vectors. A column is split over 8 lanes of
+// 16 terms each (fp64 partial sums of exact products, reduced by DPP): threads [0, 256) own the
+// 32 rotation columns, threads [256, 256 + 8 NB / 4) the NB / 4 code columns.
 // ---------------------------------------------------------------------------------------------
+constexpr int kPrepSlices = 4;
+constexpr int kPrepParts = 8;
+constexpr int kMaxVec = 9;   // 1 key + up to 8 queries
+
+// Sum over each aligned group of 8 lanes (quad exchanges, then the half-row mirror).
+__device__ __forceinline__ double group8_sum(double v) {
+  auto step = [](double x, auto ctrl) {
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), decltype(ctrl)::value, 0xf, 0xf, false);
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), decltype(ctrl)::value, 0xf, 0xf, false);
+    return x + __hiloint2double(hi, lo);
+  };
+  v = step(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  v = step(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  v = step(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
+  return v;
+}
+
 template <int NB>
-__global__ void __launch_bounds__(256)
-append_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __restrict__ vn,
-              const float* __restrict__ R, const float* __restrict__ W) {
+__global__ void __launch_bounds__(256 + kPrepParts * NB / kPrepSlices)
+prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __restrict__ vn,
+            const void* __restrict__ q, const float* __restrict__ R, const float* __restrict__ W,
+            float* __restrict__ qrot, uint32_t* __restrict__ qcode, float* __restrict__ dbg_qrot,
+            uint32_t* __restrict__ dbg_qcode) {
   constexpr int NW = NB / 32;
-  const int g = blockIdx.x, b = blockIdx.y;
-  const int t = c.seq_lens[b];
-  if (t < 0 || t >= s.Lmax) return;
+  constexpr int CC = NB / kPrepSlices;          // code columns per slice (32 or 64)
+  constexpr int WPS = CC / 32;                  // code words per slice (1 or 2)
+  constexpr int T = kD / kPrepParts;            // terms per lane (16)
+  const int sl = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
-  __shared__ float xk[kD];
+  const int t = c.seq_lens[b];
+  const bool app = kn != nullptr && t >= 0 && t < s.Lmax;
+  const int v0 = app ? 1 : 0;                    // first query vector
+  const int nq = q ? s.G : 0;
+  const int nvec = v0 + nq;
+  if (nvec == 0) return;
 
-  const size_t src = (size_t(b) * s.Hkv + g) * kD;
-  const size_t row = (size_t(b) * s.Hkv + g) * s.Lmax + t;
-  if (tid < kD) {
+  __shared__ float xs[kMaxVec][kD];
+  __shared__ uint8_t bits[kMaxVec][CC];
+
+  const size_t krow = (size_t(b) * s.Hkv + g) * kD;
+  const size_t row = (size_t(b) * s.Hkv + g) * s.Lmax + (app ? t : 0);
+  if (app && tid < kD) {
     if (s.kv_bf16) {
-      const uint16_t kb = reinterpret_cast<const uint16_t*>(kn)[src + tid];
-      reinterpret_cast<uint16_t*>(c.K)[row * kD + tid] = kb;
-      reinterpret_cast<uint16_t*>(c.V)[row * kD + tid] = reinterpret_cast<const uint16_t*>(vn)[src + tid];
-      xk[tid] = bf16_bits_to_f32(kb);
+      const uint16_t kb = reinterpret_cast<const uint16_t*>(kn)[krow + tid];
+      if ((tid >> 5) == sl) {
+        reinterpret_cast<uint16_t*>(c.K)[row * kD + tid] = kb;
+        reinterpret_cast<uint16_t*>(c.V)[row * kD + tid] = reinterpret_cast<const uint16_t*>(vn)[krow + tid];
+      }
+      xs[0][tid] = bf16_bits_to_f32(kb);
     } else {
-      const float kf = reinterpret_cast<const float*>(kn)[src + tid];
-      reinterpret_cast<float*>(c.K)[row * kD + tid] = kf;
-      reinterpret_cast<float*>(c.V)[row * kD + tid] = reinterpret_cast<const float*>(vn)[src + tid];
-      xk[tid] = kf;
+      const float kf = reinterpret_cast<const float*>(kn)[krow + tid];
+      if ((tid >> 5) == sl) {
+        reinterpret_cast<float*>(c.K)[row * kD + tid] = kf;
+        reinterpret_cast<float*>(c.V)[row * kD + tid] = reinterpret_cast<const float*>(vn)[krow + tid];
+      }
+      xs[0][tid] = kf;
     }
+  }
+  for (int e = tid; e < nq * kD; e += blockDim.x) {
+    const int hh = e / kD, i = e % kD;
+    xs[v0 + hh][i] = load_elem(q, (size_t(b) * s.Hq + g * s.G + hh) * kD + i, s.q_bf16);
   }
   __syncthreads();
 
-  // Rotated key on threads [128, 256): fp64 dot, one rounding; fold into the page extrema.
-  if (tid >= kD) {
-    const int j = tid - kD;
-    const float* rc = R + size_t(g) * kD * kD + j;
-    double a = 0.0;
-#pragma unroll 8
-    for (int i = 0; i < kD; ++i) a += double(xk[i]) * double(rc[size_t(i) * kD]);
-    const float kt = float(a);
-    const int p = t / s.S;
-    const size_t si = ((size_t(b) * s.Hkv + g) * kD + j) * s.Pmax + p;
-    if (t % s.S == 0) {
-      c.pmin[si] = kt;
-      c.pmax[si] = kt;
-    } else {
-      c.pmin[si] = fminf(c.pmin[si], kt);
-      c.pmax[si] = fmaxf(c.pmax[si], kt);
+  const int part = tid & (kPrepParts - 1);
+  if (tid < 256) {
+    // ---- rotation column j, terms [16 part, 16 part + 16)
+    const int j = sl * 32 + (tid >> 3);
+    const float* rc = R + size_t(g) * kD * kD + size_t(part * T) * kD + j;
+    float rv[T];
+#pragma unroll
+    for (int i = 0; i < T; ++i) rv[i] = rc[size_t(i) * kD];
+    double acc[kMaxVec];
+#pragma unroll
+    for (int v = 0; v < kMaxVec; ++v) {
+      double a = 0.0;
+      if (v < nvec) {
+        const float* x = &xs[v][part * T];
+#pragma unroll
+        for (int i = 0; i < T; ++i) a += double(x[i]) * double(rv[i]);
+      }
+      acc[v] = group8_sum(a);
+    }
+    if (part == 0) {
+      if (app) {
+        const float kt = float(acc[0]);
+        const int p = t / s.S;
+        const size_t si = ((size_t(b) * s.Hkv + g) * kD + j) * s.Pmax + p;
+        if (t % s.S == 0) {
+          c.pmin[si] = kt;
+          c.pmax[si] = kt;
+        } else {
+          c.pmin[si] = fminf(c.pmin[si], kt);
+          c.pmax[si] = fmaxf(c.pmax[si], kt);
+        }
+      }
+#pragma unroll
+      for (int v = 0; v < kMaxVec; ++v) {
+        if (v >= v0 && v < nvec) {
+          const size_t o = (size_t(b) * s.Hq + g * s.G + (v - v0)) * kD + j;
+          qrot[o] = float(acc[v]);
+          if (dbg_qrot) dbg_qrot[o] = float(acc[v]);
+        }
+      }
+    }
+  } else {
+    // ---- code column cc, terms [16 part, 16 part + 16)
+    const int lc = (tid - 256) >> 3;              // column within the slice
+    const int cc = sl * CC + lc;
+    const float* wc = W + size_t(g) * kD * NB + size_t(part * T) * NB + cc;
+    float wv[T];
+#pragma unroll
+    for (int i = 0; i < T; ++i) wv[i] = wc[size_t(i) * NB];
+    double z[kMaxVec], sa[kMaxVec];
+#pragma unroll
+    for (int v = 0; v < kMaxVec; ++v) {
+      double zz = 0.0, ss = 0.0;
+      if (v < nvec) {
+        const float* x = &xs[v][part * T];
+#pragma unroll
+        for (int i = 0; i < T; ++i) {
+          const double pr = double(x[i]) * double(wv[i]);
+          zz += pr;
+          ss += fabs(pr);
+        }
+      }
+      z[v] = group8_sum(zz);
+      sa[v] = group8_sum(ss);
+    }
+    if (part == 0) {
+      const float* wcol = W + size_t(g) * kD * NB + cc;
+      for (int v = 0; v < nvec; ++v) {
+        int cb = certain_bit(z[v], sa[v]);
+        if (cb < 0) cb = int(exact_bit(static_cast<const float*>(&xs[v][0]), wcol, NB));
+        bits[v][lc] = uint8_t(cb);
+      }
     }
   }
-
-  // Code bit c on thread c.
-  uint32_t bit = 0;
-  if (tid < NB) bit = certified_bit(static_cast<const float*>(xk), W + size_t(g) * kD * NB + tid, NB);
-  const uint64_t mask = __ballot(bit);
-  if (lane_id() == 0 && tid < NB) {
-    *reinterpret_cast<uint2*>(c.codes + row * NW + 2 * (tid / kWave)) =
-        make_uint2(uint32_t(mask), uint32_t(mask >> 32));
-  }
-
-  __threadfence();
   __syncthreads();
-  if (tid == 0) {
-    const int done = atomicAdd(&c.ticket[b], 1);
-    if (done == s.Hkv - 1) {
-      c.ticket[b] = 0;
-      c.seq_lens[b] = t + 1;
+  // ---- pack this slice's code words: thread (v, w) builds word w of vector v
+  if (tid < nvec * WPS) {
+    const int v = tid / WPS, wi = tid % WPS;
+    uint32_t word = 0;
+#pragma unroll
+    for (int i = 0; i < 32; ++i) word |= uint32_t(bits[v][32 * wi + i]) << i;
+    const int wg = sl * WPS + wi;                 // word index within the code
+    if (v < v0) {
+      c.codes[row * NW + wg] = word;
+    } else {
+      const size_t o = (size_t(b) * s.Hq + g * s.G + (v - v0)) * NW + wg;
+      qcode[o] = word;
+      if (dbg_qcode) dbg_qcode[o] = word;
+    }
+  }
+  if (app) {
+    // Every workgroup of sequence b has read seq_lens[b] (the load completed before the
+    // barrier) before it takes a ticket, so the last one can advance it; the following kernels
+    // see the new value at the kernel boundary. No device-scope fence is needed (on gfx950 one
+    // would write back and invalidate the whole L2 of the XCD).
+    __syncthreads();
+    if (tid == 0) {
+      const int done = atomicAdd(&c.ticket[b], 1);
+      if (done == s.Hkv * kPrepSlices - 1) {
+        c.ticket[b] = 0;
+        c.seq_lens[b] = t + 1;
+      }
     }
   }
 }
 
-hipError_t launch_append(const Shape& s, const CacheView& c, const void* k_new,
-                         const void* v_new, const float* R, const float* W, hipStream_t st) {
-  dim3 grid(s.Hkv, s.B);
+hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, const void* v_new,
+                       const void* q, const float* R, const float* W, float* qrot,
+                       uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, hipStream_t st) {
+  dim3 grid(kPrepSlices, s.Hkv, s.B);
   if (s.NB == 128)
-    hipLaunchKernelGGL((append_kernel<128>), grid, dim3(256), 0, st, s, c, k_new, v_new, R, W);
+    hipLaunchKernelGGL((prep_kernel<128>), grid, dim3(256 + kPrepParts * 128 / kPrepSlices), 0,
+                       st, s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
   else
-    hipLaunchKernelGGL((append_kernel<256>), grid, dim3(256), 0, st, s, c, k_new, v_new, R, W);
+    hipLaunchKernelGGL((prep_kernel<256>), grid, dim3(256 + kPrepParts * 256 / kPrepSlices), 0,
+                       st, s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
   return hipGetLastError();
 }
 

@@ -13,8 +13,14 @@
 //   select_kernel      grid (Hq, B), 1024 threads: query code, exact top-n_keep pages by a
 //                      range-adapted radix select, Hamming distances of the kept pages' keys,
 //                      exact top-k tokens by a histogram select; writes ascending indices.
-//   attn_kernel        grid (nsplit, Hq, B): split-K softmax attention over gathered K/V rows;
-//                      the last workgroup of each (b, h) merges the partial (m, l, o).
+//   attn_kernel        grid (nsplit, Hq, B): split-K softmax attention over gathered K/V rows,
+//                      one partial (m, l, o) per workgroup;
+//   combine_kernel     grid (B * Hq): merges the partials of each (b, h) into the output.
+// The merge is a kernel of its own: an in-kernel "last workgroup merges" scheme needs a
+// device-scope release and acquire in every workgroup, which on gfx950 write back and
+// invalidate the whole L2 of an XCD, and costs far more than one small launch.
+#include <type_traits>
+
 #include "hhr_device.h"
 #include "hhr_launch.h"
 
@@ -28,17 +34,16 @@ constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kDistCache = 32768;      // candidate slots whose distance stays in LDS
 
 // ---------------------------------------------------------------------------------------------
-// Coarse stage: page bounds (Eq. 3) with the query rotated on the fly (Eq. 4).
-// Lane l of wave w covers pages p0 + 4l .. p0 + 4l + 3 and channels 16w .. 16w + 15; the 16
-// float4 loads of l and u are issued first, q~ for those channels is computed while they are in
-// flight, and the 8 waves' partial sums meet in LDS.
+// Coarse stage: page bounds (Eq. 3) for the G query heads of one KV head from ONE read of the
+// page extrema. Lane l of wave w covers pages p0 + 4l .. p0 + 4l + 3 and channels
+// 16w .. 16w + 15: 32 float4 loads per lane are issued at once, q~ (prepared by the preparation
+// kernel) is read with wave-uniform scalar loads, and the 8 waves' partial sums meet in LDS.
 // ---------------------------------------------------------------------------------------------
 template <int G>
 __global__ void __launch_bounds__(kBoundThreads)
 page_bound_kernel(Shape s, const float* __restrict__ pmin, const float* __restrict__ pmax,
-                  const int32_t* __restrict__ seq_lens, const void* __restrict__ q,
-                  const float* __restrict__ R, float* __restrict__ U, float* __restrict__ dbg_U,
-                  float* __restrict__ dbg_qrot) {
+                  const int32_t* __restrict__ seq_lens, const float* __restrict__ qrot,
+                  float* __restrict__ U, float* __restrict__ dbg_U) {
   const int b = blockIdx.z, g = blockIdx.y, p0 = blockIdx.x * kBoundPages;
   const int L = min(max(seq_lens[b], 0), s.Lmax);
   const int P = (L + s.S - 1) / s.S;
@@ -60,23 +65,7 @@ page_bound_kernel(Shape s, const float* __restrict__ pmin, const float* __restri
 #pragma unroll
     for (int jj = 0; jj < 16; ++jj) lo[jj] = hi[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
   }
-
-  // q~[hh][j0 + (lane & 15)] for hh = (lane >> 4) + 4 r.
-  constexpr int QPL = (G + 3) / 4;
-  float qt[QPL];
-  const float* Rg = R + size_t(g) * kD * kD + j0 + (lane & 15);
-#pragma unroll
-  for (int r = 0; r < QPL; ++r) {
-    const int hh = (lane >> 4) + 4 * r;
-    float a = 0.f;
-    if (hh < G) {
-      const size_t qo = (size_t(b) * s.Hq + g * G + hh) * kD;
-#pragma unroll 8
-      for (int i = 0; i < kD; ++i) a = fmaf(load_elem(q, qo + i, s.q_bf16), Rg[size_t(i) * kD], a);
-      if (dbg_qrot && blockIdx.x == 0) dbg_qrot[qo + j0 + (lane & 15)] = a;
-    }
-    qt[r] = a;
-  }
+  const float* qb = qrot + (size_t(b) * s.Hq + size_t(g) * G) * kD + j0;
 
   float acc[G][4];
 #pragma unroll
@@ -86,8 +75,7 @@ page_bound_kernel(Shape s, const float* __restrict__ pmin, const float* __restri
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       // max(q l, q u) = q * (q >= 0 ? u : l) since l <= u; q is wave-uniform.
-      const float qv = __int_as_float(
-          __builtin_amdgcn_readlane(__float_as_int(qt[hh >> 2]), (hh & 3) * 16 + jj));
+      const float qv = qb[hh * kD + jj];
       const float4 e = (qv >= 0.f) ? hi[jj] : lo[jj];
       acc[hh][0] = fmaf(qv, e.x, acc[hh][0]);
       acc[hh][1] = fmaf(qv, e.y, acc[hh][1]);
@@ -117,76 +105,32 @@ page_bound_kernel(Shape s, const float* __restrict__ pmin, const float* __restri
 }
 
 // ---------------------------------------------------------------------------------------------
-// Block-wide scans for 1024 threads.
+// Block-wide scan for 1024 threads: DPP wave scans, then the 16 wave totals through LDS.
+// The totals are double-buffered, so one barrier per scan suffices as long as consecutive scans
+// alternate buffers (the barrier of the scan in between orders the reuse).
 // ---------------------------------------------------------------------------------------------
-struct ScanScratch {
-  int wtot[kSelWaves];
+struct BlockScan {
+  int (*wt)[kSelWaves];
+  int buf;
+  // Exclusive prefix of v in thread order; *total gets the block sum.
+  __device__ __forceinline__ int excl(int v, int* total) {
+    const int incl = wave_incl_sum(v);
+    const int w = wave_id();
+    int* t = wt[buf];
+    buf ^= 1;
+    if (lane_id() == kWave - 1) t[w] = incl;
+    __syncthreads();
+    int base = 0, tot = 0;
+#pragma unroll
+    for (int i = 0; i < kSelWaves; ++i) {
+      const int x = t[i];
+      base += (i < w) ? x : 0;
+      tot += x;
+    }
+    *total = tot;
+    return base + incl - v;
+  }
 };
-
-// Exclusive prefix sum of v over the block in thread order; *total receives the sum.
-__device__ __forceinline__ int block_excl_scan(int v, ScanScratch& sc, int* total) {
-  const int lane = lane_id(), w = wave_id();
-  int x = v;
-#pragma unroll
-  for (int o = 1; o < kWave; o <<= 1) {
-    const int y = __shfl_up(x, o);
-    if (lane >= o) x += y;
-  }
-  if (lane == kWave - 1) sc.wtot[w] = x;
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
-    const int t = sc.wtot[i];
-    base += (i < w) ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + x - v;
-}
-
-// Exclusive prefix count of a flag over the block in thread order.
-__device__ __forceinline__ int block_flag_prefix(bool f, ScanScratch& sc, int* total) {
-  const uint64_t m = __ballot(f);
-  const int w = wave_id();
-  if (lane_id() == 0) sc.wtot[w] = __popcll(m);
-  __syncthreads();
-  int base = 0, tot = 0;
-#pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) {
-    const int t = sc.wtot[i];
-    base += (i < w) ? t : 0;
-    tot += t;
-  }
-  __syncthreads();
-  *total = tot;
-  return base + int(lanes_below(m));
-}
-
-__device__ __forceinline__ uint32_t block_min_u32(uint32_t v, ScanScratch& sc) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = min(v, uint32_t(__shfl_xor(int(v), o)));
-  if (lane_id() == 0) sc.wtot[wave_id()] = int(v);
-  __syncthreads();
-  uint32_t r = 0xFFFFFFFFu;
-#pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) r = min(r, uint32_t(sc.wtot[i]));
-  __syncthreads();
-  return r;
-}
-
-__device__ __forceinline__ uint32_t block_max_u32(uint32_t v, ScanScratch& sc) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = max(v, uint32_t(__shfl_xor(int(v), o)));
-  if (lane_id() == 0) sc.wtot[wave_id()] = int(v);
-  __syncthreads();
-  uint32_t r = 0u;
-#pragma unroll
-  for (int i = 0; i < kSelWaves; ++i) r = max(r, uint32_t(sc.wtot[i]));
-  __syncthreads();
-  return r;
-}
 
 // Order-preserving map of a bound to uint32 where SMALLER means LARGER U (so the kept pages are
 // the smallest keys); -0 and +0 map to the same key.
@@ -198,26 +142,35 @@ __device__ __forceinline__ uint32_t desc_key(float u) {
 }
 
 struct SelectArgs {
+  const uint32_t* qcode;  // [B][Hq][NW]
   const float* U;
   int32_t* idx;       // [B][Hq][kcap]
   int32_t* cnt;       // [B][Hq]
-  uint32_t* tickets;  // [B][Hq]
   double rho;
   int kcap;
 };
 
 // ---------------------------------------------------------------------------------------------
 // Selection, one workgroup per (b, h).
-//   EPT: pages per thread (contiguous: thread i owns pages [i EPT, i EPT + EPT)).
+//   Coarse: the n_keep pages of largest U, ties to the lower index. Keys are ranked by a radix
+//   select over rel = key - min(key), 12 bits at a time from the top set bit of the range; the
+//   threshold bin's ties are broken in page order by one scan. EPT pages per thread
+//   (contiguous: thread i owns pages [i EPT, i EPT + EPT)).
+//   Fine: Hamming distance of every key of the kept pages (slots in ascending token order),
+//   histogram over D in [0, NB], the smallest D* with #(D <= D*) >= k_eff, and one scan that
+//   places every slot with D < D* and the first k_eff - #(D < D*) slots with D == D*.
 // ---------------------------------------------------------------------------------------------
 constexpr int kRadixBits = 12;
 constexpr int kRadixBins = 1 << kRadixBits;
+constexpr int kEmitSPT = 16;   // cached distances per thread per emit chunk
 
 template <int NB, int EPT>
 __global__ void __launch_bounds__(kSelThreads)
-select_kernel(Shape s, CacheView c, const void* __restrict__ q, const float* __restrict__ W,
-              SelectArgs a, DebugView dbg) {
+select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   constexpr int NW = NB / 32;
+  using DT = typename std::conditional<NB == 128, uint8_t, uint16_t>::type;
+  constexpr uint32_t kNone = NB == 128 ? 0xFFu : 0xFFFFu;   // distance of a slot past the end
+  constexpr int HB = kRadixBins > kSelWaves * (NB + 1) ? kRadixBins : kSelWaves * (NB + 1);
   const int h = blockIdx.x, b = blockIdx.y, g = h / s.G;
   const int bh = b * s.Hq + h;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
@@ -225,17 +178,18 @@ select_kernel(Shape s, CacheView c, const void* __restrict__ q, const float* __r
   const int P = (L + s.S - 1) / s.S;
 
   __shared__ int32_t s_pages[kMaxPages];
-  __shared__ uint16_t s_dist[kDistCache];
-  __shared__ uint32_t s_hist[kRadixBins > kSelWaves * (NB + 1) ? kRadixBins : kSelWaves * (NB + 1)];
-  __shared__ float s_q[kD];
+  __shared__ __align__(16) DT s_dist[kDistCache];
+  __shared__ uint32_t s_hist[HB];
   __shared__ uint32_t s_qw[NW];
-  __shared__ ScanScratch sc;
-  __shared__ int s_pick[2];
+  __shared__ int s_wt[2][kSelWaves];
+  __shared__ uint32_t s_mm[2][kSelWaves];
+  __shared__ int s_pick[3];
+  BlockScan scan{s_wt, 0};
+  (void)lane;
 
   if (L == 0) {
     if (tid == 0) {
       a.cnt[bh] = 0;
-      a.tickets[bh] = 0;
       if (dbg.page_count) dbg.page_count[bh] = 0;
       if (dbg.token_count) dbg.token_count[bh] = 0;
     }
@@ -243,31 +197,34 @@ select_kernel(Shape s, CacheView c, const void* __restrict__ q, const float* __r
   }
   const int n_keep = min(P, max(1, int(ceil(a.rho * double(P)))));
 
-  // ---- query to LDS, page keys to registers
-  if (tid < kD) s_q[tid] = load_elem(q, size_t(bh) * kD + tid, s.q_bf16);
+  // ---- query code (from the preparation kernel), page keys to registers, histograms cleared
+  if (tid < NW) s_qw[tid] = a.qcode[size_t(bh) * NW + tid];
+  for (int i = tid; i < HB; i += kSelThreads) s_hist[i] = 0;
   uint32_t key[EPT];
-  const float* Ub = a.U + size_t(bh) * s.Pmax;
-#pragma unroll
-  for (int e = 0; e < EPT; ++e) {
-    const int p = tid * EPT + e;
-    key[e] = (p < P) ? desc_key(Ub[p]) : 0xFFFFFFFFu;
-  }
-  __syncthreads();
-
-  // ---- query code (§3.1 Eq. 1): thread cc < NB computes bit cc, certified / exact
   {
-    uint32_t bit = 0;
-    if (tid < NB) bit = certified_bit(static_cast<const float*>(s_q), W + size_t(g) * kD * NB + tid, NB);
-    const uint64_t m = __ballot(bit);
-    if (lane == 0 && w < NB / kWave) {
-      s_qw[2 * w] = uint32_t(m);
-      s_qw[2 * w + 1] = uint32_t(m >> 32);
+    const float* Ub = a.U + size_t(bh) * s.Pmax + size_t(tid) * EPT;
+    float u[EPT];
+    if ((tid + 1) * EPT <= P) {
+      if constexpr (EPT >= 4) {
+#pragma unroll
+        for (int e = 0; e < EPT; e += 4) {
+          const float4 x = *reinterpret_cast<const float4*>(Ub + e);
+          u[e] = x.x; u[e + 1] = x.y; u[e + 2] = x.z; u[e + 3] = x.w;
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) u[e] = Ub[e];
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) u[e] = (tid * EPT + e < P) ? Ub[e] : 0.f;
     }
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) key[e] = (tid * EPT + e < P) ? desc_key(u[e]) : 0xFFFFFFFFu;
   }
 
-  // ---- coarse selection: the n_keep smallest keys, ties to the lower page index.
-  // Radix select over rel = key - kmin, 12 bits at a time from the top set bit of the range.
-  bool sel[EPT];
+  // ---- key range (one barrier for both reductions)
+  uint32_t kmin, kmax;
   {
     uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
 #pragma unroll
@@ -277,89 +234,96 @@ select_kernel(Shape s, CacheView c, const void* __restrict__ q, const float* __r
         lmax = max(lmax, key[e]);
       }
     }
-    const uint32_t kmin = block_min_u32(lmin, sc);
-    const uint32_t kmax = block_max_u32(lmax, sc);
-    int need = n_keep;           // still to take among elements matching `prefix`
-    uint32_t prefix = 0;         // high bits of rel fixed so far
-    int cur_hi = (kmax == kmin) ? -1 : 31 - __clz(int(kmax - kmin));
-    int res_lo = 0;              // resolution: elements compare on rel >> res_lo
-    if (n_keep < P) {
-      while (cur_hi >= 0) {
-        const int cur_lo = max(cur_hi - (kRadixBits - 1), 0);
-        const int width = cur_hi - cur_lo + 1;
-        const uint32_t dmask = (1u << width) - 1u;
-        for (int i = tid; i < kRadixBins; i += kSelThreads) s_hist[i] = 0;
-        __syncthreads();
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) {
-          if (tid * EPT + e < P) {
-            const uint32_t rel = key[e] - kmin;
-            if (uint32_t(uint64_t(rel) >> (cur_hi + 1)) == prefix)
-              atomicAdd(&s_hist[(rel >> cur_lo) & dmask], 1u);
-          }
-        }
-        __syncthreads();
-        // scan bins: thread i owns bins [4 i, 4 i + 4)
-        constexpr int BPT = kRadixBins / kSelThreads;
-        uint32_t hb[BPT];
-        int loc = 0;
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-          hb[j] = s_hist[tid * BPT + j];
-          loc += int(hb[j]);
-        }
-        int tot;
-        int run = block_excl_scan(loc, sc, &tot);
-#pragma unroll
-        for (int j = 0; j < BPT; ++j) {
-          const int cnt = int(hb[j]);
-          if (cnt > 0 && run < need && need <= run + cnt) {
-            s_pick[0] = tid * BPT + j;
-            s_pick[1] = run;
-          }
-          run += cnt;
-        }
-        __syncthreads();
-        const int d = s_pick[0], before = s_pick[1];
-        const int in_bin = int(s_hist[d]);
-        __syncthreads();
-        prefix = (prefix << width) | uint32_t(d);
-        need -= before;
-        res_lo = cur_lo;
-        cur_hi = cur_lo - 1;
-        if (in_bin == need) break;   // the whole bin is taken: no finer digit is needed
-      }
+    lmin = wave_min_u32(lmin);
+    lmax = wave_max_u32(lmax);
+    if (lane_id() == 0) {
+      s_mm[0][w] = lmin;
+      s_mm[1][w] = lmax;
     }
-    // Final: rel >> res_lo below prefix -> taken; equal -> taken in index order up to `need`.
+    __syncthreads();   // also publishes s_qw and the cleared histograms
+    kmin = 0xFFFFFFFFu;
+    kmax = 0u;
+#pragma unroll
+    for (int i = 0; i < kSelWaves; ++i) {
+      kmin = min(kmin, s_mm[0][i]);
+      kmax = max(kmax, s_mm[1][i]);
+    }
+  }
+
+  // ---- coarse selection
+  int need = n_keep;        // still to take among elements matching `prefix`
+  uint32_t prefix = 0;      // high bits of rel fixed so far
+  int res_lo = 0;           // elements compare on rel >> res_lo
+  if (n_keep < P) {
+    int cur_hi = (kmax == kmin) ? -1 : 31 - __clz(int(kmax - kmin));
+    while (cur_hi >= 0) {
+      const int cur_lo = max(cur_hi - (kRadixBits - 1), 0);
+      const int width = cur_hi - cur_lo + 1;
+      const uint32_t dmask = (1u << width) - 1u;
+#pragma unroll
+      for (int e = 0; e < EPT; ++e) {
+        if (tid * EPT + e < P) {
+          const uint32_t rel = key[e] - kmin;
+          if (uint32_t(uint64_t(rel) >> (cur_hi + 1)) == prefix)
+            atomicAdd(&s_hist[(rel >> cur_lo) & dmask], 1u);
+        }
+      }
+      __syncthreads();
+      // thread i owns bins [4 i, 4 i + 4): read them, clear them for the next pass
+      constexpr int BPT = kRadixBins / kSelThreads;
+      uint32_t hb[BPT];
+      int loc = 0;
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        hb[j] = s_hist[tid * BPT + j];
+        s_hist[tid * BPT + j] = 0;
+        loc += int(hb[j]);
+      }
+      int tot;
+      int run = scan.excl(loc, &tot);
+#pragma unroll
+      for (int j = 0; j < BPT; ++j) {
+        const int cnt = int(hb[j]);
+        if (cnt > 0 && run < need && need <= run + cnt) {
+          s_pick[0] = tid * BPT + j;
+          s_pick[1] = run;
+          s_pick[2] = cnt;
+        }
+        run += cnt;
+      }
+      __syncthreads();
+      const int d = s_pick[0], before = s_pick[1], in_bin = s_pick[2];
+      prefix = (prefix << width) | uint32_t(d);
+      need -= before;
+      res_lo = cur_lo;
+      cur_hi = cur_lo - 1;
+      if (in_bin == need) break;   // the whole bin is taken: no finer digit is needed
+    }
+  } else {
+    need = P;
+  }
+  // rel >> res_lo below prefix: taken; equal: taken in page order up to `need`
+  {
     bool lt[EPT], eq[EPT];
-    int neq = 0;
+    int nlt = 0, neq = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
       const bool ok = tid * EPT + e < P;
       const uint32_t v = (key[e] - kmin) >> res_lo;
       lt[e] = ok && (n_keep < P) && v < prefix;
       eq[e] = ok && ((n_keep >= P) || v == prefix);
+      nlt += lt[e] ? 1 : 0;
       neq += eq[e] ? 1 : 0;
     }
-    if (n_keep >= P) need = P;
     int tot;
-    int rank = block_excl_scan(neq, sc, &tot);
+    const int ex = scan.excl((nlt << 16) | neq, &tot);
+    int eq_seen = ex & 0xFFFF;
+    int pos = (ex >> 16) + min(eq_seen, need);
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      sel[e] = lt[e] || (eq[e] && rank < need);
-      rank += eq[e] ? 1 : 0;
-    }
-  }
-  // compaction: kept pages in ascending order
-  {
-    int nsel = 0;
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) nsel += sel[e] ? 1 : 0;
-    int tot;
-    int pos = block_excl_scan(nsel, sc, &tot);
-#pragma unroll
-    for (int e = 0; e < EPT; ++e) {
-      if (sel[e]) {
+      const bool take = lt[e] || (eq[e] && eq_seen < need);
+      eq_seen += eq[e] ? 1 : 0;
+      if (take) {
         s_pages[pos] = tid * EPT + e;
         if (dbg.page_ids) dbg.page_ids[size_t(bh) * s.Pmax + pos] = tid * EPT + e;
         ++pos;
@@ -367,8 +331,6 @@ select_kernel(Shape s, CacheView c, const void* __restrict__ q, const float* __r
     }
     if (tid == 0 && dbg.page_count) dbg.page_count[bh] = n_keep;
   }
-  if (dbg.q_code && tid < NW) dbg.q_code[size_t(bh) * NW + tid] = s_qw[tid];
-  for (int i = tid; i < kSelWaves * (NB + 1); i += kSelThreads) s_hist[i] = 0;
   __syncthreads();
 
   // ---- fine stage: Hamming distance of every candidate slot (§3.1 Eq. 2)
@@ -379,12 +341,11 @@ select_kernel(Shape s, CacheView c, const void* __restrict__ q, const float* __r
   const int nslots = n_keep << lgS;
   const bool cache_d = nslots <= kDistCache;
   const uint32_t* cbase = c.codes + (size_t(b) * s.Hkv + g) * s.Lmax * NW;
-  auto distance = [&](int slot, int* t_out) -> int {
-    const int t = (s_pages[slot >> lgS] << lgS) + (slot & (s.S - 1));
-    *t_out = t;
-    if (t >= L) return 0xFFFF;
+  auto slot_token = [&](int slot) { return (s_pages[slot >> lgS] << lgS) + (slot & (s.S - 1)); };
+  auto distance = [&](int t) -> uint32_t {
+    if (t >= L) return kNone;
     const uint4* cp = reinterpret_cast<const uint4*>(cbase + size_t(t) * NW);
-    int dd = 0;
+    uint32_t dd = 0;
 #pragma unroll
     for (int v = 0; v < NW / 4; ++v) {
       const uint4 x = cp[v];
@@ -394,17 +355,42 @@ select_kernel(Shape s, CacheView c, const void* __restrict__ q, const float* __r
     return dd;
   };
   uint32_t* whist = s_hist + w * (NB + 1);
-  for (int slot = tid; slot < nslots; slot += kSelThreads) {
-    int t;
-    const int dd = distance(slot, &t);
-    if (dd != 0xFFFF) atomicAdd(&whist[dd], 1u);
-    if (cache_d) s_dist[slot] = uint16_t(dd);
-    if (dbg.dist) dbg.dist[size_t(bh) * s.Lmax + slot] = uint16_t(dd);
+  // Batches of 8 slots per thread: all code loads of a batch are issued before any is used.
+  constexpr int BAT = 8;
+  for (int base = 0; base < nslots; base += BAT * kSelThreads) {
+    int tt[BAT];
+    uint4 cw[BAT][NW / 4];
+#pragma unroll
+    for (int u = 0; u < BAT; ++u) {
+      const int slot = base + u * kSelThreads + tid;
+      tt[u] = (slot < nslots) ? slot_token(min(slot, nslots - 1)) : L;
+      const int tl = min(tt[u], L - 1);
+      const uint4* cp = reinterpret_cast<const uint4*>(cbase + size_t(tl) * NW);
+#pragma unroll
+      for (int v = 0; v < NW / 4; ++v) cw[u][v] = cp[v];
+    }
+#pragma unroll
+    for (int u = 0; u < BAT; ++u) {
+      const int slot = base + u * kSelThreads + tid;
+      if (slot < nslots) {
+        uint32_t dd = kNone;
+        if (tt[u] < L) {
+          dd = 0;
+#pragma unroll
+          for (int v = 0; v < NW / 4; ++v)
+            dd += __popc(cw[u][v].x ^ qw[4 * v]) + __popc(cw[u][v].y ^ qw[4 * v + 1]) +
+                  __popc(cw[u][v].z ^ qw[4 * v + 2]) + __popc(cw[u][v].w ^ qw[4 * v + 3]);
+          atomicAdd(&whist[dd], 1u);
+        }
+        if (cache_d) s_dist[slot] = DT(dd);
+        if (dbg.dist) dbg.dist[size_t(bh) * s.Lmax + slot] = uint16_t(dd == kNone ? 0xFFFFu : dd);
+      }
+    }
   }
   __syncthreads();
 
   // ---- token threshold: smallest D* with #(D <= D*) >= k_eff
-  int dstar, before, k_eff;
+  int dstar, need_eq, k_eff;
   {
     int tot_d = 0;
     if (tid <= NB) {
@@ -412,7 +398,7 @@ select_kernel(Shape s, CacheView c, const void* __restrict__ q, const float* __r
       for (int i = 0; i < kSelWaves; ++i) tot_d += int(s_hist[i * (NB + 1) + tid]);
     }
     int C;
-    const int run = block_excl_scan(tot_d, sc, &C);
+    const int run = scan.excl(tot_d, &C);
     k_eff = min(a.kcap, C);
     if (tot_d > 0 && run < k_eff && k_eff <= run + tot_d) {
       s_pick[0] = tid;
@@ -420,41 +406,88 @@ select_kernel(Shape s, CacheView c, const void* __restrict__ q, const float* __r
     }
     __syncthreads();
     dstar = s_pick[0];
-    before = s_pick[1];
+    need_eq = k_eff - s_pick[1];
   }
-  const int need_eq = k_eff - before;
 
-  // ---- emit the selected tokens in ascending position (slots are in ascending t)
+  // ---- emit the selected tokens in ascending position (slots are in ascending t): one scan
+  // of the per-thread (#lt, #eq) counts places every slot.
   int32_t* out_idx = a.idx + size_t(bh) * a.kcap;
-  int run_eq = 0, run_sel = 0;
-  for (int base = 0; base < nslots; base += kSelThreads) {
-    const int slot = base + tid;
-    int t = 0, dd = 0xFFFF;
-    if (slot < nslots) {
-      if (cache_d) {
-        dd = s_dist[slot];
-        t = (s_pages[slot >> lgS] << lgS) + (slot & (s.S - 1));
+  int32_t* dbg_idx = dbg.token_idx ? dbg.token_idx + size_t(bh) * a.kcap : nullptr;
+  int run_lt = 0, run_eq = 0;
+  if (cache_d) {
+    const int nchunks = (nslots + kSelThreads * kEmitSPT - 1) / (kSelThreads * kEmitSPT);
+    for (int ch = 0; ch < nchunks; ++ch) {
+      const int s0 = (ch * kSelThreads + tid) * kEmitSPT;
+      uint32_t dv[kEmitSPT];
+      if (s0 < nslots) {
+        if constexpr (sizeof(DT) == 1) {
+          const uint4 x = *reinterpret_cast<const uint4*>(&s_dist[s0]);
+          const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+#pragma unroll
+          for (int u = 0; u < kEmitSPT; ++u) dv[u] = (wv[u >> 2] >> (8 * (u & 3))) & 0xFFu;
+        } else {
+          const uint4 x0 = *reinterpret_cast<const uint4*>(&s_dist[s0]);
+          const uint4 x1 = *reinterpret_cast<const uint4*>(&s_dist[s0 + 8]);
+          const uint32_t wv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
+#pragma unroll
+          for (int u = 0; u < kEmitSPT; ++u) dv[u] = (wv[u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
+        }
+#pragma unroll
+        for (int u = 0; u < kEmitSPT; ++u)
+          if (s0 + u >= nslots) dv[u] = kNone;
       } else {
-        dd = distance(slot, &t);
+#pragma unroll
+        for (int u = 0; u < kEmitSPT; ++u) dv[u] = kNone;
       }
+      int nlt = 0, neq = 0;
+#pragma unroll
+      for (int u = 0; u < kEmitSPT; ++u) {
+        nlt += dv[u] < uint32_t(dstar) ? 1 : 0;
+        neq += dv[u] == uint32_t(dstar) ? 1 : 0;
+      }
+      int tot;
+      const int ex = scan.excl((nlt << 16) | neq, &tot);
+      int eq_seen = run_eq + (ex & 0xFFFF);
+      int pos = run_lt + (ex >> 16) + min(eq_seen, need_eq);
+#pragma unroll
+      for (int u = 0; u < kEmitSPT; ++u) {
+        const bool is_eq = dv[u] == uint32_t(dstar);
+        const bool take = dv[u] < uint32_t(dstar) || (is_eq && eq_seen < need_eq);
+        eq_seen += is_eq ? 1 : 0;
+        if (take) {
+          const int t = slot_token(s0 + u);
+          out_idx[pos] = t;
+          if (dbg_idx) dbg_idx[pos] = t;
+          ++pos;
+        }
+      }
+      run_lt += tot >> 16;
+      run_eq += tot & 0xFFFF;
     }
-    const bool is_eq = dd == dstar;
-    const bool is_lt = dd < dstar;
-    int eq_tot;
-    const int eq_rank = run_eq + block_flag_prefix(is_eq, sc, &eq_tot);
-    const bool take = is_lt || (is_eq && eq_rank < need_eq);
-    int sel_tot;
-    const int pos = run_sel + block_flag_prefix(take, sc, &sel_tot);
-    if (take) {
-      out_idx[pos] = t;
-      if (dbg.token_idx) dbg.token_idx[size_t(bh) * a.kcap + pos] = t;
+  } else {
+    for (int base = 0; base < nslots; base += kSelThreads) {
+      const int slot = base + tid;
+      int t = 0;
+      uint32_t dd = kNone;
+      if (slot < nslots) {
+        t = slot_token(slot);
+        dd = distance(t);
+      }
+      const bool is_lt = dd < uint32_t(dstar), is_eq = dd == uint32_t(dstar);
+      int tot;
+      const int ex = scan.excl((int(is_lt) << 16) | int(is_eq), &tot);
+      const int eq_seen = run_eq + (ex & 0xFFFF);
+      const int pos = run_lt + (ex >> 16) + min(eq_seen, need_eq);
+      if (is_lt || (is_eq && eq_seen < need_eq)) {
+        out_idx[pos] = t;
+        if (dbg_idx) dbg_idx[pos] = t;
+      }
+      run_lt += tot >> 16;
+      run_eq += tot & 0xFFFF;
     }
-    run_eq += eq_tot;
-    run_sel += sel_tot;
   }
   if (tid == 0) {
     a.cnt[bh] = k_eff;
-    a.tickets[bh] = 0;
     if (dbg.token_count) dbg.token_count[bh] = k_eff;
   }
 }
@@ -490,8 +523,7 @@ __device__ __forceinline__ void unpack(const uint4& x, float (&f)[4]) {
 struct AttnArgs {
   const int32_t* idx;
   const int32_t* cnt;
-  float* part;        // [B][Hq][nsplit][kD + 2]
-  uint32_t* tickets;  // [B][Hq]
+  float* part;        // [B][Hq][nsplit][kD + 2]: o[0..127], m, l
   int kcap, nsplit;
   float scale_log2e;
 };
@@ -499,7 +531,7 @@ struct AttnArgs {
 template <int BF16>
 __global__ void __launch_bounds__(256)
 attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
-            const void* __restrict__ q, AttnArgs a, float* __restrict__ out) {
+            const void* __restrict__ q, AttnArgs a) {
   using A = AttnShape<BF16>;
   constexpr int EPL = A::EPL, LPR = A::LPR, RPI = A::RPI, ITER = A::ITER;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / s.G;
@@ -509,87 +541,109 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
   const int rg = lane / LPR, sub = lane % LPR;
   const int row0 = split * A::CHUNK + w * A::RPW;
   const size_t esz = BF16 ? 2 : 4;
+  const bool live = split * A::CHUNK < count;   // uniform over the workgroup
 
-  float qv[EPL];
-#pragma unroll
-  for (int e = 0; e < EPL; ++e)
-    qv[e] = load_elem(q, size_t(bh) * kD + sub * EPL + e, s.q_bf16) * a.scale_log2e;
-
-  const size_t kvrow0 = (size_t(b) * s.Hkv + g) * s.Lmax;
-  const int32_t* ib = a.idx + size_t(bh) * a.kcap;
-  int tok[ITER];
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    const int r = row0 + it * RPI + rg;
-    // indices come from select_kernel and are < seq_len; the clamp only keeps any reader in
-    // bounds of the cache
-    tok[it] = (r < count) ? min(max(ib[r], 0), s.Lmax - 1) : -1;
-  }
-  uint4 kr[ITER], vr[ITER];
-  const char* Kc = static_cast<const char*>(K);
-  const char* Vc = static_cast<const char*>(V);
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    if (tok[it] >= 0) {
-      const size_t off = ((kvrow0 + size_t(tok[it])) * kD + sub * EPL) * esz;
-      kr[it] = *reinterpret_cast<const uint4*>(Kc + off);
-      vr[it] = *reinterpret_cast<const uint4*>(Vc + off);
-    } else {
-      kr[it] = vr[it] = make_uint4(0u, 0u, 0u, 0u);
-    }
-  }
-
-  // logits (log2 domain)
-  float sc[ITER];
-  float mx = -INFINITY;
-#pragma unroll
-  for (int it = 0; it < ITER; ++it) {
-    float f[EPL];
-    unpack(kr[it], f);
-    float d = 0.f;
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) d = fmaf(qv[e], f[e], d);
-#pragma unroll
-    for (int o = LPR / 2; o >= 1; o >>= 1) d += __shfl_xor(d, o);
-    sc[it] = (tok[it] >= 0) ? d : -INFINITY;
-    mx = fmaxf(mx, sc[it]);
-  }
   __shared__ float s_m[4], s_l[4];
   __shared__ float s_o[4][kD];
-  __shared__ int s_last;
-  mx = wave_max(mx);
-  if (lane == 0) s_m[w] = mx;
-  __syncthreads();
-  const float M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
 
+  float M = -INFINITY;
   float l = 0.f;
   float o[EPL];
 #pragma unroll
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
-  if (M != -INFINITY) {
+
+  if (live) {
+    // query slice (scaled into the log2 domain)
+    float qv[EPL];
+    const size_t qo = size_t(bh) * kD + sub * EPL;
+    if (s.q_bf16) {
+      if constexpr (EPL == 8) {
+        float f[8];
+        unpack(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + qo), f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = f[e];
+      } else {
+        const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q) + qo);
+        qv[0] = __uint_as_float(x.x << 16); qv[1] = __uint_as_float(x.x & 0xFFFF0000u);
+        qv[2] = __uint_as_float(x.y << 16); qv[3] = __uint_as_float(x.y & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4) {
+        const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(q) + qo + e);
+        qv[e] = x.x; qv[e + 1] = x.y; qv[e + 2] = x.z; qv[e + 3] = x.w;
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[e] *= a.scale_log2e;
+
+    // selected rows: indices first (no branches, so all loads stay in flight together)
+    const size_t kvrow0 = (size_t(b) * s.Hkv + g) * s.Lmax;
+    const int32_t* ib = a.idx + size_t(bh) * a.kcap;
+    int tok[ITER];
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) tok[it] = ib[min(row0 + it * RPI + rg, count - 1)];
+    uint4 kr[ITER], vr[ITER];
+    const char* Kc = static_cast<const char*>(K);
+    const char* Vc = static_cast<const char*>(V);
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
-      const float p = (tok[it] >= 0) ? exp2f(sc[it] - M) : 0.f;
+      // indices come from select_kernel and are < seq_len; the clamp only keeps any reader in
+      // bounds of the cache
+      const int t = min(max(tok[it], 0), s.Lmax - 1);
+      const size_t off = ((kvrow0 + size_t(t)) * kD + sub * EPL) * esz;
+      kr[it] = *reinterpret_cast<const uint4*>(Kc + off);
+      vr[it] = *reinterpret_cast<const uint4*>(Vc + off);
+    }
+    // keep all 2 x ITER row loads in flight before the first use
+    __builtin_amdgcn_sched_barrier(0);
+
+    // logits (log2 domain)
+    float sc[ITER];
+    float mx = -INFINITY;
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      float f[EPL];
+      unpack(kr[it], f);
+      float d = 0.f;
+#pragma unroll
+      for (int e = 0; e < EPL; ++e) d = fmaf(qv[e], f[e], d);
+#pragma unroll
+      for (int off = LPR / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      sc[it] = (row0 + it * RPI + rg < count) ? d : -INFINITY;
+      mx = fmaxf(mx, sc[it]);
+    }
+    mx = wave_max(mx);
+    if (lane == 0) s_m[w] = mx;
+    __syncthreads();
+    M = fmaxf(fmaxf(s_m[0], s_m[1]), fmaxf(s_m[2], s_m[3]));
+#pragma unroll
+    for (int it = 0; it < ITER; ++it) {
+      const float p = (sc[it] == -INFINITY) ? 0.f : exp2f(sc[it] - M);
       l += p;
       float f[EPL];
       unpack(vr[it], f);
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, f[e], o[e]);
     }
-  }
-  // reduce across the row groups of the wave (lanes that share `sub`)
+    // reduce across the row groups of the wave (lanes that share `sub`)
 #pragma unroll
-  for (int off = LPR; off < kWave; off <<= 1) {
-    l += __shfl_xor(l, off);
+    for (int off = LPR; off < kWave; off <<= 1) {
+      l += __shfl_xor(l, off);
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], off);
-  }
-  if (rg == 0) {
+      for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], off);
+    }
+    if (rg == 0) {
 #pragma unroll
-    for (int e = 0; e < EPL; ++e) s_o[w][sub * EPL + e] = o[e];
-    if (sub == 0) s_l[w] = l;
+      for (int e = 0; e < EPL; ++e) s_o[w][sub * EPL + e] = o[e];
+      if (sub == 0) s_l[w] = l;
+    }
+    __syncthreads();
+  } else {
+    for (int i = threadIdx.x; i < 4 * kD; i += blockDim.x) s_o[i / kD][i % kD] = 0.f;
+    if (threadIdx.x < 4) s_l[threadIdx.x] = 0.f;
+    __syncthreads();
   }
-  __syncthreads();
   float* pp = a.part + (size_t(bh) * a.nsplit + split) * (kD + 2);
   if (threadIdx.x < kD) {
     const int d = threadIdx.x;
@@ -599,31 +653,46 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
     pp[kD] = M;
     pp[kD + 1] = s_l[0] + s_l[1] + s_l[2] + s_l[3];
   }
-  __threadfence();
-  __syncthreads();
-  if (threadIdx.x == 0) s_last = (atomicAdd(&a.tickets[bh], 1u) == uint32_t(a.nsplit - 1));
-  __syncthreads();
-  if (!s_last) return;
-  __threadfence();
-  if (threadIdx.x < kD) {
-    const int d = threadIdx.x;
-    const float* pb = a.part + size_t(bh) * a.nsplit * (kD + 2);
-    float Mx = -INFINITY;
-    for (int i = 0; i < a.nsplit; ++i) Mx = fmaxf(Mx, pb[i * (kD + 2) + kD]);
-    float Ls = 0.f, Os = 0.f;
-    if (Mx != -INFINITY) {
-      for (int i = 0; i < a.nsplit; ++i) {
-        const float* pi = pb + i * (kD + 2);
-        const float li = pi[kD + 1];
-        if (li > 0.f) {
-          const float f = exp2f(pi[kD] - Mx);
-          Ls = fmaf(li, f, Ls);
-          Os = fmaf(pi[d], f, Os);
-        }
+}
+
+// Merge of the split partials of one (b, h): o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
+// Partials are read in batches of 16 with no branch between the loads of a batch; an empty
+// partial has m = -inf and l = 0 and contributes nothing.
+__global__ void __launch_bounds__(kD)
+combine_kernel(const float* __restrict__ part, int nsplit, float* __restrict__ out) {
+  constexpr int CB = 16;
+  const int bh = blockIdx.x, d = threadIdx.x;
+  const float* pb = part + size_t(bh) * nsplit * (kD + 2);
+  float Mx = -INFINITY, Ls = 0.f, Os = 0.f;
+  for (int i0 = 0; i0 < nsplit; i0 += CB) {
+    float m[CB], l[CB], o[CB];
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      const float* pi = pb + size_t(min(i0 + u, nsplit - 1)) * (kD + 2);
+      m[u] = pi[kD];
+      l[u] = pi[kD + 1];
+      o[u] = pi[d];
+    }
+    float bm = Mx;
+#pragma unroll
+    for (int u = 0; u < CB; ++u)
+      if (i0 + u < nsplit) bm = fmaxf(bm, m[u]);
+    if (bm == -INFINITY) continue;
+    // rescale what has been summed so far to the new maximum, then add this batch
+    const float f0 = (Mx == -INFINITY) ? 0.f : exp2f(Mx - bm);
+    Ls *= f0;
+    Os *= f0;
+#pragma unroll
+    for (int u = 0; u < CB; ++u) {
+      if (i0 + u < nsplit && l[u] > 0.f) {
+        const float f = exp2f(m[u] - bm);
+        Ls = fmaf(l[u], f, Ls);
+        Os = fmaf(o[u], f, Os);
       }
     }
-    out[size_t(bh) * kD + d] = (Ls > 0.f) ? Os / Ls : 0.f;
+    Mx = bm;
   }
+  out[size_t(bh) * kD + d] = (Ls > 0.f) ? Os / Ls : 0.f;
 }
 
 // ---------------------------------------------------------------------------------------------
@@ -640,80 +709,90 @@ DecodePlan plan_decode(const Shape& s, double rho, int k, float scale) {
   p.scale = scale;
   const size_t BH = size_t(s.B) * s.Hq;
   size_t off = 0;
+  p.off_qrot = off;   off = align256(off + BH * kD * sizeof(float));
+  p.off_qcode = off;  off = align256(off + BH * s.NW * sizeof(uint32_t));
   p.off_U = off;      off = align256(off + BH * s.Pmax * sizeof(float));
   p.off_idx = off;    off = align256(off + BH * p.kcap * sizeof(int32_t));
   p.off_cnt = off;    off = align256(off + BH * sizeof(int32_t));
-  p.off_ticket = off; off = align256(off + BH * sizeof(uint32_t));
   p.off_part = off;   off = align256(off + BH * p.nsplit * (kD + 2) * sizeof(float));
   p.total = off;
   return p;
 }
 
 template <int G>
-static void launch_bound_t(const Shape& s, const CacheView& c, const void* q, const float* R,
-                           float* U, const DebugView& dbg, hipStream_t st) {
+static void launch_bound_t(const Shape& s, const CacheView& c, const float* qrot, float* U,
+                           const DebugView& dbg, hipStream_t st) {
   dim3 grid((s.Pmax + kBoundPages - 1) / kBoundPages, s.Hkv, s.B);
   hipLaunchKernelGGL((page_bound_kernel<G>), grid, dim3(kBoundThreads), 0, st, s, c.pmin, c.pmax,
-                     c.seq_lens, q, R, U, dbg.bounds, dbg.q_rot);
+                     c.seq_lens, qrot, U, dbg.bounds);
 }
 
 template <int NB, int EPT>
-static void launch_select_t(const Shape& s, const CacheView& c, const void* q, const float* W,
-                            const SelectArgs& a, const DebugView& dbg, hipStream_t st) {
+static void launch_select_t(const Shape& s, const CacheView& c, const SelectArgs& a,
+                            const DebugView& dbg, hipStream_t st) {
   hipLaunchKernelGGL((select_kernel<NB, EPT>), dim3(s.Hq, s.B), dim3(kSelThreads), 0, st, s, c,
-                     q, W, a, dbg);
+                     a, dbg);
 }
 
 template <int NB>
-static void launch_select_nb(const Shape& s, const CacheView& c, const void* q, const float* W,
-                             const SelectArgs& a, const DebugView& dbg, hipStream_t st) {
+static void launch_select_nb(const Shape& s, const CacheView& c, const SelectArgs& a,
+                             const DebugView& dbg, hipStream_t st) {
   const int ept = (s.Pmax + kSelThreads - 1) / kSelThreads;
-  if (ept <= 1) launch_select_t<NB, 1>(s, c, q, W, a, dbg, st);
-  else if (ept <= 2) launch_select_t<NB, 2>(s, c, q, W, a, dbg, st);
-  else if (ept <= 4) launch_select_t<NB, 4>(s, c, q, W, a, dbg, st);
-  else if (ept <= 8) launch_select_t<NB, 8>(s, c, q, W, a, dbg, st);
-  else launch_select_t<NB, 16>(s, c, q, W, a, dbg, st);
+  if (ept <= 1) launch_select_t<NB, 1>(s, c, a, dbg, st);
+  else if (ept <= 2) launch_select_t<NB, 2>(s, c, a, dbg, st);
+  else if (ept <= 4) launch_select_t<NB, 4>(s, c, a, dbg, st);
+  else if (ept <= 8) launch_select_t<NB, 8>(s, c, a, dbg, st);
+  else launch_select_t<NB, 16>(s, c, a, dbg, st);
 }
 
-hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c, const void* q,
-                         const float* R, const float* W, void* ws, float* out,
-                         const DebugView& dbg, hipStream_t st) {
+hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c,
+                         const void* k_new, const void* v_new, const void* q, const float* R,
+                         const float* W, void* ws, float* out, const DebugView& dbg,
+                         hipStream_t st) {
   char* base = static_cast<char*>(ws);
+  float* qrot = reinterpret_cast<float*>(base + p.off_qrot);
+  uint32_t* qcode = reinterpret_cast<uint32_t*>(base + p.off_qcode);
   float* U = reinterpret_cast<float*>(base + p.off_U);
   int32_t* idx = reinterpret_cast<int32_t*>(base + p.off_idx);
   int32_t* cnt = reinterpret_cast<int32_t*>(base + p.off_cnt);
-  uint32_t* tick = reinterpret_cast<uint32_t*>(base + p.off_ticket);
   float* part = reinterpret_cast<float*>(base + p.off_part);
-
   hipError_t e = hipSuccess;
-  if (dbg.events && (e = hipEventRecord(dbg.events[0], st)) != hipSuccess) return e;
+#define HHR_MARK(i) \
+  if (dbg.events && (e = hipEventRecord(dbg.events[i], st)) != hipSuccess) return e;
+#define HHR_CHECK() \
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+
+  HHR_MARK(0);
+  e = launch_prep(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg.q_rot, dbg.q_code, st);
+  if (e != hipSuccess) return e;
+  HHR_MARK(1);
   switch (s.G) {
-    case 1: launch_bound_t<1>(s, c, q, R, U, dbg, st); break;
-    case 2: launch_bound_t<2>(s, c, q, R, U, dbg, st); break;
-    case 4: launch_bound_t<4>(s, c, q, R, U, dbg, st); break;
-    default: launch_bound_t<8>(s, c, q, R, U, dbg, st); break;
+    case 1: launch_bound_t<1>(s, c, qrot, U, dbg, st); break;
+    case 2: launch_bound_t<2>(s, c, qrot, U, dbg, st); break;
+    case 4: launch_bound_t<4>(s, c, qrot, U, dbg, st); break;
+    default: launch_bound_t<8>(s, c, qrot, U, dbg, st); break;
   }
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (dbg.events && (e = hipEventRecord(dbg.events[1], st)) != hipSuccess) return e;
-
-  SelectArgs sa{U, idx, cnt, tick, p.rho, p.kcap};
-  if (s.NB == 128) launch_select_nb<128>(s, c, q, W, sa, dbg, st);
-  else launch_select_nb<256>(s, c, q, W, sa, dbg, st);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (dbg.events && (e = hipEventRecord(dbg.events[2], st)) != hipSuccess) return e;
-
-  AttnArgs aa{idx, cnt, part, tick, p.kcap, p.nsplit, p.scale * 1.4426950408889634f};
+  HHR_CHECK();
+  HHR_MARK(2);
+  SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap};
+  if (s.NB == 128) launch_select_nb<128>(s, c, sa, dbg, st);
+  else launch_select_nb<256>(s, c, sa, dbg, st);
+  HHR_CHECK();
+  HHR_MARK(3);
+  AttnArgs aa{idx, cnt, part, p.kcap, p.nsplit, p.scale * 1.4426950408889634f};
   dim3 grid(p.nsplit, s.Hq, s.B);
   if (s.kv_bf16)
-    hipLaunchKernelGGL((attn_kernel<1>), grid, dim3(256), 0, st, s, c.K, c.V, q, aa, out);
+    hipLaunchKernelGGL((attn_kernel<1>), grid, dim3(256), 0, st, s, c.K, c.V, q, aa);
   else
-    hipLaunchKernelGGL((attn_kernel<0>), grid, dim3(256), 0, st, s, c.K, c.V, q, aa, out);
-  e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  if (dbg.events) e = hipEventRecord(dbg.events[3], st);
-  return e;
+    hipLaunchKernelGGL((attn_kernel<0>), grid, dim3(256), 0, st, s, c.K, c.V, q, aa);
+  HHR_CHECK();
+  HHR_MARK(4);
+  hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(kD), 0, st, part, p.nsplit, out);
+  HHR_CHECK();
+  HHR_MARK(5);
+#undef HHR_MARK
+#undef HHR_CHECK
+  return hipSuccess;
 }
 
 }  // namespace hhr

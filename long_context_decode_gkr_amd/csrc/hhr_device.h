@@ -127,6 +127,64 @@ __device__ __forceinline__ uint32_t lanes_below(uint64_t mask) {
   return __builtin_amdgcn_mbcnt_hi(uint32_t(mask >> 32), __builtin_amdgcn_mbcnt_lo(uint32_t(mask), 0u));
 }
 
+// ---- DPP (data-parallel primitives): cross-lane moves at ALU latency, no LDS round trip.
+// Controls (gfx9 encoding): quad_perm, row_shr:n = 0x110 + n, row_mirror = 0x140,
+// row_half_mirror = 0x141, row_bcast:15 = 0x142, row_bcast:31 = 0x143. Lanes whose source is
+// outside the row keep `old` (bound_ctrl off), which the scans set to the identity.
+template <int CTRL, int ROW_MASK = 0xf>
+__device__ __forceinline__ int dpp_i(int old, int v) {
+  return __builtin_amdgcn_update_dpp(old, v, CTRL, ROW_MASK, 0xf, false);
+}
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float v) {
+  return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xf, 0xf, false));
+}
+
+// Inclusive prefix sum over the 64 lanes of the wave.
+__device__ __forceinline__ int wave_incl_sum(int v) {
+  v += dpp_i<0x111>(0, v);
+  v += dpp_i<0x112>(0, v);
+  v += dpp_i<0x114>(0, v);
+  v += dpp_i<0x118>(0, v);
+  v += dpp_i<0x142, 0xa>(0, v);
+  v += dpp_i<0x143, 0xc>(0, v);
+  return v;
+}
+
+// Sum / min / max over the wave, returned in every lane (through lane 63).
+__device__ __forceinline__ int wave_total(int v) {
+  return __builtin_amdgcn_readlane(wave_incl_sum(v), 63);
+}
+__device__ __forceinline__ uint32_t wave_min_u32(uint32_t v) {
+  const int big = int(0xFFFFFFFFu);
+  v = min(v, uint32_t(dpp_i<0x111>(big, int(v))));
+  v = min(v, uint32_t(dpp_i<0x112>(big, int(v))));
+  v = min(v, uint32_t(dpp_i<0x114>(big, int(v))));
+  v = min(v, uint32_t(dpp_i<0x118>(big, int(v))));
+  v = min(v, uint32_t(dpp_i<0x142, 0xa>(big, int(v))));
+  v = min(v, uint32_t(dpp_i<0x143, 0xc>(big, int(v))));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, uint32_t(dpp_i<0x111>(0, int(v))));
+  v = max(v, uint32_t(dpp_i<0x112>(0, int(v))));
+  v = max(v, uint32_t(dpp_i<0x114>(0, int(v))));
+  v = max(v, uint32_t(dpp_i<0x118>(0, int(v))));
+  v = max(v, uint32_t(dpp_i<0x142, 0xa>(0, int(v))));
+  v = max(v, uint32_t(dpp_i<0x143, 0xc>(0, int(v))));
+  return uint32_t(__builtin_amdgcn_readlane(int(v), 63));
+}
+
+// Sum over each row of 16 lanes, returned in every lane of the row (butterfly: quad
+// exchanges, then half-row and row mirrors).
+__device__ __forceinline__ float row16_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
+  v += dpp_f<0x140>(v);  // row_mirror
+  return v;
+}
+
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
   for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));

@@ -31,7 +31,7 @@ struct DebugView {
   uint16_t* dist;
   int32_t* token_idx;
   int32_t* token_count;
-  hipEvent_t* events;  // NULL or 4 events around the three decode kernels
+  hipEvent_t* events;  // NULL or 6 events around the five decode kernels
 };
 
 // Workspace carve-up of one decode call (byte offsets from the workspace base).
@@ -41,7 +41,7 @@ struct DecodePlan {
   int nsplit;      // attention workgroups per (b, h)
   double rho;
   float scale;
-  size_t off_U, off_idx, off_cnt, off_ticket, off_part, total;
+  size_t off_qrot, off_qcode, off_U, off_idx, off_cnt, off_part, total;
 };
 
 DecodePlan plan_decode(const Shape& s, double rho, int k, float scale);
@@ -50,10 +50,15 @@ hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R,
                              hipStream_t st);
 hipError_t launch_build_mfma(const Shape& s, const CacheView& c, const float* R, const float* W,
                              hipStream_t st);
-hipError_t launch_append(const Shape& s, const CacheView& c, const void* k_new,
-                         const void* v_new, const float* R, const float* W, hipStream_t st);
-hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c, const void* q,
-                         const float* R, const float* W, void* ws, float* out,
-                         const DebugView& dbg, hipStream_t st);
+// Optional append of one token (k_new != NULL) and preparation of the queries (q != NULL):
+// q~ into qrot [B][Hq][128], query codes into qcode [B][Hq][NW].
+hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, const void* v_new,
+                       const void* q, const float* R, const float* W, float* qrot,
+                       uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, hipStream_t st);
+// The decode step, preceded by an append when k_new != NULL.
+hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c,
+                         const void* k_new, const void* v_new, const void* q, const float* R,
+                         const float* W, void* ws, float* out, const DebugView& dbg,
+                         hipStream_t st);
 
 }  // namespace hhr

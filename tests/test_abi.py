@@ -113,3 +113,15 @@ def test_workspace_size_grows_with_shapes():
     assert 0 < a < b < c
     # U + indices + counters + split partials: at least the bounds and the token indices
     assert b >= 32 * (131072 // 16) * 4 + 32 * 2048 * 4
+
+
+def test_append_decode_needs_new_token_and_ticket():
+    lib = hb.load()
+    d, p = good_dims(), hb.Params(0.125, 2048, 0.0)
+
+    def call(cache, kn=FAKE, vn=FAKE):
+        return lib.hhr_append_decode(ctypes.byref(d), ctypes.byref(p), ctypes.byref(cache), kn, vn,
+                                     FAKE, FAKE, FAKE, FAKE * 256, 1 << 40, FAKE, None, None)
+    assert call(fake_cache(), kn=None) == 1
+    assert call(fake_cache(), vn=None) == 1
+    assert call(fake_cache(append_ticket=None)) == 1

@@ -187,3 +187,29 @@ def test_append_at_capacity_is_a_no_op():
     torch.cuda.synchronize()
     assert int(lay.cache.seq_lens[0]) == 64
     assert torch.equal(before, lay.cache.codes)
+
+
+def test_append_decode_equals_append_then_decode():
+    torch = _torch()
+    cfg = _cfg(3, 4000, n_plant=8)
+    a = hc.GpuLayer(cfg, max_seq_len=4096)
+    a.build(method="fp64")
+    b = hc.GpuLayer(cfg, data={k: (v.copy() if hasattr(v, "copy") else v) for k, v in a.data.items()})
+    b.build(method="fp64")
+    kn, vn = synth.append_tokens(cfg, 3)
+    dec_a = hb.Decoder(a.dims, 1 / 16, 300)
+    dec_b = hb.Decoder(b.dims, 1 / 16, 300)
+    for i in range(3):
+        k_i, v_i = hc.to_dev(kn[i], a.tdt), hc.to_dev(vn[i], a.tdt)
+        oa = torch.empty((1, 32, 128), dtype=torch.float32, device="cuda")
+        ob = torch.empty_like(oa)
+        da, db = hb.Debug(a.dims, 300), hb.Debug(b.dims, 300)
+        hb.append(a.cache, k_i, v_i, a.R, a.W)
+        dec_a(a.cache, a.q, a.R, a.W, oa, da)
+        dec_b(b.cache, b.q, b.R, b.W, ob, db, k_new=k_i, v_new=v_i)
+        torch.cuda.synchronize()
+        assert torch.equal(oa, ob)
+        assert torch.equal(da.token_idx, db.token_idx) and torch.equal(da.q_code, db.q_code)
+    for name in ("K", "V", "page_min", "page_max", "codes", "seq_lens", "append_ticket"):
+        assert torch.equal(getattr(a.cache, name), getattr(b.cache, name)), name
+    assert int(b.cache.seq_lens[0]) == 4003
