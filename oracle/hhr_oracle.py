@@ -30,14 +30,12 @@ Readings where the paper is silent (each one also listed in the design notes):
 * Page extrema are fp32 values of the fp32-rounded rotated keys; a partial last page covers
   only its valid tokens.
 
-Precision: fp64 throughout, with an exact rational fallback for code signs whose fp64 value
-is within its rounding-error bound of zero.
+Precision: fp64 throughout, with an exact fallback (math.fsum of the exact fp64 products) for
+code signs whose fp64 value is within its rounding-error bound of zero.
 """
 from __future__ import annotations
 
 import math
-from fractions import Fraction
-
 import numpy as np
 
 U64 = 2.0 ** -53  # unit roundoff of IEEE double
@@ -75,11 +73,13 @@ def page_extrema(kt: np.ndarray, L: int, S: int):
 # §3.1 Eq. (1), §3.3.2 Eq. (10): sign codes
 # ----------------------------------------------------------------------------------------------
 def _exact_positive(x_row: np.ndarray, w_col: np.ndarray) -> bool:
-    """Is sum_j x_j w_j > 0, computed exactly with rationals?"""
-    total = Fraction(0)
-    for a, b in zip(x_row.tolist(), w_col.tolist()):
-        total += Fraction(a) * Fraction(b)
-    return total > 0
+    """Is sum_j x_j w_j > 0 for the exact real value?
+
+    Each product of two fp32 values is exact in fp64 (at most 48 significant bits, exponent
+    within range), and math.fsum returns the correctly rounded value of the exact sum of its
+    arguments, whose sign is the sign of the exact sum (0.0 exactly when the sum is 0).
+    """
+    return math.fsum(float(a) * float(b) for a, b in zip(x_row.tolist(), w_col.tolist())) > 0.0
 
 
 def sign_bits(x: np.ndarray, W: np.ndarray) -> np.ndarray:

@@ -7,7 +7,6 @@ library routine that a special case reduces to. Runs on the CPU only.
 import json
 import math
 import os
-from fractions import Fraction
 
 import numpy as np
 import pytest
