@@ -81,6 +81,7 @@ hhr_status hhr_build_pages(const hhr_dims* dims, const hhr_cache* cache, const f
   if ((st = check_cache(cache, false, &c)) != HHR_OK) return st;
   if (!R || !W) return HHR_ERR_INVALID_ARG;
   hipStream_t hs = reinterpret_cast<hipStream_t>(stream);
+  if (s.kv_bf16) return hip_status(launch_build_mfma(s, c, R, W, hs));
   return hip_status(launch_build_fp64(s, c, R, W, hs));
 }
 

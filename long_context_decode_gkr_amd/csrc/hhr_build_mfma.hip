@@ -1,0 +1,243 @@
+// Index build on the matrix cores (MFMA) for bf16 keys.
+//
+// Method: "HHR: Hierarchical Hash Retrieval for Efficient LLM Generation", §3.3.1 (page extrema of
+// the rotated keys k~ = k R, Eq. 4) and §3.1 Eq. 1 / §3.3.2 Eq. 10 (key code = sign of z = k W).
+// Both are one GEMM of the key tile against [R_g | W_g], done with v_mfma_f32_32x32x16_bf16.
+//
+// Precision. The keys are bf16, so they are exact MFMA A operands. The fp32 R and W are split
+// into bf16 pieces (R = r1 + r2 + r3 to ~2^-27, W = w1 + w2 to ~2^-18 relative); every
+// bf16 x bf16 product is exact in fp32 and the MFMA accumulates in fp32.
+//   * Rotation: k~ carries fp32 accumulation error only (a few ulps of |k|); the page extrema
+//     are taken from it.
+//   * Codes: a bit is accepted when |z| > tau = 2^-13 |k|_2 |w_c|_2. By Cauchy-Schwarz the
+//     accumulated error is at most about 256 * 2^-23 + 2^-18 <= 2^-14.9 times |k|_2 |w_c|_2,
+//     so tau has a margin of ~4x. Bits inside tau (about 1e-3 of them for Gaussian data) are
+//     queued in LDS and recomputed from the stored operands in fp64 (exact products), with
+//     the exact long accumulator behind that: every code equals the sign of the exact z.
+//
+// Grid (tiles x roles, Hkv, B): role 0 = rotation and page extrema, role 1 + s = code words
+// [4 s, 4 s + 4) (128 code columns). A workgroup of 4 waves covers 512 tokens; each wave walks
+// 32-token sub-tiles: 8 A fragments (one 16-byte load each per lane) are reused against all
+// 4 column tiles x 8 k-steps x pieces, B fragments come from LDS.
+#include "hhr_device.h"
+#include "hhr_launch.h"
+
+namespace hhr {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kMTok = 512;            // tokens per workgroup
+constexpr int kMThreads = 256;
+constexpr int kBStride = kD + 8;      // padded k-stride of a transposed B column (bf16 elements)
+constexpr int kFbCap = 2048;          // queued uncertain code bits per workgroup
+constexpr float kCertScale = 1.0f / 8192.0f;   // 2^-13
+
+// One stored bf16 key row, read as fp32 values.
+struct Bf16Row {
+  const uint16_t* p;
+  __device__ __forceinline__ float operator[](int j) const { return bf16_bits_to_f32(p[j]); }
+};
+
+__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
+  const uint32_t u = __float_as_uint(x);
+  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
+}
+
+template <int S>
+__global__ void __launch_bounds__(kMThreads)
+build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float* __restrict__ W,
+                  int ntiles) {
+  const int role = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+  const int g = blockIdx.y, b = blockIdx.z;
+  const int L = min(max(c.seq_lens[b], 0), s.Lmax);
+  const int t0 = tile * kMTok;
+  if (t0 >= L) return;
+  const int ntok = min(kMTok, L - t0);
+  const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  const int npieces = role == 0 ? 3 : 2;
+
+  __shared__ __align__(16) uint16_t Bt[3][kD][kBStride];     // Bt[piece][n][k]
+  __shared__ float stage_f[2][kD][kMTok / 16];               // page min / max (role 0)
+  __shared__ uint32_t stage_c[kMTok][4];                     // code words (role > 0)
+  __shared__ float wnorm[kD];
+  __shared__ uint32_t fb_list[kFbCap];
+  __shared__ int fb_n;
+
+  // ---- B operand: split the fp32 matrix into bf16 pieces, transposed (k contiguous)
+  const float* src = role == 0 ? R + size_t(g) * kD * kD
+                               : W + size_t(g) * kD * s.NB + (role - 1) * kD;
+  const int src_ld = role == 0 ? kD : s.NB;
+  for (int e = tid; e < kD * kD; e += kMThreads) {
+    const int k = e / kD, n = e % kD;
+    const float x = src[size_t(k) * src_ld + n];
+    const uint16_t p1 = f32_to_bf16_rne(x);
+    const float r1 = x - bf16_bits_to_f32(p1);
+    const uint16_t p2 = f32_to_bf16_rne(r1);
+    Bt[0][n][k] = p1;
+    Bt[1][n][k] = p2;
+    if (role == 0) Bt[2][n][k] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(p2));
+  }
+  if (role != 0 && tid < kD) {
+    double ss = 0.0;
+    for (int k = 0; k < kD; ++k) {
+      const double x = src[size_t(k) * src_ld + tid];
+      ss += x * x;
+    }
+    wnorm[tid] = float(sqrt(ss)) * (1.0f + 1e-6f);
+  }
+  if (tid == 0) fb_n = 0;
+  __syncthreads();
+
+  const size_t row0 = (size_t(b) * s.Hkv + g) * s.Lmax;
+  const uint16_t* Kb = reinterpret_cast<const uint16_t*>(c.K);
+  const int half = lane >> 5, col = lane & 31;
+
+  for (int st = w; st < kMTok / 32; st += kMThreads / kWave) {
+    const int tl0 = st * 32;                 // first token of the sub-tile (block-local)
+    if (tl0 >= ntok) break;
+    // A fragments: row tl0 + col, k = 16 ks + 8 half + 0..7
+    const int tr = t0 + tl0 + col;
+    const int trc = min(tr, L - 1);
+    bf16x8 a[8];
+    const uint4* ap = reinterpret_cast<const uint4*>(Kb + (row0 + trc) * kD + 8 * half);
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      const uint4 v = ap[2 * ks];
+      a[ks] = __builtin_bit_cast(bf16x8, v);
+    }
+    f32x16 acc[4];
+#pragma unroll
+    for (int nt = 0; nt < 4; ++nt)
+#pragma unroll
+      for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
+    for (int p = 0; p < npieces; ++p) {
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Bt[p][nt * 32 + col][16 * ks + 8 * half]);
+          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bv, acc[nt], 0, 0, 0);
+        }
+      }
+    }
+    // result rows of this lane: i(r) = 8 (r / 4) + 4 half + r % 4
+    if (role == 0) {
+      // ---- page extrema of k~ over the valid rows (pages are 16 or 32 rows of the sub-tile)
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int j = nt * 32 + col;
+        constexpr int PPS = 32 / S;            // pages per sub-tile
+#pragma unroll
+        for (int pp = 0; pp < PPS; ++pp) {
+          float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+          for (int r = pp * (16 / PPS); r < (pp + 1) * (16 / PPS); ++r) {
+            const int i = 8 * (r / 4) + 4 * half + (r % 4);
+            if (tl0 + i < ntok) {
+              lo = fminf(lo, acc[nt][r]);
+              hi = fmaxf(hi, acc[nt][r]);
+            }
+          }
+          lo = fminf(lo, __shfl_xor(lo, 32));
+          hi = fmaxf(hi, __shfl_xor(hi, 32));
+          if (half == 0) {
+            stage_f[0][j][tl0 / S + pp] = lo;
+            stage_f[1][j][tl0 / S + pp] = hi;
+          }
+        }
+      }
+    } else {
+      // ---- code bits: certified sign of z, or queued for the exact path
+      float xn2 = 0.f;
+#pragma unroll
+      for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const float v = float(a[ks][e]);
+          xn2 = fmaf(v, v, xn2);
+        }
+      xn2 += __shfl_xor(xn2, 32);
+      const float xnorm = sqrtf(xn2) * (1.0f + 1e-6f);   // |k_row|, row = tl0 + col
+#pragma unroll
+      for (int nt = 0; nt < 4; ++nt) {
+        const int lc = nt * 32 + col;                    // code column within the slice
+        const float wn = wnorm[lc];
+#pragma unroll
+        for (int r = 0; r < 16; ++r) {
+          const int i = 8 * (r / 4) + 4 * half + (r % 4);
+          const float xi = __shfl(xnorm, i);
+          const float tau = kCertScale * xi * wn;
+          const float z = acc[nt][r];
+          const bool valid = tl0 + i < ntok;
+          const bool sure = fabsf(z) > tau && xi * wn > 1e-30f;
+          bool bit = z > 0.f;
+          if (valid && !sure) {
+            const int pos = atomicAdd(&fb_n, 1);
+            if (pos < kFbCap) {
+              fb_list[pos] = (uint32_t(tl0 + i) << 8) | uint32_t(lc);
+            } else {
+              // queue full: decide this bit here
+              const uint16_t* kr = Kb + (row0 + t0 + tl0 + i) * kD;
+              const float* wc = W + size_t(g) * kD * s.NB + (role - 1) * kD + lc;
+              bit = certified_bit(Bf16Row{kr}, wc, s.NB) != 0;
+            }
+          }
+          const uint64_t m = __ballot(bit);
+          if (lane == 0) {
+            // bits 0..31 of the ballot are row i(r) of half 0, bits 32..63 row i(r) + 4
+            const int i0 = 8 * (r / 4) + (r % 4);
+            stage_c[tl0 + i0][nt] = uint32_t(m);
+            stage_c[tl0 + i0 + 4][nt] = uint32_t(m >> 32);
+          }
+        }
+      }
+    }
+  }
+  __syncthreads();
+
+  if (role == 0) {
+    // ---- write the page extrema: channel-major rows of this tile's pages
+    const int npg = (ntok + S - 1) / S;
+    const int pg0 = t0 / S;
+    const size_t sbase = (size_t(b) * s.Hkv + g) * kD;
+    for (int e = tid; e < kD * npg; e += kMThreads) {
+      const int j = e / npg, pl = e % npg;
+      c.pmin[(sbase + j) * s.Pmax + pg0 + pl] = stage_f[0][j][pl];
+      c.pmax[(sbase + j) * s.Pmax + pg0 + pl] = stage_f[1][j][pl];
+    }
+  } else {
+    // ---- exact path for the queued bits, then the code words
+    const int nfb = min(fb_n, kFbCap);
+    for (int e = tid; e < nfb; e += kMThreads) {
+      const uint32_t ent = fb_list[e];
+      const int tl = int(ent >> 8), lc = int(ent & 0xFFu);
+      const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
+      const float* wc = W + size_t(g) * kD * s.NB + (role - 1) * kD + lc;
+      const uint32_t bit = certified_bit(Bf16Row{kr}, wc, s.NB);
+      const uint32_t mask = 1u << (lc & 31);
+      if (bit) atomicOr(&stage_c[tl][lc >> 5], mask);
+      else atomicAnd(&stage_c[tl][lc >> 5], ~mask);
+    }
+    __syncthreads();
+    const int wbase = (role - 1) * 4;
+    for (int tl = tid; tl < ntok; tl += kMThreads) {
+      const uint4 v = make_uint4(stage_c[tl][0], stage_c[tl][1], stage_c[tl][2], stage_c[tl][3]);
+      *reinterpret_cast<uint4*>(c.codes + (row0 + t0 + tl) * s.NW + wbase) = v;
+    }
+  }
+}
+
+hipError_t launch_build_mfma(const Shape& s, const CacheView& c, const float* R, const float* W,
+                             hipStream_t st) {
+  const int ntiles = (s.Lmax + kMTok - 1) / kMTok;
+  const int nroles = 1 + s.NB / kD;
+  dim3 grid(ntiles * nroles, s.Hkv, s.B);
+  if (s.S == 16)
+    hipLaunchKernelGGL((build_mfma_kernel<16>), grid, dim3(kMThreads), 0, st, s, c, R, W, ntiles);
+  else
+    hipLaunchKernelGGL((build_mfma_kernel<32>), grid, dim3(kMThreads), 0, st, s, c, R, W, ntiles);
+  return hipGetLastError();
+}
+
+}  // namespace hhr

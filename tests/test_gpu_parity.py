@@ -213,3 +213,55 @@ def test_append_decode_equals_append_then_decode():
     for name in ("K", "V", "page_min", "page_max", "codes", "seq_lens", "append_ticket"):
         assert torch.equal(getattr(a.cache, name), getattr(b.cache, name)), name
     assert int(b.cache.seq_lens[0]) == 4003
+
+
+# ---------------------------------------------------------------------------------------------
+# Index build on the matrix cores (bf16 keys): codes bit-exact; page extrema carry fp32
+# accumulation error of a 128-term dot product (tolerance 8e-6 |k|_2, ~20 fp32 ulps of |k|)
+# ---------------------------------------------------------------------------------------------
+MFMA_EXTREMA_SCALE = 20.0
+
+
+@pytest.mark.parametrize("cfg_id,L,batch,lens", [(2, 5003, None, None), (3, 1500, None, None),
+                                                 (4, 3000, 3, [3000, 1, 2049]),
+                                                 (5, 2085, 2, None)])
+def test_build_mfma_matches_oracle(cfg_id, L, batch, lens):
+    _torch()
+    cfg = _cfg(cfg_id, L, batch=batch, lens=lens, n_plant=8)
+    lay = hc.GpuLayer(cfg, max_seq_len=L + 4 * cfg.page_size * 2)
+    lay.build(method="auto")
+    hc.check_index(lay, hc.oracle_index(lay), extrema_atol_scale=MFMA_EXTREMA_SCALE)
+
+
+def test_build_mfma_exact_path_for_zero_and_tiny_projections():
+    # 16 code columns give z = k0 - k1 = 0 exactly (k0 == k1), 8 give z = 2^-30 k2: all of them
+    # fall inside the certification band, which overflows the per-workgroup queue (8192 > 2048).
+    _torch()
+    cfg = _cfg(3, 2048, n_plant=0, num_q_heads=4, num_kv_heads=1)
+    data = synth.make_layer(cfg)
+    data["K"][:, :, :, 1] = data["K"][:, :, :, 0]
+    W = data["W"]
+    W[:, :, :24] = 0.0
+    W[:, 0, :24] = 1.0
+    W[:, 1, :24] = -1.0
+    W[:, 2, 16:24] = np.float32(2.0 ** -30)
+    lay = hc.GpuLayer(cfg, data=data)
+    lay.build(method="auto")
+    ref = hc.oracle_index(lay)
+    hc.check_index(lay, ref, extrema_atol_scale=MFMA_EXTREMA_SCALE)
+    bits0 = ref["codes"][0, :, :2048, 0]
+    assert np.all(bits0 & 0xFFFF == 0)                                     # z == 0 gives 0
+    k2pos = (data["K"][0, :, :2048, 2] > 0).astype(np.uint32)
+    assert np.array_equal((bits0 >> 16) & 0xFF, k2pos * 0xFF)              # sign of 2^-30 k2
+
+
+def test_decode_on_mfma_index_matches_oracle():
+    _torch()
+    cfg = _cfg(3, 9000, n_plant=16)
+    lay = hc.GpuLayer(cfg, max_seq_len=9024)
+    lay.build(method="auto")
+    ref = hc.oracle_index(lay)
+    hc.check_index(lay, ref, extrema_atol_scale=MFMA_EXTREMA_SCALE)
+    out, dbg = lay.decode(1 / 16, 512)
+    st = hc.check_decode(lay, out, dbg, 1 / 16, 512, ref_index=ref)
+    print(f"mfma index: max out rel err {st['max_out_rel']:.2e}, page swaps {st['swaps']}")
