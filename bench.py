@@ -15,7 +15,8 @@ warm-up steps then exactly K timed steps bracketed by torch.cuda.synchronize():
   2. replay of one captured HIP graph per layer instance: the headline us/step/layer.
 
 Prints ONE JSON line. Options: --gpus (must be 1), --steps, --warmup, --layers,
---no-cpu-baseline, --quiet.
+--no-cpu-baseline, --quiet, --copy-calibration (a 512 MiB device copy only, to scale the HBM
+byte counters of rocprofv3).
 """
 from __future__ import annotations
 
@@ -164,6 +165,19 @@ def cpu_baseline(cfg, data, quiet, budget_s=10.0):
                        f"{cfg.num_kv_heads} KV groups; index build untimed")}
 
 
+def copy_calibration(mib=512, reps=3):
+    """A plain device-to-device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
+    counters: each launch reads and writes exactly `mib` MiB."""
+    import torch
+    n = mib * 1024 * 1024 // 4
+    src = torch.ones(n, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_per_launch": n * 4, "launches": reps}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__.splitlines()[0])
     ap.add_argument("--gpus", type=int, default=1)
@@ -172,7 +186,12 @@ def main():
     ap.add_argument("--layers", type=int, default=8)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--quiet", action="store_true")
+    ap.add_argument("--copy-calibration", action="store_true",
+                    help="only run a 512 MiB device copy (for HBM counter scaling)")
     args = ap.parse_args()
+    if args.copy_calibration:
+        copy_calibration()
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: the HHR decode path has no multi-GPU mode "
               "(it would shard by KV head with no exchange); run with --gpus 1", file=sys.stderr)

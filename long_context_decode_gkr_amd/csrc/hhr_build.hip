@@ -149,19 +149,6 @@ constexpr int kPrepSlices = 4;
 constexpr int kPrepParts = 8;
 constexpr int kMaxVec = 9;   // 1 key + up to 8 queries
 
-// Sum over each aligned group of 8 lanes (quad exchanges, then the half-row mirror).
-__device__ __forceinline__ double group8_sum(double v) {
-  auto step = [](double x, auto ctrl) {
-    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), decltype(ctrl)::value, 0xf, 0xf, false);
-    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), decltype(ctrl)::value, 0xf, 0xf, false);
-    return x + __hiloint2double(hi, lo);
-  };
-  v = step(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
-  v = step(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
-  v = step(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
-  return v;
-}
-
 template <int NB>
 __global__ void __launch_bounds__(256 + kPrepParts * NB / kPrepSlices)
 prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __restrict__ vn,
@@ -226,7 +213,7 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
 #pragma unroll
         for (int i = 0; i < T; ++i) a += double(x[i]) * double(rv[i]);
       }
-      acc[v] = group8_sum(a);
+      acc[v] = group_sum_f64<3>(a);
     }
     if (part == 0) {
       if (app) {
@@ -271,8 +258,8 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
           ss += fabs(pr);
         }
       }
-      z[v] = group8_sum(zz);
-      sa[v] = group8_sum(ss);
+      z[v] = group_sum_f64<3>(zz);
+      sa[v] = group_sum_f64<3>(ss);
     }
     if (part == 0) {
       const float* wcol = W + size_t(g) * kD * NB + cc;

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace hhr {
 
 constexpr int kD = 128;         // head dimension
@@ -13,6 +15,16 @@ constexpr int kWave = 64;
 // Element loads: K, V, q are fp32 or bf16; everything is computed in fp32 / fp64.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// Raw 16- or 32-bit element load; convert with raw_to_f32 after the other loads are issued so
+// that the conversion's wait does not sit in front of them.
+__device__ __forceinline__ uint32_t load_raw(const void* base, size_t i, int is_bf16) {
+  return is_bf16 ? uint32_t(reinterpret_cast<const uint16_t*>(base)[i])
+                 : reinterpret_cast<const uint32_t*>(base)[i];
+}
+__device__ __forceinline__ float raw_to_f32(uint32_t r, int is_bf16) {
+  return is_bf16 ? __uint_as_float(r << 16) : __uint_as_float(r);
+}
 
 __device__ __forceinline__ float load_elem(const void* base, size_t i, int is_bf16) {
   if (is_bf16) return bf16_bits_to_f32(reinterpret_cast<const uint16_t*>(base)[i]);
@@ -41,32 +53,33 @@ struct LongAcc {
     uint64_t ma = ua & 0x7FFFFFu, mb = ub & 0x7FFFFFu;
     if (ea) ma |= 0x800000u; else ea = 1;
     if (eb) mb |= 0x800000u; else eb = 1;
-    uint64_t m = ma * mb;
-    if (m == 0) return;
-    int sh = int(ea + eb) - 2;
-    int li = sh >> 5, bs = sh & 31;
-    uint64_t t0 = (m & 0xFFFFFFFFull) << bs;
-    uint64_t t1 = (m >> 32) << bs;
+    const uint64_t m = ma * mb;
+    const int sh = int(ea + eb) - 2;
+    const int li = sh >> 5, bs = sh & 31;
+    const uint64_t t0 = (m & 0xFFFFFFFFull) << bs;
+    const uint64_t t1 = (m >> 32) << bs;
     int64_t c0 = int64_t(t0 & 0xFFFFFFFFull);
     int64_t c1 = int64_t((t0 >> 32) + (t1 & 0xFFFFFFFFull));
     int64_t c2 = int64_t(t1 >> 32);
     if ((ua ^ ub) >> 31) { c0 = -c0; c1 = -c1; c2 = -c2; }
-    limb[li] += c0;
-    limb[li + 1] += c1;
-    limb[li + 2] += c2;
+    // limbs li, li + 1, li + 2 receive c0, c1, c2; unrolled selects keep the limbs in
+    // registers (a runtime index would place them in scratch memory)
+#pragma unroll
+    for (int i = 0; i < 18; ++i)
+      limb[i] += (i == li) ? c0 : (i == li + 1) ? c1 : (i == li + 2) ? c2 : 0;
   }
   // +1, 0 or -1.
   __device__ __forceinline__ int sign() {
+#pragma unroll
     for (int i = 0; i < 17; ++i) {
-      int64_t carry = limb[i] >> 32;  // floor division by 2^32
+      const int64_t carry = limb[i] >> 32;  // floor division by 2^32
       limb[i] -= carry * 4294967296ll;
       limb[i + 1] += carry;
     }
-    if (limb[17] > 0) return 1;
-    if (limb[17] < 0) return -1;
-    for (int i = 16; i >= 0; --i)
-      if (limb[i] != 0) return 1;
-    return 0;
+    int sg = limb[17] > 0 ? 1 : (limb[17] < 0 ? -1 : 0);
+#pragma unroll
+    for (int i = 16; i >= 0; --i) sg = (sg == 0 && limb[i] != 0) ? 1 : sg;
+    return sg;
   }
 };
 
@@ -84,7 +97,7 @@ __device__ __forceinline__ int certain_bit(double z, double s) {
 // Exact code bit [sum_j x[j] * w[j * w_stride] > 0] (j < 128); x: fp32 values through any
 // indexable accessor, w: fp32 in global memory.
 template <typename XPtr>
-__device__ __noinline__ uint32_t exact_bit(XPtr xs, const float* __restrict__ w, int w_stride) {
+__device__ __forceinline__ uint32_t exact_bit(XPtr xs, const float* __restrict__ w, int w_stride) {
   LongAcc acc;
   acc.clear();
   for (int j = 0; j < kD; ++j) acc.add_product(float(xs[j]), w[size_t(j) * w_stride]);
@@ -182,6 +195,22 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp_f<0x141>(v);  // row_half_mirror
   v += dpp_f<0x140>(v);  // row_mirror
+  return v;
+}
+
+// Sum of an fp64 value over aligned groups of 2^LOG lanes (LOG <= 3), returned in every lane
+// of the group: quad exchanges, then the half-row mirror.
+template <int LOG>
+__device__ __forceinline__ double group_sum_f64(double v) {
+  auto step = [](double x, auto ctrl) {
+    constexpr int C = decltype(ctrl)::value;
+    const int hi = __builtin_amdgcn_update_dpp(0, __double2hiint(x), C, 0xf, 0xf, false);
+    const int lo = __builtin_amdgcn_update_dpp(0, __double2loint(x), C, 0xf, 0xf, false);
+    return x + __hiloint2double(hi, lo);
+  };
+  if constexpr (LOG >= 1) v = step(v, std::integral_constant<int, 0xB1>{});   // quad_perm [1,0,3,2]
+  if constexpr (LOG >= 2) v = step(v, std::integral_constant<int, 0x4E>{});   // quad_perm [2,3,0,1]
+  if constexpr (LOG >= 3) v = step(v, std::integral_constant<int, 0x141>{});  // row_half_mirror
   return v;
 }
 
