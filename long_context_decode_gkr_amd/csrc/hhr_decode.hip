@@ -29,8 +29,6 @@ namespace hhr {
 constexpr int kMaxPages = 16384;       // = HHR_MAX_PAGES
 constexpr int kBoundPages = 256;       // pages per bound workgroup (4 per lane)
 constexpr int kBoundThreads = 512;     // 8 waves x 16 channels
-constexpr int kSelThreads = 1024;
-constexpr int kSelWaves = kSelThreads / kWave;
 constexpr int kDistCache = 32768;      // candidate slots whose distance stays in LDS
 
 // ---------------------------------------------------------------------------------------------
@@ -109,8 +107,9 @@ page_bound_kernel(Shape s, const float* __restrict__ pmin, const float* __restri
 // The totals are double-buffered, so one barrier per scan suffices as long as consecutive scans
 // alternate buffers (the barrier of the scan in between orders the reuse).
 // ---------------------------------------------------------------------------------------------
+template <int NWV>
 struct BlockScan {
-  int (*wt)[kSelWaves];
+  int (*wt)[NWV];
   int buf;
   // Exclusive prefix of v in thread order; *total gets the block sum.
   __device__ __forceinline__ int excl(int v, int* total) {
@@ -122,7 +121,7 @@ struct BlockScan {
     __syncthreads();
     int base = 0, tot = 0;
 #pragma unroll
-    for (int i = 0; i < kSelWaves; ++i) {
+    for (int i = 0; i < NWV; ++i) {
       const int x = t[i];
       base += (i < w) ? x : 0;
       tot += x;
@@ -164,9 +163,11 @@ constexpr int kRadixBits = 12;
 constexpr int kRadixBins = 1 << kRadixBits;
 constexpr int kEmitSPT = 16;   // cached distances per thread per emit chunk
 
-template <int NB, int EPT>
-__global__ void __launch_bounds__(kSelThreads)
+template <int NB, int EPT, int NT>
+__global__ void __launch_bounds__(NT)
 select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
+  constexpr int kSelThreads = NT;
+  constexpr int kSelWaves = NT / kWave;
   constexpr int NW = NB / 32;
   using DT = typename std::conditional<NB == 128, uint8_t, uint16_t>::type;
   constexpr uint32_t kNone = NB == 128 ? 0xFFu : 0xFFFFu;   // distance of a slot past the end
@@ -184,7 +185,7 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   __shared__ int s_wt[2][kSelWaves];
   __shared__ uint32_t s_mm[2][kSelWaves];
   __shared__ int s_pick[3];
-  BlockScan scan{s_wt, 0};
+  BlockScan<kSelWaves> scan{s_wt, 0};
   (void)lane;
 
   if (L == 0) {
@@ -355,8 +356,9 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
     return dd;
   };
   uint32_t* whist = s_hist + w * (NB + 1);
-  // Batches of 8 slots per thread: all code loads of a batch are issued before any is used.
-  constexpr int BAT = 8;
+  // Batches of 8 x (1024 / NT) slots per thread: all code loads of a batch are issued before
+  // any is used.
+  constexpr int BAT = 8 * (1024 / NT) / (NW / 4);
   for (int base = 0; base < nslots; base += BAT * kSelThreads) {
     int tt[BAT];
     uint4 cw[BAT][NW / 4];
@@ -392,17 +394,31 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   // ---- token threshold: smallest D* with #(D <= D*) >= k_eff
   int dstar, need_eq, k_eff;
   {
+    // thread i owns distance bins [DB i, DB i + DB)
+    constexpr int DB = (NB + 1 + kSelThreads - 1) / kSelThreads;
+    int cnt[DB];
     int tot_d = 0;
-    if (tid <= NB) {
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+      const int bin = tid * DB + j;
+      int v = 0;
+      if (bin <= NB) {
 #pragma unroll 4
-      for (int i = 0; i < kSelWaves; ++i) tot_d += int(s_hist[i * (NB + 1) + tid]);
+        for (int i = 0; i < kSelWaves; ++i) v += int(s_hist[i * (NB + 1) + bin]);
+      }
+      cnt[j] = v;
+      tot_d += v;
     }
     int C;
-    const int run = scan.excl(tot_d, &C);
+    int run = scan.excl(tot_d, &C);
     k_eff = min(a.kcap, C);
-    if (tot_d > 0 && run < k_eff && k_eff <= run + tot_d) {
-      s_pick[0] = tid;
-      s_pick[1] = run;
+#pragma unroll
+    for (int j = 0; j < DB; ++j) {
+      if (cnt[j] > 0 && run < k_eff && k_eff <= run + cnt[j]) {
+        s_pick[0] = tid * DB + j;
+        s_pick[1] = run;
+      }
+      run += cnt[j];
     }
     __syncthreads();
     dstar = s_pick[0];
@@ -656,8 +672,8 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
 }
 
 // Merge of the split partials of one (b, h): o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-// Partials are read in batches of 16 with no branch between the loads of a batch; an empty
-// partial has m = -inf and l = 0 and contributes nothing.
+// Partials are read in batches of 16, all loads of a batch issued before any use, and merged
+// without branches (an empty partial has m = -inf, l = 0 and gets weight 0).
 __global__ void __launch_bounds__(kD)
 combine_kernel(const float* __restrict__ part, int nsplit, float* __restrict__ out) {
   constexpr int CB = 16;
@@ -673,22 +689,20 @@ combine_kernel(const float* __restrict__ part, int nsplit, float* __restrict__ o
       l[u] = pi[kD + 1];
       o[u] = pi[d];
     }
+    __builtin_amdgcn_sched_barrier(0);
     float bm = Mx;
 #pragma unroll
-    for (int u = 0; u < CB; ++u)
-      if (i0 + u < nsplit) bm = fmaxf(bm, m[u]);
-    if (bm == -INFINITY) continue;
+    for (int u = 0; u < CB; ++u) bm = (i0 + u < nsplit) ? fmaxf(bm, m[u]) : bm;
     // rescale what has been summed so far to the new maximum, then add this batch
-    const float f0 = (Mx == -INFINITY) ? 0.f : exp2f(Mx - bm);
+    const float f0 = (bm == -INFINITY || Mx == -INFINITY) ? 0.f : exp2f(Mx - bm);
     Ls *= f0;
     Os *= f0;
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
-      if (i0 + u < nsplit && l[u] > 0.f) {
-        const float f = exp2f(m[u] - bm);
-        Ls = fmaf(l[u], f, Ls);
-        Os = fmaf(o[u], f, Os);
-      }
+      const bool ok = i0 + u < nsplit && l[u] > 0.f;
+      const float f = ok ? exp2f(m[u] - bm) : 0.f;
+      Ls = fmaf(ok ? l[u] : 0.f, f, Ls);
+      Os = fmaf(ok ? o[u] : 0.f, f, Os);
     }
     Mx = bm;
   }
@@ -727,22 +741,26 @@ static void launch_bound_t(const Shape& s, const CacheView& c, const float* qrot
                      c.seq_lens, qrot, U, dbg.bounds);
 }
 
-template <int NB, int EPT>
+template <int NB, int EPT, int NT>
 static void launch_select_t(const Shape& s, const CacheView& c, const SelectArgs& a,
                             const DebugView& dbg, hipStream_t st) {
-  hipLaunchKernelGGL((select_kernel<NB, EPT>), dim3(s.Hq, s.B), dim3(kSelThreads), 0, st, s, c,
-                     a, dbg);
+  hipLaunchKernelGGL((select_kernel<NB, EPT, NT>), dim3(s.Hq, s.B), dim3(NT), 0, st, s, c, a, dbg);
 }
+
+// Workgroup size of the selection (measured on MI355X: 1024 and 512 threads tie; 256 threads
+// are slower because the per-thread histogram and load batches grow); pages per thread follow
+// from the page capacity.
+constexpr int kSelNT = 1024;
 
 template <int NB>
 static void launch_select_nb(const Shape& s, const CacheView& c, const SelectArgs& a,
                              const DebugView& dbg, hipStream_t st) {
-  const int ept = (s.Pmax + kSelThreads - 1) / kSelThreads;
-  if (ept <= 1) launch_select_t<NB, 1>(s, c, a, dbg, st);
-  else if (ept <= 2) launch_select_t<NB, 2>(s, c, a, dbg, st);
-  else if (ept <= 4) launch_select_t<NB, 4>(s, c, a, dbg, st);
-  else if (ept <= 8) launch_select_t<NB, 8>(s, c, a, dbg, st);
-  else launch_select_t<NB, 16>(s, c, a, dbg, st);
+  const int ept = (s.Pmax + kSelNT - 1) / kSelNT;
+  if (ept <= 4) launch_select_t<NB, 4, kSelNT>(s, c, a, dbg, st);
+  else if (ept <= 8) launch_select_t<NB, 8, kSelNT>(s, c, a, dbg, st);
+  else if (ept <= 16) launch_select_t<NB, 16, kSelNT>(s, c, a, dbg, st);
+  else if (ept <= 32) launch_select_t<NB, 32, kSelNT>(s, c, a, dbg, st);
+  else launch_select_t<NB, 64, kSelNT>(s, c, a, dbg, st);
 }
 
 hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c,
