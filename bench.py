@@ -8,11 +8,13 @@ one new token appended per step (the index is updated), then the decode step run
 
 A "step" is hhr_append_decode (append one token, then decode) on one layer. The benchmark
 cycles over --layers distinct layer instances (separate K/V, index and sequence state in HBM) so
-the ~256 MB Infinity Cache cannot serve a step from the previous visit. Two passes, each W
+the ~256 MB Infinity Cache cannot serve a step from the previous visit. Three passes, each W
 warm-up steps then exactly K timed steps bracketed by torch.cuda.synchronize():
-  1. eager launches with HIP events recorded by the library around each of its five kernels on
-     the decode stream: per-kernel durations, the roofline figure, and eager_us_per_step;
-  2. replay of one captured HIP graph per layer instance: the headline us/step/layer.
+  1. launches with HIP events recorded by the library around each of its five kernels on the
+     decode stream: per-kernel durations and the roofline figure (events_us_per_step);
+  2. plain launches on one stream, no events: the headline us/step/layer;
+  3. replay of one captured HIP graph per layer instance (graph_us_per_step; on this stack a
+     graph replay of the five kernels is slower than the plain launches).
 
 Prints ONE JSON line. Options: --gpus (must be 1), --steps, --warmup, --layers,
 --no-cpu-baseline, --quiet, --copy-calibration (a 512 MiB device copy only, to scale the HBM
@@ -209,7 +211,7 @@ def main():
     hb.load()
     cfg = synth.CONFIGS[3]
     NL, K, Wm = args.layers, args.steps, args.warmup
-    visits = -(-(2 * (K + Wm)) // NL)     # appends per layer over both passes
+    visits = -(-(3 * (K + Wm)) // NL)     # appends per layer over the three passes
     L0 = CTX - visits                      # every layer ends at <= 128K tokens
     log(f"generating the 128K layer (L0={L0})", q)
     t0 = time.time()
@@ -251,13 +253,13 @@ def main():
                              vnd[v].data_ptr(), P["q"], P["R"], P["W"], P["ws"], dec.ws_bytes,
                              P["out"], dbg, stream)
 
-    # ---- pass 1 (eager launches): per-kernel durations from HIP events on the decode stream
+    # ---- pass 1 (launches with events): per-kernel durations from HIP events on the decode stream
     stream = hb.current_stream()
     NE = len(KERNELS) + 1
     ev = hb.HipEvents(NE * K)
     dbgs = [hb.DebugStruct(None, None, None, None, None, None, None, None, ev.address(NE * i))
             for i in range(K)]
-    log(f"eager pass: warm-up {Wm}, timed {K} steps over {NL} layer instances", q)
+    log(f"events pass: warm-up {Wm}, timed {K} steps over {NL} layer instances", q)
     for i in range(Wm):
         step(i, None, stream)
     torch.cuda.synchronize()
@@ -265,13 +267,25 @@ def main():
     for i in range(K):
         step(Wm + i, dbgs[i], stream)
     torch.cuda.synchronize()
-    eager_ms = (time.perf_counter() - t_start) * 1e3 / K
+    events_ms = (time.perf_counter() - t_start) * 1e3 / K
     # events [NE i + j] precede kernel j of step i; [NE i + NE - 1] follows the last one
     per = {n: [ev.elapsed_ms(NE * i + j, NE * i + j + 1) for i in range(K)]
            for j, n in enumerate(KERNELS)}
     ev.close()
 
-    # ---- pass 2 (graph replay): the timed K steps; one captured step per layer instance
+    # ---- pass 2 (plain launches on one stream): the headline figure
+    log(f"stream pass: warm-up {Wm}, timed {K} steps", q)
+    base = Wm + K
+    for i in range(Wm):
+        step(base + i, None, stream)
+    torch.cuda.synchronize()
+    t_start = time.perf_counter()
+    for i in range(K):
+        step(base + Wm + i, None, stream)
+    torch.cuda.synchronize()
+    stream_ms = (time.perf_counter() - t_start) * 1e3 / K
+
+    # ---- pass 3 (graph replay): one captured step per layer instance
     graphs = []
     gstream = torch.cuda.Stream()
     with torch.cuda.stream(gstream):
@@ -290,7 +304,7 @@ def main():
         graphs[(Wm + i) % NL].replay()
     torch.cuda.synchronize()
     graph_ms = (time.perf_counter() - t_start) * 1e3 / K
-    ms_step = graph_ms
+    ms_step = stream_ms
     avg_ms = {n: float(np.mean(v)) for n, v in per.items()}
     Lavg = L0 + visits // 2
     alg = algorithmic_bytes(cfg, Lavg)
@@ -313,7 +327,8 @@ def main():
         "steps": K,
         "warmup": Wm,
         "ms_per_step": round(ms_step, 5),
-        "eager_us_per_step": round(eager_ms * 1e3, 2),
+        "events_us_per_step": round(events_ms * 1e3, 2),
+        "graph_us_per_step": round(graph_ms * 1e3, 2),
         "higher_is_better": False,
         "scaling": "weak",
         "vs_baseline": None,

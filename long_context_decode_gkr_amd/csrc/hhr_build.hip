@@ -140,8 +140,8 @@ hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R,
 //     per-sequence ticket, left at 0);
 //   * prepares the G queries of the group when q is given: its 32 channels of q~ = q R_g (Eq. 4)
 //     and its code words of sign(q W_g) (Eq. 1, Eq. 10), written to the decode workspace.
-// The new key and the G queries are the "vectors" v = 0 .. nvec-1; each R_g / W_g column of
-// the slice is read once and multiplied into all vectors. A column is split over 8 lanes of
+// The new key (vector 0) and the G queries (vectors 1 .. G) share every R_g / W_g column of
+// the slice, which is read once. A column is split over 8 lanes of
 // 16 terms each (fp64 partial sums of exact products, reduced by DPP): threads [0, 256) own the
 // 32 rotation columns, threads [256, 256 + 8 NB / 4) the NB / 4 code columns.
 // ---------------------------------------------------------------------------------------------
@@ -149,7 +149,7 @@ constexpr int kPrepSlices = 4;
 constexpr int kPrepParts = 8;
 constexpr int kMaxVec = 9;   // 1 key + up to 8 queries
 
-template <int NB>
+template <int NB, int KB, int QB>   // KB, QB: keys/values, queries in bf16
 __global__ void __launch_bounds__(256 + kPrepParts * NB / kPrepSlices)
 prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __restrict__ vn,
             const void* __restrict__ q, const float* __restrict__ R, const float* __restrict__ W,
@@ -159,79 +159,100 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   constexpr int CC = NB / kPrepSlices;          // code columns per slice (32 or 64)
   constexpr int WPS = CC / 32;                  // code words per slice (1 or 2)
   constexpr int T = kD / kPrepParts;            // terms per lane (16)
+  constexpr int NT = 256 + kPrepParts * NB / kPrepSlices;   // workgroup size
   const int sl = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
-  const int t = c.seq_lens[b];
-  const bool app = kn != nullptr && t >= 0 && t < s.Lmax;
-  const int v0 = app ? 1 : 0;                    // first query vector
+  const int part = tid & (kPrepParts - 1);
+  const bool rot = tid < 256;                   // rotation lanes; the others compute code bits
   const int nq = q ? s.G : 0;
-  const int nvec = v0 + nq;
-  if (nvec == 0) return;
+  const bool has_k = kn != nullptr;
+  if (!has_k && nq == 0) return;
 
-  __shared__ float xs[kMaxVec][kD];
+  __shared__ float xs[kMaxVec][kD];             // row 0: the new key; rows 1 .. G: the queries
   __shared__ uint8_t bits[kMaxVec][CC];
 
-  const size_t krow = (size_t(b) * s.Hkv + g) * kD;
-  const size_t row = (size_t(b) * s.Hkv + g) * s.Lmax + (app ? t : 0);
-  if (app && tid < kD) {
-    if (s.kv_bf16) {
-      const uint16_t kb = reinterpret_cast<const uint16_t*>(kn)[krow + tid];
-      if ((tid >> 5) == sl) {
-        reinterpret_cast<uint16_t*>(c.K)[row * kD + tid] = kb;
-        reinterpret_cast<uint16_t*>(c.V)[row * kD + tid] = reinterpret_cast<const uint16_t*>(vn)[krow + tid];
-      }
-      xs[0][tid] = bf16_bits_to_f32(kb);
-    } else {
-      const float kf = reinterpret_cast<const float*>(kn)[krow + tid];
-      if ((tid >> 5) == sl) {
-        reinterpret_cast<float*>(c.K)[row * kD + tid] = kf;
-        reinterpret_cast<float*>(c.V)[row * kD + tid] = reinterpret_cast<const float*>(vn)[krow + tid];
-      }
-      xs[0][tid] = kf;
-    }
+  // Everything that does not depend on the sequence length is loaded together with it: this
+  // lane's 16 column terms, the new key and value elements and the queries.
+  const int t = c.seq_lens[b];
+  const int j = sl * 32 + (tid >> 3);           // rotation column (rotation lanes)
+  const int lc = (tid - 256) >> 3;              // code column within the slice (code lanes)
+  const int cc = sl * CC + lc;
+  float cv[T];
+  {
+    const float* col = rot ? R + size_t(g) * kD * kD + size_t(part * T) * kD + j
+                           : W + size_t(g) * kD * NB + size_t(part * T) * NB + cc;
+    const int stride = rot ? kD : NB;
+#pragma unroll
+    for (int i = 0; i < T; ++i) cv[i] = col[size_t(i) * stride];
   }
-  for (int e = tid; e < nq * kD; e += blockDim.x) {
-    const int hh = e / kD, i = e % kD;
-    xs[v0 + hh][i] = load_elem(q, (size_t(b) * s.Hq + g * s.G + hh) * kD + i, s.q_bf16);
+  // The vector loads carry no branch (a branch would make the compiler wait for each load
+  // before the join): a missing key or query input is replaced by the other input, whose
+  // values are then loaded but not used, and indices are clamped.
+  const size_t krow = (size_t(b) * s.Hkv + g) * kD;
+  const bool own = (tid >> 5) == sl;            // this workgroup stores K/V element tid
+  const int kel = min(tid, kD - 1);
+  const uint32_t kraw = load_raw(has_k ? kn : q, has_k ? krow + kel : 0, KB);
+  const uint32_t vraw = load_raw(has_k ? vn : q, has_k ? krow + kel : 0, KB);
+  static_assert(2 * NT >= 8 * kD, "two query elements per thread cover G <= 8 queries");
+  uint32_t qraw[2];
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int e = min(tid + r * NT, nq * kD - 1);
+    qraw[r] = load_raw(q ? q : kn, q ? (size_t(b) * s.Hq + g * s.G) * kD + e : 0, QB);
+  }
+  // The open page's extrema (page t / S) for this lane's rotation column (code lanes read
+  // column 32 sl, unused): in bounds whatever t is; needed only after the dot products.
+  const bool app = has_k && t >= 0 && t < s.Lmax;
+  const int p = app ? t / s.S : 0;
+  const size_t si = ((size_t(b) * s.Hkv + g) * kD + (rot ? j : sl * 32)) * s.Pmax + p;
+  const float omin = c.pmin[si];
+  const float omax = c.pmax[si];
+
+  const size_t row = (size_t(b) * s.Hkv + g) * s.Lmax + (app ? t : 0);
+  if (tid < kD && has_k) {
+    if (app && own) {
+      if (KB) {
+        reinterpret_cast<uint16_t*>(c.K)[row * kD + tid] = uint16_t(kraw);
+        reinterpret_cast<uint16_t*>(c.V)[row * kD + tid] = uint16_t(vraw);
+      } else {
+        reinterpret_cast<uint32_t*>(c.K)[row * kD + tid] = kraw;
+        reinterpret_cast<uint32_t*>(c.V)[row * kD + tid] = vraw;
+      }
+    }
+    xs[0][tid] = raw_to_f32(kraw, KB);
+  }
+#pragma unroll
+  for (int r = 0; r < 2; ++r) {
+    const int e = tid + r * NT;
+    if (e < nq * kD) xs[1 + e / kD][e % kD] = raw_to_f32(qraw[r], QB);
   }
   __syncthreads();
 
-  const int part = tid & (kPrepParts - 1);
-  if (tid < 256) {
+  auto active = [&](int v) { return v == 0 ? app : v <= nq; };
+  if (rot) {
     // ---- rotation column j, terms [16 part, 16 part + 16)
-    const int j = sl * 32 + (tid >> 3);
-    const float* rc = R + size_t(g) * kD * kD + size_t(part * T) * kD + j;
-    float rv[T];
-#pragma unroll
-    for (int i = 0; i < T; ++i) rv[i] = rc[size_t(i) * kD];
     double acc[kMaxVec];
 #pragma unroll
     for (int v = 0; v < kMaxVec; ++v) {
       double a = 0.0;
-      if (v < nvec) {
+      if (active(v)) {
         const float* x = &xs[v][part * T];
 #pragma unroll
-        for (int i = 0; i < T; ++i) a += double(x[i]) * double(rv[i]);
+        for (int i = 0; i < T; ++i) a += double(x[i]) * double(cv[i]);
       }
       acc[v] = group_sum_f64<3>(a);
     }
     if (part == 0) {
       if (app) {
         const float kt = float(acc[0]);
-        const int p = t / s.S;
-        const size_t si = ((size_t(b) * s.Hkv + g) * kD + j) * s.Pmax + p;
-        if (t % s.S == 0) {
-          c.pmin[si] = kt;
-          c.pmax[si] = kt;
-        } else {
-          c.pmin[si] = fminf(c.pmin[si], kt);
-          c.pmax[si] = fmaxf(c.pmax[si], kt);
-        }
+        const bool first = t % s.S == 0;        // the key opens page p
+        c.pmin[si] = first ? kt : fminf(omin, kt);
+        c.pmax[si] = first ? kt : fmaxf(omax, kt);
       }
 #pragma unroll
-      for (int v = 0; v < kMaxVec; ++v) {
-        if (v >= v0 && v < nvec) {
-          const size_t o = (size_t(b) * s.Hq + g * s.G + (v - v0)) * kD + j;
+      for (int v = 1; v < kMaxVec; ++v) {
+        if (v <= nq) {
+          const size_t o = (size_t(b) * s.Hq + g * s.G + (v - 1)) * kD + j;
           qrot[o] = float(acc[v]);
           if (dbg_qrot) dbg_qrot[o] = float(acc[v]);
         }
@@ -239,21 +260,15 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
     }
   } else {
     // ---- code column cc, terms [16 part, 16 part + 16)
-    const int lc = (tid - 256) >> 3;              // column within the slice
-    const int cc = sl * CC + lc;
-    const float* wc = W + size_t(g) * kD * NB + size_t(part * T) * NB + cc;
-    float wv[T];
-#pragma unroll
-    for (int i = 0; i < T; ++i) wv[i] = wc[size_t(i) * NB];
     double z[kMaxVec], sa[kMaxVec];
 #pragma unroll
     for (int v = 0; v < kMaxVec; ++v) {
       double zz = 0.0, ss = 0.0;
-      if (v < nvec) {
+      if (active(v)) {
         const float* x = &xs[v][part * T];
 #pragma unroll
         for (int i = 0; i < T; ++i) {
-          const double pr = double(x[i]) * double(wv[i]);
+          const double pr = double(x[i]) * double(cv[i]);
           zz += pr;
           ss += fabs(pr);
         }
@@ -263,7 +278,8 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
     }
     if (part == 0) {
       const float* wcol = W + size_t(g) * kD * NB + cc;
-      for (int v = 0; v < nvec; ++v) {
+      for (int v = 0; v <= nq; ++v) {
+        if (!active(v)) continue;
         int cb = certain_bit(z[v], sa[v]);
         if (cb < 0) cb = int(exact_bit(static_cast<const float*>(&xs[v][0]), wcol, NB));
         bits[v][lc] = uint8_t(cb);
@@ -272,18 +288,20 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   }
   __syncthreads();
   // ---- pack this slice's code words: thread (v, w) builds word w of vector v
-  if (tid < nvec * WPS) {
+  if (tid < (1 + nq) * WPS) {
     const int v = tid / WPS, wi = tid % WPS;
-    uint32_t word = 0;
+    if (active(v)) {
+      uint32_t word = 0;
 #pragma unroll
-    for (int i = 0; i < 32; ++i) word |= uint32_t(bits[v][32 * wi + i]) << i;
-    const int wg = sl * WPS + wi;                 // word index within the code
-    if (v < v0) {
-      c.codes[row * NW + wg] = word;
-    } else {
-      const size_t o = (size_t(b) * s.Hq + g * s.G + (v - v0)) * NW + wg;
-      qcode[o] = word;
-      if (dbg_qcode) dbg_qcode[o] = word;
+      for (int i = 0; i < 32; ++i) word |= uint32_t(bits[v][32 * wi + i]) << i;
+      const int wg = sl * WPS + wi;               // word index within the code
+      if (v == 0) {
+        c.codes[row * NW + wg] = word;
+      } else {
+        const size_t o = (size_t(b) * s.Hq + g * s.G + (v - 1)) * NW + wg;
+        qcode[o] = word;
+        if (dbg_qcode) dbg_qcode[o] = word;
+      }
     }
   }
   if (app) {
@@ -302,16 +320,38 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   }
 }
 
+template <int NB, int KB, int QB>
+static void launch_prep_t(const Shape& s, const CacheView& c, const void* k_new,
+                          const void* v_new, const void* q, const float* R, const float* W,
+                          float* qrot, uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode,
+                          hipStream_t st) {
+  dim3 grid(kPrepSlices, s.Hkv, s.B);
+  hipLaunchKernelGGL((prep_kernel<NB, KB, QB>), grid, dim3(256 + kPrepParts * NB / kPrepSlices),
+                     0, st, s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
+}
+
+template <int NB>
+static void launch_prep_nb(const Shape& s, const CacheView& c, const void* k_new,
+                           const void* v_new, const void* q, const float* R, const float* W,
+                           float* qrot, uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode,
+                           hipStream_t st) {
+  if (s.kv_bf16 && s.q_bf16)
+    launch_prep_t<NB, 1, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
+  else if (s.kv_bf16)
+    launch_prep_t<NB, 1, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
+  else if (s.q_bf16)
+    launch_prep_t<NB, 0, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
+  else
+    launch_prep_t<NB, 0, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
+}
+
 hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, const void* v_new,
                        const void* q, const float* R, const float* W, float* qrot,
                        uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, hipStream_t st) {
-  dim3 grid(kPrepSlices, s.Hkv, s.B);
   if (s.NB == 128)
-    hipLaunchKernelGGL((prep_kernel<128>), grid, dim3(256 + kPrepParts * 128 / kPrepSlices), 0,
-                       st, s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
+    launch_prep_nb<128>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
   else
-    hipLaunchKernelGGL((prep_kernel<256>), grid, dim3(256 + kPrepParts * 256 / kPrepSlices), 0,
-                       st, s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
+    launch_prep_nb<256>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
   return hipGetLastError();
 }
 

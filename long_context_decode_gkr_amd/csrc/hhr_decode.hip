@@ -7,9 +7,10 @@
 //   §3.1 Eq. 2    Hamming distance by XOR + popcount;
 //   §3.3.2, §1    the closest candidates are kept and attended to exactly.
 //
-// Three kernels per step, all on the caller's stream:
+// Kernels of a step, all on the caller's stream (after the preparation kernel, which appends
+// the new token and writes q~ and the query codes):
 //   page_bound_kernel  grid (ceil(Pmax/256), Hkv, B): streams the page extrema once for the G
-//                      query heads of a KV head (HBM-bound), computing q~ on the fly.
+//                      query heads of a KV head (HBM-bound).
 //   select_kernel      grid (Hq, B), 1024 threads: query code, exact top-n_keep pages by a
 //                      range-adapted radix select, Hamming distances of the kept pages' keys,
 //                      exact top-k tokens by a histogram select; writes ascending indices.
@@ -103,12 +104,14 @@ page_bound_kernel(Shape s, const float* __restrict__ pmin, const float* __restri
 }
 
 // ---------------------------------------------------------------------------------------------
-// Block-wide scan for 1024 threads: DPP wave scans, then the 16 wave totals through LDS.
+// Block-wide scan for up to 1024 threads: DPP wave scans, then the wave totals through LDS,
+// scanned again by DPP in the first row of 16 lanes of every wave (one LDS read per lane).
 // The totals are double-buffered, so one barrier per scan suffices as long as consecutive scans
 // alternate buffers (the barrier of the scan in between orders the reuse).
 // ---------------------------------------------------------------------------------------------
 template <int NWV>
 struct BlockScan {
+  static_assert(NWV <= 16, "wave totals are scanned within one row of 16 lanes");
   int (*wt)[NWV];
   int buf;
   // Exclusive prefix of v in thread order; *total gets the block sum.
@@ -119,14 +122,9 @@ struct BlockScan {
     buf ^= 1;
     if (lane_id() == kWave - 1) t[w] = incl;
     __syncthreads();
-    int base = 0, tot = 0;
-#pragma unroll
-    for (int i = 0; i < NWV; ++i) {
-      const int x = t[i];
-      base += (i < w) ? x : 0;
-      tot += x;
-    }
-    *total = tot;
+    const int ts = row16_incl_sum(t[lane_id() % NWV]);   // lanes 0 .. NWV-1: prefix of totals
+    const int base = w > 0 ? __builtin_amdgcn_readlane(ts, w - 1) : 0;
+    *total = __builtin_amdgcn_readlane(ts, NWV - 1);
     return base + incl - v;
   }
 };
@@ -147,21 +145,28 @@ struct SelectArgs {
   int32_t* cnt;       // [B][Hq]
   double rho;
   int kcap;
+  int istride;        // row stride of idx: kcap live entries, then one trash entry per lane
 };
 
 // ---------------------------------------------------------------------------------------------
 // Selection, one workgroup per (b, h).
 //   Coarse: the n_keep pages of largest U, ties to the lower index. Keys are ranked by a radix
-//   select over rel = key - min(key), 12 bits at a time from the top set bit of the range; the
-//   threshold bin's ties are broken in page order by one scan. EPT pages per thread
-//   (contiguous: thread i owns pages [i EPT, i EPT + EPT)).
+//   select over rel = key - min(key), 12 bits at a time from the top set bit of the range; as
+//   soon as the threshold bin holds at most 64 keys, one wave ranks them by (key, page) and the
+//   kept set is a lexicographic cut; only more than 64 exactly equal keys at the threshold
+//   fall back to breaking ties in page order by one scan. EPT pages per thread (contiguous:
+//   thread i owns pages [i EPT, i EPT + EPT)).
 //   Fine: Hamming distance of every key of the kept pages (slots in ascending token order),
 //   histogram over D in [0, NB], the smallest D* with #(D <= D*) >= k_eff, and one scan that
 //   places every slot with D < D* and the first k_eff - #(D < D*) slots with D == D*.
+// The kernel runs on one CU per (b, h) and is bound by instruction issue, so every per-element
+// step is branch-free: a lane with nothing to record still executes the LDS or global write,
+// aimed at a dummy entry of its own past the live data (no divergent branch, no bank conflict).
 // ---------------------------------------------------------------------------------------------
+constexpr int kRadixBins = 1 << 12;
 constexpr int kRadixBits = 12;
-constexpr int kRadixBins = 1 << kRadixBits;
 constexpr int kEmitSPT = 16;   // cached distances per thread per emit chunk
+static_assert(16 % kEmitSPT == 0, "an emit chunk must not cross a page (page sizes 16, 32)");
 
 template <int NB, int EPT, int NT>
 __global__ void __launch_bounds__(NT)
@@ -178,16 +183,20 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   const int L = min(max(c.seq_lens[b], 0), s.Lmax);
   const int P = (L + s.S - 1) / s.S;
 
-  __shared__ int32_t s_pages[kMaxPages];
-  __shared__ __align__(16) DT s_dist[kDistCache];
-  __shared__ uint32_t s_hist[HB];
+  // Live entries, then one dummy entry per lane.
+  __shared__ int32_t s_pages[kMaxPages + kWave];
+  __shared__ __align__(16) DT s_dist[kDistCache + kWave];
+  __shared__ __align__(16) uint32_t s_hist[HB + kWave];
   __shared__ uint32_t s_qw[NW];
   __shared__ int s_wt[2][kSelWaves];
   __shared__ uint32_t s_mm[2][kSelWaves];
   __shared__ int s_pick[3];
+  __shared__ uint32_t s_ckey[kWave];   // keys of the threshold bin (when it holds <= 64)
+  __shared__ int s_cidx[kWave];
+  __shared__ int s_ncand;
   BlockScan<kSelWaves> scan{s_wt, 0};
-  (void)lane;
 
+  int32_t* out_idx = a.idx + size_t(bh) * a.istride;
   if (L == 0) {
     if (tid == 0) {
       a.cnt[bh] = 0;
@@ -200,28 +209,26 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
 
   // ---- query code (from the preparation kernel), page keys to registers, histograms cleared
   if (tid < NW) s_qw[tid] = a.qcode[size_t(bh) * NW + tid];
+  if (tid == 0) s_ncand = 0;
   for (int i = tid; i < HB; i += kSelThreads) s_hist[i] = 0;
   uint32_t key[EPT];
+  bool valid[EPT];
   {
-    const float* Ub = a.U + size_t(bh) * s.Pmax + size_t(tid) * EPT;
+    // whole float4 loads at clamped addresses (rows are Pmax long, Pmax a multiple of 4)
+    const float4* U4 = reinterpret_cast<const float4*>(a.U + size_t(bh) * s.Pmax);
+    const int last4 = s.Pmax / 4 - 1;
     float u[EPT];
-    if ((tid + 1) * EPT <= P) {
-      if constexpr (EPT >= 4) {
 #pragma unroll
-        for (int e = 0; e < EPT; e += 4) {
-          const float4 x = *reinterpret_cast<const float4*>(Ub + e);
-          u[e] = x.x; u[e + 1] = x.y; u[e + 2] = x.z; u[e + 3] = x.w;
-        }
-      } else {
-#pragma unroll
-        for (int e = 0; e < EPT; ++e) u[e] = Ub[e];
-      }
-    } else {
-#pragma unroll
-      for (int e = 0; e < EPT; ++e) u[e] = (tid * EPT + e < P) ? Ub[e] : 0.f;
+    for (int e = 0; e < EPT; e += 4) {
+      const float4 x = U4[min(tid * (EPT / 4) + e / 4, last4)];
+      u[e] = x.x; u[e + 1] = x.y; u[e + 2] = x.z; u[e + 3] = x.w;
     }
 #pragma unroll
-    for (int e = 0; e < EPT; ++e) key[e] = (tid * EPT + e < P) ? desc_key(u[e]) : 0xFFFFFFFFu;
+    for (int e = 0; e < EPT; ++e) {
+      valid[e] = tid * EPT + e < P;
+      const uint32_t k = materialize(desc_key(u[e]));   // computed by every lane
+      key[e] = valid[e] ? k : 0xFFFFFFFFu;
+    }
   }
 
   // ---- key range (one barrier for both reductions)
@@ -230,47 +237,57 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
     uint32_t lmin = 0xFFFFFFFFu, lmax = 0u;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      if (tid * EPT + e < P) {
-        lmin = min(lmin, key[e]);
-        lmax = max(lmax, key[e]);
-      }
+      lmin = min(lmin, key[e]);                  // an invalid key is the largest value
+      lmax = max(lmax, valid[e] ? key[e] : 0u);
     }
     lmin = wave_min_u32(lmin);
     lmax = wave_max_u32(lmax);
-    if (lane_id() == 0) {
+    if (lane == 0) {
       s_mm[0][w] = lmin;
       s_mm[1][w] = lmax;
     }
     __syncthreads();   // also publishes s_qw and the cleared histograms
-    kmin = 0xFFFFFFFFu;
-    kmax = 0u;
-#pragma unroll
-    for (int i = 0; i < kSelWaves; ++i) {
-      kmin = min(kmin, s_mm[0][i]);
-      kmax = max(kmax, s_mm[1][i]);
-    }
+    kmin = wave_min_u32(s_mm[0][lane % kSelWaves]);
+    kmax = wave_max_u32(s_mm[1][lane % kSelWaves]);
   }
 
-  // ---- coarse selection
+  // ---- coarse selection. The kept set is described, where possible, by a cut (ck, ci): page
+  // i is kept iff (key_i, i) <= (ck, ci) lexicographically (smaller key = larger U, ties to the
+  // lower index). Otherwise (more than 64 exactly equal keys straddle the cut) by the final
+  // radix prefix plus the number `need` of its elements to take in page order.
   int need = n_keep;        // still to take among elements matching `prefix`
   uint32_t prefix = 0;      // high bits of rel fixed so far
   int res_lo = 0;           // elements compare on rel >> res_lo
+  bool cut = true;
+  uint32_t ck = 0xFFFFFFFFu;
+  int ci = 0x7FFFFFFF;
   if (n_keep < P) {
+    cut = false;
     int cur_hi = (kmax == kmin) ? -1 : 31 - __clz(int(kmax - kmin));
+    bool first = true;
     while (cur_hi >= 0) {
       const int cur_lo = max(cur_hi - (kRadixBits - 1), 0);
       const int width = cur_hi - cur_lo + 1;
       const uint32_t dmask = (1u << width) - 1u;
+      if (first) {
+        // every valid key matches the empty prefix
 #pragma unroll
-      for (int e = 0; e < EPT; ++e) {
-        if (tid * EPT + e < P) {
+        for (int e = 0; e < EPT; ++e) {
           const uint32_t rel = key[e] - kmin;
-          if (uint32_t(uint64_t(rel) >> (cur_hi + 1)) == prefix)
+          atomicAdd(&s_hist[valid[e] ? (rel >> cur_lo) & dmask : HB + lane], 1u);
+        }
+      } else {
+        // few keys match a longer prefix: waves without a match skip the atomic
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          const uint32_t rel = key[e] - kmin;
+          if (valid[e] && uint32_t(uint64_t(rel) >> (cur_hi + 1)) == prefix)
             atomicAdd(&s_hist[(rel >> cur_lo) & dmask], 1u);
         }
       }
+      first = false;
       __syncthreads();
-      // thread i owns bins [4 i, 4 i + 4): read them, clear them for the next pass
+      // thread i owns bins [BPT i, BPT i + BPT): read them, clear them for the next pass
       constexpr int BPT = kRadixBins / kSelThreads;
       uint32_t hb[BPT];
       int loc = 0;
@@ -282,15 +299,20 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
       }
       int tot;
       int run = scan.excl(loc, &tot);
+      int fbin = -1, fbefore = 0, fcnt = 0;
 #pragma unroll
       for (int j = 0; j < BPT; ++j) {
         const int cnt = int(hb[j]);
-        if (cnt > 0 && run < need && need <= run + cnt) {
-          s_pick[0] = tid * BPT + j;
-          s_pick[1] = run;
-          s_pick[2] = cnt;
-        }
+        const bool hit = cnt > 0 && run < need && need <= run + cnt;
+        fbin = hit ? tid * BPT + j : fbin;
+        fbefore = hit ? run : fbefore;
+        fcnt = hit ? cnt : fcnt;
         run += cnt;
+      }
+      if (fbin >= 0) {   // exactly one thread
+        s_pick[0] = fbin;
+        s_pick[1] = fbefore;
+        s_pick[2] = fcnt;
       }
       __syncthreads();
       const int d = s_pick[0], before = s_pick[1], in_bin = s_pick[2];
@@ -298,21 +320,72 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
       need -= before;
       res_lo = cur_lo;
       cur_hi = cur_lo - 1;
-      if (in_bin == need) break;   // the whole bin is taken: no finer digit is needed
+      if (in_bin == need) {
+        // the whole bin is taken: keep every key with rel >> res_lo <= prefix
+        const uint64_t top = uint64_t(kmin) + ((uint64_t(prefix) + 1) << res_lo) - 1;
+        ck = top > 0xFFFFFFFFull ? 0xFFFFFFFFu : uint32_t(top);
+        ci = 0x7FFFFFFF;
+        cut = true;
+        break;
+      }
+      if (in_bin <= kWave) {
+        // few keys share the threshold bin: wave 0 ranks them by (key, index) and the
+        // need-th smallest becomes the cut
+#pragma unroll
+        for (int e = 0; e < EPT; ++e) {
+          if (valid[e] && ((key[e] - kmin) >> res_lo) == prefix) {
+            const int j = atomicAdd(&s_ncand, 1);
+            s_ckey[j] = key[e];
+            s_cidx[j] = tid * EPT + e;
+          }
+        }
+        __syncthreads();
+        if (w == 0) {
+          const uint32_t kl = lane < in_bin ? s_ckey[lane] : 0xFFFFFFFFu;
+          const int il = lane < in_bin ? s_cidx[lane] : 0x7FFFFFFF;
+          int rank = 0;
+          for (int j = 0; j < in_bin; ++j) {
+            const uint32_t kj = s_ckey[j];
+            const int ij = s_cidx[j];
+            rank += (kj < kl || (kj == kl && ij < il)) ? 1 : 0;
+          }
+          if (lane < in_bin && rank == need - 1) {
+            s_pick[0] = int(kl);
+            s_pick[1] = il;
+          }
+        }
+        __syncthreads();
+        ck = uint32_t(s_pick[0]);
+        ci = s_pick[1];
+        cut = true;
+        break;
+      }
+    }
+  }
+  if (cut) {
+    bool tk[EPT];
+    int n = 0;
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      tk[e] = valid[e] && (key[e] < ck || (key[e] == ck && tid * EPT + e <= ci));
+      n += tk[e] ? 1 : 0;
+    }
+    int tot;
+    int pos = scan.excl(n, &tot);
+#pragma unroll
+    for (int e = 0; e < EPT; ++e) {
+      s_pages[tk[e] ? pos : kMaxPages + lane] = tid * EPT + e;
+      pos += tk[e] ? 1 : 0;
     }
   } else {
-    need = P;
-  }
-  // rel >> res_lo below prefix: taken; equal: taken in page order up to `need`
-  {
+    // rel >> res_lo below prefix: taken; equal: taken in page order up to `need`
     bool lt[EPT], eq[EPT];
     int nlt = 0, neq = 0;
 #pragma unroll
     for (int e = 0; e < EPT; ++e) {
-      const bool ok = tid * EPT + e < P;
       const uint32_t v = (key[e] - kmin) >> res_lo;
-      lt[e] = ok && (n_keep < P) && v < prefix;
-      eq[e] = ok && ((n_keep >= P) || v == prefix);
+      lt[e] = valid[e] && v < prefix;
+      eq[e] = valid[e] && v == prefix;
       nlt += lt[e] ? 1 : 0;
       neq += eq[e] ? 1 : 0;
     }
@@ -324,15 +397,18 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
     for (int e = 0; e < EPT; ++e) {
       const bool take = lt[e] || (eq[e] && eq_seen < need);
       eq_seen += eq[e] ? 1 : 0;
-      if (take) {
-        s_pages[pos] = tid * EPT + e;
-        if (dbg.page_ids) dbg.page_ids[size_t(bh) * s.Pmax + pos] = tid * EPT + e;
-        ++pos;
-      }
+      s_pages[take ? pos : kMaxPages + lane] = tid * EPT + e;
+      pos += take ? 1 : 0;
     }
-    if (tid == 0 && dbg.page_count) dbg.page_count[bh] = n_keep;
   }
   __syncthreads();
+  if (dbg.page_ids) {
+    for (int i = tid; i < n_keep; i += kSelThreads)
+      dbg.page_ids[size_t(bh) * s.Pmax + i] = s_pages[i];
+    if (tid == 0 && dbg.page_count) dbg.page_count[bh] = n_keep;
+  } else if (tid == 0 && dbg.page_count) {
+    dbg.page_count[bh] = n_keep;
+  }
 
   // ---- fine stage: Hamming distance of every candidate slot (§3.1 Eq. 2)
   uint32_t qw[NW];
@@ -365,7 +441,8 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
 #pragma unroll
     for (int u = 0; u < BAT; ++u) {
       const int slot = base + u * kSelThreads + tid;
-      tt[u] = (slot < nslots) ? slot_token(min(slot, nslots - 1)) : L;
+      const int tk = materialize(slot_token(min(slot, nslots - 1)));   // every lane
+      tt[u] = (slot < nslots) ? tk : L;
       const int tl = min(tt[u], L - 1);
       const uint4* cp = reinterpret_cast<const uint4*>(cbase + size_t(tl) * NW);
 #pragma unroll
@@ -374,111 +451,146 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
 #pragma unroll
     for (int u = 0; u < BAT; ++u) {
       const int slot = base + u * kSelThreads + tid;
-      if (slot < nslots) {
-        uint32_t dd = kNone;
-        if (tt[u] < L) {
-          dd = 0;
+      uint32_t dd = 0;
 #pragma unroll
-          for (int v = 0; v < NW / 4; ++v)
-            dd += __popc(cw[u][v].x ^ qw[4 * v]) + __popc(cw[u][v].y ^ qw[4 * v + 1]) +
-                  __popc(cw[u][v].z ^ qw[4 * v + 2]) + __popc(cw[u][v].w ^ qw[4 * v + 3]);
-          atomicAdd(&whist[dd], 1u);
-        }
-        if (cache_d) s_dist[slot] = DT(dd);
-        if (dbg.dist) dbg.dist[size_t(bh) * s.Lmax + slot] = uint16_t(dd == kNone ? 0xFFFFu : dd);
-      }
+      for (int v = 0; v < NW / 4; ++v)
+        dd += __popc(cw[u][v].x ^ qw[4 * v]) + __popc(cw[u][v].y ^ qw[4 * v + 1]) +
+              __popc(cw[u][v].z ^ qw[4 * v + 2]) + __popc(cw[u][v].w ^ qw[4 * v + 3]);
+      const bool live = tt[u] < L;                // implies slot < nslots
+      atomicAdd(live ? &whist[dd] : &s_hist[HB + lane], 1u);
+      // (without the LDS cache every lane writes its dummy entry; the emit recomputes)
+      s_dist[cache_d && slot < nslots ? slot : kDistCache + lane] = DT(live ? dd : kNone);
     }
   }
   __syncthreads();
-
-  // ---- token threshold: smallest D* with #(D <= D*) >= k_eff
-  int dstar, need_eq, k_eff;
-  {
-    // thread i owns distance bins [DB i, DB i + DB)
-    constexpr int DB = (NB + 1 + kSelThreads - 1) / kSelThreads;
-    int cnt[DB];
-    int tot_d = 0;
-#pragma unroll
-    for (int j = 0; j < DB; ++j) {
-      const int bin = tid * DB + j;
-      int v = 0;
-      if (bin <= NB) {
-#pragma unroll 4
-        for (int i = 0; i < kSelWaves; ++i) v += int(s_hist[i * (NB + 1) + bin]);
-      }
-      cnt[j] = v;
-      tot_d += v;
+  if (cache_d && dbg.dist) {
+    for (int i = tid; i < nslots; i += kSelThreads) {
+      const uint32_t dd = s_dist[i];
+      dbg.dist[size_t(bh) * s.Lmax + i] = uint16_t(dd == kNone ? 0xFFFFu : dd);
     }
-    int C;
-    int run = scan.excl(tot_d, &C);
-    k_eff = min(a.kcap, C);
-#pragma unroll
-    for (int j = 0; j < DB; ++j) {
-      if (cnt[j] > 0 && run < k_eff && k_eff <= run + cnt[j]) {
-        s_pick[0] = tid * DB + j;
-        s_pick[1] = run;
-      }
-      run += cnt[j];
-    }
-    __syncthreads();
-    dstar = s_pick[0];
-    need_eq = k_eff - s_pick[1];
   }
 
+  // ---- token threshold: smallest D* with #(D <= D*) >= k_eff, found by wave 0 alone
+  if (w == 0) {
+    constexpr int BPL = (NB + 1 + kWave - 1) / kWave;   // distance bins per lane
+    int cnt[BPL];
+    int tot_d = 0;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const int bin = lane * BPL + j;
+      const int bc = min(bin, NB);
+      int v = 0;
+#pragma unroll
+      for (int i = 0; i < kSelWaves; ++i) v += int(s_hist[i * (NB + 1) + bc]);
+      cnt[j] = bin <= NB ? v : 0;
+      tot_d += cnt[j];
+    }
+    const int incl = wave_incl_sum(tot_d);
+    const int C = __builtin_amdgcn_readlane(incl, kWave - 1);
+    const int k_eff = min(a.kcap, C);
+    int run = incl - tot_d;
+    int fbin = -1, fbefore = 0;
+#pragma unroll
+    for (int j = 0; j < BPL; ++j) {
+      const bool hit = cnt[j] > 0 && run < k_eff && k_eff <= run + cnt[j];
+      fbin = hit ? lane * BPL + j : fbin;
+      fbefore = hit ? run : fbefore;
+      run += cnt[j];
+    }
+    if (fbin >= 0) {   // exactly one lane
+      s_pick[0] = fbin;
+      s_pick[1] = fbefore;
+      s_pick[2] = k_eff;
+    }
+  }
+  __syncthreads();
+  const int dstar = s_pick[0];
+  const int k_eff = s_pick[2];
+  const int need_eq = k_eff - s_pick[1];
+
   // ---- emit the selected tokens in ascending position (slots are in ascending t): one scan
-  // of the per-thread (#lt, #eq) counts places every slot.
-  int32_t* out_idx = a.idx + size_t(bh) * a.kcap;
+  // of the per-thread (#lt, #eq) counts places every slot. The list is assembled in LDS (the
+  // histograms are done with) and copied out coalesced when it fits; otherwise it is written
+  // straight to global memory. A slot not taken goes to the lane's trash entry.
+  int32_t* trash = out_idx + a.kcap + lane;
   int32_t* dbg_idx = dbg.token_idx ? dbg.token_idx + size_t(bh) * a.kcap : nullptr;
+  int32_t* stage = reinterpret_cast<int32_t*>(s_hist);
+  const bool staged = k_eff <= HB;
   int run_lt = 0, run_eq = 0;
   if (cache_d) {
     const int nchunks = (nslots + kSelThreads * kEmitSPT - 1) / (kSelThreads * kEmitSPT);
     for (int ch = 0; ch < nchunks; ++ch) {
       const int s0 = (ch * kSelThreads + tid) * kEmitSPT;
+      const bool any = s0 < nslots;
+      const int sc = any ? s0 : 0;                // read position (in bounds)
       uint32_t dv[kEmitSPT];
-      if (s0 < nslots) {
-        if constexpr (sizeof(DT) == 1) {
-          const uint4 x = *reinterpret_cast<const uint4*>(&s_dist[s0]);
-          const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
+      if constexpr (sizeof(DT) == 1) {
+        const uint4 x = *reinterpret_cast<const uint4*>(&s_dist[sc]);
+        const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
-          for (int u = 0; u < kEmitSPT; ++u) dv[u] = (wv[u >> 2] >> (8 * (u & 3))) & 0xFFu;
-        } else {
-          const uint4 x0 = *reinterpret_cast<const uint4*>(&s_dist[s0]);
-          const uint4 x1 = *reinterpret_cast<const uint4*>(&s_dist[s0 + 8]);
-          const uint32_t wv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
-#pragma unroll
-          for (int u = 0; u < kEmitSPT; ++u) dv[u] = (wv[u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
-        }
-#pragma unroll
-        for (int u = 0; u < kEmitSPT; ++u)
-          if (s0 + u >= nslots) dv[u] = kNone;
+        for (int u = 0; u < kEmitSPT; ++u) dv[u] = (wv[u >> 2] >> (8 * (u & 3))) & 0xFFu;
       } else {
+        const uint4 x0 = *reinterpret_cast<const uint4*>(&s_dist[sc]);
+        const uint4 x1 = *reinterpret_cast<const uint4*>(&s_dist[sc + 8]);
+        const uint32_t wv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-        for (int u = 0; u < kEmitSPT; ++u) dv[u] = kNone;
+        for (int u = 0; u < kEmitSPT; ++u) dv[u] = (wv[u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
       }
+#pragma unroll
+      for (int u = 0; u < kEmitSPT; ++u) dv[u] = (any && s0 + u < nslots) ? dv[u] : kNone;
       int nlt = 0, neq = 0;
 #pragma unroll
       for (int u = 0; u < kEmitSPT; ++u) {
         nlt += dv[u] < uint32_t(dstar) ? 1 : 0;
         neq += dv[u] == uint32_t(dstar) ? 1 : 0;
       }
+      // the chunk's slots lie in one page (kEmitSPT divides the page size)
+      const int t0 = slot_token(sc);
       int tot;
       const int ex = scan.excl((nlt << 16) | neq, &tot);
-      int eq_seen = run_eq + (ex & 0xFFFF);
-      int pos = run_lt + (ex >> 16) + min(eq_seen, need_eq);
+      const int eq0 = run_eq + (ex & 0xFFFF);
+      const int pos0 = run_lt + (ex >> 16) + min(eq0, need_eq);
+      int eq_seen = eq0, pos = pos0;
+      if (staged) {
 #pragma unroll
-      for (int u = 0; u < kEmitSPT; ++u) {
-        const bool is_eq = dv[u] == uint32_t(dstar);
-        const bool take = dv[u] < uint32_t(dstar) || (is_eq && eq_seen < need_eq);
-        eq_seen += is_eq ? 1 : 0;
-        if (take) {
-          const int t = slot_token(s0 + u);
-          out_idx[pos] = t;
-          if (dbg_idx) dbg_idx[pos] = t;
-          ++pos;
+        for (int u = 0; u < kEmitSPT; ++u) {
+          const bool is_eq = dv[u] == uint32_t(dstar);
+          const bool take = dv[u] < uint32_t(dstar) || (is_eq && eq_seen < need_eq);
+          eq_seen += is_eq ? 1 : 0;
+          stage[take ? pos : HB + lane] = t0 + u;
+          pos += take ? 1 : 0;
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < kEmitSPT; ++u) {
+          const bool is_eq = dv[u] == uint32_t(dstar);
+          const bool take = dv[u] < uint32_t(dstar) || (is_eq && eq_seen < need_eq);
+          eq_seen += is_eq ? 1 : 0;
+          *(take ? out_idx + pos : trash) = t0 + u;
+          pos += take ? 1 : 0;
+        }
+      }
+      if (dbg_idx && !staged) {
+        eq_seen = eq0;
+        pos = pos0;
+        for (int u = 0; u < kEmitSPT; ++u) {
+          const bool is_eq = dv[u] == uint32_t(dstar);
+          const bool take = dv[u] < uint32_t(dstar) || (is_eq && eq_seen < need_eq);
+          eq_seen += is_eq ? 1 : 0;
+          if (take) dbg_idx[pos++] = t0 + u;
         }
       }
       run_lt += tot >> 16;
       run_eq += tot & 0xFFFF;
+    }
+    if (staged) {
+      __syncthreads();
+      const int n4 = k_eff >> 2;   // rows of idx start 16-byte aligned
+      for (int i = tid; i < n4; i += kSelThreads)
+        reinterpret_cast<int4*>(out_idx)[i] = reinterpret_cast<const int4*>(stage)[i];
+      for (int i = 4 * n4 + tid; i < k_eff; i += kSelThreads) out_idx[i] = stage[i];
+      if (dbg_idx)
+        for (int i = tid; i < k_eff; i += kSelThreads) dbg_idx[i] = stage[i];
     }
   } else {
     for (int base = 0; base < nslots; base += kSelThreads) {
@@ -488,6 +600,7 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
       if (slot < nslots) {
         t = slot_token(slot);
         dd = distance(t);
+        if (dbg.dist) dbg.dist[size_t(bh) * s.Lmax + slot] = uint16_t(dd == kNone ? 0xFFFFu : dd);
       }
       const bool is_lt = dd < uint32_t(dstar), is_eq = dd == uint32_t(dstar);
       int tot;
@@ -509,11 +622,11 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
 }
 
 // ---------------------------------------------------------------------------------------------
-// Sparse attention over the selected rows: split-K with an in-kernel merge.
+// Sparse attention over the selected rows, split-K: one chunk of rows per workgroup.
 // A row of d = 128 is read as 16-byte pieces: 16 lanes per row for bf16, 32 for fp32. Every
 // wave issues all its K and V loads up front, then computes logits, the workgroup maximum, the
-// exponentials and the weighted V sum. The workgroup writes (o, m, l) for its chunk; the last
-// workgroup of (b, h) to finish (ticket) merges them into the output.
+// exponentials and the weighted V sum. The workgroup writes (o, m, l) for its chunk; the
+// combine kernel merges the chunks of each (b, h).
 // ---------------------------------------------------------------------------------------------
 template <int BF16>
 struct AttnShape {
@@ -540,7 +653,7 @@ struct AttnArgs {
   const int32_t* idx;
   const int32_t* cnt;
   float* part;        // [B][Hq][nsplit][kD + 2]: o[0..127], m, l
-  int kcap, nsplit;
+  int kcap, istride, nsplit;
   float scale_log2e;
 };
 
@@ -595,7 +708,7 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
 
     // selected rows: indices first (no branches, so all loads stay in flight together)
     const size_t kvrow0 = (size_t(b) * s.Hkv + g) * s.Lmax;
-    const int32_t* ib = a.idx + size_t(bh) * a.kcap;
+    const int32_t* ib = a.idx + size_t(bh) * a.istride;
     int tok[ITER];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) tok[it] = ib[min(row0 + it * RPI + rg, count - 1)];
@@ -726,7 +839,8 @@ DecodePlan plan_decode(const Shape& s, double rho, int k, float scale) {
   p.off_qrot = off;   off = align256(off + BH * kD * sizeof(float));
   p.off_qcode = off;  off = align256(off + BH * s.NW * sizeof(uint32_t));
   p.off_U = off;      off = align256(off + BH * s.Pmax * sizeof(float));
-  p.off_idx = off;    off = align256(off + BH * p.kcap * sizeof(int32_t));
+  p.istride = ((p.kcap + 3) & ~3) + kWave;   // 16-byte aligned rows, then the trash entries
+  p.off_idx = off;    off = align256(off + BH * p.istride * sizeof(int32_t));
   p.off_cnt = off;    off = align256(off + BH * sizeof(int32_t));
   p.off_part = off;   off = align256(off + BH * p.nsplit * (kD + 2) * sizeof(float));
   p.total = off;
@@ -792,12 +906,12 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
   }
   HHR_CHECK();
   HHR_MARK(2);
-  SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap};
+  SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap, p.istride};
   if (s.NB == 128) launch_select_nb<128>(s, c, sa, dbg, st);
   else launch_select_nb<256>(s, c, sa, dbg, st);
   HHR_CHECK();
   HHR_MARK(3);
-  AttnArgs aa{idx, cnt, part, p.kcap, p.nsplit, p.scale * 1.4426950408889634f};
+  AttnArgs aa{idx, cnt, part, p.kcap, p.istride, p.nsplit, p.scale * 1.4426950408889634f};
   dim3 grid(p.nsplit, s.Hq, s.B);
   if (s.kv_bf16)
     hipLaunchKernelGGL((attn_kernel<1>), grid, dim3(256), 0, st, s, c.K, c.V, q, aa);

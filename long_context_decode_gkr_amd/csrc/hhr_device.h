@@ -131,6 +131,16 @@ struct Strided {
 // Wave-level helpers
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
+
+// The value x, computed by every lane at this point: an empty asm statement with x as an
+// in/out VGPR operand, which keeps the compiler from sinking x's computation (a load, an LDS
+// read) into a branch when x is only used under a condition. No instruction is emitted.
+template <class T>
+__device__ __forceinline__ T materialize(T x) {
+  static_assert(sizeof(T) == 4, "one VGPR");
+  asm volatile("" : "+v"(x));
+  return x;
+}
 __device__ __forceinline__ int wave_id() {
   return __builtin_amdgcn_readfirstlane(int(threadIdx.x) / kWave);
 }
@@ -161,6 +171,15 @@ __device__ __forceinline__ int wave_incl_sum(int v) {
   v += dpp_i<0x118>(0, v);
   v += dpp_i<0x142, 0xa>(0, v);
   v += dpp_i<0x143, 0xc>(0, v);
+  return v;
+}
+
+// Inclusive prefix sum within each row of 16 lanes.
+__device__ __forceinline__ int row16_incl_sum(int v) {
+  v += dpp_i<0x111>(0, v);
+  v += dpp_i<0x112>(0, v);
+  v += dpp_i<0x114>(0, v);
+  v += dpp_i<0x118>(0, v);
   return v;
 }
 

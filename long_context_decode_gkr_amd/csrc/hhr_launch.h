@@ -37,6 +37,7 @@ struct DebugView {
 // Workspace carve-up of one decode call (byte offsets from the workspace base).
 struct DecodePlan {
   int kcap;        // token budget clamped to max_seq_len
+  int istride;     // per-(b, h) stride of the index list: kcap entries + one trash entry per lane
   int chunk;       // tokens per attention workgroup
   int nsplit;      // attention workgroups per (b, h)
   double rho;

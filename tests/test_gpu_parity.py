@@ -132,6 +132,38 @@ def test_decode_ties_all_bounds_equal():
     del torch
 
 
+@pytest.mark.parametrize("mode", ["cluster", "equal"])
+def test_decode_clustered_bounds(mode):
+    """Page extrema written directly (lo = hi = c_p v), so U_p = c_p (q~ . v): a clear top group,
+    then a cluster that straddles the n_keep cut. "cluster": 300 pages within 2e-6 of each
+    other (several radix passes, then one wave ranks the threshold bin); "equal": 200 pages
+    with exactly equal bounds (ties broken in page order by the scan)."""
+    torch = _torch()
+    cfg = _cfg(2, 16384, n_plant=0)
+    lay = hc.GpuLayer(cfg, max_seq_len=16384)
+    lay.build(method="fp64")
+    ref = hc.oracle_index(lay)
+    P, Hkv = 1024, cfg.num_kv_heads
+    rng = np.random.default_rng(11)
+    v = rng.choice([-1.0, 1.0], size=128).astype(np.float32)
+    c = rng.uniform(0.0, 1.5, size=P)
+    top = rng.choice(P, size=400, replace=False)
+    c[top[:100]] = rng.uniform(2.5, 3.0, size=100)
+    if mode == "cluster":
+        c[top[100:]] = 2.0 * (1.0 + rng.uniform(0.0, 2e-6, size=300))
+    else:
+        c[top[100:300]] = 2.0
+    ext = (c[:, None] * v[None, :]).astype(np.float32)          # [P][128]
+    lo = np.broadcast_to(ext, (1, Hkv, P, 128)).copy()
+    ref["lo"], ref["hi"] = lo, lo.copy()
+    dev = torch.from_numpy(lo).permute(0, 1, 3, 2).contiguous().cuda()
+    lay.cache.page_min.copy_(dev)
+    lay.cache.page_max.copy_(dev)
+    out, dbg = lay.decode(1 / 8, 400)
+    st = hc.check_decode(lay, out, dbg, 1 / 8, 400, ref_index=ref)
+    print(f"{mode}: page swaps vs the oracle {st['swaps']}")
+
+
 def test_decode_is_deterministic():
     torch = _torch()
     cfg = _cfg(2, 6000, n_plant=16)
