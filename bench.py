@@ -44,17 +44,18 @@ def log(msg, quiet):
 
 
 def algorithmic_bytes(cfg, L):
-    """Bytes each kernel must move per launch (one layer, one step) at context L.
+    """Bytes each kernel must move per launch (one layer, one append + decode step) at context L.
 
-    page_bound: min+max of every page of every KV head (128 ch x 8 B per page), q and R read,
-                U written (4 B per query head and page).
-    select:     U read, the codes of the kept pages' tokens (16 B per candidate and query head),
-                W read, the selected indices written.
+    prep:       q, k_new, v_new and R read, q~ written; the appended token's K and V rows
+                and its page's extrema column pair read and written.
+    page_bound: min+max of every page of every KV head (128 ch x 8 B per page), q~ read, U
+                written (4 B per query head and page); the code workgroups: q, k_new and W
+                read, the query codes and the new key's code written.
+    select:     U and the query code read, the codes of the kept pages' tokens (16 B per
+                candidate and query head), the selected indices written.
     sparse_attn: K and V rows of the selected tokens (2 x 256 B per token and query head),
                 indices and q read, one (o, m, l) partial per 256 tokens written.
     combine:    the partials read, the output written.
-    prep:       the appended token (one K and V row, the page extrema column pair and the code
-                per KV head), q read, R and W read, q~ and the query codes written.
     """
     d, S, nb = cfg.head_dim, cfg.page_size, cfg.hash_bits
     Hq, Hkv = cfg.num_q_heads, cfg.num_kv_heads
@@ -62,15 +63,15 @@ def algorithmic_bytes(cfg, L):
     n_keep = min(P, max(1, math.ceil(cfg.keep_ratio * P)))
     k = min(cfg.token_budget, n_keep * S)
     esz = 2
-    rw = Hkv * d * d * 4 + Hkv * d * nb * 4
     return {
-        "page_bound": Hkv * P * d * 8 + Hq * P * 4 + Hq * d * esz + Hkv * d * d * 4,
-        "select": Hq * P * 4 + Hq * n_keep * S * (nb // 8) + Hkv * d * nb * 4 + Hq * k * 4,
+        "prep": Hq * d * esz + Hkv * 2 * d * esz + Hkv * d * d * 4 + Hq * d * 4
+                + Hkv * 2 * d * esz + Hkv * 2 * d * 4 * 2,
+        "page_bound": Hkv * P * d * 8 + Hq * d * 4 + Hq * P * 4
+                      + Hq * d * esz + Hkv * d * esz + Hkv * d * nb * 4 + Hq * nb // 8 + Hkv * nb // 8,
+        "select": Hq * P * 4 + Hq * nb // 8 + Hq * n_keep * S * (nb // 8) + Hq * k * 4,
         "sparse_attn": Hq * k * 2 * d * esz + Hq * k * 4 + Hq * d * esz
         + Hq * -(-k // 256) * (d + 2) * 4,
         "combine": Hq * -(-k // 256) * (d + 2) * 4 + Hq * d * 4,
-        "prep": Hkv * (2 * d * esz + 2 * d * 4 * 2 + nb // 8) + rw + Hq * d * esz
-                + Hq * (d * 4 + nb // 8),
     }
 
 

@@ -122,9 +122,11 @@ typedef struct {
  *   token_count [B][Hq]             how many were selected
  *   kernel_events  NULL or 6 caller-created events recorded on the stream around the five
  *                  kernels of a decode step (per-kernel timing): before the preparation kernel
- *                  (query rotation and code, and the append of hhr_append_decode), before the
- *                  page-bound kernel, before the selection kernel, before the attention kernel,
- *                  before the kernel that merges the attention partials, and after it */
+ *                  (query rotation; in hhr_append_decode also the new token's K/V rows and page
+ *                  extrema), before the page-bound kernel (which also computes the query codes
+ *                  and the new key's code), before the selection kernel, before the attention
+ *                  kernel, before the kernel that merges the attention partials (and commits
+ *                  the append), and after it */
 typedef struct {
   float* q_rot;
   uint32_t* q_code;
@@ -175,10 +177,11 @@ hhr_status hhr_decode(const hhr_dims* dims, const hhr_params* params, const hhr_
                       const void* q, const float* R, const float* W, void* ws, size_t ws_bytes,
                       float* out, const hhr_debug* dbg, hhr_stream_t stream);
 
-/* hhr_append followed by hhr_decode in one call (the query attends over the new token too).
- * The append is folded into the decode's first kernel, so a generation step costs one launch
- * less than the two calls. Same arguments and rules as the two calls; append_ticket is
- * required. */
+/* hhr_append followed by hhr_decode in one call (the query attends over the new token too),
+ * with the same results. The append is folded into the decode's kernels (the preparation
+ * kernel stores the K/V rows and updates the page, the page-bound kernel computes and stores
+ * the key's code, the last kernel advances seq_lens), so a generation step costs no launch
+ * beyond the decode. Same arguments and rules as the two calls; append_ticket is required. */
 hhr_status hhr_append_decode(const hhr_dims* dims, const hhr_params* params,
                              const hhr_cache* cache, const void* k_new, const void* v_new,
                              const void* q, const float* R, const float* W, void* ws,

@@ -133,23 +133,26 @@ hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Step preparation, grid (4 column slices, KV head g, sequence b). Each workgroup
-//   * appends the new token when k_new is given: writes its slice of the K and V rows, folds its
-//     32 channels of k~ = k R_g into page t / S (opens the page when t % S == 0) and writes its
-//     code words; the last workgroup of the sequence to finish advances seq_lens[b] (a
-//     per-sequence ticket, left at 0);
-//   * prepares the G queries of the group when q is given: its 32 channels of q~ = q R_g (Eq. 4)
-//     and its code words of sign(q W_g) (Eq. 1, Eq. 10), written to the decode workspace.
-// The new key (vector 0) and the G queries (vectors 1 .. G) share every R_g / W_g column of
-// the slice, which is read once. A column is split over 8 lanes of
-// 16 terms each (fp64 partial sums of exact products, reduced by DPP): threads [0, 256) own the
-// 32 rotation columns, threads [256, 256 + 8 NB / 4) the NB / 4 code columns.
+// Step preparation, grid (4 column slices, KV head g, sequence b), 256 + 8 NB / 4 threads.
+// Each workgroup owns 32 channels of the rotation and NB / 4 code columns. Vector 0 is the new
+// key (when k_new is given and seq_lens[b] < max_seq_len), vectors 1 .. G the queries (decode
+// mode). Each R_g / W_g column of the slice is read once and applied to every vector.
+//   * rotation lanes [0, 256): column j over 8 lanes of 16 terms, fp64 sums of exact products
+//     reduced by DPP: k~ is folded into page t / S (which it opens when t % S == 0), q~
+//     (Eq. 4) goes to the decode workspace; the workgroup also stores its slice of the K and V
+//     rows of t;
+//   * code lanes: column c of W the same way in fp32 with a certificate for the sign, the few
+//     uncertain bits recomputed in fp64 and, where that is not certain either, exactly:
+//     sign(k W_g) into the cache and sign(q W_g) (Eq. 1, Eq. 10) into the decode workspace.
+// Append mode (hhr_append) also advances seq_lens[b]: the last workgroup of the sequence to
+// finish does it (a per-sequence ticket, left at 0). In decode mode the step's last kernel
+// does it, after every kernel of the step has worked on t + 1 tokens.
 // ---------------------------------------------------------------------------------------------
 constexpr int kPrepSlices = 4;
 constexpr int kPrepParts = 8;
 constexpr int kMaxVec = 9;   // 1 key + up to 8 queries
 
-template <int NB, int KB, int QB>   // KB, QB: keys/values, queries in bf16
+template <int NB, int KB, int QB, int DEC>   // KB, QB: keys/values, queries in bf16
 __global__ void __launch_bounds__(256 + kPrepParts * NB / kPrepSlices)
 prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __restrict__ vn,
             const void* __restrict__ q, const float* __restrict__ R, const float* __restrict__ W,
@@ -160,31 +163,24 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   constexpr int WPS = CC / 32;                  // code words per slice (1 or 2)
   constexpr int T = kD / kPrepParts;            // terms per lane (16)
   constexpr int NT = 256 + kPrepParts * NB / kPrepSlices;   // workgroup size
+  constexpr int QPT = DEC ? (8 * kD + NT - 1) / NT : 1;     // query elements per thread
   const int sl = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int part = tid & (kPrepParts - 1);
   const bool rot = tid < 256;                   // rotation lanes; the others compute code bits
-  const int nq = q ? s.G : 0;
+  const int nq = DEC ? s.G : 0;
   const bool has_k = kn != nullptr;
   if (!has_k && nq == 0) return;
 
-  __shared__ float xs[kMaxVec][kD];             // row 0: the new key; rows 1 .. G: the queries
+  __shared__ float xs[kMaxVec][kD];
   __shared__ uint8_t bits[kMaxVec][CC];
 
-  // Everything that does not depend on the sequence length is loaded together with it: this
-  // lane's 16 column terms, the new key and value elements and the queries.
+  // Everything that does not depend on the sequence length is loaded together with it: the
+  // new key and value elements, the queries, then this lane's 16 column terms.
   const int t = c.seq_lens[b];
   const int j = sl * 32 + (tid >> 3);           // rotation column (rotation lanes)
   const int lc = (tid - 256) >> 3;              // code column within the slice (code lanes)
   const int cc = sl * CC + lc;
-  float cv[T];
-  {
-    const float* col = rot ? R + size_t(g) * kD * kD + size_t(part * T) * kD + j
-                           : W + size_t(g) * kD * NB + size_t(part * T) * NB + cc;
-    const int stride = rot ? kD : NB;
-#pragma unroll
-    for (int i = 0; i < T; ++i) cv[i] = col[size_t(i) * stride];
-  }
   // The vector loads carry no branch (a branch would make the compiler wait for each load
   // before the join): a missing key or query input is replaced by the other input, whose
   // values are then loaded but not used, and indices are clamped.
@@ -193,12 +189,21 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   const int kel = min(tid, kD - 1);
   const uint32_t kraw = load_raw(has_k ? kn : q, has_k ? krow + kel : 0, KB);
   const uint32_t vraw = load_raw(has_k ? vn : q, has_k ? krow + kel : 0, KB);
-  static_assert(2 * NT >= 8 * kD, "two query elements per thread cover G <= 8 queries");
-  uint32_t qraw[2];
+  uint32_t qraw[QPT];
+  if constexpr (DEC) {
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int e = min(tid + r * NT, nq * kD - 1);
-    qraw[r] = load_raw(q ? q : kn, q ? (size_t(b) * s.Hq + g * s.G) * kD + e : 0, QB);
+    for (int r = 0; r < QPT; ++r) {
+      const int e = min(tid + r * NT, nq * kD - 1);
+      qraw[r] = load_raw(q, (size_t(b) * s.Hq + g * s.G) * kD + e, QB);
+    }
+  }
+  float cv[T];
+  {
+    const float* col = rot ? R + size_t(g) * kD * kD + size_t(part * T) * kD + j
+                           : W + size_t(g) * kD * NB + size_t(part * T) * NB + cc;
+    const int stride = rot ? kD : NB;
+#pragma unroll
+    for (int i = 0; i < T; ++i) cv[i] = col[size_t(i) * stride];
   }
   // The open page's extrema (page t / S) for this lane's rotation column (code lanes read
   // column 32 sl, unused): in bounds whatever t is; needed only after the dot products.
@@ -221,10 +226,12 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
     }
     xs[0][tid] = raw_to_f32(kraw, KB);
   }
+  if constexpr (DEC) {
 #pragma unroll
-  for (int r = 0; r < 2; ++r) {
-    const int e = tid + r * NT;
-    if (e < nq * kD) xs[1 + e / kD][e % kD] = raw_to_f32(qraw[r], QB);
+    for (int r = 0; r < QPT; ++r) {
+      const int e = tid + r * NT;
+      if (e < nq * kD) xs[1 + e / kD][e % kD] = raw_to_f32(qraw[r], QB);
+    }
   }
   __syncthreads();
 
@@ -259,29 +266,28 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
       }
     }
   } else {
-    // ---- code column cc, terms [16 part, 16 part + 16)
-    double z[kMaxVec], sa[kMaxVec];
+    // ---- code column cc, terms [16 part, 16 part + 16): fp32 with a certificate
+    float z[kMaxVec], sa[kMaxVec];
 #pragma unroll
     for (int v = 0; v < kMaxVec; ++v) {
-      double zz = 0.0, ss = 0.0;
+      float zz = 0.f, ss = 0.f;
       if (active(v)) {
         const float* x = &xs[v][part * T];
 #pragma unroll
         for (int i = 0; i < T; ++i) {
-          const double pr = double(x[i]) * double(cv[i]);
-          zz += pr;
-          ss += fabs(pr);
+          zz = fmaf(x[i], cv[i], zz);
+          ss = fmaf(fabsf(x[i]), fabsf(cv[i]), ss);
         }
       }
-      z[v] = group_sum_f64<3>(zz);
-      sa[v] = group_sum_f64<3>(ss);
+      z[v] = group8_sum(zz);
+      sa[v] = group8_sum(ss);
     }
     if (part == 0) {
       const float* wcol = W + size_t(g) * kD * NB + cc;
-      for (int v = 0; v <= nq; ++v) {
+      for (int v = 0; v < kMaxVec; ++v) {
         if (!active(v)) continue;
-        int cb = certain_bit(z[v], sa[v]);
-        if (cb < 0) cb = int(exact_bit(static_cast<const float*>(&xs[v][0]), wcol, NB));
+        int cb = certain_bit_f32(z[v], sa[v]);
+        if (cb < 0) cb = int(certified_bit(static_cast<const float*>(&xs[v][0]), wcol, NB));
         bits[v][lc] = uint8_t(cb);
       }
     }
@@ -304,17 +310,19 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
       }
     }
   }
-  if (app) {
-    // Every workgroup of sequence b has read seq_lens[b] (the load completed before the
-    // barrier) before it takes a ticket, so the last one can advance it; the following kernels
-    // see the new value at the kernel boundary. No device-scope fence is needed (on gfx950 one
-    // would write back and invalidate the whole L2 of the XCD).
-    __syncthreads();
-    if (tid == 0) {
-      const int done = atomicAdd(&c.ticket[b], 1);
-      if (done == s.Hkv * kPrepSlices - 1) {
-        c.ticket[b] = 0;
-        c.seq_lens[b] = t + 1;
+  if constexpr (!DEC) {
+    if (app) {
+      // Every workgroup of sequence b has read seq_lens[b] (the load completed before the
+      // barrier) before it takes a ticket, so the last one can advance it; the following
+      // kernels see the new value at the kernel boundary. No device-scope fence is needed (on
+      // gfx950 one would write back and invalidate the whole L2 of the XCD).
+      __syncthreads();
+      if (tid == 0) {
+        const int done = atomicAdd(&c.ticket[b], 1);
+        if (done == s.Hkv * kPrepSlices - 1) {
+          c.ticket[b] = 0;
+          c.seq_lens[b] = t + 1;
+        }
       }
     }
   }
@@ -324,34 +332,40 @@ template <int NB, int KB, int QB>
 static void launch_prep_t(const Shape& s, const CacheView& c, const void* k_new,
                           const void* v_new, const void* q, const float* R, const float* W,
                           float* qrot, uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode,
-                          hipStream_t st) {
+                          PrepMode mode, hipStream_t st) {
   dim3 grid(kPrepSlices, s.Hkv, s.B);
-  hipLaunchKernelGGL((prep_kernel<NB, KB, QB>), grid, dim3(256 + kPrepParts * NB / kPrepSlices),
-                     0, st, s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
+  dim3 block(256 + kPrepParts * NB / kPrepSlices);
+  if (mode == PrepMode::kDecode)
+    hipLaunchKernelGGL((prep_kernel<NB, KB, QB, 1>), grid, block, 0, st, s, c, k_new, v_new, q,
+                       R, W, qrot, qcode, dbg_qrot, dbg_qcode);
+  else
+    hipLaunchKernelGGL((prep_kernel<NB, KB, QB, 0>), grid, block, 0, st, s, c, k_new, v_new, q,
+                       R, W, qrot, qcode, dbg_qrot, dbg_qcode);
 }
 
 template <int NB>
 static void launch_prep_nb(const Shape& s, const CacheView& c, const void* k_new,
                            const void* v_new, const void* q, const float* R, const float* W,
                            float* qrot, uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode,
-                           hipStream_t st) {
+                           PrepMode mode, hipStream_t st) {
   if (s.kv_bf16 && s.q_bf16)
-    launch_prep_t<NB, 1, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
+    launch_prep_t<NB, 1, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
   else if (s.kv_bf16)
-    launch_prep_t<NB, 1, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
+    launch_prep_t<NB, 1, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
   else if (s.q_bf16)
-    launch_prep_t<NB, 0, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
+    launch_prep_t<NB, 0, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
   else
-    launch_prep_t<NB, 0, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
+    launch_prep_t<NB, 0, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
 }
 
 hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, const void* v_new,
                        const void* q, const float* R, const float* W, float* qrot,
-                       uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, hipStream_t st) {
+                       uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, PrepMode mode,
+                       hipStream_t st) {
   if (s.NB == 128)
-    launch_prep_nb<128>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
+    launch_prep_nb<128>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
   else
-    launch_prep_nb<256>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, st);
+    launch_prep_nb<256>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
   return hipGetLastError();
 }
 

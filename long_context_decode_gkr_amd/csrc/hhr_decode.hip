@@ -36,35 +36,38 @@ constexpr int kDistCache = 32768;      // candidate slots whose distance stays i
 // Coarse stage: page bounds (Eq. 3) for the G query heads of one KV head from ONE read of the
 // page extrema. Lane l of wave w covers pages p0 + 4l .. p0 + 4l + 3 and channels
 // 16w .. 16w + 15: 32 float4 loads per lane are issued at once, q~ (prepared by the preparation
-// kernel) is read with wave-uniform scalar loads, and the 8 waves' partial sums meet in LDS.
+// kernel) is read with wave-uniform loads, and the 8 waves' partial sums meet in LDS.
+// Nothing else happens here: while the extrema stream in, any other load waits behind them, so
+// work that depends on one would sit on the kernel's tail.
 // ---------------------------------------------------------------------------------------------
+struct BoundArgs {
+  const float* qrot;      // [B][Hq][128] q~ from the preparation kernel
+  float* U;               // [B][Hq][Pmax]
+  int appended;           // a token is appended in this step (seq_lens is advanced at its end)
+};
+
 template <int G>
 __global__ void __launch_bounds__(kBoundThreads)
-page_bound_kernel(Shape s, const float* __restrict__ pmin, const float* __restrict__ pmax,
-                  const int32_t* __restrict__ seq_lens, const float* __restrict__ qrot,
-                  float* __restrict__ U, float* __restrict__ dbg_U) {
+page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) {
   const int b = blockIdx.z, g = blockIdx.y, p0 = blockIdx.x * kBoundPages;
-  const int L = min(max(seq_lens[b], 0), s.Lmax);
+  const int t = c.seq_lens[b];
+  const bool app = a.appended && t >= 0 && t < s.Lmax;
+  const int L = min(max(t, 0) + (app ? 1 : 0), s.Lmax);
   const int P = (L + s.S - 1) / s.S;
   if (p0 >= P) return;
   const int w = wave_id(), lane = lane_id();
   const int j0 = w * 16;
   const int pl = p0 + lane * 4;
-  const bool live = pl < P;
+  const int plc = min(pl, s.Pmax - 4);             // in bounds for every lane
   const size_t srow = (size_t(b) * s.Hkv + g) * kD + j0;
 
   float4 lo[16], hi[16];
-  if (live) {
 #pragma unroll
-    for (int jj = 0; jj < 16; ++jj) {
-      lo[jj] = *reinterpret_cast<const float4*>(pmin + (srow + jj) * s.Pmax + pl);
-      hi[jj] = *reinterpret_cast<const float4*>(pmax + (srow + jj) * s.Pmax + pl);
-    }
-  } else {
-#pragma unroll
-    for (int jj = 0; jj < 16; ++jj) lo[jj] = hi[jj] = make_float4(0.f, 0.f, 0.f, 0.f);
+  for (int jj = 0; jj < 16; ++jj) {
+    lo[jj] = *reinterpret_cast<const float4*>(c.pmin + (srow + jj) * s.Pmax + plc);
+    hi[jj] = *reinterpret_cast<const float4*>(c.pmax + (srow + jj) * s.Pmax + plc);
   }
-  const float* qb = qrot + (size_t(b) * s.Hq + size_t(g) * G) * kD + j0;
+  const float* qb = a.qrot + (size_t(b) * s.Hq + size_t(g) * G) * kD + j0;
 
   float acc[G][4];
 #pragma unroll
@@ -97,7 +100,7 @@ page_bound_kernel(Shape s, const float* __restrict__ pmin, const float* __restri
       for (int w2 = 0; w2 < kBoundThreads / kWave; ++w2)
         sum += reinterpret_cast<const float*>(&red[w2][hh][0])[pp];
       const size_t oi = (size_t(b) * s.Hq + g * G + hh) * s.Pmax + p;
-      U[oi] = sum;
+      a.U[oi] = sum;
       if (dbg_U) dbg_U[oi] = sum;
     }
   }
@@ -146,6 +149,7 @@ struct SelectArgs {
   double rho;
   int kcap;
   int istride;        // row stride of idx: kcap live entries, then one trash entry per lane
+  int appended;       // a token is appended in this step (seq_lens is advanced at its end)
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -180,14 +184,16 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   const int h = blockIdx.x, b = blockIdx.y, g = h / s.G;
   const int bh = b * s.Hq + h;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-  const int L = min(max(c.seq_lens[b], 0), s.Lmax);
+  const int t = c.seq_lens[b];                   // position of the appended token, if any
+  const bool app = a.appended && t >= 0 && t < s.Lmax;
+  const int L = min(max(t, 0) + (app ? 1 : 0), s.Lmax);
   const int P = (L + s.S - 1) / s.S;
 
   // Live entries, then one dummy entry per lane.
   __shared__ int32_t s_pages[kMaxPages + kWave];
   __shared__ __align__(16) DT s_dist[kDistCache + kWave];
   __shared__ __align__(16) uint32_t s_hist[HB + kWave];
-  __shared__ uint32_t s_qw[NW];
+  __shared__ uint32_t s_qw[NW];       // query code
   __shared__ int s_wt[2][kSelWaves];
   __shared__ uint32_t s_mm[2][kSelWaves];
   __shared__ int s_pick[3];
@@ -207,7 +213,8 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   }
   const int n_keep = min(P, max(1, int(ceil(a.rho * double(P)))));
 
-  // ---- query code (from the preparation kernel), page keys to registers, histograms cleared
+  // ---- query code (from the code workgroups of the bound kernel), page keys to registers,
+  // histograms cleared
   if (tid < NW) s_qw[tid] = a.qcode[size_t(bh) * NW + tid];
   if (tid == 0) s_ncand = 0;
   for (int i = tid; i < HB; i += kSelThreads) s_hist[i] = 0;
@@ -250,6 +257,7 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
     kmin = wave_min_u32(s_mm[0][lane % kSelWaves]);
     kmax = wave_max_u32(s_mm[1][lane % kSelWaves]);
   }
+
 
   // ---- coarse selection. The kept set is described, where possible, by a cut (ck, ci): page
   // i is kept iff (key_i, i) <= (ck, ci) lexicographically (smaller key = larger U, ties to the
@@ -419,9 +427,9 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   const bool cache_d = nslots <= kDistCache;
   const uint32_t* cbase = c.codes + (size_t(b) * s.Hkv + g) * s.Lmax * NW;
   auto slot_token = [&](int slot) { return (s_pages[slot >> lgS] << lgS) + (slot & (s.S - 1)); };
-  auto distance = [&](int t) -> uint32_t {
-    if (t >= L) return kNone;
-    const uint4* cp = reinterpret_cast<const uint4*>(cbase + size_t(t) * NW);
+  auto distance = [&](int tk) -> uint32_t {
+    if (tk >= L) return kNone;
+    const uint4* cp = reinterpret_cast<const uint4*>(cbase + size_t(tk) * NW);
     uint32_t dd = 0;
 #pragma unroll
     for (int v = 0; v < NW / 4; ++v) {
@@ -595,11 +603,11 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   } else {
     for (int base = 0; base < nslots; base += kSelThreads) {
       const int slot = base + tid;
-      int t = 0;
+      int tk = 0;
       uint32_t dd = kNone;
       if (slot < nslots) {
-        t = slot_token(slot);
-        dd = distance(t);
+        tk = slot_token(slot);
+        dd = distance(tk);
         if (dbg.dist) dbg.dist[size_t(bh) * s.Lmax + slot] = uint16_t(dd == kNone ? 0xFFFFu : dd);
       }
       const bool is_lt = dd < uint32_t(dstar), is_eq = dd == uint32_t(dstar);
@@ -608,8 +616,8 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
       const int eq_seen = run_eq + (ex & 0xFFFF);
       const int pos = run_lt + (ex >> 16) + min(eq_seen, need_eq);
       if (is_lt || (is_eq && eq_seen < need_eq)) {
-        out_idx[pos] = t;
-        if (dbg_idx) dbg_idx[pos] = t;
+        out_idx[pos] = tk;
+        if (dbg_idx) dbg_idx[pos] = tk;
       }
       run_lt += tot >> 16;
       run_eq += tot & 0xFFFF;
@@ -787,10 +795,18 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
 // Merge of the split partials of one (b, h): o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
 // Partials are read in batches of 16, all loads of a batch issued before any use, and merged
 // without branches (an empty partial has m = -inf, l = 0 and gets weight 0).
+// The step's last kernel also commits an append: every earlier kernel of the step read
+// seq_lens[b] = t and worked on t + 1 tokens; the workgroup of head 0 now stores t + 1.
 __global__ void __launch_bounds__(kD)
-combine_kernel(const float* __restrict__ part, int nsplit, float* __restrict__ out) {
+combine_kernel(const float* __restrict__ part, int nsplit, float* __restrict__ out,
+               int32_t* __restrict__ seq_lens, int Hq, int Lmax, int appended) {
   constexpr int CB = 16;
   const int bh = blockIdx.x, d = threadIdx.x;
+  if (appended && d == 0 && bh % Hq == 0) {
+    const int b = bh / Hq;
+    const int t = seq_lens[b];
+    if (t >= 0 && t < Lmax) seq_lens[b] = t + 1;
+  }
   const float* pb = part + size_t(bh) * nsplit * (kD + 2);
   float Mx = -INFINITY, Ls = 0.f, Os = 0.f;
   for (int i0 = 0; i0 < nsplit; i0 += CB) {
@@ -848,11 +864,11 @@ DecodePlan plan_decode(const Shape& s, double rho, int k, float scale) {
 }
 
 template <int G>
-static void launch_bound_t(const Shape& s, const CacheView& c, const float* qrot, float* U,
+static void launch_bound_t(const Shape& s, const CacheView& c, const BoundArgs& a,
                            const DebugView& dbg, hipStream_t st) {
   dim3 grid((s.Pmax + kBoundPages - 1) / kBoundPages, s.Hkv, s.B);
-  hipLaunchKernelGGL((page_bound_kernel<G>), grid, dim3(kBoundThreads), 0, st, s, c.pmin, c.pmax,
-                     c.seq_lens, qrot, U, dbg.bounds);
+  hipLaunchKernelGGL((page_bound_kernel<G>), grid, dim3(kBoundThreads), 0, st, s, c, a,
+                     dbg.bounds);
 }
 
 template <int NB, int EPT, int NT>
@@ -869,12 +885,11 @@ constexpr int kSelNT = 1024;
 template <int NB>
 static void launch_select_nb(const Shape& s, const CacheView& c, const SelectArgs& a,
                              const DebugView& dbg, hipStream_t st) {
+  static_assert(kMaxPages <= 16 * kSelNT, "16 pages per thread cover the page capacity");
   const int ept = (s.Pmax + kSelNT - 1) / kSelNT;
   if (ept <= 4) launch_select_t<NB, 4, kSelNT>(s, c, a, dbg, st);
   else if (ept <= 8) launch_select_t<NB, 8, kSelNT>(s, c, a, dbg, st);
-  else if (ept <= 16) launch_select_t<NB, 16, kSelNT>(s, c, a, dbg, st);
-  else if (ept <= 32) launch_select_t<NB, 32, kSelNT>(s, c, a, dbg, st);
-  else launch_select_t<NB, 64, kSelNT>(s, c, a, dbg, st);
+  else launch_select_t<NB, 16, kSelNT>(s, c, a, dbg, st);
 }
 
 hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c,
@@ -894,19 +909,23 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
 #define HHR_CHECK() \
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
+  // seq_lens[b] stays t during the step; every kernel works on t + 1 tokens when a token is
+  // appended, and the last kernel stores t + 1.
   HHR_MARK(0);
-  e = launch_prep(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg.q_rot, dbg.q_code, st);
+  e = launch_prep(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg.q_rot, dbg.q_code,
+                  PrepMode::kDecode, st);
   if (e != hipSuccess) return e;
   HHR_MARK(1);
+  BoundArgs ba{qrot, U, k_new != nullptr ? 1 : 0};
   switch (s.G) {
-    case 1: launch_bound_t<1>(s, c, qrot, U, dbg, st); break;
-    case 2: launch_bound_t<2>(s, c, qrot, U, dbg, st); break;
-    case 4: launch_bound_t<4>(s, c, qrot, U, dbg, st); break;
-    default: launch_bound_t<8>(s, c, qrot, U, dbg, st); break;
+    case 1: launch_bound_t<1>(s, c, ba, dbg, st); break;
+    case 2: launch_bound_t<2>(s, c, ba, dbg, st); break;
+    case 4: launch_bound_t<4>(s, c, ba, dbg, st); break;
+    default: launch_bound_t<8>(s, c, ba, dbg, st); break;
   }
   HHR_CHECK();
   HHR_MARK(2);
-  SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap, p.istride};
+  SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap, p.istride, k_new != nullptr ? 1 : 0};
   if (s.NB == 128) launch_select_nb<128>(s, c, sa, dbg, st);
   else launch_select_nb<256>(s, c, sa, dbg, st);
   HHR_CHECK();
@@ -919,7 +938,8 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
     hipLaunchKernelGGL((attn_kernel<0>), grid, dim3(256), 0, st, s, c.K, c.V, q, aa);
   HHR_CHECK();
   HHR_MARK(4);
-  hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(kD), 0, st, part, p.nsplit, out);
+  hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(kD), 0, st, part, p.nsplit, out,
+                     c.seq_lens, s.Hq, s.Lmax, k_new != nullptr ? 1 : 0);
   HHR_CHECK();
   HHR_MARK(5);
 #undef HHR_MARK

@@ -94,6 +94,22 @@ __device__ __forceinline__ int certain_bit(double z, double s) {
   return -1;
 }
 
+// Certainty test for a code bit from fp32 sums over 128 products p_i = x_i w_i, computed as
+// 8 lanes of 16 fused multiply-adds in index order (the first with a zero addend) combined by
+// a 3-level tree: z = sum p_i, s = sum |p_i|. Along any path a product meets 19 roundings and
+// no other error (inside an FMA the product is exact), so |z - exact| <= gamma_19 sum|p| with
+// gamma_19 = 19 u / (1 - 19 u), u = 2^-24, i.e. below 1.2e-6 sum|p|, and s differs from sum|p|
+// by the same relative amount; tau = 2^-19 s (1.9e-6 s) covers both, and 2^-140 covers the
+// absolute error of underflowing additions (each below 2^-150). Returns 1 / 0 when the sign of
+// z is certain, -1 otherwise (also for s == 0, whose products may have underflowed, and for
+// an overflow to inf or NaN, where both comparisons fail).
+__device__ __forceinline__ int certain_bit_f32(float z, float s) {
+  const float tau = s * 0x1p-19f + 0x1p-140f;
+  if (s > 0.f && z > tau) return 1;
+  if (s > 0.f && z < -tau) return 0;
+  return -1;
+}
+
 // Exact code bit [sum_j x[j] * w[j * w_stride] > 0] (j < 128); x: fp32 values through any
 // indexable accessor, w: fp32 in global memory.
 template <typename XPtr>
@@ -214,6 +230,14 @@ __device__ __forceinline__ float row16_sum(float v) {
   v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
   v += dpp_f<0x141>(v);  // row_half_mirror
   v += dpp_f<0x140>(v);  // row_mirror
+  return v;
+}
+
+// Sum of an fp32 value over aligned groups of 8 lanes, returned in every lane of the group.
+__device__ __forceinline__ float group8_sum(float v) {
+  v += dpp_f<0xB1>(v);   // quad_perm [1,0,3,2]
+  v += dpp_f<0x4E>(v);   // quad_perm [2,3,0,1]
+  v += dpp_f<0x141>(v);  // row_half_mirror
   return v;
 }
 

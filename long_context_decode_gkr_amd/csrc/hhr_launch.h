@@ -51,12 +51,18 @@ hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R,
                              hipStream_t st);
 hipError_t launch_build_mfma(const Shape& s, const CacheView& c, const float* R, const float* W,
                              hipStream_t st);
-// Optional append of one token (k_new != NULL) and preparation of the queries (q != NULL):
-// q~ into qrot [B][Hq][128], query codes into qcode [B][Hq][NW].
+// Preparation kernel.
+//   kAppend (hhr_append): appends k_new / v_new: K/V rows, page extrema, key code, then
+//     advances seq_lens.
+//   kDecode (first kernel of a decode step): q~ of every query head into qrot [B][Hq][128],
+//     the query codes into qcode [B][Hq][NW] and, when k_new != NULL, the appended token's K/V
+//     rows, page extrema and code (seq_lens is advanced by the step's last kernel).
+enum class PrepMode { kAppend, kDecode };
 hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, const void* v_new,
                        const void* q, const float* R, const float* W, float* qrot,
-                       uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, hipStream_t st);
-// The decode step, preceded by an append when k_new != NULL.
+                       uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, PrepMode mode,
+                       hipStream_t st);
+// The decode step, with the append of k_new / v_new folded into its kernels when given.
 hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c,
                          const void* k_new, const void* v_new, const void* q, const float* R,
                          const float* W, void* ws, float* out, const DebugView& dbg,

@@ -287,6 +287,42 @@ def test_build_mfma_exact_path_for_zero_and_tiny_projections():
     assert np.array_equal((bits0 >> 16) & 0xFF, k2pos * 0xFF)              # sign of 2^-30 k2
 
 
+def test_step_codes_exact_for_zero_and_tiny_projections():
+    """Codes computed in the decode step (queries) and by appends (keys) where the projection
+    is exactly 0 (16 columns: x0 - x1 with x0 == x1) or tiny (8 columns: 2^-30 x2): the
+    certified fp32 test must defer to the exact path and still match the oracle."""
+    torch = _torch()
+    cfg = _cfg(3, 2000, n_plant=0, num_q_heads=4, num_kv_heads=1)
+    data = synth.make_layer(cfg, max_seq_len=2048)
+    data["q"][..., 1] = data["q"][..., 0]
+    W = data["W"]
+    W[:, :, :24] = 0.0
+    W[:, 0, :24] = 1.0
+    W[:, 1, :24] = -1.0
+    W[:, 2, 16:24] = np.float32(2.0 ** -30)
+    lay = hc.GpuLayer(cfg, data=data)
+    lay.build(method="fp64")
+    kn, vn = synth.append_tokens(cfg, 4)
+    kn[..., 1] = kn[..., 0]
+    dec = hb.Decoder(lay.dims, cfg.keep_ratio, 200)
+    out = torch.empty((1, 4, 128), dtype=torch.float32, device="cuda")
+    for i in range(3):
+        hb.append(lay.cache, hc.to_dev(kn[i], lay.tdt), hc.to_dev(vn[i], lay.tdt), lay.R, lay.W)
+    dbg = hb.Debug(lay.dims, 200)
+    dec(lay.cache, lay.q, lay.R, lay.W, out, dbg, k_new=hc.to_dev(kn[3], lay.tdt),
+        v_new=hc.to_dev(vn[3], lay.tdt))
+    torch.cuda.synchronize()
+    d = lay.data
+    d["K"][0, :, 2000:2004] = kn[:, 0].transpose(1, 0, 2)
+    d["V"][0, :, 2000:2004] = vn[:, 0].transpose(1, 0, 2)
+    d["seq_lens"][:] = 2004
+    ref = hc.oracle_index(lay)
+    hc.check_index(lay, ref)
+    hc.check_decode(lay, out, dbg, cfg.keep_ratio, 200, ref_index=ref)
+    qc = dbg.q_code.cpu().numpy().view(np.uint32)[0, :, 0]
+    assert np.all(qc & 0xFFFF == 0)                                        # z == 0 gives 0
+
+
 def test_decode_on_mfma_index_matches_oracle():
     _torch()
     cfg = _cfg(3, 9000, n_plant=16)
