@@ -122,11 +122,10 @@ typedef struct {
  *   token_count [B][Hq]             how many were selected
  *   kernel_events  NULL or 6 caller-created events recorded on the stream around the five
  *                  kernels of a decode step (per-kernel timing): before the preparation kernel
- *                  (query rotation; in hhr_append_decode also the new token's K/V rows and page
- *                  extrema), before the page-bound kernel (which also computes the query codes
- *                  and the new key's code), before the selection kernel, before the attention
- *                  kernel, before the kernel that merges the attention partials (and commits
- *                  the append), and after it */
+ *                  (query rotations and codes; in hhr_append_decode also the new token's K/V
+ *                  rows, page extrema and code), before the page-bound kernel, before the
+ *                  selection kernel, before the attention kernel, before the kernel that merges
+ *                  the attention partials (and commits the append), and after it */
 typedef struct {
   float* q_rot;
   uint32_t* q_code;
@@ -179,9 +178,9 @@ hhr_status hhr_decode(const hhr_dims* dims, const hhr_params* params, const hhr_
 
 /* hhr_append followed by hhr_decode in one call (the query attends over the new token too),
  * with the same results. The append is folded into the decode's kernels (the preparation
- * kernel stores the K/V rows and updates the page, the page-bound kernel computes and stores
- * the key's code, the last kernel advances seq_lens), so a generation step costs no launch
- * beyond the decode. Same arguments and rules as the two calls; append_ticket is required. */
+ * kernel stores the K/V rows, updates the page and stores the key's code; the last kernel
+ * advances seq_lens), so a generation step costs no launch beyond the decode. Same arguments
+ * and rules as the two calls; append_ticket is required. */
 hhr_status hhr_append_decode(const hhr_dims* dims, const hhr_params* params,
                              const hhr_cache* cache, const void* k_new, const void* v_new,
                              const void* q, const float* R, const float* W, void* ws,

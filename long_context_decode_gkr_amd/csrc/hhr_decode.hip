@@ -16,7 +16,8 @@
 //                      exact top-k tokens by a histogram select; writes ascending indices.
 //   attn_kernel        grid (nsplit, Hq, B): split-K softmax attention over gathered K/V rows,
 //                      one partial (m, l, o) per workgroup;
-//   combine_kernel     grid (B * Hq): merges the partials of each (b, h) into the output.
+//   combine_kernel     grid (B * Hq): merges the partials of each (b, h) into the output and
+//                      advances seq_lens when the step appended a token.
 // The merge is a kernel of its own: an in-kernel "last workgroup merges" scheme needs a
 // device-scope release and acquire in every workgroup, which on gfx950 write back and
 // invalidate the whole L2 of an XCD, and costs far more than one small launch.
