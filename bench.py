@@ -10,8 +10,8 @@ A "step" is hhr_append_decode (append one token, then decode) on one layer. The 
 cycles over --layers distinct layer instances (separate K/V, index and sequence state in HBM) so
 the ~256 MB Infinity Cache cannot serve a step from the previous visit. Three passes, each W
 warm-up steps then exactly K timed steps bracketed by torch.cuda.synchronize():
-  1. launches with HIP events recorded by the library around each of its five kernels on the
-     decode stream: per-kernel durations and the roofline figure (events_us_per_step);
+  1. launches with HIP start/stop events that the runtime records around each of the five
+     kernels' own execution: per-kernel durations and the roofline figure (events_us_per_step);
   2. plain launches on one stream, no events: the headline us/step/layer;
   3. replay of one captured HIP graph per layer instance (graph_us_per_step; on this stack a
      graph replay of the five kernels is slower than the plain launches).
@@ -46,11 +46,11 @@ def log(msg, quiet):
 def algorithmic_bytes(cfg, L):
     """Bytes each kernel must move per launch (one layer, one append + decode step) at context L.
 
-    prep:       q, k_new, v_new and R read, q~ written; the appended token's K and V rows
-                and its page's extrema column pair read and written.
+    prep:       q, k_new, v_new, R and W read; q~ and the query codes written; the appended
+                token's K and V rows and code written, its page's extrema column pair read and
+                written.
     page_bound: min+max of every page of every KV head (128 ch x 8 B per page), q~ read, U
-                written (4 B per query head and page); the code workgroups: q, k_new and W
-                read, the query codes and the new key's code written.
+                written (4 B per query head and page).
     select:     U and the query code read, the codes of the kept pages' tokens (16 B per
                 candidate and query head), the selected indices written.
     sparse_attn: K and V rows of the selected tokens (2 x 256 B per token and query head),
@@ -64,10 +64,10 @@ def algorithmic_bytes(cfg, L):
     k = min(cfg.token_budget, n_keep * S)
     esz = 2
     return {
-        "prep": Hq * d * esz + Hkv * 2 * d * esz + Hkv * d * d * 4 + Hq * d * 4
-                + Hkv * 2 * d * esz + Hkv * 2 * d * 4 * 2,
-        "page_bound": Hkv * P * d * 8 + Hq * d * 4 + Hq * P * 4
-                      + Hq * d * esz + Hkv * d * esz + Hkv * d * nb * 4 + Hq * nb // 8 + Hkv * nb // 8,
+        "prep": Hq * d * esz + Hkv * 2 * d * esz + Hkv * d * d * 4 + Hkv * d * nb * 4
+                + Hq * d * 4 + Hq * nb // 8
+                + Hkv * 2 * d * esz + Hkv * nb // 8 + Hkv * 2 * d * 4 * 2,
+        "page_bound": Hkv * P * d * 8 + Hq * d * 4 + Hq * P * 4,
         "select": Hq * P * 4 + Hq * nb // 8 + Hq * n_keep * S * (nb // 8) + Hq * k * 4,
         "sparse_attn": Hq * k * 2 * d * esz + Hq * k * 4 + Hq * d * esz
         + Hq * -(-k // 256) * (d + 2) * 4,
@@ -254,9 +254,10 @@ def main():
                              vnd[v].data_ptr(), P["q"], P["R"], P["W"], P["ws"], dec.ws_bytes,
                              P["out"], dbg, stream)
 
-    # ---- pass 1 (launches with events): per-kernel durations from HIP events on the decode stream
+    # ---- pass 1 (launches with events): per-kernel durations from HIP events that the runtime
+    # records around each kernel's own execution on the decode stream (hipExtLaunchKernel)
     stream = hb.current_stream()
-    NE = len(KERNELS) + 1
+    NE = 2 * len(KERNELS)
     ev = hb.HipEvents(NE * K)
     dbgs = [hb.DebugStruct(None, None, None, None, None, None, None, None, ev.address(NE * i))
             for i in range(K)]
@@ -269,8 +270,8 @@ def main():
         step(Wm + i, dbgs[i], stream)
     torch.cuda.synchronize()
     events_ms = (time.perf_counter() - t_start) * 1e3 / K
-    # events [NE i + j] precede kernel j of step i; [NE i + NE - 1] follows the last one
-    per = {n: [ev.elapsed_ms(NE * i + j, NE * i + j + 1) for i in range(K)]
+    # events [NE i + 2 j] and [NE i + 2 j + 1]: start and stop of kernel j of step i
+    per = {n: [ev.elapsed_ms(NE * i + 2 * j, NE * i + 2 * j + 1) for i in range(K)]
            for j, n in enumerate(KERNELS)}
     ev.close()
 

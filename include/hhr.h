@@ -120,12 +120,13 @@ typedef struct {
  *                                   for a slot past the end of the sequence
  *   token_idx   [B][Hq][k]          the selected token positions, ascending
  *   token_count [B][Hq]             how many were selected
- *   kernel_events  NULL or 6 caller-created events recorded on the stream around the five
- *                  kernels of a decode step (per-kernel timing): before the preparation kernel
- *                  (query rotations and codes; in hhr_append_decode also the new token's K/V
- *                  rows, page extrema and code), before the page-bound kernel, before the
- *                  selection kernel, before the attention kernel, before the kernel that merges
- *                  the attention partials (and commits the append), and after it */
+ *   kernel_events  NULL or 10 caller-created events: the start and stop of each of the five
+ *                  kernels of a decode step, in launch order, recorded by the runtime around the
+ *                  kernel's own execution (hipExtLaunchKernel), so that their elapsed times are
+ *                  the kernels' durations: the preparation kernel (query rotations and codes;
+ *                  in hhr_append_decode also the new token's K/V rows, page extrema and code),
+ *                  the page-bound kernel, the selection kernel, the attention kernel, and the
+ *                  kernel that merges the attention partials (and commits the append) */
 typedef struct {
   float* q_rot;
   uint32_t* q_code;

@@ -105,7 +105,8 @@ hhr_status hhr_append(const hhr_dims* dims, const hhr_cache* cache, const void* 
   if ((st = check_cache(cache, true, &c)) != HHR_OK) return st;
   if (!k_new || !v_new || !R || !W) return HHR_ERR_INVALID_ARG;
   return hip_status(launch_prep(s, c, k_new, v_new, nullptr, R, W, nullptr, nullptr, nullptr,
-                                nullptr, PrepMode::kAppend, reinterpret_cast<hipStream_t>(stream)));
+                                nullptr, PrepMode::kAppend, KernelTimer{nullptr, nullptr},
+                                reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t hhr_decode_workspace_bytes(const hhr_dims* dims, const hhr_params* params) {

@@ -332,40 +332,40 @@ template <int NB, int KB, int QB>
 static void launch_prep_t(const Shape& s, const CacheView& c, const void* k_new,
                           const void* v_new, const void* q, const float* R, const float* W,
                           float* qrot, uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode,
-                          PrepMode mode, hipStream_t st) {
+                          PrepMode mode, KernelTimer tm, hipStream_t st) {
   dim3 grid(kPrepSlices, s.Hkv, s.B);
   dim3 block(256 + kPrepParts * NB / kPrepSlices);
   if (mode == PrepMode::kDecode)
-    hipLaunchKernelGGL((prep_kernel<NB, KB, QB, 1>), grid, block, 0, st, s, c, k_new, v_new, q,
-                       R, W, qrot, qcode, dbg_qrot, dbg_qcode);
+    launch_kernel(prep_kernel<NB, KB, QB, 1>, grid, block, st, tm, s, c, k_new, v_new, q, R, W,
+                  qrot, qcode, dbg_qrot, dbg_qcode);
   else
-    hipLaunchKernelGGL((prep_kernel<NB, KB, QB, 0>), grid, block, 0, st, s, c, k_new, v_new, q,
-                       R, W, qrot, qcode, dbg_qrot, dbg_qcode);
+    launch_kernel(prep_kernel<NB, KB, QB, 0>, grid, block, st, tm, s, c, k_new, v_new, q, R, W,
+                  qrot, qcode, dbg_qrot, dbg_qcode);
 }
 
 template <int NB>
 static void launch_prep_nb(const Shape& s, const CacheView& c, const void* k_new,
                            const void* v_new, const void* q, const float* R, const float* W,
                            float* qrot, uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode,
-                           PrepMode mode, hipStream_t st) {
+                           PrepMode mode, KernelTimer tm, hipStream_t st) {
   if (s.kv_bf16 && s.q_bf16)
-    launch_prep_t<NB, 1, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
+    launch_prep_t<NB, 1, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
   else if (s.kv_bf16)
-    launch_prep_t<NB, 1, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
+    launch_prep_t<NB, 1, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
   else if (s.q_bf16)
-    launch_prep_t<NB, 0, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
+    launch_prep_t<NB, 0, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
   else
-    launch_prep_t<NB, 0, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
+    launch_prep_t<NB, 0, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
 }
 
 hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, const void* v_new,
                        const void* q, const float* R, const float* W, float* qrot,
                        uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, PrepMode mode,
-                       hipStream_t st) {
+                       KernelTimer tm, hipStream_t st) {
   if (s.NB == 128)
-    launch_prep_nb<128>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
+    launch_prep_nb<128>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
   else
-    launch_prep_nb<256>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, st);
+    launch_prep_nb<256>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
   return hipGetLastError();
 }
 

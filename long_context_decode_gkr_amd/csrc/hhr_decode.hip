@@ -868,14 +868,15 @@ template <int G>
 static void launch_bound_t(const Shape& s, const CacheView& c, const BoundArgs& a,
                            const DebugView& dbg, hipStream_t st) {
   dim3 grid((s.Pmax + kBoundPages - 1) / kBoundPages, s.Hkv, s.B);
-  hipLaunchKernelGGL((page_bound_kernel<G>), grid, dim3(kBoundThreads), 0, st, s, c, a,
-                     dbg.bounds);
+  launch_kernel(page_bound_kernel<G>, grid, dim3(kBoundThreads), st, kernel_timer(dbg, 1), s, c,
+                a, dbg.bounds);
 }
 
 template <int NB, int EPT, int NT>
 static void launch_select_t(const Shape& s, const CacheView& c, const SelectArgs& a,
                             const DebugView& dbg, hipStream_t st) {
-  hipLaunchKernelGGL((select_kernel<NB, EPT, NT>), dim3(s.Hq, s.B), dim3(NT), 0, st, s, c, a, dbg);
+  launch_kernel(select_kernel<NB, EPT, NT>, dim3(s.Hq, s.B), dim3(NT), st, kernel_timer(dbg, 2),
+                s, c, a, dbg);
 }
 
 // Workgroup size of the selection (measured on MI355X: 1024 and 512 threads tie; 256 threads
@@ -905,18 +906,14 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
   int32_t* cnt = reinterpret_cast<int32_t*>(base + p.off_cnt);
   float* part = reinterpret_cast<float*>(base + p.off_part);
   hipError_t e = hipSuccess;
-#define HHR_MARK(i) \
-  if (dbg.events && (e = hipEventRecord(dbg.events[i], st)) != hipSuccess) return e;
 #define HHR_CHECK() \
   if ((e = hipGetLastError()) != hipSuccess) return e;
 
   // seq_lens[b] stays t during the step; every kernel works on t + 1 tokens when a token is
   // appended, and the last kernel stores t + 1.
-  HHR_MARK(0);
   e = launch_prep(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg.q_rot, dbg.q_code,
-                  PrepMode::kDecode, st);
+                  PrepMode::kDecode, kernel_timer(dbg, 0), st);
   if (e != hipSuccess) return e;
-  HHR_MARK(1);
   BoundArgs ba{qrot, U, k_new != nullptr ? 1 : 0};
   switch (s.G) {
     case 1: launch_bound_t<1>(s, c, ba, dbg, st); break;
@@ -925,25 +922,20 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
     default: launch_bound_t<8>(s, c, ba, dbg, st); break;
   }
   HHR_CHECK();
-  HHR_MARK(2);
   SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap, p.istride, k_new != nullptr ? 1 : 0};
   if (s.NB == 128) launch_select_nb<128>(s, c, sa, dbg, st);
   else launch_select_nb<256>(s, c, sa, dbg, st);
   HHR_CHECK();
-  HHR_MARK(3);
   AttnArgs aa{idx, cnt, part, p.kcap, p.istride, p.nsplit, p.scale * 1.4426950408889634f};
   dim3 grid(p.nsplit, s.Hq, s.B);
   if (s.kv_bf16)
-    hipLaunchKernelGGL((attn_kernel<1>), grid, dim3(256), 0, st, s, c.K, c.V, q, aa);
+    launch_kernel(attn_kernel<1>, grid, dim3(256), st, kernel_timer(dbg, 3), s, c.K, c.V, q, aa);
   else
-    hipLaunchKernelGGL((attn_kernel<0>), grid, dim3(256), 0, st, s, c.K, c.V, q, aa);
+    launch_kernel(attn_kernel<0>, grid, dim3(256), st, kernel_timer(dbg, 3), s, c.K, c.V, q, aa);
   HHR_CHECK();
-  HHR_MARK(4);
-  hipLaunchKernelGGL(combine_kernel, dim3(s.B * s.Hq), dim3(kD), 0, st, part, p.nsplit, out,
-                     c.seq_lens, s.Hq, s.Lmax, k_new != nullptr ? 1 : 0);
+  launch_kernel(combine_kernel, dim3(s.B * s.Hq), dim3(kD), st, kernel_timer(dbg, 4), part,
+                p.nsplit, out, c.seq_lens, s.Hq, s.Lmax, k_new != nullptr ? 1 : 0);
   HHR_CHECK();
-  HHR_MARK(5);
-#undef HHR_MARK
 #undef HHR_CHECK
   return hipSuccess;
 }

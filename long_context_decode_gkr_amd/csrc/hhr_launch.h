@@ -1,6 +1,7 @@
 // Internal launch interface between the C-ABI host layer and the kernel translation units.
 #pragma once
 
+#include <hip/hip_ext.h>
 #include <hip/hip_runtime.h>
 #include <stddef.h>
 #include <stdint.h>
@@ -31,8 +32,25 @@ struct DebugView {
   uint16_t* dist;
   int32_t* token_idx;
   int32_t* token_count;
-  hipEvent_t* events;  // NULL or 6 events around the five decode kernels
+  hipEvent_t* events;  // NULL or 10 events: start and stop of each of the five kernels
 };
+
+// Start and stop events of one kernel's execution; both NULL for a plain launch.
+struct KernelTimer {
+  hipEvent_t start, stop;
+};
+inline KernelTimer kernel_timer(const DebugView& d, int k) {
+  return d.events ? KernelTimer{d.events[2 * k], d.events[2 * k + 1]} : KernelTimer{nullptr, nullptr};
+}
+// Launch on stream st; with a timer the runtime records its events around the kernel itself.
+template <typename F, typename... Args>
+inline void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t st, KernelTimer tm,
+                          Args... args) {
+  if (tm.start)
+    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, tm.start, tm.stop, 0, args...);
+  else
+    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+}
 
 // Workspace carve-up of one decode call (byte offsets from the workspace base).
 struct DecodePlan {
@@ -61,7 +79,7 @@ enum class PrepMode { kAppend, kDecode };
 hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, const void* v_new,
                        const void* q, const float* R, const float* W, float* qrot,
                        uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, PrepMode mode,
-                       hipStream_t st);
+                       KernelTimer tm, hipStream_t st);
 // The decode step, with the append of k_new / v_new folded into its kernels when given.
 hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c,
                          const void* k_new, const void* v_new, const void* q, const float* R,
