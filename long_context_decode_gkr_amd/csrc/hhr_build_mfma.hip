@@ -16,7 +16,7 @@
 //     the exact long accumulator behind that: every code equals the sign of the exact z.
 //
 // Grid (tiles x roles, Hkv, B): role 0 = rotation and page extrema, role 1 + s = code words
-// [4 s, 4 s + 4) (128 code columns). A workgroup of 4 waves covers 512 tokens; each wave walks
+// [4 s, 4 s + 4) (128 code columns). A workgroup of 8 waves covers 512 tokens; each wave walks
 // 32-token sub-tiles: 8 A fragments (one 16-byte load each per lane) are reused against all
 // 4 column tiles x 8 k-steps x pieces, B fragments come from LDS.
 #include "hhr_device.h"
@@ -25,10 +25,11 @@
 namespace hhr {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
 
 constexpr int kMTok = 512;            // tokens per workgroup
-constexpr int kMThreads = 256;
+constexpr int kMThreads = 512;       // 8 waves: two per SIMD, so MFMA and VALU work overlap
 constexpr int kBStride = kD + 8;      // padded k-stride of a transposed B column (bf16 elements)
 constexpr int kFbCap = 2048;          // queued uncertain code bits per workgroup
 constexpr float kCertScale = 1.0f / 8192.0f;   // 2^-13
@@ -39,10 +40,6 @@ struct Bf16Row {
   __device__ __forceinline__ float operator[](int j) const { return bf16_bits_to_f32(p[j]); }
 };
 
-__device__ __forceinline__ uint16_t f32_to_bf16_rne(float x) {
-  const uint32_t u = __float_as_uint(x);
-  return uint16_t((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
-}
 
 template <int S>
 __global__ void __launch_bounds__(kMThreads)
@@ -61,51 +58,76 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   __shared__ float stage_f[2][kD][kMTok / 16];               // page min / max (role 0)
   __shared__ uint32_t stage_c[kMTok][4];                     // code words (role > 0)
   __shared__ float wnorm[kD];
+  __shared__ float wpart[kMThreads];
   __shared__ uint32_t fb_list[kFbCap];
   __shared__ int fb_n;
 
-  // ---- B operand: split the fp32 matrix into bf16 pieces, transposed (k contiguous)
+  // ---- B operand: split the fp32 matrix into bf16 pieces (hardware round-to-nearest-even,
+  // two values per conversion), transposed (k contiguous). Thread tid owns column
+  // n = tid % 128 and the row pairs k = 2 (tid / 128 + 4 i), +1: its 32 loads are issued
+  // together, and its quarter of the column's squared norm (code roles) is summed on the way.
+  constexpr int kTPC = kMThreads / kD;                // threads per column
+  constexpr int kPPT = kD * kD / (2 * kMThreads);     // row pairs per thread
   const float* src = role == 0 ? R + size_t(g) * kD * kD
                                : W + size_t(g) * kD * s.NB + (role - 1) * kD;
   const int src_ld = role == 0 ? kD : s.NB;
-  for (int e = tid; e < kD * kD; e += kMThreads) {
-    const int k = e / kD, n = e % kD;
-    const float x = src[size_t(k) * src_ld + n];
-    const uint16_t p1 = f32_to_bf16_rne(x);
-    const float r1 = x - bf16_bits_to_f32(p1);
-    const uint16_t p2 = f32_to_bf16_rne(r1);
-    Bt[0][n][k] = p1;
-    Bt[1][n][k] = p2;
-    if (role == 0) Bt[2][n][k] = f32_to_bf16_rne(r1 - bf16_bits_to_f32(p2));
+  const int bn = tid % kD, bk0 = tid / kD;
+  float bx[kPPT][2];
+#pragma unroll
+  for (int i = 0; i < kPPT; ++i) {
+    const int k = 2 * (bk0 + kTPC * i);
+    bx[i][0] = src[size_t(k) * src_ld + bn];
+    bx[i][1] = src[size_t(k + 1) * src_ld + bn];
   }
-  if (role != 0 && tid < kD) {
-    double ss = 0.0;
-    for (int k = 0; k < kD; ++k) {
-      const double x = src[size_t(k) * src_ld + tid];
-      ss += x * x;
-    }
-    wnorm[tid] = float(sqrt(ss)) * (1.0f + 1e-6f);
+  float ss = 0.f;
+  auto pack = [](float a, float b) {
+    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
+  };
+  auto lo16 = [](uint32_t v) { return __uint_as_float(v << 16); };
+  auto hi16 = [](uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); };
+#pragma unroll
+  for (int i = 0; i < kPPT; ++i) {
+    const int k = 2 * (bk0 + kTPC * i);
+    const float x0 = bx[i][0], x1 = bx[i][1];
+    const uint32_t p1 = pack(x0, x1);
+    const float r0 = x0 - lo16(p1), r1 = x1 - hi16(p1);
+    const uint32_t p2 = pack(r0, r1);
+    *reinterpret_cast<uint32_t*>(&Bt[0][bn][k]) = p1;
+    *reinterpret_cast<uint32_t*>(&Bt[1][bn][k]) = p2;
+    if (role == 0)
+      *reinterpret_cast<uint32_t*>(&Bt[2][bn][k]) = pack(r0 - lo16(p2), r1 - hi16(p2));
+    ss = fmaf(x0, x0, fmaf(x1, x1, ss));
   }
+  wpart[tid] = ss;
   if (tid == 0) fb_n = 0;
+  __syncthreads();
+  // |w_c| from fp32 sums of squares (relative error below 2^-16), rounded up by 2^-14
+  if (role != 0 && tid < kD) {
+    float q = 0.f;
+#pragma unroll
+    for (int i = 0; i < kTPC; ++i) q += wpart[tid + i * kD];
+    wnorm[tid] = sqrtf(q) * (1.0f + 0x1p-14f);
+  }
   __syncthreads();
 
   const size_t row0 = (size_t(b) * s.Hkv + g) * s.Lmax;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(c.K);
   const int half = lane >> 5, col = lane & 31;
 
-  for (int st = w; st < kMTok / 32; st += kMThreads / kWave) {
-    const int tl0 = st * 32;                 // first token of the sub-tile (block-local)
-    if (tl0 >= ntok) break;
-    // A fragments: row tl0 + col, k = 16 ks + 8 half + 0..7
-    const int tr = t0 + tl0 + col;
-    const int trc = min(tr, L - 1);
-    bf16x8 a[8];
+  // A fragments of a sub-tile: row tl0 + col, k = 16 ks + 8 half + 0..7 (rows past the end
+  // read the last valid row).
+  auto load_a = [&](int tl0, bf16x8 (&a)[8]) {
+    const int trc = min(t0 + tl0 + col, L - 1);
     const uint4* ap = reinterpret_cast<const uint4*>(Kb + (row0 + trc) * kD + 8 * half);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) {
-      const uint4 v = ap[2 * ks];
-      a[ks] = __builtin_bit_cast(bf16x8, v);
-    }
+    for (int ks = 0; ks < 8; ++ks) a[ks] = __builtin_bit_cast(bf16x8, ap[2 * ks]);
+  };
+  constexpr int kStep = kMThreads / kWave;   // sub-tiles between a wave's consecutive ones
+  for (int st = w; st < kMTok / 32; st += kStep) {
+    const int tl0 = st * 32;                 // first token of the sub-tile (block-local)
+    if (tl0 >= ntok) break;
+    bf16x8 a[8];
+    load_a(tl0, a);
     f32x16 acc[4];
 #pragma unroll
     for (int nt = 0; nt < 4; ++nt)
@@ -159,6 +181,9 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
         }
       xn2 += __shfl_xor(xn2, 32);
       const float xnorm = sqrtf(xn2) * (1.0f + 1e-6f);   // |k_row|, row = tl0 + col
+      float xr[16];                                      // |k| of the rows of acc[.][r]
+#pragma unroll
+      for (int r = 0; r < 16; ++r) xr[r] = __shfl(xnorm, 8 * (r / 4) + 4 * half + (r % 4));
 #pragma unroll
       for (int nt = 0; nt < 4; ++nt) {
         const int lc = nt * 32 + col;                    // code column within the slice
@@ -166,22 +191,16 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
 #pragma unroll
         for (int r = 0; r < 16; ++r) {
           const int i = 8 * (r / 4) + 4 * half + (r % 4);
-          const float xi = __shfl(xnorm, i);
+          const float xi = xr[r];
           const float tau = kCertScale * xi * wn;
           const float z = acc[nt][r];
           const bool valid = tl0 + i < ntok;
           const bool sure = fabsf(z) > tau && xi * wn > 1e-30f;
           bool bit = z > 0.f;
           if (valid && !sure) {
+            // queued for the exact path (past the capacity only counted: see below)
             const int pos = atomicAdd(&fb_n, 1);
-            if (pos < kFbCap) {
-              fb_list[pos] = (uint32_t(tl0 + i) << 8) | uint32_t(lc);
-            } else {
-              // queue full: decide this bit here
-              const uint16_t* kr = Kb + (row0 + t0 + tl0 + i) * kD;
-              const float* wc = W + size_t(g) * kD * s.NB + (role - 1) * kD + lc;
-              bit = certified_bit(Bf16Row{kr}, wc, s.NB) != 0;
-            }
+            if (pos < kFbCap) fb_list[pos] = (uint32_t(tl0 + i) << 8) | uint32_t(lc);
           }
           const uint64_t m = __ballot(bit);
           if (lane == 0) {
@@ -207,17 +226,29 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
       c.pmax[(sbase + j) * s.Pmax + pg0 + pl] = stage_f[1][j][pl];
     }
   } else {
-    // ---- exact path for the queued bits, then the code words
-    const int nfb = min(fb_n, kFbCap);
-    for (int e = tid; e < nfb; e += kMThreads) {
-      const uint32_t ent = fb_list[e];
-      const int tl = int(ent >> 8), lc = int(ent & 0xFFu);
-      const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
-      const float* wc = W + size_t(g) * kD * s.NB + (role - 1) * kD + lc;
-      const uint32_t bit = certified_bit(Bf16Row{kr}, wc, s.NB);
-      const uint32_t mask = 1u << (lc & 31);
-      if (bit) atomicOr(&stage_c[tl][lc >> 5], mask);
-      else atomicAnd(&stage_c[tl][lc >> 5], ~mask);
+    // ---- exact path for the queued bits, then the code words. If more bits were uncertain
+    // than the queue holds (degenerate projections), every word of the tile is recomputed from
+    // the stored operands instead: slow, and only for such inputs.
+    const float* wbase_p = W + size_t(g) * kD * s.NB + (role - 1) * kD;
+    if (fb_n <= kFbCap) {
+      for (int e = tid; e < fb_n; e += kMThreads) {
+        const uint32_t ent = fb_list[e];
+        const int tl = int(ent >> 8), lc = int(ent & 0xFFu);
+        const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
+        const uint32_t bit = certified_bit(Bf16Row{kr}, wbase_p + lc, s.NB);
+        const uint32_t mask = 1u << (lc & 31);
+        if (bit) atomicOr(&stage_c[tl][lc >> 5], mask);
+        else atomicAnd(&stage_c[tl][lc >> 5], ~mask);
+      }
+    } else {
+      for (int e = tid; e < ntok * 4; e += kMThreads) {
+        const int tl = e >> 2, wd = e & 3;
+        const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
+        uint32_t word = 0;
+        for (int i = 0; i < 32; ++i)
+          word |= certified_bit(Bf16Row{kr}, wbase_p + 32 * wd + i, s.NB) << i;
+        stage_c[tl][wd] = word;
+      }
     }
     __syncthreads();
     const int wbase = (role - 1) * 4;
