@@ -170,8 +170,8 @@ struct SelectArgs {
 // ---------------------------------------------------------------------------------------------
 constexpr int kRadixBins = 1 << 12;
 constexpr int kRadixBits = 12;
-constexpr int kEmitSPT = 16;   // cached distances per thread per emit chunk
-static_assert(16 % kEmitSPT == 0, "an emit chunk must not cross a page (page sizes 16, 32)");
+constexpr int kEmitSPT = 8;    // cached distances per thread per emit chunk
+static_assert(16 % kEmitSPT == 0 && kEmitSPT >= 8, "an emit chunk must not cross a page (page sizes 16, 32)");
 
 template <int NB, int EPT, int NT>
 __global__ void __launch_bounds__(NT)
@@ -181,7 +181,7 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   constexpr int NW = NB / 32;
   using DT = typename std::conditional<NB == 128, uint8_t, uint16_t>::type;
   constexpr uint32_t kNone = NB == 128 ? 0xFFu : 0xFFFFu;   // distance of a slot past the end
-  constexpr int HB = kRadixBins > kSelWaves * (NB + 1) ? kRadixBins : kSelWaves * (NB + 1);
+  constexpr int HB = kRadixBins > NB + 1 ? kRadixBins : NB + 1;
   const int h = blockIdx.x, b = blockIdx.y, g = h / s.G;
   const int bh = b * s.Hq + h;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
@@ -350,13 +350,16 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
         }
         __syncthreads();
         if (w == 0) {
+          // (key, index) of every lane compared with the in_bin entries through register
+          // reads (in_bin is uniform and usually a handful)
           const uint32_t kl = lane < in_bin ? s_ckey[lane] : 0xFFFFFFFFu;
-          const int il = lane < in_bin ? s_cidx[lane] : 0x7FFFFFFF;
+          const uint32_t il = lane < in_bin ? uint32_t(s_cidx[lane]) : 0x7FFFFFFFu;
+          const uint64_t vl = (uint64_t(kl) << 32) | il;
           int rank = 0;
           for (int j = 0; j < in_bin; ++j) {
-            const uint32_t kj = s_ckey[j];
-            const int ij = s_cidx[j];
-            rank += (kj < kl || (kj == kl && ij < il)) ? 1 : 0;
+            const uint64_t vj = (uint64_t(__builtin_amdgcn_readlane(kl, j)) << 32) |
+                                uint32_t(__builtin_amdgcn_readlane(il, j));
+            rank += vj < vl ? 1 : 0;
           }
           if (lane < in_bin && rank == need - 1) {
             s_pick[0] = int(kl);
@@ -440,7 +443,7 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
     }
     return dd;
   };
-  uint32_t* whist = s_hist + w * (NB + 1);
+  uint32_t* whist = s_hist;   // bins 0..NB (cleared by the coarse stage's last pass)
   // Batches of 8 x (1024 / NT) slots per thread: all code loads of a batch are issued before
   // any is used.
   constexpr int BAT = 8 * (1024 / NT) / (NW / 4);
@@ -487,10 +490,7 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
 #pragma unroll
     for (int j = 0; j < BPL; ++j) {
       const int bin = lane * BPL + j;
-      const int bc = min(bin, NB);
-      int v = 0;
-#pragma unroll
-      for (int i = 0; i < kSelWaves; ++i) v += int(s_hist[i * (NB + 1) + bc]);
+      const int v = int(s_hist[min(bin, NB)]);
       cnt[j] = bin <= NB ? v : 0;
       tot_d += cnt[j];
     }
@@ -532,19 +532,24 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
       const int s0 = (ch * kSelThreads + tid) * kEmitSPT;
       const bool any = s0 < nslots;
       const int sc = any ? s0 : 0;                // read position (in bounds)
-      uint32_t dv[kEmitSPT];
-      if constexpr (sizeof(DT) == 1) {
-        const uint4 x = *reinterpret_cast<const uint4*>(&s_dist[sc]);
-        const uint32_t wv[4] = {x.x, x.y, x.z, x.w};
-#pragma unroll
-        for (int u = 0; u < kEmitSPT; ++u) dv[u] = (wv[u >> 2] >> (8 * (u & 3))) & 0xFFu;
+      // the chunk's distances as 32-bit words (sc is a multiple of kEmitSPT: aligned)
+      constexpr int kPer = 4 / int(sizeof(DT));            // distances per word
+      constexpr int kWords = kEmitSPT / kPer;
+      uint32_t wv[kWords];
+      if constexpr (kWords == 2) {
+        const uint2 x = *reinterpret_cast<const uint2*>(&s_dist[sc]);
+        wv[0] = x.x; wv[1] = x.y;
       } else {
-        const uint4 x0 = *reinterpret_cast<const uint4*>(&s_dist[sc]);
-        const uint4 x1 = *reinterpret_cast<const uint4*>(&s_dist[sc + 8]);
-        const uint32_t wv[8] = {x0.x, x0.y, x0.z, x0.w, x1.x, x1.y, x1.z, x1.w};
 #pragma unroll
-        for (int u = 0; u < kEmitSPT; ++u) dv[u] = (wv[u >> 1] >> (16 * (u & 1))) & 0xFFFFu;
+        for (int i = 0; i < kWords; i += 4) {
+          const uint4 x = *reinterpret_cast<const uint4*>(&s_dist[sc + i * kPer]);
+          wv[i] = x.x; wv[i + 1] = x.y; wv[i + 2] = x.z; wv[i + 3] = x.w;
+        }
       }
+      uint32_t dv[kEmitSPT];
+#pragma unroll
+      for (int u = 0; u < kEmitSPT; ++u)
+        dv[u] = (wv[u / kPer] >> (8 * sizeof(DT) * (u % kPer))) & kNone;
 #pragma unroll
       for (int u = 0; u < kEmitSPT; ++u) dv[u] = (any && s0 + u < nslots) ? dv[u] : kNone;
       int nlt = 0, neq = 0;

@@ -116,6 +116,35 @@ def test_decode_many_candidates_recompute_path():
     hc.check_decode(lay, out, dbg, 1.0, 3000, heads=heads)
 
 
+def test_kernel_events_time_the_five_kernels():
+    """The optional start/stop events (10) are recorded around each of the step's five kernels,
+    and timing does not change the result."""
+    torch = _torch()
+    cfg = _cfg(3, 4096 + 5, n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=4096 + 64)
+    lay.build()
+    dec = hb.Decoder(lay.dims, 1 / 16, 256)
+    outs = []
+    ev = hb.HipEvents(10)
+    try:
+        for timed in (False, True):
+            out = torch.full((1, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
+            dbg = (hb.DebugStruct(None, None, None, None, None, None, None, None, ev.address(0))
+                   if timed else None)
+            hb.hhr_decode(lay.dims, dec.params, lay.cache.struct(), lay.q.data_ptr(),
+                          lay.R.data_ptr(), lay.W.data_ptr(), dec.ws.data_ptr(), dec.ws_bytes,
+                          out.data_ptr(), dbg, hb.current_stream())
+            torch.cuda.synchronize()
+            outs.append(out.cpu().numpy())
+        ms = [ev.elapsed_ms(2 * j, 2 * j + 1) for j in range(5)]
+        gaps = [ev.elapsed_ms(2 * j + 1, 2 * j + 2) for j in range(4)]
+    finally:
+        ev.close()
+    assert np.array_equal(outs[0], outs[1])
+    assert all(0.0 < m < 50.0 for m in ms), ms
+    assert all(g > -0.005 for g in gaps), gaps  # launch order
+
+
 def test_decode_ties_all_bounds_equal():
     # identical keys: every page bound and every distance ties; lower indices must win
     torch = _torch()
