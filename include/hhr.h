@@ -89,11 +89,23 @@ typedef struct {
  *   candidate budget is 30 %, Appendix A). Ties in U go to the lower page index.
  * token_budget k >= 1: the min(k, #candidates) candidates of smallest (Hamming distance,
  *   token position) are attended to (§3.3.2; the paper's default is 1.5 % of the context).
- * softmax_scale: logits are scale * q.k; a value <= 0 selects 1/sqrt(128) rounded to fp32. */
+ * softmax_scale: logits are scale * q.k; a value <= 0 selects 1/sqrt(128) rounded to fp32.
+ * stages: which stages choose the attended keys (hhr_stages; the stage-wise ablation of
+ *   Appendix C, Table 8). The rotation R is an input, so the "no rotation" variant of the coarse stage is
+ *   R = I (the plain per-channel min/max bound). */
+typedef enum {
+  HHR_STAGES_BOTH = 0,        /* coarse then fine: the method                                  */
+  HHR_STAGES_PAGES_ONLY = 1,  /* coarse only: every token of the kept pages is attended;
+                                 token_budget is not used                                     */
+  HHR_STAGES_CODES_ONLY = 2   /* fine only: every page is a candidate (page_keep_ratio is not
+                                 used, no page bound is computed, dbg->bounds stays untouched) */
+} hhr_stages;
+
 typedef struct {
   double page_keep_ratio;
   int32_t token_budget;
   float softmax_scale;
+  int32_t stages;       /* hhr_stages */
 } hhr_params;
 
 /* The KV cache and its derived index (page extrema and key codes). All device pointers.
@@ -118,7 +130,10 @@ typedef struct {
  *   dist        [B][Hq][max_seq_len] Hamming distance of candidate slot i, i.e. of token
  *                                   page_ids[i / S] * S + i % S, for i < n_keep * S; 0xFFFF
  *                                   for a slot past the end of the sequence
- *   token_idx   [B][Hq][k]          the selected token positions, ascending
+ *   token_idx   [B][Hq][kcap]       the selected token positions, ascending; kcap =
+ *                                   min(token_budget, max_seq_len), or with
+ *                                   HHR_STAGES_PAGES_ONLY min(max(1, ceil(rho Pmax)) *
+ *                                   page_size, max_seq_len)
  *   token_count [B][Hq]             how many were selected
  *   kernel_events  NULL or 10 caller-created events: the start and stop of each of the five
  *                  kernels of a decode step, in launch order, recorded by the runtime around the
@@ -187,6 +202,19 @@ hhr_status hhr_append_decode(const hhr_dims* dims, const hhr_params* params,
                              const void* q, const float* R, const float* W, void* ws,
                              size_t ws_bytes, float* out, const hhr_debug* dbg,
                              hhr_stream_t stream);
+
+/* Dense decode attention, the baseline of §4.3 / Fig. 7 (HHR against full attention): for
+ * every (b, h), o = softmax(scale q K^T) V over ALL seq_lens[b] tokens of the cache, fp32
+ * accumulation; no index is read (page_min, page_max, codes may be anything). Split-K over the
+ * context with the G query heads of a KV head served by one read of its K/V rows, then a merge
+ * of the partials. softmax_scale as in hhr_params. ws: at least hhr_dense_workspace_bytes
+ * bytes, 256-byte aligned, caller-owned, needing no initialisation. dbg: NULL, or its
+ * kernel_events used alone (4 events: start and stop of the attention and of the merge kernel).
+ * A sequence with no tokens gets a zero output. */
+size_t hhr_dense_workspace_bytes(const hhr_dims* dims);
+hhr_status hhr_dense_decode(const hhr_dims* dims, const hhr_cache* cache, const void* q,
+                            float softmax_scale, void* ws, size_t ws_bytes, float* out,
+                            const hhr_debug* dbg, hhr_stream_t stream);
 
 /* Static text for a status code. */
 const char* hhr_status_string(hhr_status status);

@@ -15,13 +15,16 @@ LIB_PATH = os.path.join(HERE, "libhhr.so")
 
 HHR_F32, HHR_BF16 = 0, 1
 HHR_MAX_PAGES = 16384
+HHR_STAGES_BOTH, HHR_STAGES_PAGES_ONLY, HHR_STAGES_CODES_ONLY = 0, 1, 2
+STAGES = {"both": HHR_STAGES_BOTH, "pages": HHR_STAGES_PAGES_ONLY, "codes": HHR_STAGES_CODES_ONLY}
 STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or type",
           3: "size exceeds a documented maximum", 4: "workspace too small or misaligned",
           5: "HIP launch or runtime error"}
 
 # Every exported symbol of include/hhr.h.
 EXPORTS = ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode_workspace_bytes",
-           "hhr_decode", "hhr_append_decode", "hhr_status_string")
+           "hhr_decode", "hhr_append_decode", "hhr_dense_workspace_bytes", "hhr_dense_decode",
+           "hhr_status_string")
 
 
 class Dims(ctypes.Structure):
@@ -34,7 +37,7 @@ class Dims(ctypes.Structure):
 
 class Params(ctypes.Structure):
     _fields_ = [("page_keep_ratio", ctypes.c_double), ("token_budget", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float)]
+                ("softmax_scale", ctypes.c_float), ("stages", ctypes.c_int32)]
 
 
 class CacheStruct(ctypes.Structure):
@@ -83,10 +86,14 @@ def load() -> ctypes.CDLL:
                                vp, P(DebugStruct), vp]
     lib.hhr_append_decode.argtypes = [P(Dims), P(Params), P(CacheStruct), vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp, P(DebugStruct), vp]
+    lib.hhr_dense_workspace_bytes.argtypes = [P(Dims)]
+    lib.hhr_dense_workspace_bytes.restype = ctypes.c_size_t
+    lib.hhr_dense_decode.argtypes = [P(Dims), P(CacheStruct), vp, ctypes.c_float, vp,
+                                     ctypes.c_size_t, vp, P(DebugStruct), vp]
     lib.hhr_status_string.argtypes = [ctypes.c_int]
     lib.hhr_status_string.restype = ctypes.c_char_p
     for fn in ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode",
-               "hhr_append_decode"):
+               "hhr_append_decode", "hhr_dense_decode"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -129,6 +136,18 @@ def hhr_append_decode(dims: Dims, params: Params, cache: CacheStruct, k_new: int
         ws_bytes, out, ctypes.byref(dbg) if dbg is not None else None, stream))
 
 
+def hhr_dense_workspace_bytes(dims: Dims) -> int:
+    return int(load().hhr_dense_workspace_bytes(ctypes.byref(dims)))
+
+
+def hhr_dense_decode(dims: Dims, cache: CacheStruct, q: int, softmax_scale: float, ws: int,
+                     ws_bytes: int, out: int, dbg: Optional[DebugStruct] = None,
+                     stream: int = 0) -> None:
+    _check("hhr_dense_decode", load().hhr_dense_decode(
+        ctypes.byref(dims), ctypes.byref(cache), q, softmax_scale, ws, ws_bytes, out,
+        ctypes.byref(dbg) if dbg is not None else None, stream))
+
+
 def hhr_status_string(status: int) -> str:
     return load().hhr_status_string(status).decode()
 
@@ -166,14 +185,26 @@ class Cache:
                            _ptr(self.codes), _ptr(self.seq_lens), _ptr(self.append_ticket))
 
 
+def index_capacity(dims: Dims, keep_ratio: float, token_budget: int, stages: str = "both") -> int:
+    """Entries per (b, h) of the selected-token list (hhr_debug.token_idx): the token budget
+    clamped to max_seq_len, or, with the coarse stage alone, every token of the largest kept page
+    set, min(max(1, ceil(rho * Pmax)) * page_size, max_seq_len)."""
+    import math
+    if STAGES[stages] == HHR_STAGES_PAGES_ONLY:
+        keep = max(1, math.ceil(keep_ratio * (dims.max_seq_len // dims.page_size)))
+        return min(keep * dims.page_size, dims.max_seq_len)
+    return min(token_budget, dims.max_seq_len)
+
+
 class Debug:
     """Optional side outputs of hhr_decode (all allocated)."""
 
-    def __init__(self, dims: Dims, token_budget: int, device="cuda"):
+    def __init__(self, dims: Dims, token_budget: int, keep_ratio: float = 1.0,
+                 stages: str = "both", device="cuda"):
         import torch
         B, H, d = dims.batch, dims.num_q_heads, dims.head_dim
         P = dims.max_seq_len // dims.page_size
-        k = min(token_budget, dims.max_seq_len)
+        k = index_capacity(dims, keep_ratio, token_budget, stages)
         i32 = torch.int32
         self.q_rot = torch.zeros((B, H, d), dtype=torch.float32, device=device)
         self.q_code = torch.zeros((B, H, dims.hash_bits // 32), dtype=i32, device=device)
@@ -199,10 +230,10 @@ class Decoder:
     """Holds the workspace for hhr_decode at fixed shapes and budgets."""
 
     def __init__(self, dims: Dims, keep_ratio: float, token_budget: int, softmax_scale: float = 0.0,
-                 device="cuda"):
+                 device="cuda", stages: str = "both"):
         import torch
         self.dims = dims
-        self.params = Params(keep_ratio, token_budget, softmax_scale)
+        self.params = Params(keep_ratio, token_budget, softmax_scale, STAGES[stages])
         self.ws_bytes = hhr_decode_workspace_bytes(dims, self.params)
         if self.ws_bytes == 0:
             raise HHRError("hhr_decode_workspace_bytes", 1)
@@ -220,6 +251,24 @@ class Decoder:
             hhr_append_decode(self.dims, self.params, cache.struct(), _ptr(k_new), _ptr(v_new),
                               _ptr(q), _ptr(R), _ptr(W), _ptr(self.ws), self.ws_bytes, _ptr(out),
                               d, st)
+
+
+class DenseDecoder:
+    """Holds the workspace of hhr_dense_decode (full attention over every cached token)."""
+
+    def __init__(self, dims: Dims, softmax_scale: float = 0.0, device="cuda"):
+        import torch
+        self.dims = dims
+        self.softmax_scale = softmax_scale
+        self.ws_bytes = hhr_dense_workspace_bytes(dims)
+        if self.ws_bytes == 0:
+            raise HHRError("hhr_dense_workspace_bytes", 1)
+        self.ws = torch.empty((self.ws_bytes,), dtype=torch.uint8, device=device)
+
+    def __call__(self, cache: Cache, q, out, stream: Optional[int] = None) -> None:
+        st = current_stream() if stream is None else stream
+        hhr_dense_decode(self.dims, cache.struct(), _ptr(q), self.softmax_scale, _ptr(self.ws),
+                         self.ws_bytes, _ptr(out), None, st)
 
 
 def build_pages(cache: Cache, R, W, method: str = "auto", stream: Optional[int] = None) -> None:

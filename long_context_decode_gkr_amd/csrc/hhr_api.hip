@@ -55,18 +55,33 @@ hhr_status check_cache(const hhr_cache* c, bool need_ticket, CacheView* v) {
   return HHR_OK;
 }
 
+float softmax_scale(float given) {
+  return given > 0.f ? given : float(1.0 / sqrt(double(kHeadDim)));
+}
+
 hhr_status check_params(const hhr_params* p, const Shape& s, DecodePlan* plan) {
   if (!p) return HHR_ERR_INVALID_ARG;
   const double rho = p->page_keep_ratio;
   if (!(rho > 0.0 && rho <= 1.0)) return HHR_ERR_INVALID_ARG;
   if (p->token_budget < 1) return HHR_ERR_INVALID_ARG;
   if (!isfinite(p->softmax_scale)) return HHR_ERR_INVALID_ARG;
-  const float scale = p->softmax_scale > 0.f ? p->softmax_scale : float(1.0 / sqrt(double(kHeadDim)));
-  *plan = plan_decode(s, rho, p->token_budget, scale);
+  if (p->stages != HHR_STAGES_BOTH && p->stages != HHR_STAGES_PAGES_ONLY &&
+      p->stages != HHR_STAGES_CODES_ONLY)
+    return HHR_ERR_INVALID_ARG;
+  *plan = plan_decode(s, rho, p->token_budget, softmax_scale(p->softmax_scale),
+                      static_cast<Stages>(p->stages));
   return HHR_OK;
 }
 
 hhr_status hip_status(hipError_t e) { return e == hipSuccess ? HHR_OK : HHR_ERR_HIP; }
+
+DebugView debug_view(const hhr_debug* dbg) {
+  DebugView dv{};
+  if (dbg) dv = DebugView{dbg->q_rot, dbg->q_code, dbg->bounds, dbg->page_ids,
+                          dbg->page_count, dbg->dist, dbg->token_idx, dbg->token_count,
+                          reinterpret_cast<hipEvent_t*>(dbg->kernel_events)};
+  return dv;
+}
 
 }  // namespace
 
@@ -133,12 +148,9 @@ static hhr_status decode_common(const hhr_dims* dims, const hhr_params* params,
   if (append && (!k_new || !v_new)) return HHR_ERR_INVALID_ARG;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < p.total)
     return HHR_ERR_WORKSPACE;
-  DebugView dv{};
-  if (dbg) dv = DebugView{dbg->q_rot, dbg->q_code, dbg->bounds, dbg->page_ids,
-                          dbg->page_count, dbg->dist, dbg->token_idx, dbg->token_count,
-                          reinterpret_cast<hipEvent_t*>(dbg->kernel_events)};
   return hip_status(launch_decode(s, p, c, append ? k_new : nullptr, append ? v_new : nullptr, q,
-                                  R, W, ws, out, dv, reinterpret_cast<hipStream_t>(stream)));
+                                  R, W, ws, out, debug_view(dbg),
+                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
 hhr_status hhr_decode(const hhr_dims* dims, const hhr_params* params, const hhr_cache* cache,
@@ -155,6 +167,29 @@ hhr_status hhr_append_decode(const hhr_dims* dims, const hhr_params* params,
                              hhr_stream_t stream) {
   return decode_common(dims, params, cache, k_new, v_new, true, q, R, W, ws, ws_bytes, out, dbg,
                        stream);
+}
+
+size_t hhr_dense_workspace_bytes(const hhr_dims* dims) {
+  Shape s;
+  if (check_dims(dims, &s) != HHR_OK) return 0;
+  return dense_workspace_bytes(s);
+}
+
+hhr_status hhr_dense_decode(const hhr_dims* dims, const hhr_cache* cache, const void* q,
+                            float softmax_scale_in, void* ws, size_t ws_bytes, float* out,
+                            const hhr_debug* dbg, hhr_stream_t stream) {
+  Shape s;
+  hhr_status st = check_dims(dims, &s);
+  if (st != HHR_OK) return st;
+  if (!cache || !cache->K || !cache->V || !cache->seq_lens) return HHR_ERR_INVALID_ARG;
+  if (!q || !out || !isfinite(softmax_scale_in)) return HHR_ERR_INVALID_ARG;
+  if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < dense_workspace_bytes(s))
+    return HHR_ERR_WORKSPACE;
+  const CacheView c{cache->K, cache->V, nullptr, nullptr, nullptr, cache->seq_lens, nullptr};
+  DebugView dv{};
+  if (dbg) dv.events = reinterpret_cast<hipEvent_t*>(dbg->kernel_events);
+  return hip_status(launch_dense(s, c, q, softmax_scale(softmax_scale_in), ws, out, dv,
+                                 reinterpret_cast<hipStream_t>(stream)));
 }
 
 const char* hhr_status_string(hhr_status status) {

@@ -151,6 +151,7 @@ struct SelectArgs {
   int kcap;
   int istride;        // row stride of idx: kcap live entries, then one trash entry per lane
   int appended;       // a token is appended in this step (seq_lens is advanced at its end)
+  int fine;           // 0: no Hamming ranking, every candidate is taken (pages-only stages)
 };
 
 // ---------------------------------------------------------------------------------------------
@@ -433,6 +434,7 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   auto slot_token = [&](int slot) { return (s_pages[slot >> lgS] << lgS) + (slot & (s.S - 1)); };
   auto distance = [&](int tk) -> uint32_t {
     if (tk >= L) return kNone;
+    if (!a.fine) return 0u;
     const uint4* cp = reinterpret_cast<const uint4*>(cbase + size_t(tk) * NW);
     uint32_t dd = 0;
 #pragma unroll
@@ -455,10 +457,21 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
       const int slot = base + u * kSelThreads + tid;
       const int tk = materialize(slot_token(min(slot, nslots - 1)));   // every lane
       tt[u] = (slot < nslots) ? tk : L;
-      const int tl = min(tt[u], L - 1);
-      const uint4* cp = reinterpret_cast<const uint4*>(cbase + size_t(tl) * NW);
+    }
+    if (a.fine) {   // uniform
 #pragma unroll
-      for (int v = 0; v < NW / 4; ++v) cw[u][v] = cp[v];
+      for (int u = 0; u < BAT; ++u) {
+        const uint4* cp = reinterpret_cast<const uint4*>(cbase + size_t(min(tt[u], L - 1)) * NW);
+#pragma unroll
+        for (int v = 0; v < NW / 4; ++v) cw[u][v] = cp[v];
+      }
+    } else {
+      // no fine stage: every live candidate gets distance 0 (the query code itself)
+#pragma unroll
+      for (int u = 0; u < BAT; ++u)
+#pragma unroll
+        for (int v = 0; v < NW / 4; ++v)
+          cw[u][v] = make_uint4(qw[4 * v], qw[4 * v + 1], qw[4 * v + 2], qw[4 * v + 3]);
     }
 #pragma unroll
     for (int u = 0; u < BAT; ++u) {
@@ -849,9 +862,18 @@ combine_kernel(const float* __restrict__ part, int nsplit, float* __restrict__ o
 // ---------------------------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-DecodePlan plan_decode(const Shape& s, double rho, int k, float scale) {
+DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages stages) {
   DecodePlan p{};
-  p.kcap = k < s.Lmax ? k : s.Lmax;
+  p.stages = stages;
+  if (stages == Stages::kPagesOnly) {
+    // every token of the kept pages: at most max(1, ceil(rho Pmax)) pages of S tokens
+    const long long keep = (long long)ceil(rho * double(s.Pmax));
+    const long long toks = (keep < 1 ? 1 : keep) * s.S;
+    p.kcap = toks < s.Lmax ? int(toks) : s.Lmax;
+  } else {
+    p.kcap = k < s.Lmax ? k : s.Lmax;
+  }
+  if (stages == Stages::kCodesOnly) rho = 1.0;   // every page is a candidate
   p.chunk = s.kv_bf16 ? AttnShape<1>::CHUNK : AttnShape<0>::CHUNK;
   p.nsplit = (p.kcap + p.chunk - 1) / p.chunk;
   p.rho = rho;
@@ -919,15 +941,19 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
   e = launch_prep(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg.q_rot, dbg.q_code,
                   PrepMode::kDecode, kernel_timer(dbg, 0), st);
   if (e != hipSuccess) return e;
-  BoundArgs ba{qrot, U, k_new != nullptr ? 1 : 0};
-  switch (s.G) {
-    case 1: launch_bound_t<1>(s, c, ba, dbg, st); break;
-    case 2: launch_bound_t<2>(s, c, ba, dbg, st); break;
-    case 4: launch_bound_t<4>(s, c, ba, dbg, st); break;
-    default: launch_bound_t<8>(s, c, ba, dbg, st); break;
+  // codes only: every page is kept, so no bound is needed (the selection reads U but keeps all)
+  if (p.stages != Stages::kCodesOnly) {
+    BoundArgs ba{qrot, U, k_new != nullptr ? 1 : 0};
+    switch (s.G) {
+      case 1: launch_bound_t<1>(s, c, ba, dbg, st); break;
+      case 2: launch_bound_t<2>(s, c, ba, dbg, st); break;
+      case 4: launch_bound_t<4>(s, c, ba, dbg, st); break;
+      default: launch_bound_t<8>(s, c, ba, dbg, st); break;
+    }
+    HHR_CHECK();
   }
-  HHR_CHECK();
-  SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap, p.istride, k_new != nullptr ? 1 : 0};
+  SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap, p.istride, k_new != nullptr ? 1 : 0,
+                p.stages == Stages::kPagesOnly ? 0 : 1};
   if (s.NB == 128) launch_select_nb<128>(s, c, sa, dbg, st);
   else launch_select_nb<256>(s, c, sa, dbg, st);
   HHR_CHECK();
@@ -938,11 +964,16 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
   else
     launch_kernel(attn_kernel<0>, grid, dim3(256), st, kernel_timer(dbg, 3), s, c.K, c.V, q, aa);
   HHR_CHECK();
-  launch_kernel(combine_kernel, dim3(s.B * s.Hq), dim3(kD), st, kernel_timer(dbg, 4), part,
-                p.nsplit, out, c.seq_lens, s.Hq, s.Lmax, k_new != nullptr ? 1 : 0);
-  HHR_CHECK();
+  return launch_combine(s, part, p.nsplit, out, c.seq_lens, k_new != nullptr ? 1 : 0,
+                        kernel_timer(dbg, 4), st);
 #undef HHR_CHECK
-  return hipSuccess;
+}
+
+hipError_t launch_combine(const Shape& s, const float* part, int nsplit, float* out,
+                          int32_t* seq_lens, int appended, KernelTimer tm, hipStream_t st) {
+  launch_kernel(combine_kernel, dim3(s.B * s.Hq), dim3(kD), st, tm, part, nsplit, out, seq_lens,
+                s.Hq, s.Lmax, appended);
+  return hipGetLastError();
 }
 
 }  // namespace hhr

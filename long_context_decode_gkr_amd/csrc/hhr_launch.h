@@ -52,9 +52,14 @@ inline void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t st, Kerne
     hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
 }
 
+// Which stages choose the attended tokens (the stage-wise ablation of the method).
+enum class Stages { kBoth = 0, kPagesOnly = 1, kCodesOnly = 2 };
+
 // Workspace carve-up of one decode call (byte offsets from the workspace base).
 struct DecodePlan {
-  int kcap;        // token budget clamped to max_seq_len
+  Stages stages;
+  int kcap;        // most tokens attended per (b, h): the token budget clamped to max_seq_len,
+                   // or (pages only) every token of the largest kept page set
   int istride;     // per-(b, h) stride of the index list: kcap entries + one trash entry per lane
   int chunk;       // tokens per attention workgroup
   int nsplit;      // attention workgroups per (b, h)
@@ -63,7 +68,7 @@ struct DecodePlan {
   size_t off_qrot, off_qcode, off_U, off_idx, off_cnt, off_part, total;
 };
 
-DecodePlan plan_decode(const Shape& s, double rho, int k, float scale);
+DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages stages);
 
 hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R, const float* W,
                              hipStream_t st);
@@ -80,6 +85,15 @@ hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, co
                        const void* q, const float* R, const float* W, float* qrot,
                        uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, PrepMode mode,
                        KernelTimer tm, hipStream_t st);
+// Merge of split-K attention partials [B][Hq][nsplit][128 + 2] (o, m, l) into out
+// [B][Hq][128]; with `appended` it also advances seq_lens (the sparse step's last kernel).
+hipError_t launch_combine(const Shape& s, const float* part, int nsplit, float* out,
+                          int32_t* seq_lens, int appended, KernelTimer tm, hipStream_t st);
+// Dense attention over every token (split-K, grouped-query sharing) and its merge; ws holds
+// dense_workspace_bytes(s) bytes of partials. Timers: events 0-1 (attention), 2-3 (merge).
+size_t dense_workspace_bytes(const Shape& s);
+hipError_t launch_dense(const Shape& s, const CacheView& c, const void* q, float scale,
+                        void* ws, float* out, const DebugView& dbg, hipStream_t st);
 // The decode step, with the append of k_new / v_new folded into its kernels when given.
 hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c,
                          const void* k_new, const void* v_new, const void* q, const float* R,

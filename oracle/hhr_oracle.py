@@ -210,28 +210,51 @@ def append_head(state: dict, k_new: np.ndarray, v_new: np.ndarray, R: np.ndarray
 # ----------------------------------------------------------------------------------------------
 # One decode step for one (sequence, query head)
 # ----------------------------------------------------------------------------------------------
+STAGES = ("both", "pages", "codes")
+
+
 def decode_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, L: int, lo: np.ndarray,
                 hi: np.ndarray, kcodes: np.ndarray, R: np.ndarray, W: np.ndarray, S: int,
-                rho: float, k: int, scale: float, pages: np.ndarray | None = None) -> dict:
+                rho: float, k: int, scale: float, pages: np.ndarray | None = None,
+                stages: str = "both") -> dict:
     """Coarse stage (rotate q, bound every page, keep the top pages), fine stage (query code,
     Hamming distance of every candidate, keep the top-k tokens), then exact attention.
 
     If `pages` is given, the coarse stage's choice is replaced by it (used to run the fine
     stage on another implementation's page set).
+
+    `stages` selects the variants of the stage-wise ablation (Appendix C, Table 8):
+    "both" is the method; "pages" runs the coarse stage alone and attends to every candidate
+    (no Hamming ranking, k unused); "codes" runs the fine stage alone over every token (every
+    page is a candidate, rho unused; no bound is computed).
     """
+    assert stages in STAGES
     P = num_pages(L, S)
     qt = rotate(np.asarray(q)[None, :], R)[0]
-    U = page_bounds(qt, lo[:P], hi[:P])
-    n_keep = keep_count(P, rho)
-    if pages is None:
-        pages = select_pages(U, n_keep)
+    if stages == "codes":
+        U, n_keep = None, P
+        if pages is None:
+            pages = np.arange(P)
+    else:
+        U = page_bounds(qt, lo[:P], hi[:P])
+        n_keep = keep_count(P, rho)
+        if pages is None:
+            pages = select_pages(U, n_keep)
     cand = candidates(pages, L, S)
     qc = codes(np.asarray(q)[None, :], W)[0]
-    D = hamming(qc, kcodes[cand])
-    sel = select_tokens(cand, D, k)
+    if stages == "pages":
+        D, sel = None, cand
+    else:
+        D = hamming(qc, kcodes[cand])
+        sel = select_tokens(cand, D, k)
     out = attend(q, K[sel], V[sel], scale)
     return dict(q_rot=qt, q_code=qc, U=U, n_keep=n_keep, pages=np.asarray(pages), cand=cand,
                 D=D, sel=sel, out=out)
+
+
+def dense_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, L: int, scale: float) -> np.ndarray:
+    """Full attention over the first L keys: the baseline HHR is timed against (§4.3, Fig. 7)."""
+    return attend(q, K[:L], V[:L], scale)
 
 
 # ----------------------------------------------------------------------------------------------
@@ -257,7 +280,7 @@ def build_layer(K: np.ndarray, seq_lens, R: np.ndarray, W: np.ndarray, S: int) -
 
 def decode_layer(q: np.ndarray, K: np.ndarray, V: np.ndarray, seq_lens, index: dict,
                  R: np.ndarray, W: np.ndarray, S: int, rho: float, k: int,
-                 scale: float | None = None, heads=None) -> dict:
+                 scale: float | None = None, heads=None, stages: str = "both") -> dict:
     """Run decode_head for every (b, h) (or the listed (b, h) pairs); returns {(b, h): result}."""
     B, Hq, d = q.shape
     Hkv = K.shape[1]
@@ -270,5 +293,5 @@ def decode_layer(q: np.ndarray, K: np.ndarray, V: np.ndarray, seq_lens, index: d
         g = h // G
         res[(b, h)] = decode_head(q[b, h], K[b, g], V[b, g], int(seq_lens[b]),
                                   index["lo"][b, g], index["hi"][b, g], index["codes"][b, g],
-                                  R[g], W[g], S, rho, k, scale)
+                                  R[g], W[g], S, rho, k, scale, stages=stages)
     return res

@@ -55,12 +55,12 @@ class GpuLayer:
         hb.build_pages(self.cache, self.R, self.W, method=method)
         torch_mod().cuda.synchronize()
 
-    def decode(self, rho, k, scale=0.0, debug=True):
+    def decode(self, rho, k, scale=0.0, debug=True, stages="both"):
         torch = torch_mod()
-        dec = hb.Decoder(self.dims, rho, k, scale)
+        dec = hb.Decoder(self.dims, rho, k, scale, stages=stages)
         out = torch.full((self.cfg.batch, self.cfg.num_q_heads, 128), float("nan"),
                          dtype=torch.float32, device="cuda")
-        dbg = hb.Debug(self.dims, k) if debug else None
+        dbg = hb.Debug(self.dims, k, rho, stages) if debug else None
         dec(self.cache, self.q, self.R, self.W, out, dbg)
         torch.cuda.synchronize()
         return out, dbg
@@ -114,8 +114,10 @@ def check_index(layer: GpuLayer, ref: dict, pairs=None, extrema_atol_scale=1.0):
             assert diff.max(initial=0.0) <= tol, (name, b, g, diff.max(), tol)
 
 
-def check_decode(layer: GpuLayer, out, dbg, rho, k, scale=None, heads=None, ref_index=None):
-    """Compare one decode step with the oracle on the listed (b, h) pairs (default: all)."""
+def check_decode(layer: GpuLayer, out, dbg, rho, k, scale=None, heads=None, ref_index=None,
+                 stages="both"):
+    """Compare one decode step with the oracle on the listed (b, h) pairs (default: all).
+    `stages`: "both", "pages" (coarse stage only) or "codes" (fine stage only)."""
     d, cfg = layer.data, layer.cfg
     S, G = cfg.page_size, cfg.group
     scale = orc.default_scale(128) if not scale else scale
@@ -141,35 +143,44 @@ def check_decode(layer: GpuLayer, out, dbg, rho, k, scale=None, heads=None, ref_
             continue
         o = orc.decode_head(q, d["K"][b, g], d["V"][b, g], L, ref_index["lo"][b, g],
                             ref_index["hi"][b, g], ref_index["codes"][b, g], d["R"][g], d["W"][g],
-                            S, rho, k, scale)
+                            S, rho, k, scale, stages=stages)
         P, n_keep = orc.num_pages(L, S), o["n_keep"]
         # query rotation and code
         assert np.abs(qr[b, h] - o["q_rot"]).max() <= 1e-6 * np.linalg.norm(q), (b, h)
         np.testing.assert_array_equal(qc[b, h], o["q_code"], err_msg=f"q code b={b} h={h}")
-        # bounds: GPU (own index, own q~) against the oracle
-        qt = o["q_rot"].astype(np.float64)
-        lo, hi = ref_index["lo"][b, g, :P].astype(np.float64), ref_index["hi"][b, g, :P].astype(np.float64)
-        Sp = np.abs(qt)[None, :] * np.maximum(np.abs(lo), np.abs(hi))
-        Sp = Sp.sum(axis=1)
-        assert np.all(np.abs(U[b, h, :P] - o["U"]) <= BOUND_RTOL * Sp), (b, h)
-        # page set: exact for the GPU's own bounds; swaps against the oracle only at near-ties
         assert pcnt[b, h] == n_keep
         gp = pid[b, h, :n_keep]
         assert np.all(np.diff(gp) > 0)
-        np.testing.assert_array_equal(gp, orc.select_pages(U[b, h, :P].astype(np.float64), n_keep))
-        cut = np.sort(o["U"])[::-1][n_keep - 1]
-        sym = set(gp.tolist()) ^ set(o["pages"].tolist())
-        for p in sym:
-            assert abs(o["U"][p] - cut) <= BOUND_RTOL * Sp[p], (b, h, p, o["U"][p], cut)
-        stats["swaps"] += len(sym) // 2
+        if stages == "codes":
+            np.testing.assert_array_equal(gp, np.arange(P))   # every page is a candidate
+        else:
+            # bounds: GPU (own index, own q~) against the oracle
+            qt = o["q_rot"].astype(np.float64)
+            lo = ref_index["lo"][b, g, :P].astype(np.float64)
+            hi = ref_index["hi"][b, g, :P].astype(np.float64)
+            Sp = np.abs(qt)[None, :] * np.maximum(np.abs(lo), np.abs(hi))
+            Sp = Sp.sum(axis=1)
+            assert np.all(np.abs(U[b, h, :P] - o["U"]) <= BOUND_RTOL * Sp), (b, h)
+            # page set: exact for the GPU's own bounds; swaps against the oracle only at
+            # near-ties
+            np.testing.assert_array_equal(gp, orc.select_pages(U[b, h, :P].astype(np.float64),
+                                                               n_keep))
+            cut = np.sort(o["U"])[::-1][n_keep - 1]
+            sym = set(gp.tolist()) ^ set(o["pages"].tolist())
+            for p in sym:
+                assert abs(o["U"][p] - cut) <= BOUND_RTOL * Sp[p], (b, h, p, o["U"][p], cut)
+            stats["swaps"] += len(sym) // 2
         # fine stage on the GPU's pages
         cand = orc.candidates(gp, L, S)
-        Dref = orc.hamming(o["q_code"], ref_index["codes"][b, g][cand])
-        slots = (gp[:, None] * S + np.arange(S)[None, :]).reshape(-1)
-        dgot = dist[b, h, :n_keep * S]
-        np.testing.assert_array_equal(dgot[slots < L], Dref, err_msg=f"distances b={b} h={h}")
-        assert np.all(dgot[slots >= L] == 0xFFFF)
-        sel = orc.select_tokens(cand, Dref, k)
+        if stages == "pages":
+            sel = cand                                       # every candidate is attended
+        else:
+            Dref = orc.hamming(o["q_code"], ref_index["codes"][b, g][cand])
+            slots = (gp[:, None] * S + np.arange(S)[None, :]).reshape(-1)
+            dgot = dist[b, h, :n_keep * S]
+            np.testing.assert_array_equal(dgot[slots < L], Dref, err_msg=f"distances b={b} h={h}")
+            assert np.all(dgot[slots >= L] == 0xFFFF)
+            sel = orc.select_tokens(cand, Dref, k)
         assert tcnt[b, h] == len(sel), (b, h)
         np.testing.assert_array_equal(tidx[b, h, :len(sel)], sel, err_msg=f"tokens b={b} h={h}")
         ref_out = orc.attend(q, d["K"][b, g][sel], d["V"][b, g][sel], scale)

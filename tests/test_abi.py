@@ -125,3 +125,52 @@ def test_append_decode_needs_new_token_and_ticket():
     assert call(fake_cache(), kn=None) == 1
     assert call(fake_cache(), vn=None) == 1
     assert call(fake_cache(append_ticket=None)) == 1
+
+
+@pytest.mark.parametrize("stages", [-1, 3, 100])
+def test_invalid_stages(stages):
+    p = hb.Params(0.125, 2048, 0.0, stages)
+    assert decode_status(params=p) == 1
+    assert hb.hhr_decode_workspace_bytes(good_dims(), p) == 0
+
+
+def test_pages_only_workspace_holds_every_kept_token():
+    d = good_dims(max_seq_len=131072)
+    both = hb.hhr_decode_workspace_bytes(d, hb.Params(1 / 16, 4096, 0.0, hb.HHR_STAGES_BOTH))
+    pages = hb.hhr_decode_workspace_bytes(d, hb.Params(1 / 16, 4096, 0.0,
+                                                       hb.HHR_STAGES_PAGES_ONLY))
+    codes = hb.hhr_decode_workspace_bytes(d, hb.Params(1 / 16, 4096, 0.0,
+                                                       hb.HHR_STAGES_CODES_ONLY))
+    # pages only: 512 kept pages x 16 tokens = 8192 indices per head instead of 4096
+    assert pages >= both + 32 * 4096 * 4
+    assert codes == both
+
+
+def dense_status(dims=None, cache=None, q=FAKE, scale=0.0, ws=FAKE * 256, ws_bytes=1 << 40,
+                 out=FAKE):
+    lib = hb.load()
+    dims = dims or good_dims()
+    cache = cache or fake_cache()
+    return lib.hhr_dense_decode(ctypes.byref(dims), ctypes.byref(cache), q, scale, ws, ws_bytes,
+                                out, None, None)
+
+
+def test_dense_decode_validation():
+    d = good_dims()
+    need = hb.hhr_dense_workspace_bytes(d)
+    # one partial (128 + 2 floats) per (b, h) and split
+    assert need > 0 and need % (32 * 130 * 4) == 0
+    bad = good_dims(head_dim=64)
+    assert hb.hhr_dense_workspace_bytes(bad) == 0
+    assert dense_status(dims=bad) == 2
+    for field in ("K", "V", "seq_lens"):
+        assert dense_status(cache=fake_cache(**{field: None})) == 1
+    # the index is not read: its pointers may be NULL (validation passes them; the call then
+    # fails on the workspace check below, before anything is enqueued)
+    assert dense_status(cache=fake_cache(page_min=None, page_max=None, codes=None),
+                        ws_bytes=need - 1) == 4
+    assert dense_status(q=None) == 1
+    assert dense_status(out=None) == 1
+    assert dense_status(scale=float("nan")) == 1
+    assert dense_status(ws_bytes=need - 1) == 4
+    assert dense_status(ws=FAKE * 256 + 4, ws_bytes=need) == 4

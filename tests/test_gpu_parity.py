@@ -362,3 +362,80 @@ def test_decode_on_mfma_index_matches_oracle():
     out, dbg = lay.decode(1 / 16, 512)
     st = hc.check_decode(lay, out, dbg, 1 / 16, 512, ref_index=ref)
     print(f"mfma index: max out rel err {st['max_out_rel']:.2e}, page swaps {st['swaps']}")
+
+
+# ---------------------------------------------------------------------------------------------
+# Stage variants (Appendix C, Table 8) and the dense baseline (§4.3, Fig. 7)
+# ---------------------------------------------------------------------------------------------
+STAGE_CASES = [
+    # stages, cfg, L, batch, lens, rho, k
+    ("pages", 2, 3001, None, None, 1 / 8, 300),
+    ("pages", 4, 3000, 3, [3000, 1777, 17], 0.30, 50),
+    ("pages", 1, 2000, None, None, 0.25, 7),            # fp32, G = 1
+    ("codes", 2, 3001, None, None, 1 / 8, 300),
+    ("codes", 5, 2085, 2, None, 1 / 8, 257),            # page 32, 256-bit codes
+    ("codes", 1, 2000, None, None, 0.25, 2000),         # k = L: dense
+]
+
+
+@pytest.mark.parametrize("stages,cfg_id,L,batch,lens,rho,k", STAGE_CASES)
+def test_decode_stage_variants_match_oracle(stages, cfg_id, L, batch, lens, rho, k):
+    _torch()
+    cfg = _cfg(cfg_id, L, batch=batch, lens=lens, n_plant=8)
+    lay = hc.GpuLayer(cfg, max_seq_len=L + 64)
+    lay.build()
+    ref = hc.oracle_index(lay)
+    out, dbg = lay.decode(rho, k, stages=stages)
+    st = hc.check_decode(lay, out, dbg, rho, k, ref_index=ref, stages=stages)
+    print(f"{stages} cfg{cfg_id} L={L}: max out rel err {st['max_out_rel']:.2e}")
+
+
+def test_codes_only_leaves_bounds_untouched_and_identity_rotation_works():
+    torch = _torch()
+    cfg = _cfg(2, 1500, n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=1536)
+    # R = I: the plain per-channel min/max page bound (the rotation is an input)
+    lay.R = torch.eye(128, dtype=torch.float32, device="cuda").expand(8, 128, 128).contiguous()
+    lay.data = dict(lay.data, R=np.stack([np.eye(128, dtype=np.float32)] * 8))
+    lay.build()
+    ref = hc.oracle_index(lay)
+    hc.check_index(lay, ref)
+    out, dbg = lay.decode(0.2, 100)
+    hc.check_decode(lay, out, dbg, 0.2, 100, ref_index=ref)
+    out2, dbg2 = lay.decode(0.2, 100, stages="codes", debug=True)
+    assert torch.all(dbg2.bounds == 0.0)      # freshly allocated: never written
+    hc.check_decode(lay, out2, dbg2, 0.2, 100, ref_index=ref, stages="codes")
+
+
+DENSE_CASES = [
+    # cfg, L, batch, lens
+    (1, 4096, None, None),                  # fp32, G = 1
+    (2, 5003, None, None),                  # bf16, G = 4, ragged
+    (4, 3000, 3, [3000, 0, 1]),             # empty and one-token sequences
+    (5, 4096, 2, [4096, 2049]),
+]
+
+
+@pytest.mark.parametrize("cfg_id,L,batch,lens", DENSE_CASES)
+def test_dense_decode_matches_textbook_attention(cfg_id, L, batch, lens):
+    torch = _torch()
+    cfg = _cfg(cfg_id, L, batch=batch, lens=lens, n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=L + 64)
+    dd = hb.DenseDecoder(lay.dims)
+    out = torch.full((cfg.batch, cfg.num_q_heads, 128), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    dd(lay.cache, lay.q, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    d = lay.data
+    for b in range(cfg.batch):
+        Lb = int(d["seq_lens"][b])
+        for h in range(cfg.num_q_heads):
+            if Lb == 0:
+                assert np.all(got[b, h] == 0.0)
+                continue
+            g = h // cfg.group
+            ref = orc.dense_head(d["q"][b, h], d["K"][b, g], d["V"][b, g], Lb,
+                                 orc.default_scale(128))
+            rel = np.abs(got[b, h] - ref).max() / np.abs(ref).max()
+            assert rel <= hc.OUT_RTOL, (b, h, rel)

@@ -340,3 +340,83 @@ def test_generator_planted_keys_are_selected_at_full_budget_ratio():
 def test_candidates_drop_positions_past_the_sequence_end():
     assert orc.candidates(np.array([0, 2]), 10, 4).tolist() == [0, 1, 2, 3, 8, 9]
     assert orc.candidates(np.array([1]), 10, 4).tolist() == [4, 5, 6, 7]
+
+
+# ---------------------------------------------------------------------------------------------
+# Stage variants (Appendix C, Table 8) and the dense baseline (§4.3, Fig. 7)
+# ---------------------------------------------------------------------------------------------
+def _sdpa(q, K, V, scale):
+    qt = torch.tensor(q, dtype=torch.float64)[None, None, None]
+    kt = torch.tensor(K, dtype=torch.float64)[None, None]
+    vt = torch.tensor(V, dtype=torch.float64)[None, None]
+    return torch.nn.functional.scaled_dot_product_attention(qt, kt, vt, scale=scale)[0, 0, 0].numpy()
+
+
+def test_dense_head_is_library_attention():
+    cfg = synth.CONFIGS[5].scaled(seq_len=400, batch=1, n_plant=2)
+    lay = synth.make_layer(cfg, lens=[357])
+    for h in (0, 9, 31):
+        g = h // cfg.group
+        out = orc.dense_head(lay["q"][0, h], lay["K"][0, g], lay["V"][0, g], 357, 0.07)
+        np.testing.assert_allclose(out, _sdpa(lay["q"][0, h], lay["K"][0, g, :357],
+                                              lay["V"][0, g, :357], 0.07), rtol=1e-12, atol=1e-13)
+
+
+def test_pages_only_attends_every_token_of_the_top_pages():
+    cfg = synth.CONFIGS[2].scaled(seq_len=520, n_plant=4)
+    lay = synth.make_layer(cfg)
+    idx = orc.build_layer(lay["K"], lay["seq_lens"], lay["R"], lay["W"], cfg.page_size)
+    S, L = cfg.page_size, 520
+    for h in (0, 17):
+        g = h // cfg.group
+        r = orc.decode_layer(lay["q"], lay["K"], lay["V"], lay["seq_lens"], idx, lay["R"], lay["W"],
+                             S, rho=0.25, k=1, heads=[(0, h)], stages="pages")[(0, h)]
+        # brute force: logit bound of every page from the definition, top pages by (-U, p)
+        qt = lay["q"][0, h].astype(np.float64) @ lay["R"][g].astype(np.float64)
+        P = -(-L // S)
+        U = []
+        for p in range(P):
+            kt = lay["K"][0, g, p * S:min(L, p * S + S)].astype(np.float64) @ lay["R"][g].astype(np.float64)
+            lo_, hi_ = kt.astype(np.float32).min(0), kt.astype(np.float32).max(0)
+            U.append(sum(max(a * l_, a * u_) for a, l_, u_ in zip(qt.astype(np.float32).astype(np.float64), lo_, hi_)))
+        n_keep = math.ceil(0.25 * P)
+        keep = sorted(sorted(range(P), key=lambda p: (-U[p], p))[:n_keep])
+        toks = [t for p in keep for t in range(p * S, min(L, p * S + S))]
+        assert r["sel"].tolist() == toks            # the token budget k = 1 is not used
+        np.testing.assert_allclose(r["out"], _sdpa(lay["q"][0, h], lay["K"][0, g, toks],
+                                                   lay["V"][0, g, toks], orc.default_scale(128)),
+                                   rtol=1e-12, atol=1e-13)
+
+
+def test_codes_only_is_hamming_top_k_over_every_token():
+    cfg = synth.CONFIGS[5].scaled(seq_len=300, batch=1, n_plant=2)
+    lay = synth.make_layer(cfg)
+    idx = orc.build_layer(lay["K"], lay["seq_lens"], lay["R"], lay["W"], cfg.page_size)
+    L, k = 300, 37
+    r = orc.decode_layer(lay["q"], lay["K"], lay["V"], lay["seq_lens"], idx, lay["R"], lay["W"],
+                         cfg.page_size, rho=1e-9, k=k, heads=[(0, 6)], stages="codes")[(0, 6)]
+    g = 6 // cfg.group
+    # brute force over every token: distances bit by bit (the codes themselves are pinned by
+    # the exact-sign tests above), then sorted by (D, t)
+    qc = orc.codes(lay["q"][0, 6][None, :], lay["W"][g])[0]
+    kc = idx["codes"][0, g, :L]
+    D = [sum(((int(qc[w]) ^ int(kc[t, w])) >> i) & 1 for w in range(len(qc)) for i in range(32))
+         for t in range(L)]
+    sel = sorted(sorted(range(L), key=lambda t: (D[t], t))[:k])
+    assert r["U"] is None and r["n_keep"] == -(-L // cfg.page_size)   # rho is not used
+    assert r["sel"].tolist() == sel
+
+
+def test_full_budgets_of_each_stage_give_dense_attention():
+    cfg = synth.CONFIGS[2].scaled(seq_len=333, n_plant=4)
+    lay = synth.make_layer(cfg)
+    idx = orc.build_layer(lay["K"], lay["seq_lens"], lay["R"], lay["W"], cfg.page_size)
+    L = 333
+    for stages, rho, k in (("pages", 1.0, 1), ("codes", 0.1, L)):
+        r = orc.decode_layer(lay["q"], lay["K"], lay["V"], lay["seq_lens"], idx, lay["R"],
+                             lay["W"], cfg.page_size, rho=rho, k=k, heads=[(0, 3)],
+                             stages=stages)[(0, 3)]
+        assert r["sel"].tolist() == list(range(L))
+        np.testing.assert_allclose(r["out"], orc.dense_head(lay["q"][0, 3], lay["K"][0, 0],
+                                                            lay["V"][0, 0], L, orc.default_scale(128)),
+                                   rtol=1e-12, atol=1e-13)
