@@ -20,11 +20,19 @@ each W warm-up steps then exactly K timed steps bracketed by torch.cuda.synchron
   2. plain launches on one stream, no events: the headline us/step/layer;
   3. replay of one captured HIP graph per layer instance (graph_us_per_step; on this stack a
      graph replay of the five kernels is slower than the plain launches).
-The index builder (MFMA path) is timed once over every key of the first layer instance.
+The index builder (MFMA path) is timed once over every key of the first layer instance, and the
+dense baseline (full attention over every token, hhr_dense_decode) on the same layer instances,
+for the same-hardware speedup of the sparse step over full attention (dense_us_per_step,
+speedup_vs_dense).
 
-Prints ONE JSON line. Options: --gpus (must be 1), --steps, --warmup, --workload, --layers,
---no-cpu-baseline, --no-builder, --quiet, --copy-calibration (a 512 MiB device copy only, to
-scale the HBM byte counters of rocprofv3).
+--variant times another configuration of the same workload: the coarse stage alone (pages:
+every token of the kept pages is attended), the fine stage alone (codes: Hamming top-k over
+every token), the method with R = I (identity-r: the plain per-channel min/max bound), or the
+dense baseline itself (dense).
+
+Prints ONE JSON line. Options: --gpus (must be 1), --steps, --warmup, --workload, --variant,
+--layers, --no-cpu-baseline, --no-builder, --no-dense, --quiet, --copy-calibration (a 512 MiB
+device copy only, to scale the HBM byte counters of rocprofv3).
 """
 from __future__ import annotations
 
@@ -40,12 +48,11 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
-KERNELS = ("prep", "page_bound", "select", "sparse_attn", "combine")
 CSRC = os.path.join(ROOT, "long_context_decode_gkr_amd", "csrc")
 # source files each kernel is compiled from (besides the shared device and launch headers)
 KERNEL_SOURCES = {"prep": "hhr_build.hip", "page_bound": "hhr_decode.hip", "select": "hhr_decode.hip",
                   "sparse_attn": "hhr_decode.hip", "combine": "hhr_decode.hip",
-                  "builder": "hhr_build_mfma.hip"}
+                  "builder": "hhr_build_mfma.hip", "dense_attn": "hhr_dense.hip"}
 
 # name -> (synthetic config id, append a token each step, layer instances cycled, description)
 WORKLOADS = {
@@ -64,7 +71,29 @@ def log(msg, quiet):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-def algorithmic_bytes(cfg, lens, append=True):
+# variant -> the timed kernels and their index in the library's per-step event list
+VARIANTS = {
+    "hhr": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3), ("combine", 4)),
+    "identity-r": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3),
+                   ("combine", 4)),
+    "pages": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3), ("combine", 4)),
+    "codes": (("prep", 0), ("select", 2), ("sparse_attn", 3), ("combine", 4)),
+    "dense": (("dense_attn", 0), ("combine", 1)),
+}
+
+
+def dense_splits(cfg, lmax):
+    """Split count of the dense attention grid (the library's rule: whole sub-chunks of 4 waves x
+    rows-per-load x loads, about 1024 workgroups, at most 64 sub-chunks per workgroup)."""
+    bf16 = cfg.dtype == "bf16"
+    rpi = 64 // (128 // (8 if bf16 else 4))
+    sub = 4 * rpi * (8 if cfg.group <= 4 else 4)
+    rows = lmax * cfg.batch * cfg.num_kv_heads
+    subs = min(64, max(1, -(-rows // (1024 * sub))))
+    return -(-lmax // (subs * sub))
+
+
+def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
     """Bytes each kernel must move per launch (one layer, one step) for sequence lengths `lens`.
 
     prep:       q and R, W read (once per KV head); q~ and the query codes written; with an
@@ -72,16 +101,25 @@ def algorithmic_bytes(cfg, lens, append=True):
                 written, and its page's extrema column pair read and written.
     page_bound: min+max of every page of every KV head (d x 8 B per page), q~ read, U
                 written (4 B per query head and page).
-    select:     U and the query code read, the codes of the kept pages' tokens (NB/8 B per
-                candidate and query head), the selected indices written.
+    select:     U and the query code read, the codes of the candidates (NB/8 B per candidate
+                and query head), the selected indices written. Coarse stage only: no code is
+                read and every candidate is written. Fine stage only: no U; every token is a
+                candidate.
     sparse_attn: K and V rows of the selected tokens (2 x d x 2 B per token and query head),
                 indices and q read, one (o, m, l) partial per 256 tokens written.
     combine:    the partials read, the output written.
+    dense_attn: (dense baseline) K and V rows of every token once per KV head, q read, one
+                partial per split and query head written.
     """
     d, S, nb = cfg.head_dim, cfg.page_size, cfg.hash_bits
     Hq, Hkv = cfg.num_q_heads, cfg.num_kv_heads
     esz = 2 if cfg.dtype == "bf16" else 4
     B = len(lens)
+    if variant == "dense":
+        nsplit = dense_splits(cfg, lmax or max(lens))
+        parts = B * Hq * nsplit * (d + 2) * 4
+        return {"dense_attn": B * Hq * d * esz + sum(Hkv * L * 2 * d * esz for L in lens) + parts,
+                "combine": parts + B * Hq * d * 4}
     out = {"prep": B * Hq * d * esz + Hkv * d * d * 4 + Hkv * d * nb * 4 + B * Hq * d * 4
                    + B * Hq * nb // 8,
            "page_bound": B * Hq * d * 4, "select": 0, "sparse_attn": 0, "combine": 0}
@@ -89,13 +127,21 @@ def algorithmic_bytes(cfg, lens, append=True):
         out["prep"] += B * Hkv * (2 * d * esz + 2 * d * esz + nb // 8 + 2 * d * 4 * 2)
     for L in lens:
         P = -(-L // S)
-        n_keep = min(P, max(1, math.ceil(cfg.keep_ratio * P)))
-        k = min(cfg.token_budget, min(n_keep * S, L))
+        n_keep = P if variant == "codes" else min(P, max(1, math.ceil(cfg.keep_ratio * P)))
+        ncand = min(n_keep * S, L)
+        k = ncand if variant == "pages" else min(cfg.token_budget, ncand)
         parts = Hq * -(-k // 256) * (d + 2) * 4
         out["page_bound"] += Hkv * P * d * 8 + Hq * P * 4
-        out["select"] += Hq * (P * 4 + nb // 8 + n_keep * S * (nb // 8) + k * 4)
+        if variant == "pages":
+            out["select"] += Hq * (P * 4 + k * 4)
+        elif variant == "codes":
+            out["select"] += Hq * (nb // 8 + ncand * (nb // 8) + k * 4)
+        else:
+            out["select"] += Hq * (P * 4 + nb // 8 + n_keep * S * (nb // 8) + k * 4)
         out["sparse_attn"] += Hq * (k * 2 * d * esz + k * 4 + d * esz) + parts
         out["combine"] += parts + Hq * d * 4
+    if variant == "codes":
+        del out["page_bound"]
     return out
 
 
@@ -221,10 +267,15 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD)
+    ap.add_argument("--variant", choices=sorted(VARIANTS), default="hhr",
+                    help="hhr: the method; pages / codes: coarse or fine stage alone; "
+                         "identity-r: R = I; dense: full attention over every token")
     ap.add_argument("--layers", type=int, default=None,
                     help="layer instances cycled (default: per workload, 8 or 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-builder", action="store_true")
+    ap.add_argument("--no-dense", action="store_true",
+                    help="skip timing the dense baseline on the same layers")
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 512 MiB device copy (for HBM counter scaling)")
@@ -247,7 +298,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     hb.load()
+    variant = args.variant
     cfg_id, append, nl_default, desc = WORKLOADS[args.workload]
+    append = append and variant != "dense"     # the dense baseline keeps no index to update
     cfg = synth.CONFIGS[cfg_id]
     NL, K, Wm = args.layers or nl_default, args.steps, args.warmup
     B, Hq, Hkv, d, S, nb = (cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
@@ -259,7 +312,8 @@ def main():
     else:
         visits = 0
         lens0 = cfg.lengths()
-    log(f"workload {args.workload}: generating the layer (lengths {min(lens0)}..{max(lens0)})", q)
+    log(f"workload {args.workload}, variant {variant}: generating the layer "
+        f"(lengths {min(lens0)}..{max(lens0)})", q)
     t0 = time.time()
     data = synth.make_layer(cfg, max_seq_len=Lcap, lens=lens0)
     log(f"  {time.time() - t0:.1f} s", q)
@@ -268,6 +322,8 @@ def main():
     dev = torch.device("cuda")
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     qd = torch.from_numpy(data["q"]).to(dev).to(tdt)
+    if variant == "identity-r":
+        data["R"] = np.stack([np.eye(d, dtype=np.float32)] * Hkv)
     Rd = torch.from_numpy(data["R"]).to(dev)
     Wd = torch.from_numpy(data["W"]).to(dev)
     layers = []
@@ -277,7 +333,8 @@ def main():
     first.seq_lens.copy_(torch.from_numpy(data["seq_lens"]).to(dev))
     hb.build_pages(first, Rd, Wd)
     torch.cuda.synchronize()
-    builder = None if args.no_builder else time_builder(hb, first, Rd, Wd, cfg, lens0, q)
+    builder = (None if args.no_builder or variant != "hhr"
+               else time_builder(hb, first, Rd, Wd, cfg, lens0, q))
     layers.append(first)
     for _ in range(NL - 1):
         c = hb.Cache(dims)
@@ -288,15 +345,23 @@ def main():
         kn, vn = synth.append_tokens(cfg, visits)
         knd = torch.from_numpy(kn).to(dev).to(tdt)
         vnd = torch.from_numpy(vn).to(dev).to(tdt)
-    dec = hb.Decoder(dims, cfg.keep_ratio, cfg.token_budget)
+    stages = {"pages": "pages", "codes": "codes"}.get(variant, "both")
+    dec = hb.Decoder(dims, cfg.keep_ratio, cfg.token_budget, stages=stages)
+    dense = hb.DenseDecoder(dims)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     cache_structs = [c.struct() for c in layers]
     P = dict(q=qd.data_ptr(), R=Rd.data_ptr(), W=Wd.data_ptr(), ws=dec.ws.data_ptr(),
-             out=out.data_ptr())
+             out=out.data_ptr(), dws=dense.ws.data_ptr())
+
+    def dense_step(i, dbg, stream):
+        hb.hhr_dense_decode(dims, cache_structs[i % NL], P["q"], 0.0, P["dws"], dense.ws_bytes,
+                            P["out"], dbg, stream)
 
     def step(i, dbg, stream, visit=None):
         li = i % NL
-        if append:
+        if variant == "dense":
+            dense_step(i, dbg, stream)
+        elif append:
             v = i // NL if visit is None else visit
             hb.hhr_append_decode(dims, dec.params, cache_structs[li], knd[v].data_ptr(),
                                  vnd[v].data_ptr(), P["q"], P["R"], P["W"], P["ws"],
@@ -308,7 +373,8 @@ def main():
     # ---- pass 1 (launches with events): per-kernel durations from HIP events that the runtime
     # records around each kernel's own execution on the decode stream (hipExtLaunchKernel)
     stream = hb.current_stream()
-    NE = 2 * len(KERNELS)
+    NE = 10                                   # events per step the library may record
+    timed = VARIANTS[variant]
     ev = hb.HipEvents(NE * K)
     dbgs = [hb.DebugStruct(None, None, None, None, None, None, None, None, ev.address(NE * i))
             for i in range(K)]
@@ -323,7 +389,7 @@ def main():
     events_ms = (time.perf_counter() - t_start) * 1e3 / K
     # events [NE i + 2 j] and [NE i + 2 j + 1]: start and stop of kernel j of step i
     per = {n: [ev.elapsed_ms(NE * i + 2 * j, NE * i + 2 * j + 1) for i in range(K)]
-           for j, n in enumerate(KERNELS)}
+           for n, j in timed}
     ev.close()
 
     # ---- pass 2 (plain launches on one stream): the headline figure
@@ -357,21 +423,36 @@ def main():
         graphs[(Wm + i) % NL].replay()
     torch.cuda.synchronize()
     graph_ms = (time.perf_counter() - t_start) * 1e3 / K
+
+    # ---- the dense baseline on the same layer instances (same-hardware speedup)
+    dense_ms = None
+    if variant != "dense" and not args.no_dense:
+        log(f"dense baseline: warm-up {Wm}, timed {K} steps", q)
+        for i in range(Wm):
+            dense_step(i, None, stream)
+        torch.cuda.synchronize()
+        t_start = time.perf_counter()
+        for i in range(K):
+            dense_step(i, None, stream)
+        torch.cuda.synchronize()
+        dense_ms = (time.perf_counter() - t_start) * 1e3 / K
+
     ms_step = stream_ms
     avg_ms = {n: float(np.mean(v)) for n, v in per.items()}
     lens_avg = [L + visits // 2 for L in lens0]
-    alg = algorithmic_bytes(cfg, lens_avg, append)
+    alg = algorithmic_bytes(cfg, lens_avg, append, variant, int(data["max_seq_len"]))
     kern = {}
-    for n in KERNELS:
+    for n, _ in timed:
         kern[n] = {"avg_us": round(avg_ms[n] * 1e3, 2), "p50_us": round(float(np.median(per[n])) * 1e3, 2),
                    "alg_bytes": alg[n],
                    "alg_GBps": round(alg[n] / (avg_ms[n] * 1e-3) / 1e9, 1)}
-    dominant = max(("page_bound", "sparse_attn"), key=lambda n: avg_ms[n])
-    traffic = load_traffic(args.workload, dominant)
+    cands = [n for n in ("page_bound", "sparse_attn", "dense_attn") if n in avg_ms]
+    dominant = max(cands, key=lambda n: avg_ms[n])
+    traffic = load_traffic(args.workload, dominant) if variant == "hhr" else None
     achieved = alg[dominant] / (avg_ms[dominant] * 1e-3) / 1e9
     step_bytes = sum(alg.values())
     us = ms_step * 1e3
-    if args.workload == DEFAULT_WORKLOAD:
+    if args.workload == DEFAULT_WORKLOAD and variant == "hhr":
         metric = "HHR decode us/step/layer at 128K ctx (32q/8kv, d128) + % HBM roofline"
     else:
         metric = "HHR decode us/step/layer + % HBM roofline"
@@ -393,7 +474,7 @@ def main():
                 + ("N(0,1) keys with 4 outlier channels x10" if cfg.key_dist == "outlier"
                    else "N(0,1) keys with lognormal per-channel scales")
                 + ", planted high-logit keys; random orthogonal R, Gaussian W)",
-        "config": {"workload": desc, "name": args.workload,
+        "config": {"workload": desc, "name": args.workload, "variant": variant,
                    "batch": B, "seq_len": Lcap, "q_heads": Hq, "kv_heads": Hkv, "head_dim": d,
                    "kv_dtype": cfg.dtype, "page_size": S, "hash_bits": nb,
                    "keep_ratio": cfg.keep_ratio, "token_budget": cfg.token_budget,
@@ -408,9 +489,11 @@ def main():
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
         "kernels": kern,
         "builder": builder,
+        "dense_us_per_step": None if dense_ms is None else round(dense_ms * 1e3, 2),
+        "speedup_vs_dense": None if dense_ms is None else round(dense_ms / ms_step, 3),
         "kernel_source_digest": {n: kernel_source_digest(n) for n in KERNEL_SOURCES},
     }
-    if not args.no_cpu_baseline:
+    if not args.no_cpu_baseline and variant == "hhr":
         result["cpu_baseline"] = cpu_baseline(cfg, data, append, q)
     print(json.dumps(result), flush=True)
 

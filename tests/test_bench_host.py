@@ -55,3 +55,44 @@ def test_byte_model_sums_over_sequences():
 def test_kernel_source_digest_is_stable(kernel):
     assert bench.kernel_source_digest(kernel) == bench.kernel_source_digest(kernel)
     assert len(bench.kernel_source_digest(kernel)) == 16
+
+
+def test_byte_model_of_the_variants():
+    cfg = synth.CONFIGS[3]
+    base = bench.algorithmic_bytes(cfg, [131072], False, "hhr")
+    pages = bench.algorithmic_bytes(cfg, [131072], False, "pages")
+    codes = bench.algorithmic_bytes(cfg, [131072], False, "codes")
+    # coarse stage alone: no codes read, all 512 x 16 candidates attended
+    assert pages["select"] == 32 * (8192 * 4 + 8192 * 4)
+    assert pages["sparse_attn"] > 2 * base["sparse_attn"] - 32 * 4096 * 8
+    # fine stage alone: no bound kernel, every token's code read
+    assert "page_bound" not in codes
+    assert codes["select"] == 32 * (16 + 131072 * 16 + 4096 * 4)
+    assert codes["sparse_attn"] == base["sparse_attn"]
+    dense = bench.algorithmic_bytes(cfg, [131072], False, "dense", 131072)
+    # every K and V row once per KV head (512 MiB) dominates
+    assert 8 * 131072 * 512 < dense["dense_attn"] < 1.01 * 8 * 131072 * 512
+    assert set(bench.VARIANTS) == {"hhr", "identity-r", "pages", "codes", "dense"}
+    for v, ks in bench.VARIANTS.items():
+        alg = bench.algorithmic_bytes(cfg, [131072], False, v, 131072)
+        assert {n for n, _ in ks} == set(alg), v
+
+
+def test_dense_split_rule():
+    # 128K x 8 KV heads in sub-chunks of 128 rows: 8 sub-chunks per workgroup, 128 splits
+    assert bench.dense_splits(synth.CONFIGS[3], 131072) == 128
+    assert bench.dense_splits(synth.CONFIGS[1], 4096) >= 1
+
+
+@pytest.mark.skipif(not os.path.exists(os.path.join(ROOT, "long_context_decode_gkr_amd",
+                                                    "libhhr.so")), reason="libhhr.so not built")
+@pytest.mark.parametrize("cfg_id", [1, 2, 3, 4, 5])
+def test_dense_split_rule_matches_the_library(cfg_id):
+    from long_context_decode_gkr_amd import binding as hb
+    cfg = synth.CONFIGS[cfg_id]
+    lmax = -(-cfg.seq_len // (4 * cfg.page_size)) * 4 * cfg.page_size
+    dims = hb.make_dims(cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.page_size,
+                        cfg.hash_bits, lmax,
+                        kv_dtype=hb.HHR_BF16 if cfg.dtype == "bf16" else hb.HHR_F32)
+    assert hb.hhr_dense_workspace_bytes(dims) == \
+        cfg.batch * cfg.num_q_heads * bench.dense_splits(cfg, lmax) * 130 * 4

@@ -87,3 +87,42 @@ def test_fullsize_qwen_64k_batch4():
     out, dbg = lay.decode(cfg.keep_ratio, cfg.token_budget)
     heads = [(0, 0), (3, 17), (2, 31)]
     _check(lay, out, dbg, cfg, heads, sorted({(b, h // 4) for b, h in heads}))
+
+
+@pytest.mark.parametrize("stages", ["pages", "codes"])
+def test_fullsize_128k_stage_variants(stages):
+    """The stage-wise ablation variants at 128K (keep 1/16, k = 4096), sampled heads. The fine
+    stage alone ranks all 131072 keys per head (more than the LDS distance cache holds: the
+    selection recomputes distances while emitting)."""
+    _torch()
+    cfg = synth.CONFIGS[3]
+    lay = hc.GpuLayer(cfg, max_seq_len=131072, lens=[131072 - 5])
+    lay.build()
+    out, dbg = lay.decode(cfg.keep_ratio, cfg.token_budget, stages=stages)
+    heads = [(0, 2), (0, 30)]
+    kvs = [(0, 0), (0, 7)]
+    ref = hc.oracle_index(lay, heads_kv=kvs)
+    hc.check_index(lay, ref, pairs=kvs, extrema_atol_scale=MFMA_EXTREMA_SCALE)
+    st = hc.check_decode(lay, out, dbg, cfg.keep_ratio, cfg.token_budget, heads=heads,
+                         ref_index=ref, stages=stages)
+    print(f"{stages}: max out rel err {st['max_out_rel']:.2e}")
+
+
+def test_fullsize_128k_dense_baseline():
+    """Full attention over the 128K layer (the dense baseline), sampled heads against fp64."""
+    torch = _torch()
+    from oracle import hhr_oracle as orc
+    cfg = synth.CONFIGS[3]
+    lay = hc.GpuLayer(cfg, max_seq_len=131072, lens=[131072 - 3])
+    dd = hb.DenseDecoder(lay.dims)
+    out = torch.full((1, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
+    dd(lay.cache, lay.q, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    d = lay.data
+    for h in (0, 11, 31):
+        g = h // cfg.group
+        ref = orc.dense_head(d["q"][0, h], d["K"][0, g], d["V"][0, g], 131072 - 3,
+                             orc.default_scale(128))
+        rel = np.abs(got[0, h] - ref).max() / np.abs(ref).max()
+        assert rel <= hc.OUT_RTOL, (h, rel)
