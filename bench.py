@@ -83,13 +83,14 @@ VARIANTS = {
 
 
 def dense_splits(cfg, lmax):
-    """Split count of the dense attention grid (the library's rule: whole sub-chunks of 4 waves x
-    rows-per-load x loads, about 1024 workgroups, at most 64 sub-chunks per workgroup)."""
+    """Split count of the dense attention grid (the library's rule: sub-chunks of 128 tokens for
+    bf16 K/V (4 waves x 32), of 4 waves x 2 rows x 4 (2 for G = 8) loads for fp32, about 1024
+    workgroups, an even number of 2..64 sub-chunks per workgroup)."""
     bf16 = cfg.dtype == "bf16"
-    rpi = 64 // (128 // (8 if bf16 else 4))
-    sub = 4 * rpi * (8 if cfg.group <= 4 else 4)
+    sub = 128 if bf16 else 4 * 2 * (4 if cfg.group <= 4 else 2)
     rows = lmax * cfg.batch * cfg.num_kv_heads
-    subs = min(64, max(1, -(-rows // (1024 * sub))))
+    subs = min(64, max(2, -(-rows // (1024 * sub))))
+    subs = (subs + 1) & ~1
     return -(-lmax // (subs * sub))
 
 

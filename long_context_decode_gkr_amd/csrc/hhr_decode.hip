@@ -812,23 +812,26 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
 }
 
 // Merge of the split partials of one (b, h): o = sum_s o_s 2^(m_s - M) / sum_s l_s 2^(m_s - M).
-// Partials are read in batches of 16, all loads of a batch issued before any use, and merged
-// without branches (an empty partial has m = -inf, l = 0 and gets weight 0).
-// The step's last kernel also commits an append: every earlier kernel of the step read
-// seq_lens[b] = t and worked on t + 1 tokens; the workgroup of head 0 now stores t + 1.
-__global__ void __launch_bounds__(kD)
+// NG groups of 128 threads (thread = output dimension) take every NG-th partial; each group
+// reads its partials in batches of 16, all loads of a batch issued before any use, merged
+// without branches (an empty partial has m = -inf, l = 0 and gets weight 0); the groups then
+// meet in LDS. The sparse step's last kernel also commits an append: every earlier kernel of
+// the step read seq_lens[b] = t and worked on t + 1 tokens; the workgroup of head 0 now stores
+// t + 1.
+template <int NG>
+__global__ void __launch_bounds__(kD * NG)
 combine_kernel(const float* __restrict__ part, int nsplit, float* __restrict__ out,
                int32_t* __restrict__ seq_lens, int Hq, int Lmax, int appended) {
   constexpr int CB = 16;
-  const int bh = blockIdx.x, d = threadIdx.x;
-  if (appended && d == 0 && bh % Hq == 0) {
+  const int bh = blockIdx.x, d = threadIdx.x % kD, grp = threadIdx.x / kD;
+  if (appended && threadIdx.x == 0 && bh % Hq == 0) {
     const int b = bh / Hq;
     const int t = seq_lens[b];
     if (t >= 0 && t < Lmax) seq_lens[b] = t + 1;
   }
   const float* pb = part + size_t(bh) * nsplit * (kD + 2);
   float Mx = -INFINITY, Ls = 0.f, Os = 0.f;
-  for (int i0 = 0; i0 < nsplit; i0 += CB) {
+  for (int i0 = grp * CB; i0 < nsplit; i0 += NG * CB) {
     float m[CB], l[CB], o[CB];
 #pragma unroll
     for (int u = 0; u < CB; ++u) {
@@ -853,6 +856,27 @@ combine_kernel(const float* __restrict__ part, int nsplit, float* __restrict__ o
       Os = fmaf(ok ? o[u] : 0.f, f, Os);
     }
     Mx = bm;
+  }
+  if constexpr (NG > 1) {
+    __shared__ float s_m[NG], s_l[NG], s_o[NG][kD];
+    s_o[grp][d] = Os;
+    if (d == 0) {
+      s_m[grp] = Mx;
+      s_l[grp] = Ls;
+    }
+    __syncthreads();
+    if (grp != 0) return;
+    float M = s_m[0];
+#pragma unroll
+    for (int i = 1; i < NG; ++i) M = fmaxf(M, s_m[i]);
+    Ls = 0.f;
+    Os = 0.f;
+#pragma unroll
+    for (int i = 0; i < NG; ++i) {
+      const float f = s_m[i] == -INFINITY ? 0.f : exp2f(s_m[i] - M);
+      Ls = fmaf(s_l[i], f, Ls);
+      Os = fmaf(s_o[i][d], f, Os);
+    }
   }
   out[size_t(bh) * kD + d] = (Ls > 0.f) ? Os / Ls : 0.f;
 }
@@ -971,8 +995,20 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
 
 hipError_t launch_combine(const Shape& s, const float* part, int nsplit, float* out,
                           int32_t* seq_lens, int appended, KernelTimer tm, hipStream_t st) {
-  launch_kernel(combine_kernel, dim3(s.B * s.Hq), dim3(kD), st, tm, part, nsplit, out, seq_lens,
-                s.Hq, s.Lmax, appended);
+  // one batch of 16 partials per group of 128 threads, up to 8 groups
+  const dim3 grid(s.B * s.Hq);
+  if (nsplit <= 16)
+    launch_kernel(combine_kernel<1>, grid, dim3(kD), st, tm, part, nsplit, out, seq_lens, s.Hq,
+                  s.Lmax, appended);
+  else if (nsplit <= 32)
+    launch_kernel(combine_kernel<2>, grid, dim3(2 * kD), st, tm, part, nsplit, out, seq_lens,
+                  s.Hq, s.Lmax, appended);
+  else if (nsplit <= 64)
+    launch_kernel(combine_kernel<4>, grid, dim3(4 * kD), st, tm, part, nsplit, out, seq_lens,
+                  s.Hq, s.Lmax, appended);
+  else
+    launch_kernel(combine_kernel<8>, grid, dim3(8 * kD), st, tm, part, nsplit, out, seq_lens,
+                  s.Hq, s.Lmax, appended);
   return hipGetLastError();
 }
 

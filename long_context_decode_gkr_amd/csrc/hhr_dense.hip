@@ -8,8 +8,9 @@
 // Split-K flash decoding with grouped-query sharing: workgroup (split, g, b) streams the K and V
 // rows of tokens [split T, split T + T) of KV head g ONCE and computes the partial (m, l, o) of
 // every one of the G query heads that read that KV head. Each wave keeps its own running
-// (m, l, o) over the sub-chunks it streams (online softmax, no barrier inside the loop); the
-// four waves meet in LDS at the end. The partials of a head are merged by the same kernel as
+// (m, l, o) over the sub-chunks it streams (online softmax, no barrier inside the loop), with
+// the next sub-chunk's loads in flight while one is consumed; the four waves meet in LDS at
+// the end. The partials of a head are merged by the same kernel as
 // the sparse step's.
 #include "hhr_device.h"
 #include "hhr_launch.h"
@@ -21,7 +22,7 @@ struct DenseShape {
   static constexpr int EPL = BF16 ? 8 : 4;          // elements per lane per row
   static constexpr int LPR = kD / EPL;              // lanes per row
   static constexpr int RPI = kWave / LPR;           // rows per wave-wide load
-  static constexpr int ITER = G <= 4 ? 8 : 4;       // loads per lane per sub-chunk (K and V)
+  static constexpr int ITER = G <= 4 ? 4 : 2;       // loads per lane per sub-chunk (K and V)
   static constexpr int RPW = RPI * ITER;            // rows per wave per sub-chunk
   static constexpr int SUB = 4 * RPW;               // rows per workgroup per sub-chunk
 };
@@ -72,17 +73,21 @@ dense_attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ 
   const size_t kvrow0 = (size_t(b) * s.Hkv + g) * s.Lmax;
   const char* Kc = static_cast<const char*>(K);
   const char* Vc = static_cast<const char*>(V);
-  for (int c0 = t0; c0 < t1; c0 += A::SUB) {
-    const int r0 = c0 + w * A::RPW + rg;          // this lane's first row of the sub-chunk
-    uint4 kr[ITER], vr[ITER];
+  // K and V of this lane's rows of the sub-chunk at c0 (rows past the range re-read the last
+  // one, so every load is in bounds and the loop carries no branch around its loads)
+  auto load = [&](int c0, uint4 (&kr)[ITER], uint4 (&vr)[ITER]) {
+    const int r0 = c0 + w * A::RPW + rg;
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
-      const int t = min(r0 + it * RPI, t1 - 1);   // rows past the range re-read the last one
+      const int t = max(min(r0 + it * RPI, t1 - 1), 0);
       const size_t off = ((kvrow0 + size_t(t)) * kD + sub * EPL) * esz;
       kr[it] = *reinterpret_cast<const uint4*>(Kc + off);
       vr[it] = *reinterpret_cast<const uint4*>(Vc + off);
     }
-    __builtin_amdgcn_sched_barrier(0);
+  };
+  // online softmax over one sub-chunk: logits, running maximum, rescale, weighted V sum
+  auto consume = [&](int c0, const uint4 (&kr)[ITER], const uint4 (&vr)[ITER]) {
+    const int r0 = c0 + w * A::RPW + rg;
     float sc[G][ITER];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) {
@@ -124,6 +129,16 @@ dense_attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ 
         for (int e = 0; e < EPL; ++e) o[hh][e] = fmaf(p, f[e], o[hh][e]);
       }
     }
+  };
+  // two register buffers: the next sub-chunk's loads are in flight while one is consumed
+  uint4 ka[ITER], va[ITER], kb[ITER], vb[ITER];
+  if (t0 < t1) load(t0, ka, va);
+  for (int c0 = t0; c0 < t1; c0 += 2 * A::SUB) {
+    load(c0 + A::SUB, kb, vb);
+    consume(c0, ka, va);
+    if (c0 + A::SUB >= t1) break;                // uniform
+    load(c0 + 2 * A::SUB, ka, va);
+    consume(c0 + A::SUB, kb, vb);
   }
 
   // ---- per wave: sum over the row groups (lanes sharing `sub`); then the four waves merge
@@ -166,16 +181,231 @@ dense_attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ 
   }
 }
 
-// Tokens per workgroup: whole sub-chunks, sized so that the grid holds about 1024 workgroups
-// (four per CU) when the context allows, and at most 64 sub-chunks.
+// ---------------------------------------------------------------------------------------------
+// bf16 K/V: the logits of the G heads are one small matrix product per 16 tokens on the matrix
+// cores, S[head][token] = Q K^T with v_mfma_f32_16x16x32_bf16 (Q padded to 16 rows with zeros;
+// bf16 x bf16 products are exact, fp32 accumulation). A fp32 query enters as two bf16 pieces
+// (hi + lo, relative remainder below 2^-16). The weighted V sum stays on the vector units in
+// the row layout (16 lanes x 8 dimensions per row), the probabilities handed over through LDS
+// inside the wave. Each wave streams 32 tokens per sub-chunk, two register buffers deep.
+// ---------------------------------------------------------------------------------------------
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+constexpr int kDenseTokW = 32;                      // tokens per wave per sub-chunk
+constexpr int kDenseSub = 4 * kDenseTokW;           // tokens per workgroup per sub-chunk
+
+template <int G, int QF32>
+__global__ void __launch_bounds__(256)
+dense_attn_mfma_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
+                       const void* __restrict__ q, const int32_t* __restrict__ seq_lens,
+                       float* __restrict__ part, int nsplit, int tpw, float scale_log2e) {
+  static_assert(G <= 8, "heads of a group fill rows 4 (l / 16) + i of the 16 x 16 tile");
+  const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int L = min(max(seq_lens[b], 0), s.Lmax);
+  const int w = wave_id(), lane = lane_id();
+  const int col = lane % 16, quad = lane / 16;      // MFMA: token column / k quarter
+  const int t0 = split * tpw, t1 = min(t0 + tpw, L);
+  const uint16_t* Kb = static_cast<const uint16_t*>(K);
+  const uint16_t* Vb = static_cast<const uint16_t*>(V);
+  const size_t kvrow0 = (size_t(b) * s.Hkv + g) * s.Lmax;
+
+  // A operand: Q rows = heads (col < G), k elements 32 quad + 8 ks + i of block ks (the same
+  // permutation of the 128 dimensions is used for K below, so the dot products are unchanged)
+  bf16x8_t qa[4], qb[4];
+  {
+    const bool hv = col < G;
+    const size_t qo = (size_t(b) * s.Hq + size_t(g) * G + (hv ? col : 0)) * kD + 32 * quad;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float x = 0.f;
+        if constexpr (QF32) x = static_cast<const float*>(q)[qo + 8 * ks + i];
+        else x = bf16_bits_to_f32(static_cast<const uint16_t*>(q)[qo + 8 * ks + i]);
+        x = hv ? x : 0.f;
+        const __bf16 hi = __bf16(x);
+        qa[ks][i] = hi;
+        qb[ks][i] = __bf16(x - float(hi));
+      }
+    }
+  }
+
+  // running state: M (per head, wave-uniform), l (per head, partial per MFMA lane), o (per
+  // head and the lane's 8 dimensions, partial over the lane's rows)
+  float M[G], lp[4], o[G][8];
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+    M[hh] = -INFINITY;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) o[hh][e] = 0.f;
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) lp[i] = 0.f;
+
+  __shared__ float s_p[4][kDenseTokW][8];           // probabilities [wave][token][head]
+  const int rg = lane / 16, sub = lane % 16;        // row layout for V: row group, 8 dims
+
+  // K: B operand of tile tt = token column col, elements 32 quad .. 32 quad + 31 (4 x 16 B);
+  // V: row layout, rows rg + 4 it. Rows past the range re-read the last valid one.
+  auto load = [&](int c0, uint4 (&kr)[2][4], uint4 (&vr)[8]) {
+    const int base = c0 + w * kDenseTokW;
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int t = max(min(base + 16 * tt + col, t1 - 1), 0);
+      const uint4* kp = reinterpret_cast<const uint4*>(Kb + (kvrow0 + size_t(t)) * kD + 32 * quad);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) kr[tt][j] = kp[j];
+    }
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      const int t = max(min(base + rg + 4 * it, t1 - 1), 0);
+      vr[it] = *reinterpret_cast<const uint4*>(Vb + (kvrow0 + size_t(t)) * kD + 8 * sub);
+    }
+  };
+  auto consume = [&](int c0, const uint4 (&kr)[2][4], const uint4 (&vr)[8]) {
+    const int base = c0 + w * kDenseTokW;
+    // logits S[head 4 quad + i][token 16 tt + col], scaled into the log2 domain
+    f32x4_t sc[2];
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[ks], __builtin_bit_cast(bf16x8_t, kr[tt][ks]),
+                                                      acc, 0, 0, 0);
+      if constexpr (QF32) {
+#pragma unroll
+        for (int ks = 0; ks < 4; ++ks)
+          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qb[ks], __builtin_bit_cast(bf16x8_t, kr[tt][ks]),
+                                                        acc, 0, 0, 0);
+      }
+      const bool ok = base + 16 * tt + col < t1;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) sc[tt][i] = ok ? acc[i] * scale_log2e : -INFINITY;
+    }
+    // per-head maximum of the sub-chunk (over the 16 columns of the head's row of lanes)
+    float mx[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      float m = fmaxf(sc[0][i], sc[1][i]);
+#pragma unroll
+      for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      mx[i] = m;
+    }
+    float f0[G];
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh) {
+      const float m = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(mx[hh % 4]), 16 * (hh / 4)));
+      const float Mn = fmaxf(M[hh], m);            // -inf while this wave has seen no live row
+      f0[hh] = M[hh] == -INFINITY ? 0.f : exp2f(M[hh] - Mn);
+      M[hh] = Mn;
+    }
+    // probabilities into LDS (lanes of valid heads), l partials; o rescaled
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int hh = 4 * quad + i;
+      float Mh = M[0], fh = f0[0];
+#pragma unroll
+      for (int h2 = 1; h2 < G; ++h2) {
+        Mh = hh == h2 ? M[h2] : Mh;
+        fh = hh == h2 ? f0[h2] : fh;
+      }
+      const float p0 = sc[0][i] == -INFINITY ? 0.f : exp2f(sc[0][i] - Mh);
+      const float p1 = sc[1][i] == -INFINITY ? 0.f : exp2f(sc[1][i] - Mh);
+      lp[i] = fmaf(lp[i], fh, p0 + p1);
+      if (hh < G) {
+        s_p[w][col][hh] = p0;
+        s_p[w][16 + col][hh] = p1;
+      }
+    }
+#pragma unroll
+    for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hh][e] *= f0[hh];
+    asm volatile("" ::: "memory");   // LDS writes of this wave before its reads (in order)
+#pragma unroll
+    for (int it = 0; it < 8; ++it) {
+      float pv[8];
+      const float4 pa = *reinterpret_cast<const float4*>(&s_p[w][rg + 4 * it][0]);
+      pv[0] = pa.x; pv[1] = pa.y; pv[2] = pa.z; pv[3] = pa.w;
+      if constexpr (G > 4) {
+        const float4 pb = *reinterpret_cast<const float4*>(&s_p[w][rg + 4 * it][4]);
+        pv[4] = pb.x; pv[5] = pb.y; pv[6] = pb.z; pv[7] = pb.w;
+      }
+      float f[8];
+      unpack_row(vr[it], f);
+#pragma unroll
+      for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[hh][e] = fmaf(pv[hh], f[e], o[hh][e]);
+    }
+    asm volatile("" ::: "memory");
+  };
+
+  uint4 ka[2][4], va[8], kb[2][4], vb[8];
+  if (t0 < t1) load(t0, ka, va);
+  for (int c0 = t0; c0 < t1; c0 += 2 * kDenseSub) {
+    load(c0 + kDenseSub, kb, vb);
+    consume(c0, ka, va);
+    if (c0 + kDenseSub >= t1) break;                // uniform
+    load(c0 + 2 * kDenseSub, ka, va);
+    consume(c0 + kDenseSub, kb, vb);
+  }
+
+  // ---- per wave: o over the row groups, l over the 16 token columns; then the waves merge
+  __shared__ float s_m[4][G], s_l[4][G];
+  __shared__ float s_o[4][G][kD];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    float v = lp[i];
+#pragma unroll
+    for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    const int hh = 4 * quad + i;
+    if (col == 0 && hh < G) s_l[w][hh] = v;
+  }
+#pragma unroll
+  for (int hh = 0; hh < G; ++hh) {
+#pragma unroll
+    for (int off = 16; off < kWave; off <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[hh][e] += __shfl_xor(o[hh][e], off);
+    if (rg == 0) {
+#pragma unroll
+      for (int e = 0; e < 8; ++e) s_o[w][hh][sub * 8 + e] = o[hh][e];
+    }
+    if (lane == 0) s_m[w][hh] = M[hh];
+  }
+  __syncthreads();
+  for (int i = threadIdx.x; i < G * kD; i += blockDim.x) {
+    const int hh = i / kD, d = i % kD;
+    const float Mw = fmaxf(fmaxf(s_m[0][hh], s_m[1][hh]), fmaxf(s_m[2][hh], s_m[3][hh]));
+    float os = 0.f, ls = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < 4; ++ww) {
+      const float f = s_m[ww][hh] == -INFINITY ? 0.f : exp2f(s_m[ww][hh] - Mw);
+      os = fmaf(s_o[ww][hh][d], f, os);
+      ls = fmaf(s_l[ww][hh], f, ls);
+    }
+    float* pp = part + ((size_t(b) * s.Hq + size_t(g) * G + hh) * nsplit + split) * (kD + 2);
+    pp[d] = os;
+    if (d == 0) {
+      pp[kD] = Mw;
+      pp[kD + 1] = ls;
+    }
+  }
+}
+
+// Tokens per workgroup: whole pairs of sub-chunks, sized so that the grid holds about 1024
+// workgroups (four per CU) when the context allows, and at most 64 sub-chunks.
 template <int BF16, int G>
 static int dense_tpw(const Shape& s) {
-  constexpr int SUB = DenseShape<BF16, G>::SUB;
+  constexpr int SUB = BF16 ? kDenseSub : DenseShape<BF16, G>::SUB;
   const long long rows = (long long)s.Lmax * s.B * s.Hkv;
   long long subs = (rows + 1024LL * SUB - 1) / (1024LL * SUB);
-  if (subs < 1) subs = 1;
+  if (subs < 2) subs = 2;
   if (subs > 64) subs = 64;
-  return int(subs) * SUB;
+  return int((subs + 1) & ~1LL) * SUB;   // pairs of sub-chunks (two register buffers)
 }
 
 int dense_tokens_per_split(const Shape& s) {
@@ -195,8 +425,18 @@ template <int BF16, int G>
 static void launch_dense_t(const Shape& s, const CacheView& c, const void* q, float* part,
                            int nsplit, int tpw, float scale_log2e, KernelTimer tm,
                            hipStream_t st) {
-  launch_kernel(dense_attn_kernel<BF16, G>, dim3(nsplit, s.Hkv, s.B), dim3(256), st, tm, s,
-                c.K, c.V, q, c.seq_lens, part, nsplit, tpw, scale_log2e);
+  const dim3 grid(nsplit, s.Hkv, s.B);
+  if constexpr (BF16) {
+    if (s.q_bf16)
+      launch_kernel(dense_attn_mfma_kernel<G, 0>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                    c.seq_lens, part, nsplit, tpw, scale_log2e);
+    else
+      launch_kernel(dense_attn_mfma_kernel<G, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                    c.seq_lens, part, nsplit, tpw, scale_log2e);
+  } else {
+    launch_kernel(dense_attn_kernel<BF16, G>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                  c.seq_lens, part, nsplit, tpw, scale_log2e);
+  }
 }
 
 hipError_t launch_dense(const Shape& s, const CacheView& c, const void* q, float scale,

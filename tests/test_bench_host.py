@@ -79,7 +79,7 @@ def test_byte_model_of_the_variants():
 
 
 def test_dense_split_rule():
-    # 128K x 8 KV heads in sub-chunks of 128 rows: 8 sub-chunks per workgroup, 128 splits
+    # 128K x 8 KV heads in sub-chunks of 128 tokens: 8 sub-chunks per workgroup, 128 splits
     assert bench.dense_splits(synth.CONFIGS[3], 131072) == 128
     assert bench.dense_splits(synth.CONFIGS[1], 4096) >= 1
 

@@ -439,3 +439,25 @@ def test_dense_decode_matches_textbook_attention(cfg_id, L, batch, lens):
                                  orc.default_scale(128))
             rel = np.abs(got[b, h] - ref).max() / np.abs(ref).max()
             assert rel <= hc.OUT_RTOL, (b, h, rel)
+
+
+def test_dense_decode_fp32_query_on_bf16_cache():
+    """A fp32 query (not bf16-representable) against bf16 K/V: the matrix-core logits take the
+    query as two bf16 pieces."""
+    torch = _torch()
+    cfg = _cfg(2, 3000, n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=3072)
+    dims = hb.make_dims(1, 32, 8, 16, 128, lay.data["max_seq_len"], kv_dtype=hb.HHR_BF16,
+                        q_dtype=hb.HHR_F32)
+    qf = np.random.default_rng(5).standard_normal((1, 32, 128)).astype(np.float32)
+    dd = hb.DenseDecoder(dims)
+    out = torch.full((1, 32, 128), float("nan"), dtype=torch.float32, device="cuda")
+    dd(lay.cache, torch.from_numpy(qf).cuda(), out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    d = lay.data
+    for h in range(32):
+        ref = orc.dense_head(qf[0, h], d["K"][0, h // 4], d["V"][0, h // 4], 3000,
+                             orc.default_scale(128))
+        rel = np.abs(got[0, h] - ref).max() / np.abs(ref).max()
+        assert rel <= hc.OUT_RTOL, (h, rel)
