@@ -27,8 +27,9 @@ speedup_vs_dense).
 
 --variant times another configuration of the same workload: the coarse stage alone (pages:
 every token of the kept pages is attended), the fine stage alone (codes: Hamming top-k over
-every token), the method with R = I (identity-r: the plain per-channel min/max bound), or the
-dense baseline itself (dense).
+every token), the method with R = I (identity-r: the plain per-channel min/max bound), the
+method with the page extrema stored as bf16 rounded outward (bf16-extrema: half the bytes of the
+page-bound stream), or the dense baseline itself (dense).
 
 Prints ONE JSON line. Options: --gpus (must be 1), --steps, --warmup, --workload, --variant,
 --layers, --no-cpu-baseline, --no-builder, --no-dense, --quiet, --copy-calibration (a 512 MiB
@@ -77,6 +78,8 @@ VARIANTS = {
     "identity-r": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3),
                    ("combine", 4)),
     "pages": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3), ("combine", 4)),
+    "bf16-extrema": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3),
+                     ("combine", 4)),
     "codes": (("prep", 0), ("select", 2), ("sparse_attn", 3), ("combine", 4)),
     "dense": (("dense_attn", 0), ("combine", 1)),
 }
@@ -124,15 +127,16 @@ def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
     out = {"prep": B * Hq * d * esz + Hkv * d * d * 4 + Hkv * d * nb * 4 + B * Hq * d * 4
                    + B * Hq * nb // 8,
            "page_bound": B * Hq * d * 4, "select": 0, "sparse_attn": 0, "combine": 0}
+    ex = 2 if variant == "bf16-extrema" else 4    # bytes per stored extremum
     if append:
-        out["prep"] += B * Hkv * (2 * d * esz + 2 * d * esz + nb // 8 + 2 * d * 4 * 2)
+        out["prep"] += B * Hkv * (2 * d * esz + 2 * d * esz + nb // 8 + 2 * d * ex * 2)
     for L in lens:
         P = -(-L // S)
         n_keep = P if variant == "codes" else min(P, max(1, math.ceil(cfg.keep_ratio * P)))
         ncand = min(n_keep * S, L)
         k = ncand if variant == "pages" else min(cfg.token_budget, ncand)
         parts = Hq * -(-k // 256) * (d + 2) * 4
-        out["page_bound"] += Hkv * P * d * 8 + Hq * P * 4
+        out["page_bound"] += Hkv * P * d * 2 * ex + Hq * P * 4
         if variant == "pages":
             out["select"] += Hq * (P * 4 + k * 4)
         elif variant == "codes":
@@ -270,7 +274,8 @@ def main():
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD)
     ap.add_argument("--variant", choices=sorted(VARIANTS), default="hhr",
                     help="hhr: the method; pages / codes: coarse or fine stage alone; "
-                         "identity-r: R = I; dense: full attention over every token")
+                         "identity-r: R = I; bf16-extrema: page extrema stored as bf16 "
+                         "rounded outward; dense: full attention over every token")
     ap.add_argument("--layers", type=int, default=None,
                     help="layer instances cycled (default: per workload, 8 or 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -319,7 +324,8 @@ def main():
     data = synth.make_layer(cfg, max_seq_len=Lcap, lens=lens0)
     log(f"  {time.time() - t0:.1f} s", q)
     kvt = hb.HHR_BF16 if cfg.dtype == "bf16" else hb.HHR_F32
-    dims = hb.make_dims(B, Hq, Hkv, S, nb, int(data["max_seq_len"]), kv_dtype=kvt)
+    dims = hb.make_dims(B, Hq, Hkv, S, nb, int(data["max_seq_len"]), kv_dtype=kvt,
+                        summary_dtype=hb.HHR_BF16 if variant == "bf16-extrema" else hb.HHR_F32)
     dev = torch.device("cuda")
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     qd = torch.from_numpy(data["q"]).to(dev).to(tdt)

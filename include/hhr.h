@@ -29,9 +29,12 @@
  *
  * Layouts (row-major, innermost last; Pmax = max_seq_len / page_size, nw = hash_bits / 32)
  *   K, V       [B][Hkv][max_seq_len][128]   kv_dtype
- *   page_min   [B][Hkv][128][Pmax]          fp32, channel-major ("SoA"): entry [b][g][j][p] is
- *   page_max   [B][Hkv][128][Pmax]          the min / max over the page's valid tokens of
- *                                            dimension j of the rotated key k~ = k R_g
+ *   page_min   [B][Hkv][128][Pmax]          summary_dtype, channel-major ("SoA"): entry
+ *   page_max   [B][Hkv][128][Pmax]          [b][g][j][p] is the min / max over the page's
+ *                                            valid tokens of dimension j of the rotated key
+ *                                            k~ = k R_g (fp32 values of the fp32-rounded k~; as
+ *                                            bf16, the min rounded toward -inf and the max
+ *                                            toward +inf, so Eq. 3 stays an upper bound)
  *   codes      [B][Hkv][max_seq_len][nw]    uint32; bit c of a key's code sits in word c / 32
  *                                            at bit position c % 32; bit c = 1 iff the exact
  *                                            real value of (k W_g)_c is > 0
@@ -67,7 +70,8 @@ typedef enum { HHR_F32 = 0, HHR_BF16 = 1 } hhr_dtype;
 
 /* Shapes. Supported: head_dim = 128; num_q_heads = G * num_kv_heads with G in {1, 2, 4, 8};
  * page_size in {16, 32}; hash_bits in {128, 256}; max_seq_len a multiple of 4 * page_size with
- * max_seq_len / page_size <= HHR_MAX_PAGES; kv_dtype and q_dtype in {HHR_F32, HHR_BF16}. */
+ * max_seq_len / page_size <= HHR_MAX_PAGES; kv_dtype, q_dtype and summary_dtype in {HHR_F32,
+ * HHR_BF16}. */
 typedef struct {
   int32_t batch;
   int32_t num_q_heads;
@@ -78,6 +82,8 @@ typedef struct {
   int32_t max_seq_len;
   int32_t kv_dtype;     /* hhr_dtype of K and V (and k_new, v_new) */
   int32_t q_dtype;      /* hhr_dtype of q */
+  int32_t summary_dtype;  /* hhr_dtype of page_min / page_max: HHR_F32, or HHR_BF16 rounded
+                             outward (half the bytes the page-bound kernel streams) */
 } hhr_dims;
 
 #define HHR_MAX_PAGES 16384

@@ -32,7 +32,7 @@ class Dims(ctypes.Structure):
                 ("num_kv_heads", ctypes.c_int32), ("head_dim", ctypes.c_int32),
                 ("page_size", ctypes.c_int32), ("hash_bits", ctypes.c_int32),
                 ("max_seq_len", ctypes.c_int32), ("kv_dtype", ctypes.c_int32),
-                ("q_dtype", ctypes.c_int32)]
+                ("q_dtype", ctypes.c_int32), ("summary_dtype", ctypes.c_int32)]
 
 
 class Params(ctypes.Structure):
@@ -158,9 +158,9 @@ def _ptr(t) -> Optional[int]:
 
 
 def make_dims(batch, num_q_heads, num_kv_heads, page_size, hash_bits, max_seq_len,
-              kv_dtype=HHR_BF16, q_dtype=None, head_dim=128) -> Dims:
+              kv_dtype=HHR_BF16, q_dtype=None, head_dim=128, summary_dtype=HHR_F32) -> Dims:
     return Dims(batch, num_q_heads, num_kv_heads, head_dim, page_size, hash_bits, max_seq_len,
-                kv_dtype, kv_dtype if q_dtype is None else q_dtype)
+                kv_dtype, kv_dtype if q_dtype is None else q_dtype, summary_dtype)
 
 
 class Cache:
@@ -174,8 +174,9 @@ class Cache:
         kvt = torch.bfloat16 if dims.kv_dtype == HHR_BF16 else torch.float32
         self.K = torch.zeros((B, Hkv, L, d), dtype=kvt, device=device)
         self.V = torch.zeros((B, Hkv, L, d), dtype=kvt, device=device)
-        self.page_min = torch.zeros((B, Hkv, d, P), dtype=torch.float32, device=device)
-        self.page_max = torch.zeros((B, Hkv, d, P), dtype=torch.float32, device=device)
+        st = torch.bfloat16 if dims.summary_dtype == HHR_BF16 else torch.float32
+        self.page_min = torch.zeros((B, Hkv, d, P), dtype=st, device=device)
+        self.page_max = torch.zeros((B, Hkv, d, P), dtype=st, device=device)
         self.codes = torch.zeros((B, Hkv, L, dims.hash_bits // 32), dtype=torch.int32, device=device)
         self.seq_lens = torch.zeros((B,), dtype=torch.int32, device=device)
         self.append_ticket = torch.zeros((B,), dtype=torch.int32, device=device)

@@ -20,7 +20,8 @@ hhr_status check_dims(const hhr_dims* d, Shape* s) {
   if (d->batch <= 0 || d->num_q_heads <= 0 || d->num_kv_heads <= 0 || d->head_dim <= 0 ||
       d->page_size <= 0 || d->hash_bits <= 0 || d->max_seq_len <= 0)
     return HHR_ERR_INVALID_ARG;
-  if (!dtype_ok(d->kv_dtype) || !dtype_ok(d->q_dtype)) return HHR_ERR_INVALID_ARG;
+  if (!dtype_ok(d->kv_dtype) || !dtype_ok(d->q_dtype) || !dtype_ok(d->summary_dtype))
+    return HHR_ERR_INVALID_ARG;
   if (d->num_q_heads % d->num_kv_heads != 0) return HHR_ERR_INVALID_ARG;
   const int G = d->num_q_heads / d->num_kv_heads;
   if (G != 1 && G != 2 && G != 4 && G != 8) return HHR_ERR_UNSUPPORTED;
@@ -43,6 +44,7 @@ hhr_status check_dims(const hhr_dims* d, Shape* s) {
   s->Pmax = d->max_seq_len / d->page_size;
   s->kv_bf16 = d->kv_dtype == HHR_BF16;
   s->q_bf16 = d->q_dtype == HHR_BF16;
+  s->sum_bf16 = d->summary_dtype == HHR_BF16;
   return HHR_OK;
 }
 

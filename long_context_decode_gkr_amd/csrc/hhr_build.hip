@@ -70,8 +70,7 @@ build_fp64_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
           }
         }
         const int p = (t0 + pp * S) / S;
-        c.pmin[sidx + p] = lo;
-        c.pmax[sidx + p] = hi;
+        store_extrema(s, c, sidx + p, lo, hi);
       }
     }
   } else {
@@ -210,8 +209,8 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   const bool app = has_k && t >= 0 && t < s.Lmax;
   const int p = app ? t / s.S : 0;
   const size_t si = ((size_t(b) * s.Hkv + g) * kD + (rot ? j : sl * 32)) * s.Pmax + p;
-  const float omin = c.pmin[si];
-  const float omax = c.pmax[si];
+  const float omin = load_pmin(s, c, si);
+  const float omax = load_pmax(s, c, si);
 
   const size_t row = (size_t(b) * s.Hkv + g) * s.Lmax + (app ? t : 0);
   if (tid < kD && has_k) {
@@ -253,8 +252,9 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
       if (app) {
         const float kt = float(acc[0]);
         const bool first = t % s.S == 0;        // the key opens page p
-        c.pmin[si] = first ? kt : fminf(omin, kt);
-        c.pmax[si] = first ? kt : fmaxf(omax, kt);
+        // (a stored bf16 extremum is already rounded outward, so rounding the fp32 min / max
+        // of it and k~ outward equals folding the rounded k~ into it)
+        store_extrema(s, c, si, first ? kt : fminf(omin, kt), first ? kt : fmaxf(omax, kt));
       }
 #pragma unroll
       for (int v = 1; v < kMaxVec; ++v) {

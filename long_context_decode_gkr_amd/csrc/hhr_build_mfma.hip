@@ -222,8 +222,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
     const size_t sbase = (size_t(b) * s.Hkv + g) * kD;
     for (int e = tid; e < kD * npg; e += kMThreads) {
       const int j = e / npg, pl = e % npg;
-      c.pmin[(sbase + j) * s.Pmax + pg0 + pl] = stage_f[0][j][pl];
-      c.pmax[(sbase + j) * s.Pmax + pg0 + pl] = stage_f[1][j][pl];
+      store_extrema(s, c, (sbase + j) * s.Pmax + pg0 + pl, stage_f[0][j][pl], stage_f[1][j][pl]);
     }
   } else {
     // ---- exact path for the queued bits, then the code words. If more bits were uncertain

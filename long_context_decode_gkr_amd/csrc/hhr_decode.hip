@@ -47,7 +47,7 @@ struct BoundArgs {
   int appended;           // a token is appended in this step (seq_lens is advanced at its end)
 };
 
-template <int G>
+template <int G, int SB>   // SB: extrema stored as bf16
 __global__ void __launch_bounds__(kBoundThreads)
 page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) {
   const int b = blockIdx.z, g = blockIdx.y, p0 = blockIdx.x * kBoundPages;
@@ -65,8 +65,21 @@ page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) 
   float4 lo[16], hi[16];
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) {
-    lo[jj] = *reinterpret_cast<const float4*>(c.pmin + (srow + jj) * s.Pmax + plc);
-    hi[jj] = *reinterpret_cast<const float4*>(c.pmax + (srow + jj) * s.Pmax + plc);
+    if constexpr (SB) {
+      const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(c.pmin) +
+                                                      (srow + jj) * s.Pmax + plc);
+      const uint2 y = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(c.pmax) +
+                                                      (srow + jj) * s.Pmax + plc);
+      lo[jj] = make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u),
+                           __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xFFFF0000u));
+      hi[jj] = make_float4(__uint_as_float(y.x << 16), __uint_as_float(y.x & 0xFFFF0000u),
+                           __uint_as_float(y.y << 16), __uint_as_float(y.y & 0xFFFF0000u));
+    } else {
+      lo[jj] = *reinterpret_cast<const float4*>(static_cast<const float*>(c.pmin) +
+                                                (srow + jj) * s.Pmax + plc);
+      hi[jj] = *reinterpret_cast<const float4*>(static_cast<const float*>(c.pmax) +
+                                                (srow + jj) * s.Pmax + plc);
+    }
   }
   const float* qb = a.qrot + (size_t(b) * s.Hq + size_t(g) * G) * kD + j0;
 
@@ -919,8 +932,12 @@ template <int G>
 static void launch_bound_t(const Shape& s, const CacheView& c, const BoundArgs& a,
                            const DebugView& dbg, hipStream_t st) {
   dim3 grid((s.Pmax + kBoundPages - 1) / kBoundPages, s.Hkv, s.B);
-  launch_kernel(page_bound_kernel<G>, grid, dim3(kBoundThreads), st, kernel_timer(dbg, 1), s, c,
-                a, dbg.bounds);
+  if (s.sum_bf16)
+    launch_kernel(page_bound_kernel<G, 1>, grid, dim3(kBoundThreads), st, kernel_timer(dbg, 1),
+                  s, c, a, dbg.bounds);
+  else
+    launch_kernel(page_bound_kernel<G, 0>, grid, dim3(kBoundThreads), st, kernel_timer(dbg, 1),
+                  s, c, a, dbg.bounds);
 }
 
 template <int NB, int EPT, int NT>

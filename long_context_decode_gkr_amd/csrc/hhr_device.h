@@ -6,6 +6,8 @@
 
 #include <type_traits>
 
+#include "hhr_launch.h"
+
 namespace hhr {
 
 constexpr int kD = 128;         // head dimension
@@ -15,6 +17,40 @@ constexpr int kWave = 64;
 // Element loads: K, V, q are fp32 or bf16; everything is computed in fp32 / fp64.
 // ---------------------------------------------------------------------------------------------
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+// bf16 rounded toward -inf / +inf (bits). A page minimum stored rounded down and a maximum
+// stored rounded up keep max(q l, q u) >= the exact value, so the page bound stays an upper
+// bound. The fp32 value truncated to its top 16 bits is rounded toward zero; an inexact value
+// on the wrong side of zero takes one more bf16 step away from zero.
+__device__ __forceinline__ uint32_t bf16_round_down(float x) {
+  const uint32_t u = __float_as_uint(x), t = u & 0xFFFF0000u;
+  return (t != u && x < 0.f ? t + 0x10000u : t) >> 16;
+}
+__device__ __forceinline__ uint32_t bf16_round_up(float x) {
+  const uint32_t u = __float_as_uint(x), t = u & 0xFFFF0000u;
+  return (t != u && x > 0.f ? t + 0x10000u : t) >> 16;
+}
+
+// Page extrema element i of the cache: read as fp32; written from fp32 values (as bf16 rounded
+// outward when the cache stores bf16 extrema).
+__device__ __forceinline__ float load_pmin(const Shape& s, const CacheView& c, size_t i) {
+  return s.sum_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(c.pmin)[i])
+                    : static_cast<const float*>(c.pmin)[i];
+}
+__device__ __forceinline__ float load_pmax(const Shape& s, const CacheView& c, size_t i) {
+  return s.sum_bf16 ? bf16_bits_to_f32(static_cast<const uint16_t*>(c.pmax)[i])
+                    : static_cast<const float*>(c.pmax)[i];
+}
+__device__ __forceinline__ void store_extrema(const Shape& s, const CacheView& c, size_t i,
+                                              float lo, float hi) {
+  if (s.sum_bf16) {
+    static_cast<uint16_t*>(c.pmin)[i] = uint16_t(bf16_round_down(lo));
+    static_cast<uint16_t*>(c.pmax)[i] = uint16_t(bf16_round_up(hi));
+  } else {
+    static_cast<float*>(c.pmin)[i] = lo;
+    static_cast<float*>(c.pmax)[i] = hi;
+  }
+}
 
 // Raw 16- or 32-bit element load; convert with raw_to_f32 after the other loads are issued so
 // that the conversion's wait does not sit in front of them.

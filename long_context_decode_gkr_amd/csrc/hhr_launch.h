@@ -11,13 +11,14 @@ namespace hhr {
 struct Shape {
   int B, Hq, Hkv, G, S, NB, NW, Lmax, Pmax;
   int kv_bf16, q_bf16;
+  int sum_bf16;       // page extrema stored as bf16 rounded outward (else fp32)
 };
 
 struct CacheView {
   void* K;
   void* V;
-  float* pmin;
-  float* pmax;
+  void* pmin;         // fp32 or (sum_bf16) bf16 bits, [B][Hkv][128][Pmax]
+  void* pmax;
   uint32_t* codes;
   int32_t* seq_lens;
   int32_t* ticket;

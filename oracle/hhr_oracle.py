@@ -69,6 +69,25 @@ def page_extrema(kt: np.ndarray, L: int, S: int):
     return lo, hi
 
 
+def _bf16_neighbours(x: np.ndarray):
+    """The bf16 values just below and just above each fp32 x (equal when x is one): bf16 has
+    fp32's exponent range and 8 significant bits, so near x its spacing is 2^(e - 7) with
+    e = floor(log2 |x|) (at least -126, the subnormal spacing below that)."""
+    x64 = np.asarray(x, np.float32).astype(np.float64)
+    e = np.frexp(x64)[1].astype(np.float64) - 1.0      # |x| in [2^e, 2^(e+1)); x = 0 gives -1
+    ulp = np.exp2(np.maximum(e, -126.0) - 7.0)
+    down = np.floor(x64 / ulp) * ulp
+    up = np.ceil(x64 / ulp) * ulp
+    return down, up
+
+
+def extrema_bf16(lo: np.ndarray, hi: np.ndarray):
+    """Page extrema stored as bf16 (returned as fp32 values): the minimum rounded toward -inf and
+    the maximum toward +inf, so max(q l, q u) over the stored values is never below its value
+    over the exact ones and Eq. (3) remains an upper bound."""
+    return (_bf16_neighbours(lo)[0].astype(np.float32), _bf16_neighbours(hi)[1].astype(np.float32))
+
+
 # ----------------------------------------------------------------------------------------------
 # §3.1 Eq. (1), §3.3.2 Eq. (10): sign codes
 # ----------------------------------------------------------------------------------------------
@@ -179,10 +198,14 @@ def default_scale(d: int) -> float:
 # ----------------------------------------------------------------------------------------------
 # Index build and append (one sequence, one KV head)
 # ----------------------------------------------------------------------------------------------
-def build_head(K: np.ndarray, L: int, R: np.ndarray, W: np.ndarray, S: int):
-    """Page extrema of the rotated keys and the key codes for rows [0, L) of K."""
+def build_head(K: np.ndarray, L: int, R: np.ndarray, W: np.ndarray, S: int,
+               summary: str = "f32"):
+    """Page extrema of the rotated keys and the key codes for rows [0, L) of K; with
+    summary="bf16" the extrema are the outward-rounded bf16 values."""
     kt = rotate(K[:L], R)
     lo, hi = page_extrema(kt, L, S)
+    if summary == "bf16":
+        lo, hi = extrema_bf16(lo, hi)
     return lo, hi, codes(K[:L], W)
 
 
@@ -190,7 +213,8 @@ def append_head(state: dict, k_new: np.ndarray, v_new: np.ndarray, R: np.ndarray
                 W: np.ndarray, S: int) -> None:
     """Write token t = L, extend (or open) page t // S, write its code, then L += 1.
 
-    state: dict with K, V [Lmax, d], lo, hi [Pmax, d], codes [Lmax, nw], L.
+    state: dict with K, V [Lmax, d], lo, hi [Pmax, d], codes [Lmax, nw], L, and optionally
+    summary ("f32" or "bf16": the stored extrema rounded outward).
     """
     t = int(state["L"])
     state["K"][t] = k_new
@@ -198,11 +222,14 @@ def append_head(state: dict, k_new: np.ndarray, v_new: np.ndarray, R: np.ndarray
     kt = rotate(np.asarray(k_new)[None, :], R)[0]
     p = t // S
     if t % S == 0:
-        state["lo"][p] = kt
-        state["hi"][p] = kt
+        lo, hi = kt, kt
     else:
-        state["lo"][p] = np.minimum(state["lo"][p], kt)
-        state["hi"][p] = np.maximum(state["hi"][p], kt)
+        lo = np.minimum(state["lo"][p], kt)
+        hi = np.maximum(state["hi"][p], kt)
+    if state.get("summary", "f32") == "bf16":
+        lo, hi = extrema_bf16(lo, hi)
+    state["lo"][p] = lo
+    state["hi"][p] = hi
     state["codes"][t] = codes(np.asarray(k_new)[None, :], W)[0]
     state["L"] = t + 1
 
@@ -260,7 +287,8 @@ def dense_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, L: int, scale: float
 # ----------------------------------------------------------------------------------------------
 # Whole layer (natural layouts: K, V [B][Hkv][Lmax][d], q [B][Hq][d])
 # ----------------------------------------------------------------------------------------------
-def build_layer(K: np.ndarray, seq_lens, R: np.ndarray, W: np.ndarray, S: int) -> dict:
+def build_layer(K: np.ndarray, seq_lens, R: np.ndarray, W: np.ndarray, S: int,
+                summary: str = "f32") -> dict:
     B, Hkv, Lmax, d = K.shape
     nb = W.shape[2]
     Pmax = num_pages(Lmax, S)
@@ -270,7 +298,7 @@ def build_layer(K: np.ndarray, seq_lens, R: np.ndarray, W: np.ndarray, S: int) -
     for b in range(B):
         L = int(seq_lens[b])
         for g in range(Hkv):
-            l_, h_, c_ = build_head(K[b, g], L, R[g], W[g], S)
+            l_, h_, c_ = build_head(K[b, g], L, R[g], W[g], S, summary)
             P = l_.shape[0]
             lo[b, g, :P] = l_
             hi[b, g, :P] = h_

@@ -174,3 +174,11 @@ def test_dense_decode_validation():
     assert dense_status(scale=float("nan")) == 1
     assert dense_status(ws_bytes=need - 1) == 4
     assert dense_status(ws=FAKE * 256 + 4, ws_bytes=need) == 4
+
+
+@pytest.mark.parametrize("value", [-1, 2, 9])
+def test_invalid_summary_dtype(value):
+    d = good_dims()
+    d.summary_dtype = value
+    assert decode_status(dims=d) == 1
+    assert hb.hhr_dense_workspace_bytes(d) == 0

@@ -461,3 +461,54 @@ def test_dense_decode_fp32_query_on_bf16_cache():
                              orc.default_scale(128))
         rel = np.abs(got[0, h] - ref).max() / np.abs(ref).max()
         assert rel <= hc.OUT_RTOL, (h, rel)
+
+
+# ---------------------------------------------------------------------------------------------
+# Compressed page summaries: bf16 extrema rounded outward
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("method", ["fp64", "auto"])
+@pytest.mark.parametrize("cfg_id,L,batch", [(2, 3001, None), (5, 2085, 2), (1, 1111, None)])
+def test_bf16_extrema_build_and_decode(method, cfg_id, L, batch):
+    _torch()
+    cfg = _cfg(cfg_id, L, batch=batch, n_plant=8)
+    lay = hc.GpuLayer(cfg, max_seq_len=L + 64, summary="bf16")
+    lay.build(method=method)
+    ref = hc.oracle_index(lay)
+    hc.check_index(lay, ref, extrema_atol_scale=20.0 if method == "auto" else 1.0)
+    if method == "fp64":   # the fp64 build rounds the oracle's own fp32 values: identical
+        got = lay.index_host()
+        for b in range(cfg.batch):
+            P = -(-int(lay.data["seq_lens"][b]) // cfg.page_size)
+            assert np.array_equal(got["lo"][b, :, :P], ref["lo"][b, :, :P])
+            assert np.array_equal(got["hi"][b, :, :P], ref["hi"][b, :, :P])
+    rho = cfg.keep_ratio
+    out, dbg = lay.decode(rho, 200)
+    hc.check_decode(lay, out, dbg, rho, 200, ref_index=ref)
+
+
+def test_bf16_extrema_append_decode_equals_rebuild():
+    torch = _torch()
+    base = synth.CONFIGS[3]
+    L0, n = 3 * 16 - 5, 2 * 16 + 9
+    cfg = base.scaled(seq_len=L0, n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=L0 + n + 64, summary="bf16")
+    lay.build(method="fp64")
+    kn, vn = synth.append_tokens(cfg, n)
+    dec = hb.Decoder(lay.dims, cfg.keep_ratio, 40)
+    out = torch.empty((1, 32, 128), dtype=torch.float32, device="cuda")
+    for i in range(n):   # appends folded into decode steps
+        dec(lay.cache, lay.q, lay.R, lay.W, out, k_new=hc.to_dev(kn[i], lay.tdt),
+            v_new=hc.to_dev(vn[i], lay.tdt))
+    torch.cuda.synchronize()
+    d = lay.data
+    d["K"][0, :, L0:L0 + n] = kn[:, 0].transpose(1, 0, 2)
+    d["V"][0, :, L0:L0 + n] = vn[:, 0].transpose(1, 0, 2)
+    d["seq_lens"][:] = L0 + n
+    ref = hc.oracle_index(lay)
+    got = lay.index_host()
+    P = -(-(L0 + n) // 16)
+    assert np.array_equal(got["lo"][0, :, :P], ref["lo"][0, :, :P])
+    assert np.array_equal(got["hi"][0, :, :P], ref["hi"][0, :, :P])
+    hc.check_index(lay, ref)
+    out, dbg = lay.decode(cfg.keep_ratio, 40)
+    hc.check_decode(lay, out, dbg, cfg.keep_ratio, 40, ref_index=ref)

@@ -420,3 +420,68 @@ def test_full_budgets_of_each_stage_give_dense_attention():
         np.testing.assert_allclose(r["out"], orc.dense_head(lay["q"][0, 3], lay["K"][0, 0],
                                                             lay["V"][0, 0], L, orc.default_scale(128)),
                                    rtol=1e-12, atol=1e-13)
+
+
+# ---------------------------------------------------------------------------------------------
+# bf16 page extrema rounded outward (compressed summaries): neighbours of torch's bf16 rounding
+# ---------------------------------------------------------------------------------------------
+def test_bf16_outward_rounding_brackets_round_to_nearest():
+    rng = np.random.default_rng(4)
+    x = np.concatenate([rng.standard_normal(4000).astype(np.float32) * np.float32(37.0),
+                        rng.standard_normal(500).astype(np.float32) * np.float32(1e-39),
+                        np.array([0.0, -0.0, 1.0, -1.0, 2.0 - 2.0 ** -23, -(2.0 - 2.0 ** -23),
+                                  3.0e38, -3.0e38, 2.0 ** -126, 1.5], np.float32)])
+    lo, hi = orc.extrema_bf16(x, x)
+    t = torch.from_numpy(x)
+    rne = t.to(torch.bfloat16).to(torch.float32).numpy()
+    for v in (lo, hi):   # both are bf16 values
+        assert np.array_equal(torch.from_numpy(v).to(torch.bfloat16).to(torch.float32).numpy(), v)
+    assert np.all(lo <= x) and np.all(hi >= x)
+    assert np.all((rne == lo) | (rne == hi))
+    exact = rne == x
+    assert np.all(lo[exact] == x[exact]) and np.all(hi[exact] == x[exact])
+    # otherwise the two are adjacent bf16 values: nothing representable strictly between
+    inexact = ~exact
+    mid = ((lo[inexact].astype(np.float64) + hi[inexact]) / 2).astype(np.float32)
+    back = torch.from_numpy(mid).to(torch.bfloat16).to(torch.float32).numpy()
+    assert np.all((back == lo[inexact]) | (back == hi[inexact]))
+
+
+def test_bound_from_bf16_extrema_is_valid_and_looser():
+    rng = np.random.default_rng(8)
+    d, S, L = 16, 8, 203
+    K = rng.standard_normal((L, d)).astype(np.float32)
+    R = _orth(3, d)
+    W = rng.standard_normal((d, 32)).astype(np.float32)
+    lo32, hi32, _ = orc.build_head(K, L, R, W, S)
+    lo16, hi16, _ = orc.build_head(K, L, R, W, S, summary="bf16")
+    assert np.all(lo16 <= lo32) and np.all(hi16 >= hi32)
+    for _ in range(5):
+        q = rng.standard_normal(d).astype(np.float32)
+        qt = orc.rotate(q[None, :], R)[0]
+        U32 = orc.page_bounds(qt, lo32, hi32)
+        U16 = orc.page_bounds(qt, lo16, hi16)
+        assert np.all(U16 >= U32)
+        logits = K.astype(np.float64) @ q.astype(np.float64)
+        for p in range(len(U16)):
+            assert U16[p] >= logits[p * S:min(L, p * S + S)].max() - 1e-5 * np.abs(logits).max()
+
+
+def test_append_with_bf16_extrema_equals_build():
+    rng = np.random.default_rng(10)
+    d, nb, S, L0, n = 32, 64, 4, 9, 11
+    K = rng.standard_normal((L0 + n, d)).astype(np.float32)
+    V = rng.standard_normal((L0 + n, d)).astype(np.float32)
+    R, W = _orth(6, d), rng.standard_normal((d, nb)).astype(np.float32)
+    lo, hi, kc = orc.build_head(K, L0, R, W, S, summary="bf16")
+    Pm = -(-(L0 + n) // S)
+    st = dict(K=np.zeros_like(K), V=np.zeros_like(V), lo=np.zeros((Pm, d), np.float32),
+              hi=np.zeros((Pm, d), np.float32), codes=np.zeros((L0 + n, nb // 32), np.uint32),
+              L=L0, summary="bf16")
+    st["K"][:L0], st["V"][:L0] = K[:L0], V[:L0]
+    st["lo"][:len(lo)], st["hi"][:len(hi)], st["codes"][:L0] = lo, hi, kc
+    for t in range(L0, L0 + n):
+        orc.append_head(st, K[t], V[t], R, W, S)
+    lo2, hi2, kc2 = orc.build_head(K, L0 + n, R, W, S, summary="bf16")
+    assert np.array_equal(st["lo"], lo2) and np.array_equal(st["hi"], hi2)
+    assert np.array_equal(st["codes"], kc2)
