@@ -455,7 +455,7 @@ def main():
                    "alg_GBps": round(alg[n] / (avg_ms[n] * 1e-3) / 1e9, 1)}
     cands = [n for n in ("page_bound", "sparse_attn", "dense_attn") if n in avg_ms]
     dominant = max(cands, key=lambda n: avg_ms[n])
-    traffic = load_traffic(args.workload, dominant) if variant == "hhr" else None
+    traffic = load_traffic(args.workload, dominant) if variant in ("hhr", "dense") else None
     achieved = alg[dominant] / (avg_ms[dominant] * 1e-3) / 1e9
     step_bytes = sum(alg.values())
     us = ms_step * 1e3
