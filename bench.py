@@ -31,9 +31,12 @@ every token), the method with R = I (identity-r: the plain per-channel min/max b
 method with the page extrema stored as bf16 rounded outward (bf16-extrema: half the bytes of the
 page-bound stream), or the dense baseline itself (dense).
 
+--recall instead reports retrieval quality (a diagnostic): recall of the exact top-K tokens and
+of the planted keys over a grid of keep ratios, budgets, code lengths and stage variants.
+
 Prints ONE JSON line. Options: --gpus (must be 1), --steps, --warmup, --workload, --variant,
---layers, --no-cpu-baseline, --no-builder, --no-dense, --quiet, --copy-calibration (a 512 MiB
-device copy only, to scale the HBM byte counters of rocprofv3).
+--layers, --no-cpu-baseline, --no-builder, --no-dense, --recall, --quiet, --copy-calibration (a
+512 MiB device copy only, to scale the HBM byte counters of rocprofv3).
 """
 from __future__ import annotations
 
@@ -253,6 +256,89 @@ def cpu_baseline(cfg, data, append, quiet, budget_s=10.0):
                        f"{factor:g} (KV heads x total / sampled context); index build untimed")}
 
 
+def recall_report(args, quiet):
+    """Retrieval quality on the synthetic keys (a diagnostic, no parity claim): for every query
+    head, the exact top-K tokens by q.k (K = 1.5 % of the context, the paper's default Top-K
+    ratio, HHR §4.1) and the planted keys, against the tokens the GPU path selects, over a grid
+    of keep ratios, token budgets, code lengths and stage variants. Also the coarse stage's
+    ceiling: the share of the exact top-K lying in the kept pages."""
+    import numpy as np
+    import torch
+    from long_context_decode_gkr_amd import binding as hb
+    from long_context_decode_gkr_amd import synth
+    cfg_id = WORKLOADS[args.workload][0]
+    cfg = synth.CONFIGS[cfg_id]
+    lens = cfg.lengths()
+    data = synth.make_layer(cfg, max_seq_len=cfg.seq_len, lens=lens)
+    B, Hq, Hkv, d, S, G = (cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim,
+                           cfg.page_size, cfg.group)
+    dev = torch.device("cuda")
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    kvt = hb.HHR_BF16 if cfg.dtype == "bf16" else hb.HHR_F32
+    log("recall: exact top-K of every head", quiet)
+    ref, planted = {}, {}
+    for b in range(B):
+        L = lens[b]
+        kref = max(1, int(round(0.015 * L)))
+        for h in range(Hq):
+            lg = data["K"][b, h // G, :L].astype(np.float64) @ data["q"][b, h].astype(np.float64)
+            order = np.lexsort((np.arange(L), -lg))
+            ref[(b, h)] = set(order[:kref].tolist())
+            pl = data["planted"][b, h]
+            planted[(b, h)] = set(pl[pl >= 0].tolist())
+    qd = torch.from_numpy(data["q"]).to(dev).to(tdt)
+    rows = []
+    base_k = cfg.token_budget
+    grid = ([("both", r, k) for r in (cfg.keep_ratio / 2, cfg.keep_ratio, 0.3)
+             for k in (base_k // 4, base_k, 2 * base_k)]
+            + [("pages", r, 1) for r in (cfg.keep_ratio / 2, cfg.keep_ratio, 0.3)]
+            + [("codes", 1.0, k) for k in (base_k // 4, base_k, 2 * base_k)])
+    for nb, rot in ((128, "random"), (256, "random"), (128, "identity")):
+        R = (np.stack([np.eye(d, dtype=np.float32)] * Hkv) if rot == "identity"
+             else data["R"])
+        W = np.stack([synth.projection(cfg_id, g, d, nb) for g in range(Hkv)])
+        dims = hb.make_dims(B, Hq, Hkv, S, nb, int(data["max_seq_len"]), kv_dtype=kvt)
+        cache = hb.Cache(dims)
+        cache.K.copy_(torch.from_numpy(data["K"]).to(dev).to(tdt))
+        cache.V.copy_(torch.from_numpy(data["V"]).to(dev).to(tdt))
+        cache.seq_lens.copy_(torch.from_numpy(data["seq_lens"]).to(dev))
+        Rd, Wd = torch.from_numpy(R).to(dev), torch.from_numpy(W).to(dev)
+        hb.build_pages(cache, Rd, Wd)
+        out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
+        for stages, rho, k in grid:
+            if rot == "identity" and stages == "codes":
+                continue                      # the rotation does not enter the fine stage
+            dec = hb.Decoder(dims, rho, k, stages=stages)
+            dbg = hb.Debug(dims, k, rho, stages)
+            dec(cache, qd, Rd, Wd, out, dbg)
+            torch.cuda.synchronize()
+            tidx, tcnt = dbg.token_idx.cpu().numpy(), dbg.token_count.cpu().numpy()
+            pid, pcnt = dbg.page_ids.cpu().numpy(), dbg.page_count.cpu().numpy()
+            rec, prec, plr, att = [], [], [], []
+            for (b, h), T in ref.items():
+                sel = set(tidx[b, h, :tcnt[b, h]].tolist())
+                pages = set(pid[b, h, :pcnt[b, h]].tolist())
+                rec.append(len(sel & T) / len(T))
+                prec.append(sum(1 for t in T if t // S in pages) / len(T))
+                P = planted[(b, h)]
+                if P:
+                    plr.append(len(sel & P) / len(P))
+                att.append(tcnt[b, h] / lens[b])
+            rows.append({"stages": stages, "rotation": rot, "hash_bits": nb,
+                         "keep_ratio": round(rho, 4), "token_budget": k if stages != "pages" else None,
+                         "attended_frac": round(float(np.mean(att)), 4),
+                         "topk_recall": round(float(np.mean(rec)), 4),
+                         "topk_in_kept_pages": round(float(np.mean(prec)), 4),
+                         "planted_recall": round(float(np.mean(plr)), 4) if plr else None})
+            log(f"  {rows[-1]}", quiet)
+    return {"metric": "HHR retrieval recall on synthetic keys (diagnostic)",
+            "workload": WORKLOADS[args.workload][3], "name": args.workload,
+            "reference": "exact top-K by q.k per query head, K = 1.5 % of the context; "
+                         "planted keys (q.k = mean + 4 std)",
+            "data": "synthetic (seeded; untrained random orthogonal R and Gaussian W)",
+            "rows": rows}
+
+
 def copy_calibration(mib=512, reps=3):
     """A plain device-to-device copy of known size, for scaling the FETCH_SIZE / WRITE_SIZE
     counters: each launch reads and writes exactly `mib` MiB."""
@@ -285,6 +371,8 @@ def main():
     ap.add_argument("--quiet", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="only run a 512 MiB device copy (for HBM counter scaling)")
+    ap.add_argument("--recall", action="store_true",
+                    help="only report retrieval recall against the exact top-K (diagnostic)")
     args = ap.parse_args()
     if args.copy_calibration:
         copy_calibration()
@@ -304,6 +392,9 @@ def main():
         print("bench.py needs a GPU", file=sys.stderr)
         sys.exit(1)
     hb.load()
+    if args.recall:
+        print(json.dumps(recall_report(args, q)), flush=True)
+        return
     variant = args.variant
     cfg_id, append, nl_default, desc = WORKLOADS[args.workload]
     append = append and variant != "dense"     # the dense baseline keeps no index to update

@@ -138,7 +138,8 @@ def make_layer(cfg: Config, max_seq_len: Optional[int] = None, layer: int = 0,
     """Draw one decode layer: K, V [B][Hkv][Lmax][d], q [B][Hq][d], R, W, seq_lens.
 
     Values are float32 arrays holding exactly the stored values (bf16-representable for bf16
-    configs). Rows at or beyond a sequence's length are zero.
+    configs). Rows at or beyond a sequence's length are zero. `planted` [B][Hq][n_plant] holds
+    the planted positions of each query head (-1 where a short sequence has fewer).
     Planted keys: for each query head, n_plant background keys at distinct positions are moved
     along q so that their logit is the background mean + 4 std of that head's logits.
     """
@@ -151,6 +152,7 @@ def make_layer(cfg: Config, max_seq_len: Optional[int] = None, layer: int = 0,
     K = np.zeros((B, Hkv, Lmax, d), np.float32)
     V = np.zeros((B, Hkv, Lmax, d), np.float32)
     q = np.zeros((B, Hq, d), np.float32)
+    planted = np.full((B, Hq, cfg.n_plant), -1, np.int64)   # positions, -1 where none
     for b in range(B):
         L = lens[b]
         for h in range(Hq):
@@ -168,6 +170,7 @@ def make_layer(cfg: Config, max_seq_len: Optional[int] = None, layer: int = 0,
                     logits = k64 @ qh
                     mu, sd = logits.mean(), logits.std()
                     sel = pos[i]
+                    planted[b, g * G + i, :n_plant] = sel
                     target = mu + 4.0 * sd
                     shift = (target - logits[sel]) / float(qh @ qh)
                     k[sel] = (k64[sel] + shift[:, None] * qh[None, :]).astype(np.float32)
@@ -176,7 +179,8 @@ def make_layer(cfg: Config, max_seq_len: Optional[int] = None, layer: int = 0,
                                    cfg.dtype)
     R = np.stack([rotation(cfg.cfg_id, g, d, layer) for g in range(Hkv)])
     W = np.stack([projection(cfg.cfg_id, g, d, cfg.hash_bits, layer) for g in range(Hkv)])
-    return dict(K=K, V=V, q=q, R=R, W=W, seq_lens=np.asarray(lens, np.int32), max_seq_len=Lmax)
+    return dict(K=K, V=V, q=q, R=R, W=W, seq_lens=np.asarray(lens, np.int32), max_seq_len=Lmax,
+                planted=planted)
 
 
 def append_tokens(cfg: Config, n: int, layer: int = 0) -> tuple:
