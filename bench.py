@@ -29,7 +29,8 @@ speedup_vs_dense).
 every token of the kept pages is attended), the fine stage alone (codes: Hamming top-k over
 every token), the method with R = I (identity-r: the plain per-channel min/max bound), the
 method with the page extrema stored as bf16 rounded outward (bf16-extrema: half the bytes of the
-page-bound stream), or the dense baseline itself (dense).
+page-bound stream), one selection per KV head shared by its query heads (group-shared), or the
+dense baseline itself (dense).
 
 --recall instead reports retrieval quality (a diagnostic): recall of the exact top-K tokens and
 of the planted keys over a grid of keep ratios, budgets, code lengths and stage variants.
@@ -83,6 +84,8 @@ VARIANTS = {
     "pages": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3), ("combine", 4)),
     "bf16-extrema": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3),
                      ("combine", 4)),
+    "group-shared": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3),
+                     ("combine", 4)),
     "codes": (("prep", 0), ("select", 2), ("sparse_attn", 3), ("combine", 4)),
     "dense": (("dense_attn", 0), ("combine", 1)),
 }
@@ -133,20 +136,23 @@ def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
     ex = 2 if variant == "bf16-extrema" else 4    # bytes per stored extremum
     if append:
         out["prep"] += B * Hkv * (2 * d * esz + 2 * d * esz + nb // 8 + 2 * d * ex * 2)
+    shared = variant == "group-shared"
+    Hs = Hkv if shared else Hq        # selection units per sequence
     for L in lens:
         P = -(-L // S)
         n_keep = P if variant == "codes" else min(P, max(1, math.ceil(cfg.keep_ratio * P)))
         ncand = min(n_keep * S, L)
         k = ncand if variant == "pages" else min(cfg.token_budget, ncand)
         parts = Hq * -(-k // 256) * (d + 2) * 4
-        out["page_bound"] += Hkv * P * d * 2 * ex + Hq * P * 4
+        out["page_bound"] += Hkv * P * d * 2 * ex + Hs * P * 4
         if variant == "pages":
             out["select"] += Hq * (P * 4 + k * 4)
         elif variant == "codes":
             out["select"] += Hq * (nb // 8 + ncand * (nb // 8) + k * 4)
         else:
-            out["select"] += Hq * (P * 4 + nb // 8 + n_keep * S * (nb // 8) + k * 4)
-        out["sparse_attn"] += Hq * (k * 2 * d * esz + k * 4 + d * esz) + parts
+            out["select"] += Hs * (P * 4 + n_keep * S * (nb // 8) + k * 4) + Hq * nb // 8
+        # K and V rows: once per selection unit (a KV head's group shares its rows)
+        out["sparse_attn"] += Hs * k * 2 * d * esz + Hq * (k * 4 + d * esz) + parts
         out["combine"] += parts + Hq * d * 4
     if variant == "codes":
         del out["page_bound"]
@@ -361,7 +367,8 @@ def main():
     ap.add_argument("--variant", choices=sorted(VARIANTS), default="hhr",
                     help="hhr: the method; pages / codes: coarse or fine stage alone; "
                          "identity-r: R = I; bf16-extrema: page extrema stored as bf16 "
-                         "rounded outward; dense: full attention over every token")
+                         "rounded outward; group-shared: one selection per KV head; dense: "
+                         "full attention over every token")
     ap.add_argument("--layers", type=int, default=None,
                     help="layer instances cycled (default: per workload, 8 or 16)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -444,7 +451,8 @@ def main():
         knd = torch.from_numpy(kn).to(dev).to(tdt)
         vnd = torch.from_numpy(vn).to(dev).to(tdt)
     stages = {"pages": "pages", "codes": "codes"}.get(variant, "both")
-    dec = hb.Decoder(dims, cfg.keep_ratio, cfg.token_budget, stages=stages)
+    dec = hb.Decoder(dims, cfg.keep_ratio, cfg.token_budget, stages=stages,
+                     group_shared=variant == "group-shared")
     dense = hb.DenseDecoder(dims)
     out = torch.empty((B, Hq, d), dtype=torch.float32, device=dev)
     cache_structs = [c.struct() for c in layers]

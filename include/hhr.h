@@ -112,6 +112,11 @@ typedef struct {
   int32_t token_budget;
   float softmax_scale;
   int32_t stages;       /* hhr_stages */
+  int32_t group_shared; /* 0: each query head selects its own pages and tokens (the method as
+                           read); 1: one selection per KV head for its G query heads: a page's
+                           bound is the largest of the heads' bounds, a token's distance the
+                           smallest of their distances (a quarter of the K/V rows gathered
+                           at G = 4) */
 } hhr_params;
 
 /* The KV cache and its derived index (page extrema and key codes). All device pointers.
@@ -141,6 +146,8 @@ typedef struct {
  *                                   HHR_STAGES_PAGES_ONLY min(max(1, ceil(rho Pmax)) *
  *                                   page_size, max_seq_len)
  *   token_count [B][Hq]             how many were selected
+ *   With group_shared, page_ids, page_count, dist, token_idx and token_count hold one row per
+ *   (b, KV head) instead, at row b * Hkv + g; bounds stays per query head.
  *   kernel_events  NULL or 10 caller-created events: the start and stop of each of the five
  *                  kernels of a decode step, in launch order, recorded by the runtime around the
  *                  kernel's own execution (hipExtLaunchKernel), so that their elapsed times are

@@ -37,7 +37,8 @@ class Dims(ctypes.Structure):
 
 class Params(ctypes.Structure):
     _fields_ = [("page_keep_ratio", ctypes.c_double), ("token_budget", ctypes.c_int32),
-                ("softmax_scale", ctypes.c_float), ("stages", ctypes.c_int32)]
+                ("softmax_scale", ctypes.c_float), ("stages", ctypes.c_int32),
+                ("group_shared", ctypes.c_int32)]
 
 
 class CacheStruct(ctypes.Structure):
@@ -231,10 +232,11 @@ class Decoder:
     """Holds the workspace for hhr_decode at fixed shapes and budgets."""
 
     def __init__(self, dims: Dims, keep_ratio: float, token_budget: int, softmax_scale: float = 0.0,
-                 device="cuda", stages: str = "both"):
+                 device="cuda", stages: str = "both", group_shared: bool = False):
         import torch
         self.dims = dims
-        self.params = Params(keep_ratio, token_budget, softmax_scale, STAGES[stages])
+        self.params = Params(keep_ratio, token_budget, softmax_scale, STAGES[stages],
+                             int(group_shared))
         self.ws_bytes = hhr_decode_workspace_bytes(dims, self.params)
         if self.ws_bytes == 0:
             raise HHRError("hhr_decode_workspace_bytes", 1)

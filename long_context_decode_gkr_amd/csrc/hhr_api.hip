@@ -70,8 +70,9 @@ hhr_status check_params(const hhr_params* p, const Shape& s, DecodePlan* plan) {
   if (p->stages != HHR_STAGES_BOTH && p->stages != HHR_STAGES_PAGES_ONLY &&
       p->stages != HHR_STAGES_CODES_ONLY)
     return HHR_ERR_INVALID_ARG;
+  if (p->group_shared != 0 && p->group_shared != 1) return HHR_ERR_INVALID_ARG;
   *plan = plan_decode(s, rho, p->token_budget, softmax_scale(p->softmax_scale),
-                      static_cast<Stages>(p->stages));
+                      static_cast<Stages>(p->stages), p->group_shared);
   return HHR_OK;
 }
 

@@ -43,8 +43,9 @@ constexpr int kDistCache = 32768;      // candidate slots whose distance stays i
 // ---------------------------------------------------------------------------------------------
 struct BoundArgs {
   const float* qrot;      // [B][Hq][128] q~ from the preparation kernel
-  float* U;               // [B][Hq][Pmax]
+  float* U;               // [B][Hq][Pmax], or (shared) [B][Hkv][Pmax]: max over the group
   int appended;           // a token is appended in this step (seq_lens is advanced at its end)
+  int shared;             // one selection per KV head: U of a page = max over its G heads
 };
 
 template <int G, int SB>   // SB: extrema stored as bf16
@@ -105,6 +106,27 @@ page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) 
   for (int hh = 0; hh < G; ++hh)
     red[w][hh][lane] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
   __syncthreads();
+  if (a.shared) {
+    // one bound per page for the whole group: the largest of its heads' bounds (the group's
+    // pages are chosen once; each head's own bound goes to the debug output only)
+    for (int pp = threadIdx.x; pp < kBoundPages; pp += kBoundThreads) {
+      const int p = p0 + pp;
+      if (p < P) {
+        float um = -INFINITY;
+#pragma unroll
+        for (int hh = 0; hh < G; ++hh) {
+          float sum = 0.f;
+#pragma unroll
+          for (int w2 = 0; w2 < kBoundThreads / kWave; ++w2)
+            sum += reinterpret_cast<const float*>(&red[w2][hh][0])[pp];
+          um = fmaxf(um, sum);
+          if (dbg_U) dbg_U[(size_t(b) * s.Hq + g * G + hh) * s.Pmax + p] = sum;
+        }
+        a.U[(size_t(b) * s.Hkv + g) * s.Pmax + p] = um;
+      }
+    }
+    return;
+  }
   for (int o = threadIdx.x; o < G * kBoundPages; o += kBoundThreads) {
     const int hh = o / kBoundPages, pp = o % kBoundPages;
     const int p = p0 + pp;
@@ -187,7 +209,7 @@ constexpr int kRadixBits = 12;
 constexpr int kEmitSPT = 8;    // cached distances per thread per emit chunk
 static_assert(16 % kEmitSPT == 0 && kEmitSPT >= 8, "an emit chunk must not cross a page (page sizes 16, 32)");
 
-template <int NB, int EPT, int NT>
+template <int NB, int EPT, int NT, int SHARED>
 __global__ void __launch_bounds__(NT)
 select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   constexpr int kSelThreads = NT;
@@ -196,8 +218,10 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   using DT = typename std::conditional<NB == 128, uint8_t, uint16_t>::type;
   constexpr uint32_t kNone = NB == 128 ? 0xFFu : 0xFFFFu;   // distance of a slot past the end
   constexpr int HB = kRadixBins > NB + 1 ? kRadixBins : NB + 1;
-  const int h = blockIdx.x, b = blockIdx.y, g = h / s.G;
-  const int bh = b * s.Hq + h;
+  // selection unit: a query head, or (SHARED) a KV head whose G query heads share the choice
+  const int h = blockIdx.x, b = blockIdx.y, g = SHARED ? h : h / s.G;
+  const int bh = b * (SHARED ? s.Hkv : s.Hq) + h;
+  const int ncodes = SHARED ? s.G : 1;            // query codes whose nearest distance counts
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int t = c.seq_lens[b];                   // position of the appended token, if any
   const bool app = a.appended && t >= 0 && t < s.Lmax;
@@ -208,7 +232,7 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   __shared__ int32_t s_pages[kMaxPages + kWave];
   __shared__ __align__(16) DT s_dist[kDistCache + kWave];
   __shared__ __align__(16) uint32_t s_hist[HB + kWave];
-  __shared__ uint32_t s_qw[NW];       // query code
+  __shared__ uint32_t s_qw[SHARED ? 8 : 1][NW];   // query code(s)
   __shared__ int s_wt[2][kSelWaves];
   __shared__ uint32_t s_mm[2][kSelWaves];
   __shared__ int s_pick[3];
@@ -230,7 +254,8 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
 
   // ---- query code (from the code workgroups of the bound kernel), page keys to registers,
   // histograms cleared
-  if (tid < NW) s_qw[tid] = a.qcode[size_t(bh) * NW + tid];
+  if (tid < ncodes * NW)
+    s_qw[tid / NW][tid % NW] = a.qcode[(size_t(b) * s.Hq + (SHARED ? g * s.G : h)) * NW + tid];
   if (tid == 0) s_ncand = 0;
   for (int i = tid; i < HB; i += kSelThreads) s_hist[i] = 0;
   uint32_t key[EPT];
@@ -439,7 +464,26 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   // ---- fine stage: Hamming distance of every candidate slot (§3.1 Eq. 2)
   uint32_t qw[NW];
 #pragma unroll
-  for (int i = 0; i < NW; ++i) qw[i] = s_qw[i];
+  for (int i = 0; i < NW; ++i) qw[i] = s_qw[0][i];
+  // distance of a code: to the query code, or (SHARED) the smallest over the group's codes
+  auto code_dist = [&](const uint4 (&x)[NW / 4]) -> uint32_t {
+    uint32_t dd = 0;
+#pragma unroll
+    for (int v = 0; v < NW / 4; ++v)
+      dd += __popc(x[v].x ^ qw[4 * v]) + __popc(x[v].y ^ qw[4 * v + 1]) +
+            __popc(x[v].z ^ qw[4 * v + 2]) + __popc(x[v].w ^ qw[4 * v + 3]);
+    if constexpr (SHARED) {
+      for (int i = 1; i < ncodes; ++i) {   // uniform; the other codes are LDS broadcasts
+        uint32_t di = 0;
+#pragma unroll
+        for (int v = 0; v < NW / 4; ++v)
+          di += __popc(x[v].x ^ s_qw[i][4 * v]) + __popc(x[v].y ^ s_qw[i][4 * v + 1]) +
+                __popc(x[v].z ^ s_qw[i][4 * v + 2]) + __popc(x[v].w ^ s_qw[i][4 * v + 3]);
+        dd = min(dd, di);
+      }
+    }
+    return dd;
+  };
   const int lgS = (s.S == 16) ? 4 : 5;
   const int nslots = n_keep << lgS;
   const bool cache_d = nslots <= kDistCache;
@@ -449,14 +493,10 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
     if (tk >= L) return kNone;
     if (!a.fine) return 0u;
     const uint4* cp = reinterpret_cast<const uint4*>(cbase + size_t(tk) * NW);
-    uint32_t dd = 0;
+    uint4 x[NW / 4];
 #pragma unroll
-    for (int v = 0; v < NW / 4; ++v) {
-      const uint4 x = cp[v];
-      dd += __popc(x.x ^ qw[4 * v]) + __popc(x.y ^ qw[4 * v + 1]) + __popc(x.z ^ qw[4 * v + 2]) +
-            __popc(x.w ^ qw[4 * v + 3]);
-    }
-    return dd;
+    for (int v = 0; v < NW / 4; ++v) x[v] = cp[v];
+    return code_dist(x);
   };
   uint32_t* whist = s_hist;   // bins 0..NB (cleared by the coarse stage's last pass)
   // Batches of 8 x (1024 / NT) slots per thread: all code loads of a batch are issued before
@@ -489,11 +529,8 @@ select_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
 #pragma unroll
     for (int u = 0; u < BAT; ++u) {
       const int slot = base + u * kSelThreads + tid;
-      uint32_t dd = 0;
-#pragma unroll
-      for (int v = 0; v < NW / 4; ++v)
-        dd += __popc(cw[u][v].x ^ qw[4 * v]) + __popc(cw[u][v].y ^ qw[4 * v + 1]) +
-              __popc(cw[u][v].z ^ qw[4 * v + 2]) + __popc(cw[u][v].w ^ qw[4 * v + 3]);
+      // (without the fine stage every code equals the first query code: distance 0)
+      const uint32_t dd = a.fine ? code_dist(cw[u]) : 0u;
       const bool live = tt[u] < L;                // implies slot < nslots
       atomicAdd(live ? &whist[dd] : &s_hist[HB + lane], 1u);
       // (without the LDS cache every lane writes its dummy entry; the emit recomputes)
@@ -690,10 +727,11 @@ __device__ __forceinline__ void unpack(const uint4& x, float (&f)[4]) {
 }
 
 struct AttnArgs {
-  const int32_t* idx;
+  const int32_t* idx;   // rows of selected tokens: per (b, h), or (shared) per (b, KV head)
   const int32_t* cnt;
   float* part;        // [B][Hq][nsplit][kD + 2]: o[0..127], m, l
   int kcap, istride, nsplit;
+  int shared;
   float scale_log2e;
 };
 
@@ -705,7 +743,8 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
   constexpr int EPL = A::EPL, LPR = A::LPR, RPI = A::RPI, ITER = A::ITER;
   const int split = blockIdx.x, h = blockIdx.y, b = blockIdx.z, g = h / s.G;
   const int bh = b * s.Hq + h;
-  const int count = a.cnt[bh];
+  const int bu = a.shared ? b * s.Hkv + g : bh;   // selection unit whose tokens are attended
+  const int count = a.cnt[bu];
   const int w = wave_id(), lane = lane_id();
   const int rg = lane / LPR, sub = lane % LPR;
   const int row0 = split * A::CHUNK + w * A::RPW;
@@ -748,7 +787,7 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
 
     // selected rows: indices first (no branches, so all loads stay in flight together)
     const size_t kvrow0 = (size_t(b) * s.Hkv + g) * s.Lmax;
-    const int32_t* ib = a.idx + size_t(bh) * a.istride;
+    const int32_t* ib = a.idx + size_t(bu) * a.istride;
     int tok[ITER];
 #pragma unroll
     for (int it = 0; it < ITER; ++it) tok[it] = ib[min(row0 + it * RPI + rg, count - 1)];
@@ -899,9 +938,11 @@ combine_kernel(const float* __restrict__ part, int nsplit, float* __restrict__ o
 // ---------------------------------------------------------------------------------------------
 static size_t align256(size_t x) { return (x + 255) & ~size_t(255); }
 
-DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages stages) {
+DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages stages,
+                       int shared) {
   DecodePlan p{};
   p.stages = stages;
+  p.shared = shared;
   if (stages == Stages::kPagesOnly) {
     // every token of the kept pages: at most max(1, ceil(rho Pmax)) pages of S tokens
     const long long keep = (long long)ceil(rho * double(s.Pmax));
@@ -911,18 +952,22 @@ DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages st
     p.kcap = k < s.Lmax ? k : s.Lmax;
   }
   if (stages == Stages::kCodesOnly) rho = 1.0;   // every page is a candidate
-  p.chunk = s.kv_bf16 ? AttnShape<1>::CHUNK : AttnShape<0>::CHUNK;
+  // (group-shared bf16: the gathered matrix-core attention, kGatherChunk positions per
+  // workgroup; otherwise the per-head kernel)
+  p.chunk = shared && s.kv_bf16 ? kGatherChunk
+                                : (s.kv_bf16 ? AttnShape<1>::CHUNK : AttnShape<0>::CHUNK);
   p.nsplit = (p.kcap + p.chunk - 1) / p.chunk;
   p.rho = rho;
   p.scale = scale;
   const size_t BH = size_t(s.B) * s.Hq;
+  const size_t NU = size_t(s.B) * (shared ? s.Hkv : s.Hq);   // selection units
   size_t off = 0;
   p.off_qrot = off;   off = align256(off + BH * kD * sizeof(float));
   p.off_qcode = off;  off = align256(off + BH * s.NW * sizeof(uint32_t));
-  p.off_U = off;      off = align256(off + BH * s.Pmax * sizeof(float));
+  p.off_U = off;      off = align256(off + NU * s.Pmax * sizeof(float));
   p.istride = ((p.kcap + 3) & ~3) + kWave;   // 16-byte aligned rows, then the trash entries
-  p.off_idx = off;    off = align256(off + BH * p.istride * sizeof(int32_t));
-  p.off_cnt = off;    off = align256(off + BH * sizeof(int32_t));
+  p.off_idx = off;    off = align256(off + NU * p.istride * sizeof(int32_t));
+  p.off_cnt = off;    off = align256(off + NU * sizeof(int32_t));
   p.off_part = off;   off = align256(off + BH * p.nsplit * (kD + 2) * sizeof(float));
   p.total = off;
   return p;
@@ -942,9 +987,13 @@ static void launch_bound_t(const Shape& s, const CacheView& c, const BoundArgs& 
 
 template <int NB, int EPT, int NT>
 static void launch_select_t(const Shape& s, const CacheView& c, const SelectArgs& a,
-                            const DebugView& dbg, hipStream_t st) {
-  launch_kernel(select_kernel<NB, EPT, NT>, dim3(s.Hq, s.B), dim3(NT), st, kernel_timer(dbg, 2),
-                s, c, a, dbg);
+                            const DebugView& dbg, int shared, hipStream_t st) {
+  if (shared)
+    launch_kernel(select_kernel<NB, EPT, NT, 1>, dim3(s.Hkv, s.B), dim3(NT), st,
+                  kernel_timer(dbg, 2), s, c, a, dbg);
+  else
+    launch_kernel(select_kernel<NB, EPT, NT, 0>, dim3(s.Hq, s.B), dim3(NT), st,
+                  kernel_timer(dbg, 2), s, c, a, dbg);
 }
 
 // Workgroup size of the selection (measured on MI355X: 1024 and 512 threads tie; 256 threads
@@ -954,12 +1003,12 @@ constexpr int kSelNT = 1024;
 
 template <int NB>
 static void launch_select_nb(const Shape& s, const CacheView& c, const SelectArgs& a,
-                             const DebugView& dbg, hipStream_t st) {
+                             const DebugView& dbg, int shared, hipStream_t st) {
   static_assert(kMaxPages <= 16 * kSelNT, "16 pages per thread cover the page capacity");
   const int ept = (s.Pmax + kSelNT - 1) / kSelNT;
-  if (ept <= 4) launch_select_t<NB, 4, kSelNT>(s, c, a, dbg, st);
-  else if (ept <= 8) launch_select_t<NB, 8, kSelNT>(s, c, a, dbg, st);
-  else launch_select_t<NB, 16, kSelNT>(s, c, a, dbg, st);
+  if (ept <= 4) launch_select_t<NB, 4, kSelNT>(s, c, a, dbg, shared, st);
+  else if (ept <= 8) launch_select_t<NB, 8, kSelNT>(s, c, a, dbg, shared, st);
+  else launch_select_t<NB, 16, kSelNT>(s, c, a, dbg, shared, st);
 }
 
 hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c,
@@ -984,7 +1033,7 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
   if (e != hipSuccess) return e;
   // codes only: every page is kept, so no bound is needed (the selection reads U but keeps all)
   if (p.stages != Stages::kCodesOnly) {
-    BoundArgs ba{qrot, U, k_new != nullptr ? 1 : 0};
+    BoundArgs ba{qrot, U, k_new != nullptr ? 1 : 0, p.shared};
     switch (s.G) {
       case 1: launch_bound_t<1>(s, c, ba, dbg, st); break;
       case 2: launch_bound_t<2>(s, c, ba, dbg, st); break;
@@ -995,15 +1044,21 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
   }
   SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap, p.istride, k_new != nullptr ? 1 : 0,
                 p.stages == Stages::kPagesOnly ? 0 : 1};
-  if (s.NB == 128) launch_select_nb<128>(s, c, sa, dbg, st);
-  else launch_select_nb<256>(s, c, sa, dbg, st);
+  if (s.NB == 128) launch_select_nb<128>(s, c, sa, dbg, p.shared, st);
+  else launch_select_nb<256>(s, c, sa, dbg, p.shared, st);
   HHR_CHECK();
-  AttnArgs aa{idx, cnt, part, p.kcap, p.istride, p.nsplit, p.scale * 1.4426950408889634f};
+  AttnArgs aa{idx, cnt, part, p.kcap, p.istride, p.nsplit, p.shared,
+              p.scale * 1.4426950408889634f};
   dim3 grid(p.nsplit, s.Hq, s.B);
-  if (s.kv_bf16)
+  if (p.shared && s.kv_bf16) {
+    e = launch_attn_gather(s, c, q, p.scale, idx, cnt, p.istride, part, p.nsplit,
+                           kernel_timer(dbg, 3), st);
+    if (e != hipSuccess) return e;
+  } else if (s.kv_bf16) {
     launch_kernel(attn_kernel<1>, grid, dim3(256), st, kernel_timer(dbg, 3), s, c.K, c.V, q, aa);
-  else
+  } else {
     launch_kernel(attn_kernel<0>, grid, dim3(256), st, kernel_timer(dbg, 3), s, c.K, c.V, q, aa);
+  }
   HHR_CHECK();
   return launch_combine(s, part, p.nsplit, out, c.seq_lens, k_new != nullptr ? 1 : 0,
                         kernel_timer(dbg, 4), st);

@@ -194,18 +194,43 @@ typedef float f32x4_t __attribute__((ext_vector_type(4)));
 
 constexpr int kDenseTokW = 32;                      // tokens per wave per sub-chunk
 constexpr int kDenseSub = 4 * kDenseTokW;           // tokens per workgroup per sub-chunk
+static_assert(kGatherChunk % kDenseSub == 0 && kGatherChunk <= 1024, "gathered chunk");
 
-template <int G, int QF32>
+// Gathered rows (IDX): the workgroup's positions [t0, t1) index a KV head's list of selected
+// tokens (group-shared selection) instead of the context itself.
+struct GatherList {
+  const int32_t* idx;   // [B][Hkv][istride]
+  const int32_t* cnt;   // [B][Hkv]
+  int istride;
+};
+constexpr int kGatherMax = 1024;                    // list positions per workgroup
+
+template <int G, int QF32, int IDX>
 __global__ void __launch_bounds__(256)
 dense_attn_mfma_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
                        const void* __restrict__ q, const int32_t* __restrict__ seq_lens,
-                       float* __restrict__ part, int nsplit, int tpw, float scale_log2e) {
+                       float* __restrict__ part, int nsplit, int tpw, float scale_log2e,
+                       GatherList gl) {
   static_assert(G <= 8, "heads of a group fill rows 4 (l / 16) + i of the 16 x 16 tile");
   const int split = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int L = min(max(seq_lens[b], 0), s.Lmax);
+  const int L = IDX ? gl.cnt[size_t(b) * s.Hkv + g] : min(max(seq_lens[b], 0), s.Lmax);
   const int w = wave_id(), lane = lane_id();
   const int col = lane % 16, quad = lane / 16;      // MFMA: token column / k quarter
   const int t0 = split * tpw, t1 = min(t0 + tpw, L);
+  // the workgroup's token positions (gathered rows): staged in LDS once
+  __shared__ int32_t s_tok[IDX ? kGatherMax : 1];
+  if constexpr (IDX) {
+    const int32_t* il = gl.idx + (size_t(b) * s.Hkv + g) * gl.istride;
+    for (int i = threadIdx.x; i < tpw; i += blockDim.x)
+      s_tok[i] = t1 > t0 ? min(max(il[min(t0 + i, t1 - 1)], 0), s.Lmax - 1) : 0;
+    __syncthreads();
+  }
+  // context position of list position pos (clamped into [t0, t1 - 1])
+  auto token = [&](int pos) {
+    const int c = max(min(pos, t1 - 1), 0);
+    if constexpr (IDX) return s_tok[max(c - t0, 0)];
+    else return c;
+  };
   const uint16_t* Kb = static_cast<const uint16_t*>(K);
   const uint16_t* Vb = static_cast<const uint16_t*>(V);
   const size_t kvrow0 = (size_t(b) * s.Hkv + g) * s.Lmax;
@@ -252,14 +277,14 @@ dense_attn_mfma_kernel(Shape s, const void* __restrict__ K, const void* __restri
     const int base = c0 + w * kDenseTokW;
 #pragma unroll
     for (int tt = 0; tt < 2; ++tt) {
-      const int t = max(min(base + 16 * tt + col, t1 - 1), 0);
+      const int t = token(base + 16 * tt + col);
       const uint4* kp = reinterpret_cast<const uint4*>(Kb + (kvrow0 + size_t(t)) * kD + 32 * quad);
 #pragma unroll
       for (int j = 0; j < 4; ++j) kr[tt][j] = kp[j];
     }
 #pragma unroll
     for (int it = 0; it < 8; ++it) {
-      const int t = max(min(base + rg + 4 * it, t1 - 1), 0);
+      const int t = token(base + rg + 4 * it);
       vr[it] = *reinterpret_cast<const uint4*>(Vb + (kvrow0 + size_t(t)) * kD + 8 * sub);
     }
   };
@@ -426,13 +451,14 @@ static void launch_dense_t(const Shape& s, const CacheView& c, const void* q, fl
                            int nsplit, int tpw, float scale_log2e, KernelTimer tm,
                            hipStream_t st) {
   const dim3 grid(nsplit, s.Hkv, s.B);
+  const GatherList none{nullptr, nullptr, 0};
   if constexpr (BF16) {
     if (s.q_bf16)
-      launch_kernel(dense_attn_mfma_kernel<G, 0>, grid, dim3(256), st, tm, s, c.K, c.V, q,
-                    c.seq_lens, part, nsplit, tpw, scale_log2e);
+      launch_kernel(dense_attn_mfma_kernel<G, 0, 0>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                    c.seq_lens, part, nsplit, tpw, scale_log2e, none);
     else
-      launch_kernel(dense_attn_mfma_kernel<G, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
-                    c.seq_lens, part, nsplit, tpw, scale_log2e);
+      launch_kernel(dense_attn_mfma_kernel<G, 1, 0>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                    c.seq_lens, part, nsplit, tpw, scale_log2e, none);
   } else {
     launch_kernel(dense_attn_kernel<BF16, G>, grid, dim3(256), st, tm, s, c.K, c.V, q,
                   c.seq_lens, part, nsplit, tpw, scale_log2e);
@@ -459,6 +485,33 @@ hipError_t launch_dense(const Shape& s, const CacheView& c, const void* q, float
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_combine(s, part, nsplit, out, c.seq_lens, 0, kernel_timer(dbg, 1), st);
+}
+
+template <int G>
+static void launch_gather_t(const Shape& s, const CacheView& c, const void* q, float* part,
+                            int nsplit, float scale_log2e, const GatherList& gl, KernelTimer tm,
+                            hipStream_t st) {
+  const dim3 grid(nsplit, s.Hkv, s.B);
+  if (s.q_bf16)
+    launch_kernel(dense_attn_mfma_kernel<G, 0, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                  c.seq_lens, part, nsplit, kGatherChunk, scale_log2e, gl);
+  else
+    launch_kernel(dense_attn_mfma_kernel<G, 1, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                  c.seq_lens, part, nsplit, kGatherChunk, scale_log2e, gl);
+}
+
+hipError_t launch_attn_gather(const Shape& s, const CacheView& c, const void* q, float scale,
+                              const int32_t* idx, const int32_t* cnt, int istride, float* part,
+                              int nsplit, KernelTimer tm, hipStream_t st) {
+  const GatherList gl{idx, cnt, istride};
+  const float sl2 = scale * 1.4426950408889634f;
+  switch (s.G) {
+    case 1: launch_gather_t<1>(s, c, q, part, nsplit, sl2, gl, tm, st); break;
+    case 2: launch_gather_t<2>(s, c, q, part, nsplit, sl2, gl, tm, st); break;
+    case 4: launch_gather_t<4>(s, c, q, part, nsplit, sl2, gl, tm, st); break;
+    default: launch_gather_t<8>(s, c, q, part, nsplit, sl2, gl, tm, st); break;
+  }
+  return hipGetLastError();
 }
 
 size_t dense_workspace_bytes(const Shape& s) {

@@ -59,6 +59,7 @@ enum class Stages { kBoth = 0, kPagesOnly = 1, kCodesOnly = 2 };
 // Workspace carve-up of one decode call (byte offsets from the workspace base).
 struct DecodePlan {
   Stages stages;
+  int shared;      // one page and token selection per KV head for its G query heads
   int kcap;        // most tokens attended per (b, h): the token budget clamped to max_seq_len,
                    // or (pages only) every token of the largest kept page set
   int istride;     // per-(b, h) stride of the index list: kcap entries + one trash entry per lane
@@ -69,7 +70,8 @@ struct DecodePlan {
   size_t off_qrot, off_qcode, off_U, off_idx, off_cnt, off_part, total;
 };
 
-DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages stages);
+DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages stages,
+                       int shared);
 
 hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R, const float* W,
                              hipStream_t st);
@@ -90,6 +92,13 @@ hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, co
 // [B][Hq][128]; with `appended` it also advances seq_lens (the sparse step's last kernel).
 hipError_t launch_combine(const Shape& s, const float* part, int nsplit, float* out,
                           int32_t* seq_lens, int appended, KernelTimer tm, hipStream_t st);
+// Attention of the G query heads of every KV head over that KV head's list of selected tokens
+// (group-shared selection), each gathered row read once: kGatherChunk list positions per
+// workgroup, partials [B][Hq][nsplit][128 + 2] for launch_combine.
+constexpr int kGatherChunk = 128;
+hipError_t launch_attn_gather(const Shape& s, const CacheView& c, const void* q, float scale,
+                              const int32_t* idx, const int32_t* cnt, int istride, float* part,
+                              int nsplit, KernelTimer tm, hipStream_t st);
 // Dense attention over every token (split-K, grouped-query sharing) and its merge; ws holds
 // dense_workspace_bytes(s) bytes of partials. Timers: events 0-1 (attention), 2-3 (merge).
 size_t dense_workspace_bytes(const Shape& s);

@@ -279,6 +279,41 @@ def decode_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, L: int, lo: np.ndar
                 D=D, sel=sel, out=out)
 
 
+def decode_group(qs: np.ndarray, K: np.ndarray, V: np.ndarray, L: int, lo: np.ndarray,
+                 hi: np.ndarray, kcodes: np.ndarray, R: np.ndarray, W: np.ndarray, S: int,
+                 rho: float, k: int, scale: float, pages: np.ndarray | None = None,
+                 stages: str = "both") -> dict:
+    """One selection shared by the query heads `qs` [G][d] of a KV head (a reading of the
+    group-shared variant; the pages select per head): a page's bound is the largest of the
+    heads' Eq. (3) bounds, a token's distance the smallest of the heads' Eq. (2) distances; the
+    coarse and fine stages then run once, and every head attends to the shared tokens.
+    `pages` and `stages` as in decode_head."""
+    assert stages in STAGES
+    qs = np.asarray(qs)
+    P = num_pages(L, S)
+    qt = rotate(qs, R)
+    if stages == "codes":
+        U, n_keep = None, P
+        if pages is None:
+            pages = np.arange(P)
+    else:
+        Uh = np.stack([page_bounds(qt[i], lo[:P], hi[:P]) for i in range(len(qs))])
+        U = Uh.max(axis=0)
+        n_keep = keep_count(P, rho)
+        if pages is None:
+            pages = select_pages(U, n_keep)
+    cand = candidates(pages, L, S)
+    qc = codes(qs, W)
+    if stages == "pages":
+        D, sel = None, cand
+    else:
+        D = np.stack([hamming(qc[i], kcodes[cand]) for i in range(len(qs))]).min(axis=0)
+        sel = select_tokens(cand, D, k)
+    outs = np.stack([attend(qs[i], K[sel], V[sel], scale) for i in range(len(qs))])
+    return dict(q_rot=qt, q_code=qc, U=U, n_keep=n_keep, pages=np.asarray(pages), cand=cand,
+                D=D, sel=sel, out=outs)
+
+
 def dense_head(q: np.ndarray, K: np.ndarray, V: np.ndarray, L: int, scale: float) -> np.ndarray:
     """Full attention over the first L keys: the baseline HHR is timed against (§4.3, Fig. 7)."""
     return attend(q, K[:L], V[:L], scale)

@@ -58,9 +58,9 @@ class GpuLayer:
         hb.build_pages(self.cache, self.R, self.W, method=method)
         torch_mod().cuda.synchronize()
 
-    def decode(self, rho, k, scale=0.0, debug=True, stages="both"):
+    def decode(self, rho, k, scale=0.0, debug=True, stages="both", group_shared=False):
         torch = torch_mod()
-        dec = hb.Decoder(self.dims, rho, k, scale, stages=stages)
+        dec = hb.Decoder(self.dims, rho, k, scale, stages=stages, group_shared=group_shared)
         out = torch.full((self.cfg.batch, self.cfg.num_q_heads, 128), float("nan"),
                          dtype=torch.float32, device="cuda")
         dbg = hb.Debug(self.dims, k, rho, stages) if debug else None
@@ -199,4 +199,86 @@ def check_decode(layer: GpuLayer, out, dbg, rho, k, scale=None, heads=None, ref_
         rel = np.abs(out_h[b, h] - ref_out).max() / np.abs(ref_out).max()
         assert rel <= OUT_RTOL, (b, h, rel)
         stats["max_out_rel"] = max(stats["max_out_rel"], float(rel))
+    return stats
+
+
+def check_decode_shared(layer: GpuLayer, out, dbg, rho, k, scale=None, ref_index=None,
+                        stages="both", groups=None):
+    """One selection per (b, KV head) (group_shared): per-head bounds and query codes as in
+    check_decode; the group's page set on the GPU's own U (the largest head bound) and, against
+    the oracle, swaps only at near-ties; distances (smallest over the group) and tokens
+    bit-exact on the GPU's pages; each head's output within the tolerance."""
+    d, cfg = layer.data, layer.cfg
+    S, G, Hkv = cfg.page_size, cfg.group, cfg.num_kv_heads
+    scale = orc.default_scale(128) if not scale else scale
+    ref_index = ref_index or oracle_index(layer)
+    gidx = layer.index_host()
+    if layer.summary == "bf16":
+        ref_index = dict(ref_index, lo=gidx["lo"], hi=gidx["hi"])
+    out_h = out.cpu().numpy()
+    qr = dbg.q_rot.cpu().numpy()
+    qc = dbg.q_code.cpu().numpy().view(np.uint32)
+    U = dbg.bounds.cpu().numpy()
+    pid = dbg.page_ids.cpu().numpy().reshape(-1, dbg.page_ids.shape[-1])
+    pcnt = dbg.page_count.cpu().numpy().reshape(-1)
+    dist = dbg.dist.cpu().numpy().view(np.uint16).reshape(-1, dbg.dist.shape[-1])
+    tidx = dbg.token_idx.cpu().numpy().reshape(-1, dbg.token_idx.shape[-1])
+    tcnt = dbg.token_count.cpu().numpy().reshape(-1)
+    groups = groups or [(b, g) for b in range(cfg.batch) for g in range(Hkv)]
+    stats = dict(max_out_rel=0.0, swaps=0)
+    for b, g in groups:
+        L = int(d["seq_lens"][b])
+        row = b * Hkv + g
+        heads = list(range(g * G, g * G + G))
+        qs = d["q"][b, heads]
+        if L == 0:
+            assert tcnt[row] == 0 and np.all(out_h[b, heads] == 0.0)
+            continue
+        o = orc.decode_group(qs, d["K"][b, g], d["V"][b, g], L, ref_index["lo"][b, g],
+                             ref_index["hi"][b, g], ref_index["codes"][b, g], d["R"][g],
+                             d["W"][g], S, rho, k, scale, stages=stages)
+        P, n_keep = orc.num_pages(L, S), o["n_keep"]
+        for i, h in enumerate(heads):
+            assert np.abs(qr[b, h] - o["q_rot"][i]).max() <= 1e-6 * np.linalg.norm(qs[i]), (b, h)
+            np.testing.assert_array_equal(qc[b, h], o["q_code"][i], err_msg=f"q code b={b} h={h}")
+        assert pcnt[row] == n_keep
+        gp = pid[row, :n_keep]
+        assert np.all(np.diff(gp) > 0)
+        if stages == "codes":
+            np.testing.assert_array_equal(gp, np.arange(P))
+        else:
+            lo = ref_index["lo"][b, g, :P].astype(np.float64)
+            hi = ref_index["hi"][b, g, :P].astype(np.float64)
+            Sp = np.zeros(P)
+            for i, h in enumerate(heads):
+                sp = (np.abs(o["q_rot"][i].astype(np.float64))[None, :]
+                      * np.maximum(np.abs(lo), np.abs(hi))).sum(axis=1)
+                Uh = orc.page_bounds(o["q_rot"][i], ref_index["lo"][b, g, :P],
+                                     ref_index["hi"][b, g, :P])
+                assert np.all(np.abs(U[b, h, :P] - Uh) <= BOUND_RTOL * sp), (b, h)
+                Sp = np.maximum(Sp, sp)
+            Ug = U[b, heads, :P].astype(np.float64).max(axis=0)   # the GPU's group bound
+            np.testing.assert_array_equal(gp, orc.select_pages(Ug, n_keep))
+            cut = np.sort(o["U"])[::-1][n_keep - 1]
+            sym = set(gp.tolist()) ^ set(o["pages"].tolist())
+            for p in sym:
+                assert abs(o["U"][p] - cut) <= BOUND_RTOL * Sp[p], (b, g, p)
+            stats["swaps"] += len(sym) // 2
+        cand = orc.candidates(gp, L, S)
+        if stages == "pages":
+            sel = cand
+        else:
+            Dref = np.stack([orc.hamming(o["q_code"][i], ref_index["codes"][b, g][cand])
+                             for i in range(G)]).min(axis=0)
+            slots = (gp[:, None] * S + np.arange(S)[None, :]).reshape(-1)
+            dgot = dist[row, :n_keep * S]
+            np.testing.assert_array_equal(dgot[slots < L], Dref, err_msg=f"distances b={b} g={g}")
+            sel = orc.select_tokens(cand, Dref, k)
+        assert tcnt[row] == len(sel), (b, g)
+        np.testing.assert_array_equal(tidx[row, :len(sel)], sel, err_msg=f"tokens b={b} g={g}")
+        for i, h in enumerate(heads):
+            ref_out = orc.attend(qs[i], d["K"][b, g][sel], d["V"][b, g][sel], scale)
+            rel = np.abs(out_h[b, h] - ref_out).max() / np.abs(ref_out).max()
+            assert rel <= OUT_RTOL, (b, h, rel)
+            stats["max_out_rel"] = max(stats["max_out_rel"], float(rel))
     return stats

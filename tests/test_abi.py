@@ -182,3 +182,16 @@ def test_invalid_summary_dtype(value):
     d.summary_dtype = value
     assert decode_status(dims=d) == 1
     assert hb.hhr_dense_workspace_bytes(d) == 0
+
+
+@pytest.mark.parametrize("value", [-1, 2])
+def test_invalid_group_shared(value):
+    p = hb.Params(0.125, 2048, 0.0, 0, value)
+    assert decode_status(params=p) == 1
+
+
+def test_group_shared_workspace_is_smaller():
+    d = good_dims(max_seq_len=131072)
+    per_head = hb.hhr_decode_workspace_bytes(d, hb.Params(1 / 16, 4096, 0.0, 0, 0))
+    shared = hb.hhr_decode_workspace_bytes(d, hb.Params(1 / 16, 4096, 0.0, 0, 1))
+    assert 0 < shared < per_head

@@ -73,7 +73,10 @@ def test_byte_model_of_the_variants():
     # every K and V row once per KV head (512 MiB) dominates
     assert 8 * 131072 * 512 < dense["dense_attn"] < 1.01 * 8 * 131072 * 512
     assert set(bench.VARIANTS) == {"hhr", "identity-r", "pages", "codes", "dense",
-                                   "bf16-extrema"}
+                                   "bf16-extrema", "group-shared"}
+    sh = bench.algorithmic_bytes(cfg, [131072], False, "group-shared")
+    # one row set per KV head: a quarter of the K/V gather
+    assert sh["sparse_attn"] < base["sparse_attn"] / 3
     half = bench.algorithmic_bytes(cfg, [131072], False, "bf16-extrema")
     assert half["page_bound"] == 8 * 8192 * 128 * 4 + 32 * 8192 * 4 + 32 * 128 * 4
     for v, ks in bench.VARIANTS.items():

@@ -512,3 +512,30 @@ def test_bf16_extrema_append_decode_equals_rebuild():
     hc.check_index(lay, ref)
     out, dbg = lay.decode(cfg.keep_ratio, 40)
     hc.check_decode(lay, out, dbg, cfg.keep_ratio, 40, ref_index=ref)
+
+
+# ---------------------------------------------------------------------------------------------
+# Group-shared selection: one page and token set per KV head
+# ---------------------------------------------------------------------------------------------
+SHARED_CASES = [
+    # stages, cfg, L, batch, lens, rho, k, summary
+    ("both", 2, 3001, None, None, 1 / 8, 300, "f32"),
+    ("both", 4, 3000, 3, [3000, 1777, 17], 0.30, 50, "f32"),
+    ("both", 5, 2085, 2, None, 1 / 8, 257, "f32"),       # page 32, 256-bit codes
+    ("both", 1, 1500, None, None, 0.25, 100, "f32"),     # G = 1: the per-head step
+    ("pages", 2, 2000, None, None, 0.2, 1, "f32"),
+    ("codes", 2, 2000, None, None, 0.2, 150, "f32"),
+    ("both", 3, 4096, None, None, 1 / 16, 256, "bf16"),
+]
+
+
+@pytest.mark.parametrize("stages,cfg_id,L,batch,lens,rho,k,summary", SHARED_CASES)
+def test_group_shared_selection_matches_oracle(stages, cfg_id, L, batch, lens, rho, k, summary):
+    _torch()
+    cfg = _cfg(cfg_id, L, batch=batch, lens=lens, n_plant=8)
+    lay = hc.GpuLayer(cfg, max_seq_len=L + 64, summary=summary)
+    lay.build()
+    ref = hc.oracle_index(lay)
+    out, dbg = lay.decode(rho, k, stages=stages, group_shared=True)
+    st = hc.check_decode_shared(lay, out, dbg, rho, k, ref_index=ref, stages=stages)
+    print(f"shared {stages} cfg{cfg_id}: max out rel err {st['max_out_rel']:.2e}, swaps {st['swaps']}")

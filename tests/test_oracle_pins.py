@@ -485,3 +485,50 @@ def test_append_with_bf16_extrema_equals_build():
     lo2, hi2, kc2 = orc.build_head(K, L0 + n, R, W, S, summary="bf16")
     assert np.array_equal(st["lo"], lo2) and np.array_equal(st["hi"], hi2)
     assert np.array_equal(st["codes"], kc2)
+
+
+# ---------------------------------------------------------------------------------------------
+# Group-shared selection (one page and token set per KV head)
+# ---------------------------------------------------------------------------------------------
+def test_group_of_one_head_is_the_per_head_step():
+    cfg = synth.CONFIGS[2].scaled(seq_len=700, n_plant=4)
+    lay = synth.make_layer(cfg)
+    idx = orc.build_layer(lay["K"], lay["seq_lens"], lay["R"], lay["W"], cfg.page_size)
+    args = (lay["K"][0, 1], lay["V"][0, 1], 700, idx["lo"][0, 1], idx["hi"][0, 1],
+            idx["codes"][0, 1], lay["R"][1], lay["W"][1], cfg.page_size, 0.2, 60, 0.08)
+    for stages in orc.STAGES:
+        a = orc.decode_head(lay["q"][0, 5], *args, stages=stages)
+        b = orc.decode_group(lay["q"][0, 5:6], *args, stages=stages)
+        assert np.array_equal(a["sel"], b["sel"]) and np.array_equal(a["pages"], b["pages"])
+        np.testing.assert_array_equal(a["out"], b["out"][0])
+
+
+def test_group_selection_brute_force_on_tiny_inputs():
+    rng = np.random.default_rng(12)
+    d, nb, S, L, G = 8, 32, 4, 37, 3
+    K = rng.standard_normal((L, d)).astype(np.float32)
+    V = rng.standard_normal((L, d)).astype(np.float32)
+    R = _orth(2, d)
+    W = rng.standard_normal((d, nb)).astype(np.float32)
+    qs = rng.standard_normal((G, d)).astype(np.float32)
+    lo, hi, kc = orc.build_head(K, L, R, W, S)
+    r = orc.decode_group(qs, K, V, L, lo, hi, kc, R, W, S, rho=0.4, k=7, scale=0.3)
+    P = -(-L // S)
+    # bounds by loops over heads, pages and channels; the largest head bound per page
+    qt = [[float(np.float32(sum(float(qs[i][a]) * float(R[a][j]) for a in range(d))))
+           for j in range(d)] for i in range(G)]
+    U = [max(sum(max(qt[i][j] * float(lo[p][j]), qt[i][j] * float(hi[p][j])) for j in range(d))
+             for i in range(G)) for p in range(P)]
+    keep = sorted(sorted(range(P), key=lambda p: (-U[p], p))[:math.ceil(0.4 * P)])
+    assert r["pages"].tolist() == keep
+    # distances bit by bit, the smallest over the heads
+    qbits = [[int(sum(float(qs[i][a]) * float(W[a][c]) for a in range(d)) > 0) for c in range(nb)]
+             for i in range(G)]
+    kbits = [[int((kc[t][c // 32] >> (c % 32)) & 1) for c in range(nb)] for t in range(L)]
+    cand = [t for p in keep for t in range(p * S, min(L, p * S + S))]
+    D = {t: min(sum(a != b for a, b in zip(qbits[i], kbits[t])) for i in range(G)) for t in cand}
+    sel = sorted(sorted(cand, key=lambda t: (D[t], t))[:7])
+    assert r["sel"].tolist() == sel
+    for i in range(G):
+        np.testing.assert_allclose(r["out"][i], _sdpa(qs[i], K[sel], V[sel], 0.3), rtol=1e-12,
+                                   atol=1e-13)
