@@ -149,9 +149,9 @@ hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R,
 // ---------------------------------------------------------------------------------------------
 constexpr int kPrepSlices = 4;
 constexpr int kPrepParts = 8;
-constexpr int kMaxVec = 9;   // 1 key + up to 8 queries
-
-template <int NB, int KB, int QB, int DEC>   // KB, QB: keys/values, queries in bf16
+// KB, QB: keys/values, queries in bf16; DEC: the number of queries (the group size G) in a
+// decode step, 0 for a plain append. Vector 0 is the key, vectors 1 .. DEC the queries.
+template <int NB, int KB, int QB, int DEC>
 __global__ void __launch_bounds__(256 + kPrepParts * NB / kPrepSlices)
 prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __restrict__ vn,
             const void* __restrict__ q, const float* __restrict__ R, const float* __restrict__ W,
@@ -162,17 +162,18 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   constexpr int WPS = CC / 32;                  // code words per slice (1 or 2)
   constexpr int T = kD / kPrepParts;            // terms per lane (16)
   constexpr int NT = 256 + kPrepParts * NB / kPrepSlices;   // workgroup size
-  constexpr int QPT = DEC ? (8 * kD + NT - 1) / NT : 1;     // query elements per thread
+  constexpr int QPT = DEC ? (DEC * kD + NT - 1) / NT : 1;   // query elements per thread
+  constexpr int NV = 1 + DEC;                                 // vectors
   const int sl = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int tid = threadIdx.x;
   const int part = tid & (kPrepParts - 1);
   const bool rot = tid < 256;                   // rotation lanes; the others compute code bits
-  const int nq = DEC ? s.G : 0;
+  constexpr int nq = DEC;
   const bool has_k = kn != nullptr;
   if (!has_k && nq == 0) return;
 
-  __shared__ float xs[kMaxVec][kD];
-  __shared__ uint8_t bits[kMaxVec][CC];
+  __shared__ float xs[NV][kD];
+  __shared__ uint8_t bits[NV][CC];
 
   // Everything that does not depend on the sequence length is loaded together with it: the
   // new key and value elements, the queries, then this lane's 16 column terms.
@@ -237,9 +238,9 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   auto active = [&](int v) { return v == 0 ? app : v <= nq; };
   if (rot) {
     // ---- rotation column j, terms [16 part, 16 part + 16)
-    double acc[kMaxVec];
+    double acc[NV];
 #pragma unroll
-    for (int v = 0; v < kMaxVec; ++v) {
+    for (int v = 0; v < NV; ++v) {
       double a = 0.0;
       if (active(v)) {
         const float* x = &xs[v][part * T];
@@ -257,7 +258,7 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
         store_extrema(s, c, si, first ? kt : fminf(omin, kt), first ? kt : fmaxf(omax, kt));
       }
 #pragma unroll
-      for (int v = 1; v < kMaxVec; ++v) {
+      for (int v = 1; v < NV; ++v) {
         if (v <= nq) {
           const size_t o = (size_t(b) * s.Hq + g * s.G + (v - 1)) * kD + j;
           qrot[o] = float(acc[v]);
@@ -267,9 +268,9 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
     }
   } else {
     // ---- code column cc, terms [16 part, 16 part + 16): fp32 with a certificate
-    float z[kMaxVec], sa[kMaxVec];
+    float z[NV], sa[NV];
 #pragma unroll
-    for (int v = 0; v < kMaxVec; ++v) {
+    for (int v = 0; v < NV; ++v) {
       float zz = 0.f, ss = 0.f;
       if (active(v)) {
         const float* x = &xs[v][part * T];
@@ -284,7 +285,7 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
     }
     if (part == 0) {
       const float* wcol = W + size_t(g) * kD * NB + cc;
-      for (int v = 0; v < kMaxVec; ++v) {
+      for (int v = 0; v < NV; ++v) {
         if (!active(v)) continue;
         int cb = certain_bit_f32(z[v], sa[v]);
         if (cb < 0) cb = int(certified_bit(static_cast<const float*>(&xs[v][0]), wcol, NB));
@@ -335,10 +336,18 @@ static void launch_prep_t(const Shape& s, const CacheView& c, const void* k_new,
                           PrepMode mode, KernelTimer tm, hipStream_t st) {
   dim3 grid(kPrepSlices, s.Hkv, s.B);
   dim3 block(256 + kPrepParts * NB / kPrepSlices);
-  if (mode == PrepMode::kDecode)
-    launch_kernel(prep_kernel<NB, KB, QB, 1>, grid, block, st, tm, s, c, k_new, v_new, q, R, W,
-                  qrot, qcode, dbg_qrot, dbg_qcode);
-  else
+  if (mode == PrepMode::kDecode) {
+    switch (s.G) {
+      case 1: launch_kernel(prep_kernel<NB, KB, QB, 1>, grid, block, st, tm, s, c, k_new, v_new,
+                            q, R, W, qrot, qcode, dbg_qrot, dbg_qcode); break;
+      case 2: launch_kernel(prep_kernel<NB, KB, QB, 2>, grid, block, st, tm, s, c, k_new, v_new,
+                            q, R, W, qrot, qcode, dbg_qrot, dbg_qcode); break;
+      case 4: launch_kernel(prep_kernel<NB, KB, QB, 4>, grid, block, st, tm, s, c, k_new, v_new,
+                            q, R, W, qrot, qcode, dbg_qrot, dbg_qcode); break;
+      default: launch_kernel(prep_kernel<NB, KB, QB, 8>, grid, block, st, tm, s, c, k_new, v_new,
+                             q, R, W, qrot, qcode, dbg_qrot, dbg_qcode); break;
+    }
+  } else
     launch_kernel(prep_kernel<NB, KB, QB, 0>, grid, block, st, tm, s, c, k_new, v_new, q, R, W,
                   qrot, qcode, dbg_qrot, dbg_qcode);
 }
