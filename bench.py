@@ -116,7 +116,7 @@ def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
                 read and every candidate is written. Fine stage only: no U; every token is a
                 candidate.
     sparse_attn: K and V rows of the selected tokens (2 x d x 2 B per token and query head),
-                indices and q read, one (o, m, l) partial per 256 tokens written.
+                indices and q read, one (o, m, l) partial per 128 tokens written.
     combine:    the partials read, the output written.
     dense_attn: (dense baseline) K and V rows of every token once per KV head, q read, one
                 partial per split and query head written.
@@ -143,7 +143,8 @@ def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
         n_keep = P if variant == "codes" else min(P, max(1, math.ceil(cfg.keep_ratio * P)))
         ncand = min(n_keep * S, L)
         k = ncand if variant == "pages" else min(cfg.token_budget, ncand)
-        parts = Hq * -(-k // 256) * (d + 2) * 4
+        chunk = 128 if cfg.dtype == "bf16" else 64   # rows per attention workgroup
+        parts = Hq * -(-k // chunk) * (d + 2) * 4
         out["page_bound"] += Hkv * P * d * 2 * ex + Hs * P * 4
         if variant == "pages":
             out["select"] += Hq * (P * 4 + k * 4)

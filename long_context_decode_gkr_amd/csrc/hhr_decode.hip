@@ -710,7 +710,7 @@ struct AttnShape {
   static constexpr int EPL = BF16 ? 8 : 4;        // elements per lane per row
   static constexpr int LPR = kD / EPL;            // lanes per row
   static constexpr int RPI = kWave / LPR;         // rows per wave-wide load
-  static constexpr int ITER = 16;                 // loads per lane for K (and for V)
+  static constexpr int ITER = 8;                  // loads per lane for K (and for V)
   static constexpr int RPW = RPI * ITER;          // rows per wave
   static constexpr int CHUNK = 4 * RPW;           // rows per workgroup (4 waves)
 };

@@ -33,9 +33,9 @@ def test_byte_model_128k():
     assert a["page_bound"] == 8 * 8192 * 128 * 8 + 32 * 8192 * 4 + 32 * 128 * 4
     # U row, query code, 512 pages x 16 codes of 16 B, 4096 indices, per query head
     assert a["select"] == 32 * (8192 * 4 + 16 + 512 * 16 * 16 + 4096 * 4)
-    # 4096 K + V rows of 256 B each, indices, q, 16 partials of 130 floats, per query head
-    assert a["sparse_attn"] == 32 * (4096 * 512 + 4096 * 4 + 256 + 16 * 130 * 4)
-    assert a["combine"] == 32 * (16 * 130 * 4 + 128 * 4)
+    # 4096 K + V rows of 256 B each, indices, q, 32 partials of 130 floats, per query head
+    assert a["sparse_attn"] == 32 * (4096 * 512 + 4096 * 4 + 256 + 32 * 130 * 4)
+    assert a["combine"] == 32 * (32 * 130 * 4 + 128 * 4)
     # R and W (1 MiB) dominate the preparation; the append adds 1.28 KiB per KV head
     assert a["prep"] - bench.algorithmic_bytes(synth.CONFIGS[3], [131072], False)["prep"] \
         == 8 * (512 + 512 + 16 + 2048)
