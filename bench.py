@@ -86,7 +86,8 @@ VARIANTS = {
                      ("combine", 4)),
     "group-shared": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3),
                      ("combine", 4)),
-    "codes": (("prep", 0), ("select", 2), ("sparse_attn", 3), ("combine", 4)),
+    "codes": (("prep", 0), ("hamming_scan", 1), ("token_select", 2), ("sparse_attn", 3),
+              ("combine", 4)),
     "dense": (("dense_attn", 0), ("combine", 1)),
 }
 
@@ -149,14 +150,22 @@ def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
         if variant == "pages":
             out["select"] += Hq * (P * 4 + k * 4)
         elif variant == "codes":
-            out["select"] += Hq * (nb // 8 + ncand * (nb // 8) + k * 4)
+            # the scan: every token's code read once per query head, one distance byte (two for
+            # 256 bits) written, a histogram per slice; the selection reads the distances and
+            # the histograms, writes the indices
+            dbytes = 1 if nb == 128 else 2
+            hist = -(-L // 4096) * (nb + 1) * 4
+            out["hamming_scan"] = out.get("hamming_scan", 0) + Hq * (
+                nb // 8 + ncand * (nb // 8) + ncand * dbytes + hist)
+            out["token_select"] = out.get("token_select", 0) + Hq * (
+                ncand * dbytes + -(-L // 4096) * hist + k * 4)
         else:
             out["select"] += Hs * (P * 4 + n_keep * S * (nb // 8) + k * 4) + Hq * nb // 8
         # K and V rows: once per selection unit (a KV head's group shares its rows)
         out["sparse_attn"] += Hs * k * 2 * d * esz + Hq * (k * 4 + d * esz) + parts
         out["combine"] += parts + Hq * d * 4
     if variant == "codes":
-        del out["page_bound"]
+        del out["page_bound"], out["select"]
     return out
 
 

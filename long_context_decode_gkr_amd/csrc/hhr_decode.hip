@@ -142,32 +142,6 @@ page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) 
   }
 }
 
-// ---------------------------------------------------------------------------------------------
-// Block-wide scan for up to 1024 threads: DPP wave scans, then the wave totals through LDS,
-// scanned again by DPP in the first row of 16 lanes of every wave (one LDS read per lane).
-// The totals are double-buffered, so one barrier per scan suffices as long as consecutive scans
-// alternate buffers (the barrier of the scan in between orders the reuse).
-// ---------------------------------------------------------------------------------------------
-template <int NWV>
-struct BlockScan {
-  static_assert(NWV <= 16, "wave totals are scanned within one row of 16 lanes");
-  int (*wt)[NWV];
-  int buf;
-  // Exclusive prefix of v in thread order; *total gets the block sum.
-  __device__ __forceinline__ int excl(int v, int* total) {
-    const int incl = wave_incl_sum(v);
-    const int w = wave_id();
-    int* t = wt[buf];
-    buf ^= 1;
-    if (lane_id() == kWave - 1) t[w] = incl;
-    __syncthreads();
-    const int ts = row16_incl_sum(t[lane_id() % NWV]);   // lanes 0 .. NWV-1: prefix of totals
-    const int base = w > 0 ? __builtin_amdgcn_readlane(ts, w - 1) : 0;
-    *total = __builtin_amdgcn_readlane(ts, NWV - 1);
-    return base + incl - v;
-  }
-};
-
 // Order-preserving map of a bound to uint32 where SMALLER means LARGER U (so the kept pages are
 // the smallest keys); -0 and +0 map to the same key.
 __device__ __forceinline__ uint32_t desc_key(float u) {
@@ -969,6 +943,10 @@ DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages st
   p.off_idx = off;    off = align256(off + NU * p.istride * sizeof(int32_t));
   p.off_cnt = off;    off = align256(off + NU * sizeof(int32_t));
   p.off_part = off;   off = align256(off + BH * p.nsplit * (kD + 2) * sizeof(float));
+  if (stages == Stages::kCodesOnly) {   // distances and per-slice histograms of the scan
+    p.off_dist = off;  off = align256(off + NU * s.Lmax * (s.NB == 128 ? 1 : 2));
+    p.off_hist = off;  off = align256(off + NU * scan_slices(s) * (s.NB + 1) * sizeof(int32_t));
+  }
   p.total = off;
   return p;
 }
@@ -1042,11 +1020,19 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
     }
     HHR_CHECK();
   }
-  SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap, p.istride, k_new != nullptr ? 1 : 0,
-                p.stages == Stages::kPagesOnly ? 0 : 1};
-  if (s.NB == 128) launch_select_nb<128>(s, c, sa, dbg, p.shared, st);
-  else launch_select_nb<256>(s, c, sa, dbg, p.shared, st);
-  HHR_CHECK();
+  if (p.stages == Stages::kCodesOnly) {
+    // every token is a candidate: the scan spread over slices of the context
+    ScanArgs sc{qcode, base + p.off_dist, reinterpret_cast<int32_t*>(base + p.off_hist), idx, cnt,
+                p.kcap, p.istride, scan_slices(s), k_new != nullptr ? 1 : 0, p.shared};
+    e = launch_scan_select(s, c, sc, dbg, st);
+    if (e != hipSuccess) return e;
+  } else {
+    SelectArgs sa{qcode, U, idx, cnt, p.rho, p.kcap, p.istride, k_new != nullptr ? 1 : 0,
+                  p.stages == Stages::kPagesOnly ? 0 : 1};
+    if (s.NB == 128) launch_select_nb<128>(s, c, sa, dbg, p.shared, st);
+    else launch_select_nb<256>(s, c, sa, dbg, p.shared, st);
+    HHR_CHECK();
+  }
   AttnArgs aa{idx, cnt, part, p.kcap, p.istride, p.nsplit, p.shared,
               p.scale * 1.4426950408889634f};
   dim3 grid(p.nsplit, s.Hq, s.B);

@@ -304,4 +304,30 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// ---------------------------------------------------------------------------------------------
+// Block-wide scan for up to 1024 threads: DPP wave scans, then the wave totals through LDS,
+// scanned again by DPP in the first row of 16 lanes of every wave (one LDS read per lane).
+// The totals are double-buffered, so one barrier per scan suffices as long as consecutive scans
+// alternate buffers (the barrier of the scan in between orders the reuse).
+// ---------------------------------------------------------------------------------------------
+template <int NWV>
+struct BlockScan {
+  static_assert(NWV <= 16, "wave totals are scanned within one row of 16 lanes");
+  int (*wt)[NWV];
+  int buf;
+  // Exclusive prefix of v in thread order; *total gets the block sum.
+  __device__ __forceinline__ int excl(int v, int* total) {
+    const int incl = wave_incl_sum(v);
+    const int w = wave_id();
+    int* t = wt[buf];
+    buf ^= 1;
+    if (lane_id() == kWave - 1) t[w] = incl;
+    __syncthreads();
+    const int ts = row16_incl_sum(t[lane_id() % NWV]);   // lanes 0 .. NWV-1: prefix of totals
+    const int base = w > 0 ? __builtin_amdgcn_readlane(ts, w - 1) : 0;
+    *total = __builtin_amdgcn_readlane(ts, NWV - 1);
+    return base + incl - v;
+  }
+};
+
 }  // namespace hhr

@@ -67,7 +67,7 @@ struct DecodePlan {
   int nsplit;      // attention workgroups per (b, h)
   double rho;
   float scale;
-  size_t off_qrot, off_qcode, off_U, off_idx, off_cnt, off_part, total;
+  size_t off_qrot, off_qcode, off_U, off_idx, off_cnt, off_part, off_dist, off_hist, total;
 };
 
 DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages stages,
@@ -88,6 +88,21 @@ hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, co
                        const void* q, const float* R, const float* W, float* qrot,
                        uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, PrepMode mode,
                        KernelTimer tm, hipStream_t st);
+// Fine stage over every token (fine-stage-only variant): distances and per-slice histograms,
+// then the threshold and the ordered emission of the selected tokens, kScanTok tokens per
+// workgroup in both kernels.
+constexpr int kScanTok = 4096;
+struct ScanArgs {
+  const uint32_t* qcode;  // [B][Hq][NW]
+  void* dist;             // [units][Lmax]: one byte per distance (two for 256-bit codes)
+  int32_t* hist;          // [units][nsl][NB + 1]
+  int32_t* idx;           // [units][istride]
+  int32_t* cnt;           // [units]
+  int kcap, istride, nsl, appended, shared;
+};
+int scan_slices(const Shape& s);
+hipError_t launch_scan_select(const Shape& s, const CacheView& c, const ScanArgs& a,
+                              const DebugView& dbg, hipStream_t st);
 // Merge of split-K attention partials [B][Hq][nsplit][128 + 2] (o, m, l) into out
 // [B][Hq][128]; with `appended` it also advances seq_lens (the sparse step's last kernel).
 hipError_t launch_combine(const Shape& s, const float* part, int nsplit, float* out,

@@ -143,7 +143,8 @@ def test_pages_only_workspace_holds_every_kept_token():
                                                        hb.HHR_STAGES_CODES_ONLY))
     # pages only: 512 kept pages x 16 tokens = 8192 indices per head instead of 4096
     assert pages >= both + 32 * 4096 * 4
-    assert codes == both
+    # fine only: plus the distances of every token (one byte each) and the slice histograms
+    assert codes >= both + 32 * 131072 and codes <= both + 32 * 131072 + 32 * 32 * 129 * 4 + 512
 
 
 def dense_status(dims=None, cache=None, q=FAKE, scale=0.0, ws=FAKE * 256, ws_bytes=1 << 40,

@@ -65,9 +65,9 @@ def test_byte_model_of_the_variants():
     # coarse stage alone: no codes read, all 512 x 16 candidates attended
     assert pages["select"] == 32 * (8192 * 4 + 8192 * 4)
     assert pages["sparse_attn"] > 2 * base["sparse_attn"] - 32 * 4096 * 8
-    # fine stage alone: no bound kernel, every token's code read
-    assert "page_bound" not in codes
-    assert codes["select"] == 32 * (16 + 131072 * 16 + 4096 * 4)
+    # fine stage alone: no bound kernel, every token's code read by the scan
+    assert "page_bound" not in codes and "select" not in codes
+    assert codes["hamming_scan"] == 32 * (16 + 131072 * 16 + 131072 + 32 * 129 * 4)
     assert codes["sparse_attn"] == base["sparse_attn"]
     dense = bench.algorithmic_bytes(cfg, [131072], False, "dense", 131072)
     # every K and V row once per KV head (512 MiB) dominates
