@@ -539,3 +539,53 @@ def test_group_shared_selection_matches_oracle(stages, cfg_id, L, batch, lens, r
     out, dbg = lay.decode(rho, k, stages=stages, group_shared=True)
     st = hc.check_decode_shared(lay, out, dbg, rho, k, ref_index=ref, stages=stages)
     print(f"shared {stages} cfg{cfg_id}: max out rel err {st['max_out_rel']:.2e}, swaps {st['swaps']}")
+
+
+# ---------------------------------------------------------------------------------------------
+# Group sizes other than 4 and 1, and the page capacity
+# ---------------------------------------------------------------------------------------------
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 4)])     # G = 2, G = 8
+@pytest.mark.parametrize("group_shared", [False, True])
+def test_decode_other_group_sizes(hq, hkv, group_shared):
+    _torch()
+    cfg = _cfg(2, 2500, num_q_heads=hq, num_kv_heads=hkv, n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=2560)
+    lay.build()
+    ref = hc.oracle_index(lay)
+    hc.check_index(lay, ref, extrema_atol_scale=20.0)
+    out, dbg = lay.decode(0.15, 150, group_shared=group_shared)
+    if group_shared:
+        hc.check_decode_shared(lay, out, dbg, 0.15, 150, ref_index=ref)
+    else:
+        hc.check_decode(lay, out, dbg, 0.15, 150, ref_index=ref)
+
+
+@pytest.mark.parametrize("hq,hkv", [(16, 8), (32, 4)])
+def test_dense_decode_other_group_sizes(hq, hkv):
+    torch = _torch()
+    cfg = _cfg(2, 1800, num_q_heads=hq, num_kv_heads=hkv, n_plant=2)
+    lay = hc.GpuLayer(cfg, max_seq_len=1856)
+    dd = hb.DenseDecoder(lay.dims)
+    out = torch.full((1, hq, 128), float("nan"), dtype=torch.float32, device="cuda")
+    dd(lay.cache, lay.q, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    d, G = lay.data, hq // hkv
+    for h in range(hq):
+        ref = orc.dense_head(d["q"][0, h], d["K"][0, h // G], d["V"][0, h // G], 1800,
+                             orc.default_scale(128))
+        assert np.abs(got[0, h] - ref).max() / np.abs(ref).max() <= hc.OUT_RTOL, h
+
+
+def test_decode_at_the_page_capacity():
+    """16384 pages (the documented maximum) of 16 tokens: 16 pages per selection thread."""
+    _torch()
+    L = hb.HHR_MAX_PAGES * 16
+    cfg = _cfg(2, L, num_q_heads=2, num_kv_heads=1, n_plant=8)
+    lay = hc.GpuLayer(cfg, max_seq_len=L, lens=[L - 11])
+    lay.build()
+    ref = hc.oracle_index(lay)
+    hc.check_index(lay, ref, extrema_atol_scale=20.0)
+    out, dbg = lay.decode(1 / 32, 2048)
+    st = hc.check_decode(lay, out, dbg, 1 / 32, 2048, ref_index=ref)
+    print(f"capacity: max out rel err {st['max_out_rel']:.2e}, swaps {st['swaps']}")
