@@ -48,6 +48,9 @@ struct BoundArgs {
   int shared;             // one selection per KV head: U of a page = max over its G heads
 };
 
+typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
 template <int G, int SB>   // SB: extrema stored as bf16
 __global__ void __launch_bounds__(kBoundThreads)
 page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) {
@@ -66,20 +69,23 @@ page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) 
   float4 lo[16], hi[16];
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) {
+    // non-temporal loads: the extrema are read once per step (measured 14.6 -> 13.8 us at 128K)
     if constexpr (SB) {
-      const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(c.pmin) +
-                                                      (srow + jj) * s.Pmax + plc);
-      const uint2 y = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(c.pmax) +
-                                                      (srow + jj) * s.Pmax + plc);
+      const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
+          static_cast<const uint16_t*>(c.pmin) + (srow + jj) * s.Pmax + plc));
+      const u32x2 y = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
+          static_cast<const uint16_t*>(c.pmax) + (srow + jj) * s.Pmax + plc));
       lo[jj] = make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u),
                            __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xFFFF0000u));
       hi[jj] = make_float4(__uint_as_float(y.x << 16), __uint_as_float(y.x & 0xFFFF0000u),
                            __uint_as_float(y.y << 16), __uint_as_float(y.y & 0xFFFF0000u));
     } else {
-      lo[jj] = *reinterpret_cast<const float4*>(static_cast<const float*>(c.pmin) +
-                                                (srow + jj) * s.Pmax + plc);
-      hi[jj] = *reinterpret_cast<const float4*>(static_cast<const float*>(c.pmax) +
-                                                (srow + jj) * s.Pmax + plc);
+      const f32x4v x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(
+          static_cast<const float*>(c.pmin) + (srow + jj) * s.Pmax + plc));
+      const f32x4v y = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(
+          static_cast<const float*>(c.pmax) + (srow + jj) * s.Pmax + plc));
+      lo[jj] = make_float4(x.x, x.y, x.z, x.w);
+      hi[jj] = make_float4(y.x, y.y, y.z, y.w);
     }
   }
   const float* qb = a.qrot + (size_t(b) * s.Hq + size_t(g) * G) * kD + j0;
