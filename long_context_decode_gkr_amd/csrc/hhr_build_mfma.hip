@@ -44,13 +44,13 @@ struct Bf16Row {
 template <int S>
 __global__ void __launch_bounds__(kMThreads)
 build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float* __restrict__ W,
-                  int ntiles) {
-  const int role = blockIdx.x / ntiles, tile = blockIdx.x % ntiles;
+                  int ntiles, int nper) {
+  // workgroup (role, first) stages its role's B operand once, then builds tiles first,
+  // first + nper, ... of the sequence
+  const int role = blockIdx.x / nper, first = blockIdx.x % nper;
   const int g = blockIdx.y, b = blockIdx.z;
   const int L = min(max(c.seq_lens[b], 0), s.Lmax);
-  const int t0 = tile * kMTok;
-  if (t0 >= L) return;
-  const int ntok = min(kMTok, L - t0);
+  if (first * kMTok >= L) return;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
   const int npieces = role == 0 ? 3 : 2;
 
@@ -99,7 +99,6 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
     ss = fmaf(x0, x0, fmaf(x1, x1, ss));
   }
   wpart[tid] = ss;
-  if (tid == 0) fb_n = 0;
   __syncthreads();
   // |w_c| from fp32 sums of squares (relative error below 2^-16), rounded up by 2^-14
   if (role != 0 && tid < kD) {
@@ -114,147 +113,155 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(c.K);
   const int half = lane >> 5, col = lane & 31;
 
-  // A fragments of a sub-tile: row tl0 + col, k = 16 ks + 8 half + 0..7 (rows past the end
-  // read the last valid row).
-  auto load_a = [&](int tl0, bf16x8 (&a)[8]) {
-    const int trc = min(t0 + tl0 + col, L - 1);
-    const uint4* ap = reinterpret_cast<const uint4*>(Kb + (row0 + trc) * kD + 8 * half);
+  for (int tile = first; tile < ntiles; tile += nper) {
+    const int t0 = tile * kMTok;
+    if (t0 >= L) break;
+    const int ntok = min(kMTok, L - t0);
+    if (tid == 0) fb_n = 0;
+    __syncthreads();
+    // A fragments of a sub-tile: row tl0 + col, k = 16 ks + 8 half + 0..7 (rows past the end
+    // read the last valid row).
+    auto load_a = [&](int tl0, bf16x8 (&a)[8]) {
+      const int trc = min(t0 + tl0 + col, L - 1);
+      const uint4* ap = reinterpret_cast<const uint4*>(Kb + (row0 + trc) * kD + 8 * half);
 #pragma unroll
-    for (int ks = 0; ks < 8; ++ks) a[ks] = __builtin_bit_cast(bf16x8, ap[2 * ks]);
-  };
-  constexpr int kStep = kMThreads / kWave;   // sub-tiles between a wave's consecutive ones
-  for (int st = w; st < kMTok / 32; st += kStep) {
-    const int tl0 = st * 32;                 // first token of the sub-tile (block-local)
-    if (tl0 >= ntok) break;
-    bf16x8 a[8];
-    load_a(tl0, a);
-    f32x16 acc[4];
+      for (int ks = 0; ks < 8; ++ks) a[ks] = __builtin_bit_cast(bf16x8, ap[2 * ks]);
+    };
+    constexpr int kStep = kMThreads / kWave;   // sub-tiles between a wave's consecutive ones
+    for (int st = w; st < kMTok / 32; st += kStep) {
+      const int tl0 = st * 32;                 // first token of the sub-tile (block-local)
+      if (tl0 >= ntok) break;
+      bf16x8 a[8];
+      load_a(tl0, a);
+      f32x16 acc[4];
 #pragma unroll
-    for (int nt = 0; nt < 4; ++nt)
+      for (int nt = 0; nt < 4; ++nt)
 #pragma unroll
-      for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
-    for (int p = 0; p < npieces; ++p) {
+        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
+      for (int p = 0; p < npieces; ++p) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) {
+        for (int ks = 0; ks < 8; ++ks) {
+#pragma unroll
+          for (int nt = 0; nt < 4; ++nt) {
+            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Bt[p][nt * 32 + col][16 * ks + 8 * half]);
+            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bv, acc[nt], 0, 0, 0);
+          }
+        }
+      }
+      // result rows of this lane: i(r) = 8 (r / 4) + 4 half + r % 4
+      if (role == 0) {
+        // ---- page extrema of k~ over the valid rows (pages are 16 or 32 rows of the sub-tile)
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
-          const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Bt[p][nt * 32 + col][16 * ks + 8 * half]);
-          acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bv, acc[nt], 0, 0, 0);
-        }
-      }
-    }
-    // result rows of this lane: i(r) = 8 (r / 4) + 4 half + r % 4
-    if (role == 0) {
-      // ---- page extrema of k~ over the valid rows (pages are 16 or 32 rows of the sub-tile)
+          const int j = nt * 32 + col;
+          constexpr int PPS = 32 / S;            // pages per sub-tile
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int j = nt * 32 + col;
-        constexpr int PPS = 32 / S;            // pages per sub-tile
+          for (int pp = 0; pp < PPS; ++pp) {
+            float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
-        for (int pp = 0; pp < PPS; ++pp) {
-          float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-          for (int r = pp * (16 / PPS); r < (pp + 1) * (16 / PPS); ++r) {
-            const int i = 8 * (r / 4) + 4 * half + (r % 4);
-            if (tl0 + i < ntok) {
-              lo = fminf(lo, acc[nt][r]);
-              hi = fmaxf(hi, acc[nt][r]);
+            for (int r = pp * (16 / PPS); r < (pp + 1) * (16 / PPS); ++r) {
+              const int i = 8 * (r / 4) + 4 * half + (r % 4);
+              if (tl0 + i < ntok) {
+                lo = fminf(lo, acc[nt][r]);
+                hi = fmaxf(hi, acc[nt][r]);
+              }
+            }
+            lo = fminf(lo, __shfl_xor(lo, 32));
+            hi = fmaxf(hi, __shfl_xor(hi, 32));
+            if (half == 0) {
+              stage_f[0][j][tl0 / S + pp] = lo;
+              stage_f[1][j][tl0 / S + pp] = hi;
             }
           }
-          lo = fminf(lo, __shfl_xor(lo, 32));
-          hi = fmaxf(hi, __shfl_xor(hi, 32));
-          if (half == 0) {
-            stage_f[0][j][tl0 / S + pp] = lo;
-            stage_f[1][j][tl0 / S + pp] = hi;
+        }
+      } else {
+        // ---- code bits: certified sign of z, or queued for the exact path
+        float xn2 = 0.f;
+#pragma unroll
+        for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+          for (int e = 0; e < 8; ++e) {
+            const float v = float(a[ks][e]);
+            xn2 = fmaf(v, v, xn2);
+          }
+        xn2 += __shfl_xor(xn2, 32);
+        const float xnorm = sqrtf(xn2) * (1.0f + 1e-6f);   // |k_row|, row = tl0 + col
+        float xr[16];                                      // |k| of the rows of acc[.][r]
+#pragma unroll
+        for (int r = 0; r < 16; ++r) xr[r] = __shfl(xnorm, 8 * (r / 4) + 4 * half + (r % 4));
+#pragma unroll
+        for (int nt = 0; nt < 4; ++nt) {
+          const int lc = nt * 32 + col;                    // code column within the slice
+          const float wn = wnorm[lc];
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const int i = 8 * (r / 4) + 4 * half + (r % 4);
+            const float xi = xr[r];
+            const float tau = kCertScale * xi * wn;
+            const float z = acc[nt][r];
+            const bool valid = tl0 + i < ntok;
+            const bool sure = fabsf(z) > tau && xi * wn > 1e-30f;
+            bool bit = z > 0.f;
+            if (valid && !sure) {
+              // queued for the exact path (past the capacity only counted: see below)
+              const int pos = atomicAdd(&fb_n, 1);
+              if (pos < kFbCap) fb_list[pos] = (uint32_t(tl0 + i) << 8) | uint32_t(lc);
+            }
+            const uint64_t m = __ballot(bit);
+            if (lane == 0) {
+              // bits 0..31 of the ballot are row i(r) of half 0, bits 32..63 row i(r) + 4
+              const int i0 = 8 * (r / 4) + (r % 4);
+              stage_c[tl0 + i0][nt] = uint32_t(m);
+              stage_c[tl0 + i0 + 4][nt] = uint32_t(m >> 32);
+            }
           }
         }
-      }
-    } else {
-      // ---- code bits: certified sign of z, or queued for the exact path
-      float xn2 = 0.f;
-#pragma unroll
-      for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const float v = float(a[ks][e]);
-          xn2 = fmaf(v, v, xn2);
-        }
-      xn2 += __shfl_xor(xn2, 32);
-      const float xnorm = sqrtf(xn2) * (1.0f + 1e-6f);   // |k_row|, row = tl0 + col
-      float xr[16];                                      // |k| of the rows of acc[.][r]
-#pragma unroll
-      for (int r = 0; r < 16; ++r) xr[r] = __shfl(xnorm, 8 * (r / 4) + 4 * half + (r % 4));
-#pragma unroll
-      for (int nt = 0; nt < 4; ++nt) {
-        const int lc = nt * 32 + col;                    // code column within the slice
-        const float wn = wnorm[lc];
-#pragma unroll
-        for (int r = 0; r < 16; ++r) {
-          const int i = 8 * (r / 4) + 4 * half + (r % 4);
-          const float xi = xr[r];
-          const float tau = kCertScale * xi * wn;
-          const float z = acc[nt][r];
-          const bool valid = tl0 + i < ntok;
-          const bool sure = fabsf(z) > tau && xi * wn > 1e-30f;
-          bool bit = z > 0.f;
-          if (valid && !sure) {
-            // queued for the exact path (past the capacity only counted: see below)
-            const int pos = atomicAdd(&fb_n, 1);
-            if (pos < kFbCap) fb_list[pos] = (uint32_t(tl0 + i) << 8) | uint32_t(lc);
-          }
-          const uint64_t m = __ballot(bit);
-          if (lane == 0) {
-            // bits 0..31 of the ballot are row i(r) of half 0, bits 32..63 row i(r) + 4
-            const int i0 = 8 * (r / 4) + (r % 4);
-            stage_c[tl0 + i0][nt] = uint32_t(m);
-            stage_c[tl0 + i0 + 4][nt] = uint32_t(m >> 32);
-          }
-        }
-      }
-    }
-  }
-  __syncthreads();
-
-  if (role == 0) {
-    // ---- write the page extrema: channel-major rows of this tile's pages
-    const int npg = (ntok + S - 1) / S;
-    const int pg0 = t0 / S;
-    const size_t sbase = (size_t(b) * s.Hkv + g) * kD;
-    for (int e = tid; e < kD * npg; e += kMThreads) {
-      const int j = e / npg, pl = e % npg;
-      store_extrema(s, c, (sbase + j) * s.Pmax + pg0 + pl, stage_f[0][j][pl], stage_f[1][j][pl]);
-    }
-  } else {
-    // ---- exact path for the queued bits, then the code words. If more bits were uncertain
-    // than the queue holds (degenerate projections), every word of the tile is recomputed from
-    // the stored operands instead: slow, and only for such inputs.
-    const float* wbase_p = W + size_t(g) * kD * s.NB + (role - 1) * kD;
-    if (fb_n <= kFbCap) {
-      for (int e = tid; e < fb_n; e += kMThreads) {
-        const uint32_t ent = fb_list[e];
-        const int tl = int(ent >> 8), lc = int(ent & 0xFFu);
-        const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
-        const uint32_t bit = certified_bit(Bf16Row{kr}, wbase_p + lc, s.NB);
-        const uint32_t mask = 1u << (lc & 31);
-        if (bit) atomicOr(&stage_c[tl][lc >> 5], mask);
-        else atomicAnd(&stage_c[tl][lc >> 5], ~mask);
-      }
-    } else {
-      for (int e = tid; e < ntok * 4; e += kMThreads) {
-        const int tl = e >> 2, wd = e & 3;
-        const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
-        uint32_t word = 0;
-        for (int i = 0; i < 32; ++i)
-          word |= certified_bit(Bf16Row{kr}, wbase_p + 32 * wd + i, s.NB) << i;
-        stage_c[tl][wd] = word;
       }
     }
     __syncthreads();
-    const int wbase = (role - 1) * 4;
-    for (int tl = tid; tl < ntok; tl += kMThreads) {
-      const uint4 v = make_uint4(stage_c[tl][0], stage_c[tl][1], stage_c[tl][2], stage_c[tl][3]);
-      *reinterpret_cast<uint4*>(c.codes + (row0 + t0 + tl) * s.NW + wbase) = v;
+
+    if (role == 0) {
+      // ---- write the page extrema: channel-major rows of this tile's pages
+      const int npg = (ntok + S - 1) / S;
+      const int pg0 = t0 / S;
+      const size_t sbase = (size_t(b) * s.Hkv + g) * kD;
+      for (int e = tid; e < kD * npg; e += kMThreads) {
+        const int j = e / npg, pl = e % npg;
+        store_extrema(s, c, (sbase + j) * s.Pmax + pg0 + pl, stage_f[0][j][pl], stage_f[1][j][pl]);
+      }
+    } else {
+      // ---- exact path for the queued bits, then the code words. If more bits were uncertain
+      // than the queue holds (degenerate projections), every word of the tile is recomputed from
+      // the stored operands instead: slow, and only for such inputs.
+      const float* wbase_p = W + size_t(g) * kD * s.NB + (role - 1) * kD;
+      if (fb_n <= kFbCap) {
+        for (int e = tid; e < fb_n; e += kMThreads) {
+          const uint32_t ent = fb_list[e];
+          const int tl = int(ent >> 8), lc = int(ent & 0xFFu);
+          const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
+          const uint32_t bit = certified_bit(Bf16Row{kr}, wbase_p + lc, s.NB);
+          const uint32_t mask = 1u << (lc & 31);
+          if (bit) atomicOr(&stage_c[tl][lc >> 5], mask);
+          else atomicAnd(&stage_c[tl][lc >> 5], ~mask);
+        }
+      } else {
+        for (int e = tid; e < ntok * 4; e += kMThreads) {
+          const int tl = e >> 2, wd = e & 3;
+          const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
+          uint32_t word = 0;
+          for (int i = 0; i < 32; ++i)
+            word |= certified_bit(Bf16Row{kr}, wbase_p + 32 * wd + i, s.NB) << i;
+          stage_c[tl][wd] = word;
+        }
+      }
+      __syncthreads();
+      const int wbase = (role - 1) * 4;
+      for (int tl = tid; tl < ntok; tl += kMThreads) {
+        const uint4 v = make_uint4(stage_c[tl][0], stage_c[tl][1], stage_c[tl][2], stage_c[tl][3]);
+        *reinterpret_cast<uint4*>(c.codes + (row0 + t0 + tl) * s.NW + wbase) = v;
+      }
     }
+    __syncthreads();   // this tile's LDS staging is read out before the next tile reuses it
   }
 }
 
@@ -262,11 +269,17 @@ hipError_t launch_build_mfma(const Shape& s, const CacheView& c, const float* R,
                              hipStream_t st) {
   const int ntiles = (s.Lmax + kMTok - 1) / kMTok;
   const int nroles = 1 + s.NB / kD;
-  dim3 grid(ntiles * nroles, s.Hkv, s.B);
+  // about 1024 workgroups (4 per CU): each stages its B operand once for ntiles / nper tiles
+  const long long units = (long long)nroles * s.Hkv * s.B;
+  int nper = int((1024 + units - 1) / units);
+  nper = nper < 1 ? 1 : (nper > ntiles ? ntiles : nper);
+  dim3 grid(nper * nroles, s.Hkv, s.B);
   if (s.S == 16)
-    hipLaunchKernelGGL((build_mfma_kernel<16>), grid, dim3(kMThreads), 0, st, s, c, R, W, ntiles);
+    hipLaunchKernelGGL((build_mfma_kernel<16>), grid, dim3(kMThreads), 0, st, s, c, R, W, ntiles,
+                       nper);
   else
-    hipLaunchKernelGGL((build_mfma_kernel<32>), grid, dim3(kMThreads), 0, st, s, c, R, W, ntiles);
+    hipLaunchKernelGGL((build_mfma_kernel<32>), grid, dim3(kMThreads), 0, st, s, c, R, W, ntiles,
+                       nper);
   return hipGetLastError();
 }
 
