@@ -23,7 +23,9 @@ each W warm-up steps then exactly K timed steps bracketed by torch.cuda.synchron
 The index builder (MFMA path) is timed once over every key of the first layer instance, and the
 dense baseline (full attention over every token, hhr_dense_decode) on the same layer instances,
 for the same-hardware speedup of the sparse step over full attention (dense_us_per_step,
-speedup_vs_dense).
+speedup_vs_dense). read_ceiling is the practical rate of one read pass over the dominant
+kernel's byte count on this GPU (hhr_read_probe: the same loads and nothing else, timed the same
+way), the yardstick for how much of the HBM peak a single launch of that size can reach.
 
 --variant times another configuration of the same workload: the coarse stage alone (pages:
 every token of the kept pages is attended), the fine stage alone (codes: Hamming top-k over
@@ -220,6 +222,36 @@ def time_builder(hb, cache, R, W, cfg, lens, quiet, reps=5):
             "useful_TFLOPs": round(useful / t / 1e12, 2),
             "mfma_TFLOPs": round(executed / t / 1e12, 2), "mfma_peak_TFLOPs": 2500.0,
             "mfma_frac": round(executed / t / 1e12 / 2500.0, 4), "dtype": "bf16 MFMA, fp32 acc"}
+
+
+def read_ceiling(hb, nbytes, quiet, reps=48):
+    """The practical one-pass read rate for `nbytes` on this GPU: hhr_read_probe (the page-bound
+    kernel's loads, nothing else) over buffers of that size, each launch timed with HIP events
+    on the same stream as the decode kernels. The buffers rotate so that together they exceed
+    the last-level cache (256 MB on MI355X) and every launch reads HBM."""
+    import torch
+    nbytes = -(-int(nbytes) // 16) * 16
+    nbuf = max(2, min(8, -(-(1 << 30) // nbytes)))
+    bufs = [torch.empty(nbytes // 4, dtype=torch.float32, device="cuda").normal_()
+            for _ in range(nbuf)]
+    partial = torch.empty(hb.hhr_read_probe_blocks(nbytes), dtype=torch.float32, device="cuda")
+    stream = hb.current_stream()
+    ev = hb.HipEvents(2)
+    for i in range(2 * nbuf):
+        hb.hhr_read_probe(bufs[i % nbuf].data_ptr(), nbytes, partial.data_ptr(), stream)
+    torch.cuda.synchronize()
+    us = []
+    for i in range(reps):
+        ev.record(0, stream)
+        hb.hhr_read_probe(bufs[i % nbuf].data_ptr(), nbytes, partial.data_ptr(), stream)
+        ev.record(1, stream)
+        torch.cuda.synchronize()
+        us.append(ev.elapsed_ms(0, 1) * 1e3)
+    ev.close()
+    avg = sum(us) / len(us)
+    log(f"read probe: {nbytes} bytes in {avg:.2f} us on average", quiet)
+    return {"bytes": nbytes, "buffers": nbuf, "avg_us": round(avg, 2),
+            "p50_us": round(sorted(us)[len(us) // 2], 2), "GBps": round(nbytes / avg / 1e3, 1)}
 
 
 def cpu_baseline(cfg, data, append, quiet, budget_s=10.0):
@@ -566,6 +598,8 @@ def main():
     dominant = max(cands, key=lambda n: avg_ms[n])
     traffic = load_traffic(args.workload, dominant) if variant in ("hhr", "dense") else None
     achieved = alg[dominant] / (avg_ms[dominant] * 1e-3) / 1e9
+    ceiling = read_ceiling(hb, alg[dominant], q)
+    ceiling["kernel_frac"] = round(achieved / ceiling["GBps"], 4)
     step_bytes = sum(alg.values())
     us = ms_step * 1e3
     if args.workload == DEFAULT_WORKLOAD and variant == "hhr":
@@ -603,6 +637,7 @@ def main():
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic},
+        "read_ceiling": ceiling,
         "kernels": kern,
         "builder": builder,
         "dense_us_per_step": None if dense_ms is None else round(dense_ms * 1e3, 2),

@@ -229,6 +229,16 @@ hhr_status hhr_dense_decode(const hhr_dims* dims, const hhr_cache* cache, const 
                             float softmax_scale, void* ws, size_t ws_bytes, float* out,
                             const hhr_debug* dbg, hhr_stream_t stream);
 
+/* Measurement aid, no step of the method: the practical one-pass read rate of device memory,
+ * against which the HBM-bound kernels above are judged (a single launch pays its ramp-up and
+ * drain, so it cannot reach the HBM peak). Reads the `bytes` bytes at src once with the page-
+ * bound kernel's load width and cache policy (16-byte non-temporal loads) and writes, for each
+ * block of 32 KiB (the last one partial), the fp32 sum of the floats it read to partial[i],
+ * i < hhr_read_probe_blocks(bytes). src: device, 16-byte aligned; bytes: a nonzero multiple of
+ * 16 (else HHR_ERR_INVALID_ARG); partial: device, caller-owned. Nothing else is written. */
+size_t hhr_read_probe_blocks(size_t bytes);
+hhr_status hhr_read_probe(const void* src, size_t bytes, float* partial, hhr_stream_t stream);
+
 /* Static text for a status code. */
 const char* hhr_status_string(hhr_status status);
 

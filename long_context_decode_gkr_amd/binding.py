@@ -24,7 +24,7 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or type",
 # Every exported symbol of include/hhr.h.
 EXPORTS = ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode_workspace_bytes",
            "hhr_decode", "hhr_append_decode", "hhr_dense_workspace_bytes", "hhr_dense_decode",
-           "hhr_status_string")
+           "hhr_read_probe_blocks", "hhr_read_probe", "hhr_status_string")
 
 
 class Dims(ctypes.Structure):
@@ -91,10 +91,13 @@ def load() -> ctypes.CDLL:
     lib.hhr_dense_workspace_bytes.restype = ctypes.c_size_t
     lib.hhr_dense_decode.argtypes = [P(Dims), P(CacheStruct), vp, ctypes.c_float, vp,
                                      ctypes.c_size_t, vp, P(DebugStruct), vp]
+    lib.hhr_read_probe_blocks.argtypes = [ctypes.c_size_t]
+    lib.hhr_read_probe_blocks.restype = ctypes.c_size_t
+    lib.hhr_read_probe.argtypes = [vp, ctypes.c_size_t, vp, vp]
     lib.hhr_status_string.argtypes = [ctypes.c_int]
     lib.hhr_status_string.restype = ctypes.c_char_p
     for fn in ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode",
-               "hhr_append_decode", "hhr_dense_decode"):
+               "hhr_append_decode", "hhr_dense_decode", "hhr_read_probe"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -135,6 +138,14 @@ def hhr_append_decode(dims: Dims, params: Params, cache: CacheStruct, k_new: int
     _check("hhr_append_decode", load().hhr_append_decode(
         ctypes.byref(dims), ctypes.byref(params), ctypes.byref(cache), k_new, v_new, q, R, W, ws,
         ws_bytes, out, ctypes.byref(dbg) if dbg is not None else None, stream))
+
+
+def hhr_read_probe_blocks(nbytes: int) -> int:
+    return int(load().hhr_read_probe_blocks(nbytes))
+
+
+def hhr_read_probe(src: int, nbytes: int, partial: int, stream: int = 0) -> None:
+    _check("hhr_read_probe", load().hhr_read_probe(src, nbytes, partial, stream))
 
 
 def hhr_dense_workspace_bytes(dims: Dims) -> int:

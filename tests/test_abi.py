@@ -196,3 +196,14 @@ def test_group_shared_workspace_is_smaller():
     per_head = hb.hhr_decode_workspace_bytes(d, hb.Params(1 / 16, 4096, 0.0, 0, 0))
     shared = hb.hhr_decode_workspace_bytes(d, hb.Params(1 / 16, 4096, 0.0, 0, 1))
     assert 0 < shared < per_head
+
+
+def test_read_probe_blocks_and_validation():
+    lib = hb.load()
+    assert hb.hhr_read_probe_blocks(16) == 1
+    assert hb.hhr_read_probe_blocks(32768) == 1
+    assert hb.hhr_read_probe_blocks(32768 + 16) == 2
+    assert hb.hhr_read_probe_blocks(68 * 1000 * 1000) == -(-68 * 1000 * 1000 // 32768)
+    for src, nbytes, partial in [(None, 4096, FAKE), (FAKE, 4096, None), (FAKE, 0, FAKE),
+                                 (FAKE, 4100, FAKE), (FAKE + 4, 4096, FAKE)]:
+        assert lib.hhr_read_probe(src, nbytes, partial, None) == 1

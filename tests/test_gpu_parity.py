@@ -589,3 +589,28 @@ def test_decode_at_the_page_capacity():
     out, dbg = lay.decode(1 / 32, 2048)
     st = hc.check_decode(lay, out, dbg, 1 / 32, 2048, ref_index=ref)
     print(f"capacity: max out rel err {st['max_out_rel']:.2e}, swaps {st['swaps']}")
+
+
+@pytest.mark.parametrize("nbytes", [16, 4096, 32768, 32768 * 3 + 48, 68 * 1000 * 1000])
+def test_read_probe_sums_what_it_reads(nbytes):
+    """The read-rate probe reads every byte once: its per-block sums match numpy's (fp64) over
+    the same floats, including a ragged last block; a guard word past the end is not read."""
+    torch = _torch()
+    n = nbytes // 4
+    rng = np.random.default_rng(nbytes)
+    host = rng.standard_normal(n + 4).astype(np.float32)
+    host[n:] = np.float32(1e30)          # beyond `nbytes`: would dominate any sum that read it
+    x = torch.from_numpy(host).to("cuda")
+    nb = hb.hhr_read_probe_blocks(nbytes)
+    partial = torch.full((nb + 1,), -7.0, dtype=torch.float32, device="cuda")
+    hb.hhr_read_probe(x.data_ptr(), nbytes, partial.data_ptr(),
+                      torch.cuda.current_stream().cuda_stream)
+    got = partial.cpu().numpy()
+    assert got[nb] == -7.0
+    blk = 32768 // 4
+    want = np.array([host[i * blk:min((i + 1) * blk, n)].astype(np.float64).sum()
+                     for i in range(nb)])
+    mag = np.array([np.abs(host[i * blk:min((i + 1) * blk, n)]).astype(np.float64).sum()
+                    for i in range(nb)])
+    # fp32 sums of at most 8192 terms: error below 8192 * 2^-24 of the absolute sum
+    assert np.all(np.abs(got[:nb] - want) <= 8192 * 2.0 ** -24 * mag + 1e-30)
