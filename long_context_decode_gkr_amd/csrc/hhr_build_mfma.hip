@@ -15,8 +15,9 @@
 //     queued in LDS and recomputed from the stored operands in fp64 (exact products), with
 //     the exact long accumulator behind that: every code equals the sign of the exact z.
 //
-// Grid (tiles x roles, Hkv, B): role 0 = rotation and page extrema, role 1 + s = code words
-// [4 s, 4 s + 4) (128 code columns). A workgroup of 8 waves covers 512 tokens; each wave walks
+// Grid (nper x roles, Hkv, B): role 0 = rotation and page extrema, role 1 + s = code words
+// [4 s, 4 s + 4) (128 code columns). A workgroup stages its role's B operand once, then builds
+// every nper-th tile of 512 tokens of its sequence. Per tile, each of its 8 waves walks
 // 32-token sub-tiles: 8 A fragments (one 16-byte load each per lane) are reused against all
 // 4 column tiles x 8 k-steps x pieces, B fragments come from LDS.
 #include "hhr_device.h"
@@ -269,10 +270,29 @@ hipError_t launch_build_mfma(const Shape& s, const CacheView& c, const float* R,
                              hipStream_t st) {
   const int ntiles = (s.Lmax + kMTok - 1) / kMTok;
   const int nroles = 1 + s.NB / kD;
-  // about 1024 workgroups (4 per CU): each stages its B operand once for ntiles / nper tiles
+  // The LDS staging (about 156 KB) keeps one workgroup per CU, so the build takes
+  // ceil(workgroups / CUs) rounds of ceil(ntiles / nper) tiles each. nper is the split with the
+  // fewest tiles in sequence, counting one tile for each round's B staging, among the splits
+  // of at least 4 rounds (measured on MI355X at 128K: 4 rounds of 4 tiles 340 us, 1 round of
+  // 16 tiles 372 us; sequences shorter than max_seq_len also leave room to rebalance); among
+  // equals the fewest workgroups (fewest stagings).
+  int dev = 0, ncu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      ncu <= 0)
+    ncu = 256;
   const long long units = (long long)nroles * s.Hkv * s.B;
-  int nper = int((1024 + units - 1) / units);
-  nper = nper < 1 ? 1 : (nper > ntiles ? ntiles : nper);
+  int nper = 1;
+  long long best = -1;
+  for (int n = 1; n <= ntiles; ++n) {
+    const long long rounds = (units * n + ncu - 1) / ncu;
+    const long long cost = rounds * ((ntiles + n - 1) / n + 1);
+    if (rounds < 4 && n < ntiles) continue;
+    if (best < 0 || cost < best) {
+      best = cost;
+      nper = n;
+    }
+  }
   dim3 grid(nper * nroles, s.Hkv, s.B);
   if (s.S == 16)
     hipLaunchKernelGGL((build_mfma_kernel<16>), grid, dim3(kMThreads), 0, st, s, c, R, W, ntiles,
