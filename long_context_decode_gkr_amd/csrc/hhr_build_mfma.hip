@@ -231,19 +231,47 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
         store_extrema(s, c, (sbase + j) * s.Pmax + pg0 + pl, stage_f[0][j][pl], stage_f[1][j][pl]);
       }
     } else {
-      // ---- exact path for the queued bits, then the code words. If more bits were uncertain
-      // than the queue holds (degenerate projections), every word of the tile is recomputed from
-      // the stored operands instead: slow, and only for such inputs.
+      // ---- exact path for the queued bits, then the code words. 8 lanes per queued bit form
+      // the fp64 sum of exact products (16 terms per lane: two 16-byte key loads and 16 W
+      // loads, all in flight together), certified as in any summation order; the exact long
+      // accumulator decides the rest. If more bits were uncertain than the queue holds
+      // (degenerate projections), every word of the tile is recomputed from the stored
+      // operands instead: slow, and only for such inputs.
       const float* wbase_p = W + size_t(g) * kD * s.NB + (role - 1) * kD;
       if (fb_n <= kFbCap) {
-        for (int e = tid; e < fb_n; e += kMThreads) {
+        const int gl = tid & 7;
+        for (int e = tid >> 3; e < fb_n; e += kMThreads / 8) {
           const uint32_t ent = fb_list[e];
           const int tl = int(ent >> 8), lc = int(ent & 0xFFu);
           const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
-          const uint32_t bit = certified_bit(Bf16Row{kr}, wbase_p + lc, s.NB);
-          const uint32_t mask = 1u << (lc & 31);
-          if (bit) atomicOr(&stage_c[tl][lc >> 5], mask);
-          else atomicAnd(&stage_c[tl][lc >> 5], ~mask);
+          const uint4 k0 = *reinterpret_cast<const uint4*>(kr + 16 * gl);
+          const uint4 k1 = *reinterpret_cast<const uint4*>(kr + 16 * gl + 8);
+          const float* wc = wbase_p + lc + size_t(16 * gl) * s.NB;
+          float wv[16];
+#pragma unroll
+          for (int i = 0; i < 16; ++i) wv[i] = wc[size_t(i) * s.NB];
+          const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+          double z = 0.0, sa = 0.0;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float x =
+                __uint_as_float((i & 1) ? (kw[i >> 1] & 0xFFFF0000u) : (kw[i >> 1] << 16));
+            const double pr = double(x) * double(wv[i]);
+            z += pr;
+            sa += fabs(pr);
+          }
+#pragma unroll
+          for (int o = 4; o >= 1; o >>= 1) {
+            z += __shfl_xor(z, o, 8);
+            sa += __shfl_xor(sa, o, 8);
+          }
+          if (gl == 0) {
+            int cb = certain_bit(z, sa);
+            if (cb < 0) cb = int(exact_bit(Bf16Row{kr}, wbase_p + lc, s.NB));
+            const uint32_t mask = 1u << (lc & 31);
+            if (cb) atomicOr(&stage_c[tl][lc >> 5], mask);
+            else atomicAnd(&stage_c[tl][lc >> 5], ~mask);
+          }
         }
       } else {
         for (int e = tid; e < ntok * 4; e += kMThreads) {

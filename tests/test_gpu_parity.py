@@ -294,26 +294,30 @@ def test_build_mfma_matches_oracle(cfg_id, L, batch, lens):
     hc.check_index(lay, hc.oracle_index(lay), extrema_atol_scale=MFMA_EXTREMA_SCALE)
 
 
-def test_build_mfma_exact_path_for_zero_and_tiny_projections():
-    # 16 code columns give z = k0 - k1 = 0 exactly (k0 == k1), 8 give z = 2^-30 k2: all of them
-    # fall inside the certification band, which overflows the per-workgroup queue (8192 > 2048).
+@pytest.mark.parametrize("nzero,ntiny", [(16, 8), (2, 1)])
+def test_build_mfma_exact_path_for_zero_and_tiny_projections(nzero, ntiny):
+    # nzero code columns give z = k0 - k1 = 0 exactly (k0 == k1), ntiny give z = 2^-30 k2: all
+    # of them fall inside the certification band. 24 columns x 512 rows overflow the
+    # per-workgroup queue of 2048 (every word of the tile recomputed); 3 x 512 fit (8 lanes
+    # per queued bit, z == 0 decided by the exact accumulator).
     _torch()
     cfg = _cfg(3, 2048, n_plant=0, num_q_heads=4, num_kv_heads=1)
     data = synth.make_layer(cfg)
     data["K"][:, :, :, 1] = data["K"][:, :, :, 0]
     W = data["W"]
-    W[:, :, :24] = 0.0
-    W[:, 0, :24] = 1.0
-    W[:, 1, :24] = -1.0
-    W[:, 2, 16:24] = np.float32(2.0 ** -30)
+    nc = nzero + ntiny
+    W[:, :, :nc] = 0.0
+    W[:, 0, :nc] = 1.0
+    W[:, 1, :nc] = -1.0
+    W[:, 2, nzero:nc] = np.float32(2.0 ** -30)
     lay = hc.GpuLayer(cfg, data=data)
     lay.build(method="auto")
     ref = hc.oracle_index(lay)
     hc.check_index(lay, ref, extrema_atol_scale=MFMA_EXTREMA_SCALE)
     bits0 = ref["codes"][0, :, :2048, 0]
-    assert np.all(bits0 & 0xFFFF == 0)                                     # z == 0 gives 0
+    assert np.all(bits0 & ((1 << nzero) - 1) == 0)                         # z == 0 gives 0
     k2pos = (data["K"][0, :, :2048, 2] > 0).astype(np.uint32)
-    assert np.array_equal((bits0 >> 16) & 0xFF, k2pos * 0xFF)              # sign of 2^-30 k2
+    assert np.array_equal((bits0 >> nzero) & ((1 << ntiny) - 1), k2pos * ((1 << ntiny) - 1))
 
 
 def test_step_codes_exact_for_zero_and_tiny_projections():
