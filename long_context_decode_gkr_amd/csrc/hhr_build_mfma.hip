@@ -56,7 +56,9 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   const int npieces = role == 0 ? 3 : 2;
 
   __shared__ __align__(16) uint16_t Bt[3][kD][kBStride];     // Bt[piece][n][k]
-  __shared__ float stage_f[2][kD][kMTok / 16];               // page min / max (role 0)
+  // page min / max (role 0); rows padded by one word so that the 32 channels a wave writes
+  // at once fall in different LDS banks
+  __shared__ float stage_f[2][kD][kMTok / 16 + 1];
   __shared__ uint32_t stage_c[kMTok][4];                     // code words (role > 0)
   __shared__ float wnorm[kD];
   __shared__ float wpart[kMThreads];
@@ -151,7 +153,10 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
       }
       // result rows of this lane: i(r) = 8 (r / 4) + 4 half + r % 4
       if (role == 0) {
-        // ---- page extrema of k~ over the valid rows (pages are 16 or 32 rows of the sub-tile)
+        // ---- page extrema of k~ over the valid rows (pages are 16 or 32 rows of the sub-tile).
+        // Rows past the end repeat the last valid row (load_a clamps), which lies in the same
+        // page, so they leave the partial page's extrema unchanged; pages with no valid row are
+        // not written out.
 #pragma unroll
         for (int nt = 0; nt < 4; ++nt) {
           const int j = nt * 32 + col;
@@ -161,11 +166,8 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
             float lo = INFINITY, hi = -INFINITY;
 #pragma unroll
             for (int r = pp * (16 / PPS); r < (pp + 1) * (16 / PPS); ++r) {
-              const int i = 8 * (r / 4) + 4 * half + (r % 4);
-              if (tl0 + i < ntok) {
-                lo = fminf(lo, acc[nt][r]);
-                hi = fmaxf(hi, acc[nt][r]);
-              }
+              lo = fminf(lo, acc[nt][r]);
+              hi = fmaxf(hi, acc[nt][r]);
             }
             lo = fminf(lo, __shfl_xor(lo, 32));
             hi = fmaxf(hi, __shfl_xor(hi, 32));
