@@ -76,3 +76,68 @@ def test_random_configuration_matches_oracle(seed):
     else:
         st = hc.check_decode(lay, out, dbg, c["rho"], c["k"], ref_index=ref, stages=c["stages"])
     print(f"seed {seed}: max out rel err {st['max_out_rel']:.2e}", flush=True)
+
+
+def draw_append_case(seed: int) -> dict:
+    """An append + decode case: lengths at or next to page boundaries and the capacity."""
+    r = np.random.default_rng(5000 + seed)
+    cfg_id = int(r.choice([2, 3, 4, 5]))          # bf16 K/V (the append path of the step)
+    S = synth.CONFIGS[cfg_id].page_size
+    cap = int(r.integers(4, 24)) * 4 * S
+    batch = int(r.integers(1, 4))
+    picks = [lambda: int(r.integers(1, cap)), lambda: int(r.integers(1, cap // S)) * S,
+             lambda: int(r.integers(1, cap // S)) * S - 1, lambda: cap - 1, lambda: cap]
+    lens = [picks[int(r.integers(0, len(picks)))]() for _ in range(batch)]
+    return dict(cfg_id=cfg_id, G=int(r.choice([1, 2, 4, 8])), hkv=int(r.choice([1, 2])),
+                batch=batch, cap=cap, lens=lens, steps=3,
+                rho=float(r.choice([0.05, 0.25, 1.0])), k=int(r.choice([5, 64, 300])),
+                summary=str(r.choice(["f32", "bf16"])), method=str(r.choice(["auto", "fp64"])))
+
+
+N_APPEND_CASES = 12
+
+
+def test_append_cases_reach_the_edges():
+    cases = [draw_append_case(i) for i in range(N_APPEND_CASES)]
+    lens = [(L, c["cap"], synth.CONFIGS[c["cfg_id"]].page_size) for c in cases for L in c["lens"]]
+    assert any(L == cap for L, cap, S in lens)                 # append at capacity: no-op
+    assert any(L % S == 0 and L < cap for L, cap, S in lens)   # the token opens a page
+    assert {c["summary"] for c in cases} == {"f32", "bf16"}
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", range(N_APPEND_CASES))
+def test_random_append_decode_matches_oracle(seed):
+    """hhr_append_decode for a few steps; after each, the oracle re-derives the whole index from
+    the host copy of the cache (with the same appended rows) and checks the step's selections
+    and output."""
+    torch = _torch()
+    from long_context_decode_gkr_amd import binding as hb
+    c = draw_append_case(seed)
+    print(f"seed {seed}: {c}", flush=True)
+    base = synth.CONFIGS[c["cfg_id"]]
+    cfg = base.scaled(seq_len=c["cap"], batch=c["batch"], lens=c["lens"],
+                      num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"], n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=c["cap"], summary=c["summary"])
+    lay.build(method=c["method"])
+    kn, vn = synth.append_tokens(cfg, c["steps"])
+    dec = hb.Decoder(lay.dims, c["rho"], c["k"])
+    d = lay.data
+    for i in range(c["steps"]):
+        out = torch.full((cfg.batch, cfg.num_q_heads, 128), float("nan"), dtype=torch.float32,
+                         device="cuda")
+        dbg = hb.Debug(lay.dims, c["k"], c["rho"])
+        dec(lay.cache, lay.q, lay.R, lay.W, out, dbg, k_new=hc.to_dev(kn[i], lay.tdt),
+            v_new=hc.to_dev(vn[i], lay.tdt))
+        torch.cuda.synchronize()
+        for b in range(cfg.batch):
+            t = int(d["seq_lens"][b])
+            if t < d["max_seq_len"]:
+                d["K"][b, :, t] = kn[i, b]
+                d["V"][b, :, t] = vn[i, b]
+                d["seq_lens"][b] = t + 1
+        np.testing.assert_array_equal(lay.cache.seq_lens.cpu().numpy(), d["seq_lens"])
+        ref = hc.oracle_index(lay)
+        hc.check_index(lay, ref, extrema_atol_scale=20.0 if c["method"] == "auto" else 1.0)
+        hc.check_decode(lay, out, dbg, c["rho"], c["k"], ref_index=ref)
+    assert np.all(lay.cache.append_ticket.cpu().numpy() == 0)
