@@ -141,3 +141,51 @@ def test_random_append_decode_matches_oracle(seed):
         hc.check_index(lay, ref, extrema_atol_scale=20.0 if c["method"] == "auto" else 1.0)
         hc.check_decode(lay, out, dbg, c["rho"], c["k"], ref_index=ref)
     assert np.all(lay.cache.append_ticket.cpu().numpy() == 0)
+
+
+N_DENSE_CASES = 12
+
+
+def draw_dense_case(seed: int) -> dict:
+    r = np.random.default_rng(9000 + seed)
+    cfg_id = int(r.integers(1, 6))
+    S = synth.CONFIGS[cfg_id].page_size
+    cap = int(r.integers(1, 48)) * 4 * S
+    batch = int(r.integers(1, 4))
+    lens = [int(r.choice([0, 1, int(r.integers(1, cap + 1)), cap])) for _ in range(batch)]
+    return dict(cfg_id=cfg_id, G=int(r.choice([1, 2, 4, 8])), hkv=int(r.choice([1, 2])),
+                batch=batch, cap=cap, lens=lens)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("seed", range(N_DENSE_CASES))
+def test_random_dense_decode_matches_textbook_attention(seed):
+    """The dense baseline (every token attended) on seeded shapes, against the oracle's
+    softmax attention in fp64; empty sequences give zeros."""
+    torch = _torch()
+    from long_context_decode_gkr_amd import binding as hb
+    from oracle import hhr_oracle as orc
+    c = draw_dense_case(seed)
+    print(f"seed {seed}: {c}", flush=True)
+    base = synth.CONFIGS[c["cfg_id"]]
+    cfg = base.scaled(seq_len=c["cap"], batch=c["batch"], lens=c["lens"],
+                      num_q_heads=c["G"] * c["hkv"], num_kv_heads=c["hkv"], n_plant=4)
+    lay = hc.GpuLayer(cfg, max_seq_len=c["cap"])
+    dd = hb.DenseDecoder(lay.dims)
+    out = torch.full((cfg.batch, cfg.num_q_heads, 128), float("nan"), dtype=torch.float32,
+                     device="cuda")
+    dd(lay.cache, lay.q, out)
+    torch.cuda.synchronize()
+    got = out.cpu().numpy()
+    d = lay.data
+    for b in range(cfg.batch):
+        Lb = int(d["seq_lens"][b])
+        for h in range(cfg.num_q_heads):
+            if Lb == 0:
+                assert np.all(got[b, h] == 0.0)
+                continue
+            g = h // cfg.group
+            ref = orc.dense_head(d["q"][b, h], d["K"][b, g], d["V"][b, g], Lb,
+                                 orc.default_scale(128))
+            rel = np.abs(got[b, h] - ref).max() / np.abs(ref).max()
+            assert rel <= hc.OUT_RTOL, (b, h, rel)
