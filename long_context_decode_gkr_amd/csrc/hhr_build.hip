@@ -132,10 +132,12 @@ hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R,
 }
 
 // ---------------------------------------------------------------------------------------------
-// Step preparation, grid (4 column slices, KV head g, sequence b), 256 + 8 NB / 4 threads.
-// Each workgroup owns 32 channels of the rotation and NB / 4 code columns. Vector 0 is the new
-// key (when k_new is given and seq_lens[b] < max_seq_len), vectors 1 .. G the queries (decode
-// mode). Each R_g / W_g column of the slice is read once and applied to every vector.
+// Step preparation, grid (4 column slices x 2 roles, KV head g, sequence b), max(256, 2 NB)
+// threads. Workgroups 0-3 own 32 channels of the rotation each, workgroups 4-7 NB / 4 code
+// columns each (the two roles on separate CUs: 6.8 -> 5.3 us at the 128K workload against one
+// workgroup doing both). Vector 0 is the new key (when k_new is given and seq_lens[b] <
+// max_seq_len), vectors 1 .. G the queries (decode mode). Each R_g / W_g column of the slice
+// is read once and applied to every vector.
 //   * rotation lanes [0, 256): column j over 8 lanes of 16 terms, fp64 sums of exact products
 //     reduced by DPP: k~ is folded into page t / S (which it opens when t % S == 0), q~
 //     (Eq. 4) goes to the decode workspace; the workgroup also stores its slice of the K and V
@@ -149,10 +151,15 @@ hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R,
 // ---------------------------------------------------------------------------------------------
 constexpr int kPrepSlices = 4;
 constexpr int kPrepParts = 8;
+// workgroup size: 256 rotation lanes, or 8 lanes per code column of a slice if more
+template <int NB>
+constexpr int prep_threads() {
+  return 256 > kPrepParts * NB / kPrepSlices ? 256 : kPrepParts * NB / kPrepSlices;
+}
 // KB, QB: keys/values, queries in bf16; DEC: the number of queries (the group size G) in a
 // decode step, 0 for a plain append. Vector 0 is the key, vectors 1 .. DEC the queries.
 template <int NB, int KB, int QB, int DEC>
-__global__ void __launch_bounds__(256 + kPrepParts * NB / kPrepSlices)
+__global__ void __launch_bounds__(prep_threads<NB>())
 prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __restrict__ vn,
             const void* __restrict__ q, const float* __restrict__ R, const float* __restrict__ W,
             float* __restrict__ qrot, uint32_t* __restrict__ qcode, float* __restrict__ dbg_qrot,
@@ -161,13 +168,15 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   constexpr int CC = NB / kPrepSlices;          // code columns per slice (32 or 64)
   constexpr int WPS = CC / 32;                  // code words per slice (1 or 2)
   constexpr int T = kD / kPrepParts;            // terms per lane (16)
-  constexpr int NT = 256 + kPrepParts * NB / kPrepSlices;   // workgroup size
+  constexpr int NT = prep_threads<NB>();        // workgroup size
   constexpr int QPT = DEC ? (DEC * kD + NT - 1) / NT : 1;   // query elements per thread
   constexpr int NV = 1 + DEC;                                 // vectors
-  const int sl = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
+  const int sl = blockIdx.x % kPrepSlices, g = blockIdx.y, b = blockIdx.z;
+  const bool rotwg = blockIdx.x < kPrepSlices;  // rotation workgroup; else code workgroup
   const int tid = threadIdx.x;
   const int part = tid & (kPrepParts - 1);
-  const bool rot = tid < 256;                   // rotation lanes; the others compute code bits
+  const bool rot = rotwg && tid < 256;          // rotation lanes
+  const bool codel = !rotwg && tid < kPrepParts * CC;   // code lanes
   constexpr int nq = DEC;
   const bool has_k = kn != nullptr;
   if (!has_k && nq == 0) return;
@@ -179,13 +188,13 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   // new key and value elements, the queries, then this lane's 16 column terms.
   const int t = c.seq_lens[b];
   const int j = sl * 32 + (tid >> 3);           // rotation column (rotation lanes)
-  const int lc = (tid - 256) >> 3;              // code column within the slice (code lanes)
+  const int lc = (tid >> 3) % CC;               // code column within the slice (code lanes)
   const int cc = sl * CC + lc;
   // The vector loads carry no branch (a branch would make the compiler wait for each load
   // before the join): a missing key or query input is replaced by the other input, whose
   // values are then loaded but not used, and indices are clamped.
   const size_t krow = (size_t(b) * s.Hkv + g) * kD;
-  const bool own = (tid >> 5) == sl;            // this workgroup stores K/V element tid
+  const bool own = rotwg && (tid >> 5) == sl;   // this workgroup stores K/V element tid
   const int kel = min(tid, kD - 1);
   const uint32_t kraw = load_raw(has_k ? kn : q, has_k ? krow + kel : 0, KB);
   const uint32_t vraw = load_raw(has_k ? vn : q, has_k ? krow + kel : 0, KB);
@@ -266,7 +275,7 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
         }
       }
     }
-  } else {
+  } else if (codel) {
     // ---- code column cc, terms [16 part, 16 part + 16): fp32 with a certificate
     float z[NV], sa[NV];
 #pragma unroll
@@ -295,7 +304,7 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   }
   __syncthreads();
   // ---- pack this slice's code words: thread (v, w) builds word w of vector v
-  if (tid < (1 + nq) * WPS) {
+  if (!rotwg && tid < (1 + nq) * WPS) {
     const int v = tid / WPS, wi = tid % WPS;
     if (active(v)) {
       uint32_t word = 0;
@@ -320,7 +329,7 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
       __syncthreads();
       if (tid == 0) {
         const int done = atomicAdd(&c.ticket[b], 1);
-        if (done == s.Hkv * kPrepSlices - 1) {
+        if (done == s.Hkv * kPrepSlices * 2 - 1) {
           c.ticket[b] = 0;
           c.seq_lens[b] = t + 1;
         }
@@ -334,8 +343,8 @@ static void launch_prep_t(const Shape& s, const CacheView& c, const void* k_new,
                           const void* v_new, const void* q, const float* R, const float* W,
                           float* qrot, uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode,
                           PrepMode mode, KernelTimer tm, hipStream_t st) {
-  dim3 grid(kPrepSlices, s.Hkv, s.B);
-  dim3 block(256 + kPrepParts * NB / kPrepSlices);
+  dim3 grid(2 * kPrepSlices, s.Hkv, s.B);
+  dim3 block(prep_threads<NB>());
   if (mode == PrepMode::kDecode) {
     switch (s.G) {
       case 1: launch_kernel(prep_kernel<NB, KB, QB, 1>, grid, block, st, tm, s, c, k_new, v_new,
