@@ -230,7 +230,7 @@ hhr_status hhr_dense_decode(const hhr_dims* dims, const hhr_cache* cache, const 
                             const hhr_debug* dbg, hhr_stream_t stream);
 
 /* Measurement aid, no step of the method: the practical one-pass read rate of device memory,
- * against which the HBM-bound kernels above are judged (a single launch pays its ramp-up and
+ * against which the HBM-bound kernels above are compared (a single launch pays its ramp-up and
  * drain, so it cannot reach the HBM peak). Reads the `bytes` bytes at src once with the page-
  * bound kernel's load width and cache policy (16-byte non-temporal loads) and writes, for each
  * block of 32 KiB (the last one partial), the fp32 sum of the floats it read to partial[i],

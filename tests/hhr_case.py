@@ -141,7 +141,7 @@ def check_decode(layer: GpuLayer, out, dbg, rho, k, scale=None, heads=None, ref_
     tcnt = dbg.token_count.cpu().numpy()
     gidx = layer.index_host()
     if layer.summary == "bf16":
-        # bf16 extrema: the bounds and the page set are judged on the GPU's own extrema, which
+        # bf16 extrema: the bounds and the page set are checked against the GPU's own extrema, which
         # check_index holds to the oracle's outward rounding (equal or one bf16 step apart)
         ref_index = dict(ref_index, lo=gidx["lo"], hi=gidx["hi"])
     heads = heads or [(b, h) for b in range(cfg.batch) for h in range(cfg.num_q_heads)]
