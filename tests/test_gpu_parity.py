@@ -204,6 +204,46 @@ def test_decode_is_deterministic():
     assert torch.equal(d1.token_idx, d2.token_idx) and torch.equal(d1.bounds, d2.bounds)
 
 
+@pytest.mark.parametrize("stages,group_shared", [("both", False), ("codes", False),
+                                                 ("both", True)])
+def test_decode_on_a_side_stream_and_in_a_replayed_graph(stages, group_shared):
+    """The step enqueues everything on the stream it is given: the same output on a side
+    stream, and from a captured HIP graph replayed several times with eager decodes and
+    synchronisations in between (the library records no memset and allocates nothing)."""
+    torch = _torch()
+    cfg = _cfg(2, 3001, n_plant=8)
+    lay = hc.GpuLayer(cfg, max_seq_len=3072)
+    lay.build()
+    dec = hb.Decoder(lay.dims, 1 / 8, 300, stages=stages, group_shared=group_shared)
+    shape = (1, cfg.num_q_heads, 128)
+    ref = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    dec(lay.cache, lay.q, lay.R, lay.W, ref)
+    torch.cuda.synchronize()
+    assert not torch.isnan(ref).any()
+    side = torch.cuda.Stream()
+    out_s = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.stream(side):
+        dec(lay.cache, lay.q, lay.R, lay.W, out_s, stream=side.cuda_stream)
+    side.synchronize()
+    assert torch.equal(out_s, ref)
+    graph, gstream = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+    out_g = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    with torch.cuda.graph(graph, stream=gstream):
+        dec(lay.cache, lay.q, lay.R, lay.W, out_g, stream=gstream.cuda_stream)
+    for _ in range(4):
+        out_g.fill_(float("nan"))
+        torch.cuda.synchronize()
+        graph.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(out_g, ref)
+        eager = torch.full(shape, float("nan"), dtype=torch.float32, device="cuda")
+        dec(lay.cache, lay.q, lay.R, lay.W, eager)
+        torch.cuda.synchronize()
+        assert torch.equal(eager, ref)
+
+
 # ---------------------------------------------------------------------------------------------
 # Append: one token per step; equals a rebuild; decode sees the new token
 # ---------------------------------------------------------------------------------------------
