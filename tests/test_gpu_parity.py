@@ -244,6 +244,34 @@ def test_decode_on_a_side_stream_and_in_a_replayed_graph(stages, group_shared):
         assert torch.equal(eager, ref)
 
 
+def test_concurrent_decodes_on_two_streams():
+    """Two layers (their own caches and workspaces) decoded at once on two streams, each step
+    enqueued back to back several times: every output equals its layer's eager result."""
+    torch = _torch()
+    lays, decs, refs = [], [], []
+    for layer, (cfg_id, L) in enumerate([(2, 3001), (3, 2500)]):
+        cfg = _cfg(cfg_id, L, n_plant=8)
+        lay = hc.GpuLayer(cfg, max_seq_len=3072, layer=layer)
+        lay.build()
+        dec = hb.Decoder(lay.dims, cfg.keep_ratio, 257)
+        ref = torch.full((1, cfg.num_q_heads, 128), float("nan"), dtype=torch.float32,
+                         device="cuda")
+        dec(lay.cache, lay.q, lay.R, lay.W, ref)
+        lays.append(lay), decs.append(dec), refs.append(ref)
+    torch.cuda.synchronize()
+    streams = [torch.cuda.Stream(), torch.cuda.Stream()]
+    outs = [[torch.full_like(refs[i], float("nan")) for _ in range(3)] for i in range(2)]
+    for r in range(3):
+        for i in range(2):
+            with torch.cuda.stream(streams[i]):
+                decs[i](lays[i].cache, lays[i].q, lays[i].R, lays[i].W, outs[i][r],
+                        stream=streams[i].cuda_stream)
+    torch.cuda.synchronize()
+    for i in range(2):
+        for r in range(3):
+            assert torch.equal(outs[i][r], refs[i]), (i, r)
+
+
 # ---------------------------------------------------------------------------------------------
 # Append: one token per step; equals a rebuild; decode sees the new token
 # ---------------------------------------------------------------------------------------------
