@@ -189,3 +189,42 @@ def test_random_dense_decode_matches_textbook_attention(seed):
                                  orc.default_scale(128))
             rel = np.abs(got[b, h] - ref).max() / np.abs(ref).max()
             assert rel <= hc.OUT_RTOL, (b, h, rel)
+
+
+@pytest.mark.gpu
+@pytest.mark.parametrize("stages,group_shared", [("both", False), ("codes", False), ("both", True)])
+def test_many_short_sequences(stages, group_shared):
+    """A batch of 40 ragged sequences (1 to 400 tokens; 1, 16 and 17 among them: a single token,
+    a full page, a page plus one)
+    through build, fused append + decode and decode: every (sequence, head) against the oracle."""
+    torch = _torch()
+    from long_context_decode_gkr_amd import binding as hb
+    r = np.random.default_rng(77)
+    lens = [int(x) for x in r.integers(1, 401, size=40)]
+    lens[0], lens[1], lens[2] = 1, 16, 17
+    cfg = synth.CONFIGS[2].scaled(seq_len=448, batch=40, lens=lens, num_q_heads=8,
+                                  num_kv_heads=2, n_plant=2)
+    lay = hc.GpuLayer(cfg, max_seq_len=448)
+    lay.build()
+    out, dbg = lay.decode(0.25, 48, stages=stages, group_shared=group_shared)
+    ref = hc.oracle_index(lay)
+    check = hc.check_decode_shared if group_shared else hc.check_decode
+    check(lay, out, dbg, 0.25, 48, ref_index=ref, stages=stages)
+    # one fused append + decode step on top
+    kn, vn = synth.append_tokens(cfg, 1)
+    dec = hb.Decoder(lay.dims, 0.25, 48, stages=stages, group_shared=group_shared)
+    out2 = torch.full((cfg.batch, cfg.num_q_heads, 128), float("nan"), dtype=torch.float32,
+                      device="cuda")
+    dbg2 = hb.Debug(lay.dims, 48, 0.25, stages)
+    dec(lay.cache, lay.q, lay.R, lay.W, out2, dbg2, k_new=hc.to_dev(kn[0], lay.tdt),
+        v_new=hc.to_dev(vn[0], lay.tdt))
+    torch.cuda.synchronize()
+    d = lay.data
+    for b in range(cfg.batch):
+        t = int(d["seq_lens"][b])
+        d["K"][b, :, t] = kn[0, b]
+        d["V"][b, :, t] = vn[0, b]
+        d["seq_lens"][b] = t + 1
+    ref2 = hc.oracle_index(lay)
+    hc.check_index(lay, ref2, extrema_atol_scale=20.0)
+    check(lay, out2, dbg2, 0.25, 48, ref_index=ref2, stages=stages)
