@@ -195,8 +195,8 @@ def test_random_dense_decode_matches_textbook_attention(seed):
 @pytest.mark.parametrize("stages,group_shared", [("both", False), ("codes", False), ("both", True)])
 def test_many_short_sequences(stages, group_shared):
     """A batch of 40 ragged sequences (1 to 400 tokens; 1, 16 and 17 among them: a single token,
-    a full page, a page plus one)
-    through build, fused append + decode and decode: every (sequence, head) against the oracle."""
+    a full page, a page plus one) through build, decode and a fused append + decode: every
+    (sequence, head) against the oracle."""
     torch = _torch()
     from long_context_decode_gkr_amd import binding as hb
     r = np.random.default_rng(77)
