@@ -207,3 +207,27 @@ def test_read_probe_blocks_and_validation():
     for src, nbytes, partial in [(None, 4096, FAKE), (FAKE, 4096, None), (FAKE, 0, FAKE),
                                  (FAKE, 4100, FAKE), (FAKE + 4, 4096, FAKE)]:
         assert lib.hhr_read_probe(src, nbytes, partial, None) == 1
+
+
+def test_header_compiles_as_c_and_links(tmp_path):
+    """include/hhr.h is plain C: a C11 translation unit (strict warnings) that takes the address
+    of every declared entry point compiles, links against libhhr.so and loads."""
+    import shutil
+    import subprocess
+    cc = shutil.which("gcc") or shutil.which("cc")
+    if cc is None:
+        pytest.skip("no C compiler")
+    names = declared_functions()
+    src = tmp_path / "use.c"
+    src.write_text('#include "hhr.h"\ntypedef void (*fn)(void);\nint main(void) {\n  int n = 0;\n' +
+                   "".join(f"  n += (fn)&{n} != (fn)0;\n" for n in names) +
+                   f"  return n == {len(names)} ? 0 : 1;\n}}\n")
+    exe = tmp_path / "use"
+    lib_dir = os.path.dirname(hb.LIB_PATH)
+    r = subprocess.run([cc, "-std=c11", "-Wall", "-Wextra", "-pedantic", "-Werror",
+                        f"-I{os.path.join(ROOT, 'include')}", str(src), "-o", str(exe),
+                        f"-L{lib_dir}", "-l:libhhr.so", f"-Wl,-rpath,{lib_dir}"],
+                       capture_output=True, text=True)
+    assert r.returncode == 0, r.stderr
+    run = subprocess.run([str(exe)], capture_output=True, text=True)   # resolves, calls nothing
+    assert run.returncode == 0, run.stderr
