@@ -15,11 +15,11 @@ A "step" is one decode step (with an append first in the default workload) on on
 benchmark cycles over --layers distinct layer instances (separate K/V, index and sequence state
 in HBM) so the ~256 MB Infinity Cache cannot serve a step from the previous visit. Three passes,
 each W warm-up steps then exactly K timed steps bracketed by torch.cuda.synchronize():
-  1. launches with HIP start/stop events that the runtime records around each of the five
+  1. launches with HIP start/stop events that the runtime records around each of the six
      kernels' own execution: per-kernel durations and the roofline figure (events_us_per_step);
   2. plain launches on one stream, no events: the headline us/step/layer;
   3. replay of one captured HIP graph per layer instance (graph_us_per_step; on this stack a
-     graph replay of the five kernels is slower than the plain launches).
+     graph replay of the six kernels is slower than the plain launches).
 The index builder (MFMA path) is timed once over every key of the first layer instance, and the
 dense baseline (full attention over every token, hhr_dense_decode) on the same layer instances,
 for the same-hardware speedup of the sparse step over full attention (dense_us_per_step,
@@ -57,7 +57,8 @@ sys.path.insert(0, ROOT)
 HBM_PEAK_GBS = 8000.0
 CSRC = os.path.join(ROOT, "long_context_decode_gkr_amd", "csrc")
 # source files each kernel is compiled from (besides the shared device and launch headers)
-KERNEL_SOURCES = {"prep": "hhr_build.hip", "page_bound": "hhr_decode.hip", "select": "hhr_decode.hip",
+KERNEL_SOURCES = {"prep": "hhr_build.hip", "page_bound": "hhr_decode.hip",
+                  "select": "hhr_select.hip", "select_emit": "hhr_select.hip",
                   "sparse_attn": "hhr_decode.hip", "combine": "hhr_decode.hip",
                   "builder": "hhr_build_mfma.hip", "dense_attn": "hhr_dense.hip"}
 
@@ -78,20 +79,41 @@ def log(msg, quiet):
         print(f"[bench] {msg}", file=sys.stderr, flush=True)
 
 
-# variant -> the timed kernels and their index in the library's per-step event list
-VARIANTS = {
-    "hhr": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3), ("combine", 4)),
-    "identity-r": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3),
-                   ("combine", 4)),
-    "pages": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3), ("combine", 4)),
-    "bf16-extrema": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3),
-                     ("combine", 4)),
-    "group-shared": (("prep", 0), ("page_bound", 1), ("select", 2), ("sparse_attn", 3),
-                     ("combine", 4)),
-    "codes": (("prep", 0), ("hamming_scan", 1), ("token_select", 2), ("sparse_attn", 3),
-              ("combine", 4)),
-    "dense": (("dense_attn", 0), ("combine", 1)),
-}
+# the library's per-step event slots (start and stop of slot j are events 2j and 2j + 1)
+_STEP = (("prep", 0), ("page_bound", 1), ("select", 2), ("select_emit", 3),
+         ("sparse_attn", 4), ("combine", 5))
+VARIANTS = ("hhr", "identity-r", "pages", "bf16-extrema", "group-shared", "codes", "dense")
+
+
+def timed_kernels(variant, unit):
+    """The kernels a step of this variant launches, with their event slots: no page bound for
+    the fine stage alone; the second selection kernel only in the sliced form (`unit` False)."""
+    if variant == "dense":
+        return (("dense_attn", 0), ("combine", 1))
+    drop = {"page_bound"} if variant == "codes" else set()
+    if unit:
+        drop.add("select_emit")
+    return tuple(k for k in _STEP if k[0] not in drop)
+
+
+STEP_EVENTS = 12      # events per step the library may record (six kernels)
+SLICE_PAGES, MIN_SLICE_PAGES, UNIT_SLOTS = 512, 8, 32768
+
+
+def unit_select(variant, kpages, page_size):
+    """Whether the library selects with one workgroup per unit (one kernel; the candidates of
+    the largest kept page set fit its LDS cache) rather than in slices (two kernels)."""
+    return variant != "codes" and kpages * page_size <= UNIT_SLOTS
+
+
+def select_slices(kpages, units, all_kept):
+    """Selection slices per unit (the library's rule): about 256 workgroups in all (1024 when
+    every page is kept and no page cut is repeated), between 8 and 512 kept pages per slice."""
+    target = 1024 if all_kept else 256
+    want = -(-target // units)
+    lo = -(-kpages // SLICE_PAGES)
+    hi = max(lo, -(-kpages // MIN_SLICE_PAGES))
+    return max(1, min(max(want, lo), hi))
 
 
 def dense_splits(cfg, lmax):
@@ -114,10 +136,14 @@ def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
                 written, and its page's extrema column pair read and written.
     page_bound: min+max of every page of every KV head (d x 8 B per page), q~ read, U
                 written (4 B per query head and page).
-    select:     U and the query code read, the codes of the candidates (NB/8 B per candidate
-                and query head), the selected indices written. Coarse stage only: no code is
-                read and every candidate is written. Fine stage only: no U; every token is a
-                candidate.
+    select:     per selection unit, the U row and the query code(s) read, the codes of the
+                candidates read (NB/8 B each; none for the coarse stage alone), the selected
+                indices written. In the sliced form (two kernels: the fine stage alone, or more
+                than 32768 candidates) this kernel writes a distance (1 B, 2 B for 256 bits) per
+                candidate, the kept page ids and one histogram per slice instead of the indices,
+                and the fine stage alone reads no U (every token is a candidate).
+    select_emit: (sliced form) the distances, page ids and histograms read back once, the
+                selected indices written; 0 when the selection is one kernel.
     sparse_attn: K and V rows of the selected tokens (2 x d x 2 B per token and query head),
                 indices and q read, one (o, m, l) partial per 128 tokens written.
     combine:    the partials read, the output written.
@@ -125,7 +151,7 @@ def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
                 partial per split and query head written.
     """
     d, S, nb = cfg.head_dim, cfg.page_size, cfg.hash_bits
-    Hq, Hkv = cfg.num_q_heads, cfg.num_kv_heads
+    Hq, Hkv, G = cfg.num_q_heads, cfg.num_kv_heads, cfg.group
     esz = 2 if cfg.dtype == "bf16" else 4
     B = len(lens)
     if variant == "dense":
@@ -133,14 +159,23 @@ def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
         parts = B * Hq * nsplit * (d + 2) * 4
         return {"dense_attn": B * Hq * d * esz + sum(Hkv * L * 2 * d * esz for L in lens) + parts,
                 "combine": parts + B * Hq * d * 4}
+    ex = 2 if variant == "bf16-extrema" else 4    # bytes per stored extremum
     out = {"prep": B * Hq * d * esz + Hkv * d * d * 4 + Hkv * d * nb * 4 + B * Hq * d * 4
                    + B * Hq * nb // 8,
-           "page_bound": B * Hq * d * 4, "select": 0, "sparse_attn": 0, "combine": 0}
-    ex = 2 if variant == "bf16-extrema" else 4    # bytes per stored extremum
+           "page_bound": B * Hq * d * 4, "sparse_attn": 0, "combine": 0}
     if append:
         out["prep"] += B * Hkv * (2 * d * esz + 2 * d * esz + nb // 8 + 2 * d * ex * 2)
     shared = variant == "group-shared"
     Hs = Hkv if shared else Hq        # selection units per sequence
+    ncodes = G if shared else 1       # query codes a unit compares against
+    dbytes = 1 if nb == 128 else 2
+    lmax = lmax or max(lens)
+    pmax = lmax // S
+    kpages = pmax if variant == "codes" else min(pmax, max(1, math.ceil(cfg.keep_ratio * pmax)))
+    nsl = select_slices(kpages, B * Hs, variant == "codes")
+    unit = unit_select(variant, kpages, S)
+    hist = nsl * (nb + 1) * 4
+    out["select"], out["select_emit"] = 0, 0
     for L in lens:
         P = -(-L // S)
         n_keep = P if variant == "codes" else min(P, max(1, math.ceil(cfg.keep_ratio * P)))
@@ -148,26 +183,23 @@ def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
         k = ncand if variant == "pages" else min(cfg.token_budget, ncand)
         chunk = 128 if cfg.dtype == "bf16" else 64   # rows per attention workgroup
         parts = Hq * -(-k // chunk) * (d + 2) * 4
-        out["page_bound"] += Hkv * P * d * 2 * ex + Hs * P * 4
-        if variant == "pages":
-            out["select"] += Hq * (P * 4 + k * 4)
-        elif variant == "codes":
-            # the scan: every token's code read once per query head, one distance byte (two for
-            # 256 bits) written, a histogram per slice; the selection reads the distances and
-            # the histograms, writes the indices
-            dbytes = 1 if nb == 128 else 2
-            hist = -(-L // 4096) * (nb + 1) * 4
-            out["hamming_scan"] = out.get("hamming_scan", 0) + Hq * (
-                nb // 8 + ncand * (nb // 8) + ncand * dbytes + hist)
-            out["token_select"] = out.get("token_select", 0) + Hq * (
-                ncand * dbytes + -(-L // 4096) * hist + k * 4)
+        if variant != "codes":
+            out["page_bound"] += Hkv * P * d * 2 * ex + Hs * P * 4
+        reads = ((0 if variant == "codes" else P * 4) + ncodes * nb // 8
+                 + (0 if variant == "pages" else ncand * nb // 8))
+        if unit:
+            out["select"] += Hs * (reads + k * 4)
         else:
-            out["select"] += Hs * (P * 4 + n_keep * S * (nb // 8) + k * 4) + Hq * nb // 8
+            inter = n_keep * S * dbytes + n_keep * 4 + hist   # distances, page ids, histograms
+            out["select"] += Hs * (reads + inter)
+            out["select_emit"] += Hs * (inter + k * 4)
         # K and V rows: once per selection unit (a KV head's group shares its rows)
         out["sparse_attn"] += Hs * k * 2 * d * esz + Hq * (k * 4 + d * esz) + parts
         out["combine"] += parts + Hq * d * 4
     if variant == "codes":
-        del out["page_bound"], out["select"]
+        del out["page_bound"]
+    if unit:
+        del out["select_emit"]
     return out
 
 
@@ -406,7 +438,7 @@ def main():
     ap.add_argument("--steps", type=int, default=200)
     ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default=DEFAULT_WORKLOAD)
-    ap.add_argument("--variant", choices=sorted(VARIANTS), default="hhr",
+    ap.add_argument("--variant", choices=VARIANTS, default="hhr",
                     help="hhr: the method; pages / codes: coarse or fine stage alone; "
                          "identity-r: R = I; bf16-extrema: page extrema stored as bf16 "
                          "rounded outward; group-shared: one selection per KV head; dense: "
@@ -521,8 +553,11 @@ def main():
     # ---- pass 1 (launches with events): per-kernel durations from HIP events that the runtime
     # records around each kernel's own execution on the decode stream (hipExtLaunchKernel)
     stream = hb.current_stream()
-    NE = 10                                   # events per step the library may record
-    timed = VARIANTS[variant]
+    NE = STEP_EVENTS
+    kpages_max = int(data["max_seq_len"]) // S
+    if variant != "codes":
+        kpages_max = min(kpages_max, max(1, math.ceil(cfg.keep_ratio * kpages_max)))
+    timed = timed_kernels(variant, unit_select(variant, kpages_max, S))
     ev = hb.HipEvents(NE * K)
     dbgs = [hb.DebugStruct(None, None, None, None, None, None, None, None, ev.address(NE * i))
             for i in range(K)]

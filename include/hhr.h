@@ -20,8 +20,13 @@
  *   - Arguments are validated on the host before anything is enqueued; an invalid call
  *     returns an error status and enqueues nothing. Values that live in device memory
  *     (seq_lens) cannot be checked on the host: kernels clamp them to [0, max_seq_len].
- *   - A failed kernel launch returns HHR_ERR_HIP. Faults inside a kernel surface at the
- *     caller's next synchronisation.
+ *   - A failed kernel launch returns HHR_ERR_HIP (each launch's own status is checked, so an
+ *     error left by an earlier, unrelated call is not reported). The launches before the failed
+ *     one stay enqueued: after HHR_ERR_HIP from hhr_append_decode the new token's K/V rows,
+ *     page extrema and code may already be written while seq_lens was not advanced, and after
+ *     HHR_ERR_HIP from hhr_append the same holds when the sequence's last workgroup did not
+ *     run; rebuild the index (hhr_build_pages) before the next append or decode. Faults inside
+ *     a kernel surface at the caller's next synchronisation.
  *   - Head dimension d is 128. Query head h reads KV head g = h / (Hq / Hkv) (grouped-query
  *     attention); the rotation R_g and projection W_g belong to the KV head.
  *   - Rows are row vectors: q~ = q R_g, z = x W_g.
@@ -148,13 +153,25 @@ typedef struct {
  *   token_count [B][Hq]             how many were selected
  *   With group_shared, page_ids, page_count, dist, token_idx and token_count hold one row per
  *   (b, KV head) instead, at row b * Hkv + g; bounds stays per query head.
- *   kernel_events  NULL or 10 caller-created events: the start and stop of each of the five
- *                  kernels of a decode step, in launch order, recorded by the runtime around the
- *                  kernel's own execution (hipExtLaunchKernel), so that their elapsed times are
- *                  the kernels' durations: the preparation kernel (query rotations and codes;
- *                  in hhr_append_decode also the new token's K/V rows, page extrema and code),
- *                  the page-bound kernel, the selection kernel, the attention kernel, and the
- *                  kernel that merges the attention partials (and commits the append) */
+ *   kernel_events  NULL or 12 caller-created events: the start and stop of each of the six
+ *                  kernel slots of a decode step, in launch order, recorded by the runtime around
+ *                  the kernel's own execution (hipExtLaunchKernel), so that their elapsed times
+ *                  are the kernels' durations: (0) the preparation kernel (query rotations and
+ *                  codes; in hhr_append_decode also the new token's K/V rows, page extrema and
+ *                  code),
+ *                  (1) the page-bound kernel, (2) the selection (page cut, Hamming distances of
+ *                  the kept pages' keys and, when it is one kernel, the token threshold and the
+ *                  selected positions), (3) the second selection kernel of the sliced form
+ *                  (token threshold, selected positions), (4) the attention kernel, and (5) the
+ *                  kernel that merges the attention partials (and commits the append). A slot
+ *                  whose kernel does not run in this configuration (the page bound with
+ *                  HHR_STAGES_CODES_ONLY, slot 3 when the selection is one kernel) gets its two
+ *                  events recorded back to back.
+ *   The selection runs as one workgroup per selection unit when the largest kept page set's
+ *   tokens fit its cache (at most 32768 candidates) and the stages include the coarse one, and
+ *   otherwise in slices of the kept pages over two kernels; both give identical results. For
+ *   testing, the environment variable HHR_SELECT=sliced forces the sliced form and
+ *   HHR_SELECT_SLICES=n (1..1024) its slice count. */
 typedef struct {
   float* q_rot;
   uint32_t* q_code;

@@ -119,8 +119,8 @@ template <int NB, int S>
 static hipError_t launch_build_fp64_t(const Shape& s, const CacheView& c, const float* R,
                                       const float* W, hipStream_t st) {
   dim3 grid((s.Lmax + kBuildTile - 1) / kBuildTile, s.Hkv, s.B);
-  hipLaunchKernelGGL((build_fp64_kernel<NB, S>), grid, dim3(kD + NB), 0, st, s, c, R, W);
-  return hipGetLastError();
+  return launch_kernel(build_fp64_kernel<NB, S>, grid, dim3(kD + NB), st,
+                       KernelTimer{nullptr, nullptr}, s, c, R, W);
 }
 
 hipError_t launch_build_fp64(const Shape& s, const CacheView& c, const float* R, const float* W,
@@ -339,41 +339,46 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
 }
 
 template <int NB, int KB, int QB>
-static void launch_prep_t(const Shape& s, const CacheView& c, const void* k_new,
-                          const void* v_new, const void* q, const float* R, const float* W,
-                          float* qrot, uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode,
-                          PrepMode mode, KernelTimer tm, hipStream_t st) {
+static hipError_t launch_prep_t(const Shape& s, const CacheView& c, const void* k_new,
+                                const void* v_new, const void* q, const float* R, const float* W,
+                                float* qrot, uint32_t* qcode, float* dbg_qrot,
+                                uint32_t* dbg_qcode, PrepMode mode, KernelTimer tm,
+                                hipStream_t st) {
   dim3 grid(2 * kPrepSlices, s.Hkv, s.B);
   dim3 block(prep_threads<NB>());
   if (mode == PrepMode::kDecode) {
     switch (s.G) {
-      case 1: launch_kernel(prep_kernel<NB, KB, QB, 1>, grid, block, st, tm, s, c, k_new, v_new,
-                            q, R, W, qrot, qcode, dbg_qrot, dbg_qcode); break;
-      case 2: launch_kernel(prep_kernel<NB, KB, QB, 2>, grid, block, st, tm, s, c, k_new, v_new,
-                            q, R, W, qrot, qcode, dbg_qrot, dbg_qcode); break;
-      case 4: launch_kernel(prep_kernel<NB, KB, QB, 4>, grid, block, st, tm, s, c, k_new, v_new,
-                            q, R, W, qrot, qcode, dbg_qrot, dbg_qcode); break;
-      default: launch_kernel(prep_kernel<NB, KB, QB, 8>, grid, block, st, tm, s, c, k_new, v_new,
-                             q, R, W, qrot, qcode, dbg_qrot, dbg_qcode); break;
+      case 1: return launch_kernel(prep_kernel<NB, KB, QB, 1>, grid, block, st, tm, s, c, k_new,
+                                   v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
+      case 2: return launch_kernel(prep_kernel<NB, KB, QB, 2>, grid, block, st, tm, s, c, k_new,
+                                   v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
+      case 4: return launch_kernel(prep_kernel<NB, KB, QB, 4>, grid, block, st, tm, s, c, k_new,
+                                   v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
+      default: return launch_kernel(prep_kernel<NB, KB, QB, 8>, grid, block, st, tm, s, c, k_new,
+                                    v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
     }
-  } else
-    launch_kernel(prep_kernel<NB, KB, QB, 0>, grid, block, st, tm, s, c, k_new, v_new, q, R, W,
-                  qrot, qcode, dbg_qrot, dbg_qcode);
+  }
+  return launch_kernel(prep_kernel<NB, KB, QB, 0>, grid, block, st, tm, s, c, k_new, v_new, q, R,
+                       W, qrot, qcode, dbg_qrot, dbg_qcode);
 }
 
 template <int NB>
-static void launch_prep_nb(const Shape& s, const CacheView& c, const void* k_new,
-                           const void* v_new, const void* q, const float* R, const float* W,
-                           float* qrot, uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode,
-                           PrepMode mode, KernelTimer tm, hipStream_t st) {
+static hipError_t launch_prep_nb(const Shape& s, const CacheView& c, const void* k_new,
+                                 const void* v_new, const void* q, const float* R,
+                                 const float* W, float* qrot, uint32_t* qcode, float* dbg_qrot,
+                                 uint32_t* dbg_qcode, PrepMode mode, KernelTimer tm,
+                                 hipStream_t st) {
   if (s.kv_bf16 && s.q_bf16)
-    launch_prep_t<NB, 1, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
-  else if (s.kv_bf16)
-    launch_prep_t<NB, 1, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
-  else if (s.q_bf16)
-    launch_prep_t<NB, 0, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
-  else
-    launch_prep_t<NB, 0, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
+    return launch_prep_t<NB, 1, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode,
+                                   mode, tm, st);
+  if (s.kv_bf16)
+    return launch_prep_t<NB, 1, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode,
+                                   mode, tm, st);
+  if (s.q_bf16)
+    return launch_prep_t<NB, 0, 1>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode,
+                                   mode, tm, st);
+  return launch_prep_t<NB, 0, 0>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode,
+                                 mode, tm, st);
 }
 
 hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, const void* v_new,
@@ -381,10 +386,10 @@ hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, co
                        uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, PrepMode mode,
                        KernelTimer tm, hipStream_t st) {
   if (s.NB == 128)
-    launch_prep_nb<128>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
-  else
-    launch_prep_nb<256>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode, tm, st);
-  return hipGetLastError();
+    return launch_prep_nb<128>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode,
+                               mode, tm, st);
+  return launch_prep_nb<256>(s, c, k_new, v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode, mode,
+                             tm, st);
 }
 
 }  // namespace hhr

@@ -324,13 +324,12 @@ hipError_t launch_build_mfma(const Shape& s, const CacheView& c, const float* R,
     }
   }
   dim3 grid(nper * nroles, s.Hkv, s.B);
+  const KernelTimer none{nullptr, nullptr};
   if (s.S == 16)
-    hipLaunchKernelGGL((build_mfma_kernel<16>), grid, dim3(kMThreads), 0, st, s, c, R, W, ntiles,
+    return launch_kernel(build_mfma_kernel<16>, grid, dim3(kMThreads), st, none, s, c, R, W,
+                         ntiles, nper);
+  return launch_kernel(build_mfma_kernel<32>, grid, dim3(kMThreads), st, none, s, c, R, W, ntiles,
                        nper);
-  else
-    hipLaunchKernelGGL((build_mfma_kernel<32>), grid, dim3(kMThreads), 0, st, s, c, R, W, ntiles,
-                       nper);
-  return hipGetLastError();
 }
 
 }  // namespace hhr

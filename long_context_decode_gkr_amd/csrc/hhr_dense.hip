@@ -447,21 +447,20 @@ int dense_tokens_per_split(const Shape& s) {
 }
 
 template <int BF16, int G>
-static void launch_dense_t(const Shape& s, const CacheView& c, const void* q, float* part,
+static hipError_t launch_dense_t(const Shape& s, const CacheView& c, const void* q, float* part,
                            int nsplit, int tpw, float scale_log2e, KernelTimer tm,
                            hipStream_t st) {
   const dim3 grid(nsplit, s.Hkv, s.B);
   const GatherList none{nullptr, nullptr, 0};
   if constexpr (BF16) {
     if (s.q_bf16)
-      launch_kernel(dense_attn_mfma_kernel<G, 0, 0>, grid, dim3(256), st, tm, s, c.K, c.V, q,
-                    c.seq_lens, part, nsplit, tpw, scale_log2e, none);
-    else
-      launch_kernel(dense_attn_mfma_kernel<G, 1, 0>, grid, dim3(256), st, tm, s, c.K, c.V, q,
-                    c.seq_lens, part, nsplit, tpw, scale_log2e, none);
+      return launch_kernel(dense_attn_mfma_kernel<G, 0, 0>, grid, dim3(256), st, tm, s, c.K, c.V,
+                           q, c.seq_lens, part, nsplit, tpw, scale_log2e, none);
+    return launch_kernel(dense_attn_mfma_kernel<G, 1, 0>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                         c.seq_lens, part, nsplit, tpw, scale_log2e, none);
   } else {
-    launch_kernel(dense_attn_kernel<BF16, G>, grid, dim3(256), st, tm, s, c.K, c.V, q,
-                  c.seq_lens, part, nsplit, tpw, scale_log2e);
+    return launch_kernel(dense_attn_kernel<BF16, G>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                         c.seq_lens, part, nsplit, tpw, scale_log2e);
   }
 }
 
@@ -472,32 +471,31 @@ hipError_t launch_dense(const Shape& s, const CacheView& c, const void* q, float
   float* part = static_cast<float*>(ws);
   const float sl2 = scale * 1.4426950408889634f;
   const KernelTimer tm = kernel_timer(dbg, 0);
+  hipError_t e;
   switch (s.G * 2 + s.kv_bf16) {
-    case 2: launch_dense_t<0, 1>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
-    case 3: launch_dense_t<1, 1>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
-    case 4: launch_dense_t<0, 2>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
-    case 5: launch_dense_t<1, 2>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
-    case 8: launch_dense_t<0, 4>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
-    case 9: launch_dense_t<1, 4>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
-    case 16: launch_dense_t<0, 8>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
-    default: launch_dense_t<1, 8>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
+    case 2: e = launch_dense_t<0, 1>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
+    case 3: e = launch_dense_t<1, 1>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
+    case 4: e = launch_dense_t<0, 2>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
+    case 5: e = launch_dense_t<1, 2>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
+    case 8: e = launch_dense_t<0, 4>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
+    case 9: e = launch_dense_t<1, 4>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
+    case 16: e = launch_dense_t<0, 8>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
+    default: e = launch_dense_t<1, 8>(s, c, q, part, nsplit, tpw, sl2, tm, st); break;
   }
-  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   return launch_combine(s, part, nsplit, out, c.seq_lens, 0, kernel_timer(dbg, 1), st);
 }
 
 template <int G>
-static void launch_gather_t(const Shape& s, const CacheView& c, const void* q, float* part,
+static hipError_t launch_gather_t(const Shape& s, const CacheView& c, const void* q, float* part,
                             int nsplit, float scale_log2e, const GatherList& gl, KernelTimer tm,
                             hipStream_t st) {
   const dim3 grid(nsplit, s.Hkv, s.B);
   if (s.q_bf16)
-    launch_kernel(dense_attn_mfma_kernel<G, 0, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
-                  c.seq_lens, part, nsplit, kGatherChunk, scale_log2e, gl);
-  else
-    launch_kernel(dense_attn_mfma_kernel<G, 1, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
-                  c.seq_lens, part, nsplit, kGatherChunk, scale_log2e, gl);
+    return launch_kernel(dense_attn_mfma_kernel<G, 0, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                         c.seq_lens, part, nsplit, kGatherChunk, scale_log2e, gl);
+  return launch_kernel(dense_attn_mfma_kernel<G, 1, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+                       c.seq_lens, part, nsplit, kGatherChunk, scale_log2e, gl);
 }
 
 hipError_t launch_attn_gather(const Shape& s, const CacheView& c, const void* q, float scale,
@@ -506,12 +504,11 @@ hipError_t launch_attn_gather(const Shape& s, const CacheView& c, const void* q,
   const GatherList gl{idx, cnt, istride};
   const float sl2 = scale * 1.4426950408889634f;
   switch (s.G) {
-    case 1: launch_gather_t<1>(s, c, q, part, nsplit, sl2, gl, tm, st); break;
-    case 2: launch_gather_t<2>(s, c, q, part, nsplit, sl2, gl, tm, st); break;
-    case 4: launch_gather_t<4>(s, c, q, part, nsplit, sl2, gl, tm, st); break;
-    default: launch_gather_t<8>(s, c, q, part, nsplit, sl2, gl, tm, st); break;
+    case 1: return launch_gather_t<1>(s, c, q, part, nsplit, sl2, gl, tm, st);
+    case 2: return launch_gather_t<2>(s, c, q, part, nsplit, sl2, gl, tm, st);
+    case 4: return launch_gather_t<4>(s, c, q, part, nsplit, sl2, gl, tm, st);
+    default: return launch_gather_t<8>(s, c, q, part, nsplit, sl2, gl, tm, st);
   }
-  return hipGetLastError();
 }
 
 size_t dense_workspace_bytes(const Shape& s) {

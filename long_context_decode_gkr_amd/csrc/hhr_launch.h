@@ -33,28 +33,45 @@ struct DebugView {
   uint16_t* dist;
   int32_t* token_idx;
   int32_t* token_count;
-  hipEvent_t* events;  // NULL or 10 events: start and stop of each of the five kernels
+  hipEvent_t* events;  // NULL or 2 kStepKernels events: start and stop of each kernel
 };
 
 // Start and stop events of one kernel's execution; both NULL for a plain launch.
 struct KernelTimer {
   hipEvent_t start, stop;
 };
+// Event slots of a decode step: 0 preparation, 1 page bound, 2 selection scan, 3 selection
+// emission, 4 attention, 5 merge (12 events: start and stop of each).
+constexpr int kStepKernels = 6;
 inline KernelTimer kernel_timer(const DebugView& d, int k) {
   return d.events ? KernelTimer{d.events[2 * k], d.events[2 * k + 1]} : KernelTimer{nullptr, nullptr};
 }
-// Launch on stream st; with a timer the runtime records its events around the kernel itself.
-template <typename F, typename... Args>
-inline void launch_kernel(F kernel, dim3 grid, dim3 block, hipStream_t st, KernelTimer tm,
-                          Args... args) {
-  if (tm.start)
-    hipExtLaunchKernelGGL(kernel, grid, block, 0, st, tm.start, tm.stop, 0, args...);
-  else
-    hipLaunchKernelGGL(kernel, grid, block, 0, st, args...);
+// Launch on stream st and return this launch's own status (not a sticky error left by an earlier
+// call); with a timer the runtime records its events around the kernel itself.
+template <typename... KArgs>
+inline hipError_t launch_args(const void* f, dim3 grid, dim3 block, hipStream_t st,
+                              KernelTimer tm, KArgs... v) {
+  void* argv[] = {static_cast<void*>(&v)...};
+  if (tm.start) return hipExtLaunchKernel(f, grid, block, argv, 0, st, tm.start, tm.stop, 0);
+  return hipLaunchKernel(f, grid, block, argv, 0, st);
+}
+template <typename... KArgs, typename... Args>
+inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
+                                KernelTimer tm, Args... args) {
+  static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
+  // each argument converted to the kernel's parameter type before its address is taken
+  return launch_args<KArgs...>(reinterpret_cast<const void*>(kernel), grid, block, st, tm,
+                               args...);
 }
 
 // Which stages choose the attended tokens (the stage-wise ablation of the method).
 enum class Stages { kBoth = 0, kPagesOnly = 1, kCodesOnly = 2 };
+
+// Page capacity (HHR_MAX_PAGES) and the page counts of one selection slice.
+constexpr int kMaxPages = 16384;
+constexpr int kSlicePages = 512;      // most kept pages per selection slice
+constexpr int kMinSlicePages = 8;     // fewest, when the step would not fill the GPU otherwise
+constexpr int kUnitSlots = 32768;     // most candidates of a one-workgroup-per-unit selection
 
 // Workspace carve-up of one decode call (byte offsets from the workspace base).
 struct DecodePlan {
@@ -62,12 +79,17 @@ struct DecodePlan {
   int shared;      // one page and token selection per KV head for its G query heads
   int kcap;        // most tokens attended per (b, h): the token budget clamped to max_seq_len,
                    // or (pages only) every token of the largest kept page set
-  int istride;     // per-(b, h) stride of the index list: kcap entries + one trash entry per lane
+  int istride;     // per-unit stride of the index list: kcap entries + one trash entry per lane
   int chunk;       // tokens per attention workgroup
   int nsplit;      // attention workgroups per (b, h)
+  int kpages;      // most kept pages per selection unit, min(Pmax, max(1, ceil(rho Pmax)))
+  int unit_select; // one workgroup per unit selects (else the sliced form)
+  int nsl;         // selection slices per unit (sliced form)
+  int dstride;     // per-unit stride of the candidate distances (elements, a multiple of 16)
   double rho;
   float scale;
-  size_t off_qrot, off_qcode, off_U, off_idx, off_cnt, off_part, off_dist, off_hist, total;
+  size_t off_qrot, off_qcode, off_U, off_idx, off_cnt, off_part, off_pages, off_dist, off_hist,
+      total;
 };
 
 DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages stages,
@@ -88,21 +110,28 @@ hipError_t launch_prep(const Shape& s, const CacheView& c, const void* k_new, co
                        const void* q, const float* R, const float* W, float* qrot,
                        uint32_t* qcode, float* dbg_qrot, uint32_t* dbg_qcode, PrepMode mode,
                        KernelTimer tm, hipStream_t st);
-// Fine stage over every token (fine-stage-only variant): distances and per-slice histograms,
-// then the threshold and the ordered emission of the selected tokens, kScanTok tokens per
-// workgroup in both kernels.
-constexpr int kScanTok = 4096;
-struct ScanArgs {
+// Selection of the attended tokens (select_scan_kernel, select_emit_kernel), grid
+// (nsl, units, B): the exact page cut, the Hamming distances of the kept pages' keys and one
+// histogram per slice, then the token threshold and the ordered emission.
+struct SelectArgs {
   const uint32_t* qcode;  // [B][Hq][NW]
-  void* dist;             // [units][Lmax]: one byte per distance (two for 256-bit codes)
+  const float* U;         // [units][Pmax] page bounds; NULL when every page is kept
+  int32_t* pages;         // [units][kpages] kept pages, ascending
+  void* dist;             // [units][dstride] distance per candidate slot (u8, or u16 for 256 bits)
   int32_t* hist;          // [units][nsl][NB + 1]
   int32_t* idx;           // [units][istride]
   int32_t* cnt;           // [units]
-  int kcap, istride, nsl, appended, shared;
+  double rho;
+  int kcap, istride, nsl, kpages, dstride;
+  int appended;           // a token is appended in this step (seq_lens is advanced at its end)
+  int fine;               // 0: no Hamming ranking, every candidate is taken (coarse stage only)
+  int shared;             // units are KV heads (group-shared selection)
 };
-int scan_slices(const Shape& s);
-hipError_t launch_scan_select(const Shape& s, const CacheView& c, const ScanArgs& a,
-                              const DebugView& dbg, hipStream_t st);
+// Slices per unit for kpages kept pages at most over `units` selection units.
+int select_slices(int kpages, int units, bool all_kept);
+// unit: one workgroup per unit (kpages * S <= kUnitSlots and bounds given), else the sliced form.
+hipError_t launch_select(const Shape& s, const CacheView& c, const SelectArgs& a,
+                         const DebugView& dbg, bool unit, hipStream_t st);
 // Merge of split-K attention partials [B][Hq][nsplit][128 + 2] (o, m, l) into out
 // [B][Hq][128]; with `appended` it also advances seq_lens (the sparse step's last kernel).
 hipError_t launch_combine(const Shape& s, const float* part, int nsplit, float* out,

@@ -7,6 +7,7 @@
 #include <hip/hip_runtime.h>
 
 #include "hhr.h"
+#include "hhr_launch.h"
 
 namespace {
 
@@ -53,10 +54,11 @@ hhr_status hhr_read_probe(const void* src, size_t bytes, float* partial, hhr_str
     return HHR_ERR_INVALID_ARG;
   const size_t blocks = hhr_read_probe_blocks(bytes);
   if (blocks > 0x7FFFFFFFull) return HHR_ERR_CAPACITY;
-  hipLaunchKernelGGL(read_probe_kernel, dim3(unsigned(blocks)), dim3(kProbeThreads), 0,
-                     reinterpret_cast<hipStream_t>(stream),
-                     static_cast<const f32x4v*>(src), bytes / 16, partial);
-  return hipGetLastError() == hipSuccess ? HHR_OK : HHR_ERR_HIP;
+  const hipError_t e = hhr::launch_kernel(
+      read_probe_kernel, dim3(unsigned(blocks)), dim3(kProbeThreads),
+      reinterpret_cast<hipStream_t>(stream), hhr::KernelTimer{nullptr, nullptr},
+      static_cast<const f32x4v*>(src), bytes / 16, partial);
+  return e == hipSuccess ? HHR_OK : HHR_ERR_HIP;
 }
 
 }  // extern "C"

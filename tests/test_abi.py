@@ -134,6 +134,85 @@ def test_invalid_stages(stages):
     assert hb.hhr_decode_workspace_bytes(good_dims(), p) == 0
 
 
+def _align256(x):
+    return (x + 255) // 256 * 256
+
+
+def expected_workspace(B, Hq, Hkv, S, nb, lmax, rho, k, stages, shared=False, bf16=True):
+    """The decode workspace carve-up written out: q~, query codes, bounds, index rows (kcap
+    rounded to 4 plus 64 trash entries), counts, attention partials, then the selection's kept
+    page ids, candidate distances and per-slice histograms."""
+    import math
+    import bench
+    pmax = lmax // S
+    if stages == hb.HHR_STAGES_CODES_ONLY:
+        rho = 1.0
+    kpages = min(pmax, max(1, math.ceil(rho * pmax)))
+    kcap = min(kpages * S, lmax) if stages == hb.HHR_STAGES_PAGES_ONLY else min(k, lmax)
+    chunk = 128 if bf16 else 64       # rows per attention workgroup (both bf16 kernels: 128)
+    nsplit = -(-kcap // chunk)
+    BH, NU = B * Hq, B * (Hkv if shared else Hq)
+    nsl = bench.select_slices(kpages, NU, stages == hb.HHR_STAGES_CODES_ONLY)
+    dstride = (kpages * S + 15) // 16 * 16
+    istride = (kcap + 3) // 4 * 4 + 64
+    parts = [BH * 128 * 4, BH * (nb // 32) * 4, NU * pmax * 4, NU * istride * 4, NU * 4,
+             BH * nsplit * 130 * 4, NU * kpages * 4, NU * dstride * (1 if nb == 128 else 2),
+             NU * nsl * (nb + 1) * 4]
+    return sum(_align256(x) for x in parts)
+
+
+@pytest.mark.parametrize("lmax,S,nb,rho,k,shared", [
+    (131072, 16, 128, 1 / 16, 4096, False), (32768, 16, 128, 1 / 8, 2048, False),
+    (131072, 16, 128, 1 / 16, 4096, True), (65536, 32, 256, 1 / 8, 4096, False),
+    (64, 16, 128, 0.3, 8, False), (262144, 16, 128, 1.0, 100, False)])
+@pytest.mark.parametrize("stages", [hb.HHR_STAGES_BOTH, hb.HHR_STAGES_PAGES_ONLY,
+                                    hb.HHR_STAGES_CODES_ONLY])
+def test_workspace_size_matches_its_carve_up(lmax, S, nb, rho, k, shared, stages):
+    d = hb.make_dims(1, 32, 8, S, nb, lmax)
+    p = hb.Params(rho, k, 0.0, stages, int(shared))
+    assert hb.hhr_decode_workspace_bytes(d, p) == \
+        expected_workspace(1, 32, 8, S, nb, lmax, rho, k, stages, shared)
+
+
+@pytest.mark.parametrize("lmax,S,rho,units,stages", [
+    (2112, 16, 1.0, 1, hb.HHR_STAGES_CODES_ONLY),     # max_seq_len not a multiple of 4096
+    (4160, 32, 0.3, 32, hb.HHR_STAGES_BOTH),
+    (131072, 16, 1 / 16, 32, hb.HHR_STAGES_BOTH),
+    (262144, 16, 1.0, 32, hb.HHR_STAGES_CODES_ONLY),
+    (64, 16, 1.0, 3, hb.HHR_STAGES_PAGES_ONLY)])
+def test_sliced_selection_reads_stay_in_its_rows(lmax, S, rho, units, stages):
+    """The sliced selection's addressing, written out: for every sequence length, slice i of n
+    owns kept-page ranks [i n_keep / n, (i + 1) n_keep / n); its emission reads its slots' one-
+    or two-byte distances 16 at a time from a clamped start and one page id per 16 slots. Every
+    read must stay within the unit's row of kpages * S distances (rounded up to 16), which is
+    what the workspace holds per unit."""
+    import math
+    import bench
+    pmax = lmax // S
+    r = 1.0 if stages == hb.HHR_STAGES_CODES_ONLY else rho
+    kpages = min(pmax, max(1, math.ceil(r * pmax)))
+    nsl = bench.select_slices(kpages, units, stages == hb.HHR_STAGES_CODES_ONLY)
+    dstride = (kpages * S + 15) // 16 * 16
+    assert -(-kpages // nsl) <= 512                    # a slice's pages fit its LDS list
+    for L in sorted({1, S - 1, S, S + 1, lmax // 2 + 7, lmax - 1, lmax}):
+        P = -(-L // S)
+        n_keep = min(P, max(1, math.ceil(r * P)))
+        assert n_keep <= kpages
+        for i in range(nsl):
+            r0, r1 = i * n_keep // nsl, (i + 1) * n_keep // nsl
+            nslots = (r1 - r0) * S
+            if nslots == 0:
+                continue
+            assert nslots % 16 == 0
+            for base in range(0, nslots, 256 * 16):
+                for tid in (0, 1, 255):
+                    s0 = min(base + 16 * tid, max(nslots - 16, 0))
+                    assert 0 <= r0 * S + s0 and r0 * S + s0 + 16 <= dstride
+                    assert r0 + s0 // S < r1                # its page id is in the slice
+            # the scan writes 4 distances per unit of 4 slots
+            assert r1 * S <= dstride
+
+
 def test_pages_only_workspace_holds_every_kept_token():
     d = good_dims(max_seq_len=131072)
     both = hb.hhr_decode_workspace_bytes(d, hb.Params(1 / 16, 4096, 0.0, hb.HHR_STAGES_BOTH))
@@ -143,8 +222,8 @@ def test_pages_only_workspace_holds_every_kept_token():
                                                        hb.HHR_STAGES_CODES_ONLY))
     # pages only: 512 kept pages x 16 tokens = 8192 indices per head instead of 4096
     assert pages >= both + 32 * 4096 * 4
-    # fine only: plus the distances of every token (one byte each) and the slice histograms
-    assert codes >= both + 32 * 131072 and codes <= both + 32 * 131072 + 32 * 32 * 129 * 4 + 512
+    # fine only: every token a candidate (a distance byte each) and every page kept
+    assert codes >= both + 32 * (131072 - 8192) + 32 * (8192 - 512) * 4
 
 
 def dense_status(dims=None, cache=None, q=FAKE, scale=0.0, ws=FAKE * 256, ws_bytes=1 << 40,

@@ -31,7 +31,9 @@ def test_byte_model_128k():
     a = bench.algorithmic_bytes(synth.CONFIGS[3], [131072], append=True)
     # extrema: 8 KV heads x 8192 pages x 128 channels x (min + max) x 4 B; U: 32 x 8192 x 4 B
     assert a["page_bound"] == 8 * 8192 * 128 * 8 + 32 * 8192 * 4 + 32 * 128 * 4
-    # U row, query code, 512 pages x 16 codes of 16 B, 4096 indices, per query head
+    # per query head, one selection kernel: the U row, the query code, 512 pages x 16 codes of
+    # 16 B read, 4096 indices written
+    assert bench.unit_select("hhr", 512, 16)
     assert a["select"] == 32 * (8192 * 4 + 16 + 512 * 16 * 16 + 4096 * 4)
     # 4096 K + V rows of 256 B each, indices, q, 32 partials of 130 floats, per query head
     assert a["sparse_attn"] == 32 * (4096 * 512 + 4096 * 4 + 256 + 32 * 130 * 4)
@@ -39,12 +41,13 @@ def test_byte_model_128k():
     # R and W (1 MiB) dominate the preparation; the append adds 1.28 KiB per KV head
     assert a["prep"] - bench.algorithmic_bytes(synth.CONFIGS[3], [131072], False)["prep"] \
         == 8 * (512 + 512 + 16 + 2048)
+    assert "select_emit" not in a
 
 
 def test_byte_model_sums_over_sequences():
     cfg = synth.CONFIGS[4]
-    one = [bench.algorithmic_bytes(cfg, [L], False) for L in (8192, 20000)]
-    both = bench.algorithmic_bytes(cfg, [8192, 20000], False)
+    one = [bench.algorithmic_bytes(cfg, [L], False, lmax=32768) for L in (8192, 20000)]
+    both = bench.algorithmic_bytes(cfg, [8192, 20000], False, lmax=32768)
     for k in ("page_bound", "select", "sparse_attn", "combine"):
         assert both[k] == one[0][k] + one[1][k]
     # R and W are read once per KV head, not once per sequence
@@ -63,25 +66,48 @@ def test_byte_model_of_the_variants():
     pages = bench.algorithmic_bytes(cfg, [131072], False, "pages")
     codes = bench.algorithmic_bytes(cfg, [131072], False, "codes")
     # coarse stage alone: no codes read, all 512 x 16 candidates attended
-    assert pages["select"] == 32 * (8192 * 4 + 8192 * 4)
+    assert pages["select"] == 32 * (8192 * 4 + 16 + 8192 * 4)
     assert pages["sparse_attn"] > 2 * base["sparse_attn"] - 32 * 4096 * 8
-    # fine stage alone: no bound kernel, every token's code read by the scan
-    assert "page_bound" not in codes and "select" not in codes
-    assert codes["hamming_scan"] == 32 * (16 + 131072 * 16 + 131072 + 32 * 129 * 4)
+    # fine stage alone: no bound kernel; the sliced selection (8192 pages in 32 slices of 256
+    # per query head) reads every token's code once and writes a distance byte per token, the
+    # page ids and the histograms, which the emission reads back with the 4096 indices written
+    assert "page_bound" not in codes
+    assert not bench.unit_select("codes", 8192, 16)
+    assert bench.select_slices(8192, 32, True) == 32
+    inter = 131072 + 8192 * 4 + 32 * 129 * 4
+    assert codes["select"] == 32 * (16 + 131072 * 16 + inter)
+    assert codes["select_emit"] == 32 * (inter + 4096 * 4)
     assert codes["sparse_attn"] == base["sparse_attn"]
     dense = bench.algorithmic_bytes(cfg, [131072], False, "dense", 131072)
     # every K and V row once per KV head (512 MiB) dominates
     assert 8 * 131072 * 512 < dense["dense_attn"] < 1.01 * 8 * 131072 * 512
     assert set(bench.VARIANTS) == {"hhr", "identity-r", "pages", "codes", "dense",
                                    "bf16-extrema", "group-shared"}
+    assert "prep" in codes and "prep" in base
     sh = bench.algorithmic_bytes(cfg, [131072], False, "group-shared")
     # one row set per KV head: a quarter of the K/V gather
     assert sh["sparse_attn"] < base["sparse_attn"] / 3
     half = bench.algorithmic_bytes(cfg, [131072], False, "bf16-extrema")
     assert half["page_bound"] == 8 * 8192 * 128 * 4 + 32 * 8192 * 4 + 32 * 128 * 4
-    for v, ks in bench.VARIANTS.items():
+    for v in bench.VARIANTS:
         alg = bench.algorithmic_bytes(cfg, [131072], False, v, 131072)
-        assert {n for n, _ in ks} == set(alg), v
+        unit = bench.unit_select(v, 8192 if v == "codes" else 512, 16)
+        assert {n for n, _ in bench.timed_kernels(v, unit)} == set(alg), v
+
+
+def test_select_form_rule():
+    # one workgroup per unit while the largest kept page set's tokens fit 32768 LDS slots
+    assert bench.unit_select("hhr", 2048, 16) and not bench.unit_select("hhr", 2049, 16)
+    assert bench.unit_select("pages", 1024, 32) and not bench.unit_select("codes", 4, 16)
+
+
+def test_select_slice_rule():
+    # about 256 workgroups with a page cut, 1024 without; 8..512 kept pages per slice
+    assert bench.select_slices(256, 32, False) == 8            # 32K, batch 1: 32 pages each
+    assert bench.select_slices(512, 8, False) == 32            # 128K, group-shared
+    assert bench.select_slices(615, 256, False) == 2           # 8 sequences: the 512-page cap
+    assert bench.select_slices(4, 1, False) == 1               # tiny: at least 8 pages a slice
+    assert bench.select_slices(16384, 1, True) == 1024
 
 
 def test_dense_split_rule():
