@@ -2,8 +2,13 @@
 ABI, run the CPU oracle on the same arrays, and compare them by the parity rules:
 
   * query codes, key codes, Hamming distances: bit-exact;
-  * kept page sets: a page in the symmetric difference must have an oracle bound within
-    1e-5 * S_p of the oracle's cut value, S_p = sum_j |q~_j| max(|l_j|, |u_j|);
+  * page extrema: inside their admissible sets (within the builder's fp32 error of the oracle's
+    rotated keys; for bf16 summaries, rounded outward from such a value);
+  * page bounds: within tau_p = 1e-5 * S_p (S_p = sum_j |q~_j| max(|l_j|, |u_j|)) plus, for
+    bf16 summaries, the bound's spread over the admissible extrema, of the oracle's bound on its
+    own extrema;
+  * kept page sets: exact for the GPU's own bounds; against the oracle a page in the symmetric
+    difference must have an oracle bound within tau_p + max(tau) of the oracle's cut value;
   * token indices: bit-exact against the oracle's fine stage run on the GPU's page set;
   * attention output: max |o - o*| / max |o*| <= 2e-3 against exact attention over those
     indices.
@@ -18,6 +23,10 @@ from oracle import hhr_oracle as orc
 
 OUT_RTOL = 2e-3
 BOUND_RTOL = 1e-5
+# The matrix-core index build rounds its fp32 accumulation of a 128-term dot product (bf16 pieces
+# of R, fp32 sums): its page extrema may sit up to ~20 fp32 ulps of |k|_2 (8e-6 |k|_2) from the
+# correctly rounded rotated keys, against the few ulps of the fp64 build and the append.
+MFMA_EXTREMA_SCALE = 20.0
 
 
 def torch_mod():
@@ -57,6 +66,12 @@ class GpuLayer:
     def build(self, method="auto"):
         hb.build_pages(self.cache, self.R, self.W, method=method)
         torch_mod().cuda.synchronize()
+        self.built = method
+
+    def extrema_scale(self) -> float:
+        """The extrema tolerance scale of the builder that made this index."""
+        mfma = getattr(self, "built", "auto") == "auto" and self.cfg.dtype == "bf16"
+        return MFMA_EXTREMA_SCALE if mfma else 1.0
 
     def decode(self, rho, k, scale=0.0, debug=True, stages="both", group_shared=False):
         torch = torch_mod()
@@ -78,21 +93,29 @@ class GpuLayer:
 
 
 def oracle_index(layer: GpuLayer, heads_kv=None):
+    """The oracle's index of the layer: key codes, page extrema as stored (bf16 rounded outward
+    for a bf16 summary) in lo / hi, and the fp32 extrema before that rounding in lo32 / hi32."""
     d, cfg = layer.data, layer.cfg
-    if heads_kv is None:
-        return orc.build_layer(d["K"], d["seq_lens"], d["R"], d["W"], cfg.page_size,
-                               layer.summary)
     B, Hkv, Lmax, dd = d["K"].shape
     Pmax = Lmax // cfg.page_size
     lo = np.zeros((B, Hkv, Pmax, dd), np.float32)
     hi = np.zeros_like(lo)
     kc = np.zeros((B, Hkv, Lmax, cfg.hash_bits // 32), np.uint32)
-    for b, g in heads_kv:
+    pairs = heads_kv or [(b, g) for b in range(B) for g in range(Hkv)]
+    for b, g in pairs:
         L = int(d["seq_lens"][b])
-        l_, h_, c_ = orc.build_head(d["K"][b, g], L, d["R"][g], d["W"][g], cfg.page_size,
-                                    layer.summary)
+        l_, h_, c_ = orc.build_head(d["K"][b, g], L, d["R"][g], d["W"][g], cfg.page_size, "f32")
         lo[b, g, :len(l_)], hi[b, g, :len(h_)], kc[b, g, :L] = l_, h_, c_
-    return dict(lo=lo, hi=hi, codes=kc)
+    return summary_index(dict(lo32=lo, hi32=hi, codes=kc), layer.summary)
+
+
+def summary_index(ref: dict, summary: str) -> dict:
+    """lo / hi as the cache stores them, from the fp32 extrema lo32 / hi32."""
+    if summary == "bf16":
+        lo, hi = orc.extrema_bf16(ref["lo32"], ref["hi32"])
+    else:
+        lo, hi = ref["lo32"], ref["hi32"]
+    return dict(ref, lo=lo, hi=hi)
 
 
 def extrema_tolerance(K_bg: np.ndarray, L: int) -> float:
@@ -102,34 +125,94 @@ def extrema_tolerance(K_bg: np.ndarray, L: int) -> float:
     return 4e-7 * float(np.linalg.norm(K_bg[:L].astype(np.float64), axis=1).max())
 
 
-def check_index(layer: GpuLayer, ref: dict, pairs=None, extrema_atol_scale=1.0):
-    """Key codes bit-exact; page extrema within a few fp32 ulps (bf16 extrema: the outward
-    rounding of values a few fp32 ulps apart, so equal or one bf16 step apart)."""
+def bf16_down_up(x):
+    """The bf16 grid values at or below and at or above each float64 x (the oracle's directed
+    bf16 rounding, on float64 inputs)."""
+    x = np.asarray(x, np.float64)
+    e = np.frexp(x)[1].astype(np.float64) - 1.0
+    ulp = np.exp2(np.maximum(e, -126.0) - 7.0)
+    return np.floor(x / ulp) * ulp, np.ceil(x / ulp) * ulp
+
+
+def admissible_extrema(lo32, hi32, tol, summary):
+    """[min, max] of what a correct GPU may store for each extremum: the fp32 value within tol
+    of the oracle's (the builders' rounding of the rotated keys), stored as is (fp32 summary)
+    or, for a bf16 summary, the minimum rounded toward -inf and the maximum toward +inf."""
+    lo32 = np.asarray(lo32, np.float64)
+    hi32 = np.asarray(hi32, np.float64)
+    if summary == "bf16":
+        lmin, lmax = bf16_down_up(lo32 - tol)[0], bf16_down_up(lo32 + tol)[0]
+        hmin, hmax = bf16_down_up(hi32 - tol)[1], bf16_down_up(hi32 + tol)[1]
+        return (lmin, lmax), (hmin, hmax)
+    return (lo32 - tol, lo32 + tol), (hi32 - tol, hi32 + tol)
+
+
+def check_index(layer: GpuLayer, ref: dict, pairs=None, extrema_atol_scale=None):
+    """Key codes bit-exact; each stored extremum inside its admissible set (admissible_extrema:
+    within a few fp32 ulps of the oracle's, and for a bf16 summary a bf16 value rounded in the
+    right direction from such an fp32 value)."""
     got = layer.index_host()
     d, S = layer.data, layer.cfg.page_size
     B, Hkv = d["K"].shape[:2]
     pairs = pairs or [(b, g) for b in range(B) for g in range(Hkv)]
+    if extrema_atol_scale is None:
+        extrema_atol_scale = layer.extrema_scale()
     for b, g in pairs:
         L = int(d["seq_lens"][b])
         P = orc.num_pages(L, S)
         np.testing.assert_array_equal(got["codes"][b, g, :L], ref["codes"][b, g, :L],
                                       err_msg=f"key codes differ at b={b} g={g}")
         tol = extrema_tolerance(d["K"][b, g], L) * extrema_atol_scale
-        for name in ("lo", "hi"):
-            r = ref[name][b, g, :P].astype(np.float64)
-            diff = np.abs(got[name][b, g, :P].astype(np.float64) - r)
-            allow = tol + (np.abs(r) * 2.0 ** -7 if layer.summary == "bf16" else 0.0)
-            assert np.all(diff <= allow), (name, b, g, diff.max(), tol)
+        adm = admissible_extrema(ref["lo32"][b, g, :P], ref["hi32"][b, g, :P], tol, layer.summary)
+        for name, (amin, amax) in zip(("lo", "hi"), adm):
+            v = got[name][b, g, :P].astype(np.float64)
+            assert np.all((amin <= v) & (v <= amax)), (name, b, g, float(np.max(amin - v)),
+                                                        float(np.max(v - amax)), tol)
+            if layer.summary == "bf16":   # a bf16 value (the storage is 16 bits wide)
+                assert np.array_equal(bf16_down_up(v)[0], v), (name, b, g)
+
+
+def bound_tolerance(qt, ref: dict, b: int, g: int, P: int, tol: float, summary: str):
+    """Allowed |U_gpu - U_oracle| per page: 1e-5 S_p (S_p = sum_j |q~_j| max(|l_j|, |u_j|)),
+    plus sum_j |q~_j| w_j with w_j the width of the admissible set of the extremum q~_j selects
+    (u_j for q~_j >= 0, l_j otherwise): the GPU's stored extrema may be any admissible value."""
+    qt = np.asarray(qt, np.float64)
+    lo = ref["lo"][b, g, :P].astype(np.float64)
+    hi = ref["hi"][b, g, :P].astype(np.float64)
+    Sp = (np.abs(qt)[None, :] * np.maximum(np.abs(lo), np.abs(hi))).sum(axis=1)
+    (lmin, lmax), (hmin, hmax) = admissible_extrema(ref["lo32"][b, g, :P], ref["hi32"][b, g, :P],
+                                                    tol, summary)
+    if summary == "bf16":
+        width = np.where(qt[None, :] >= 0, hmax - hmin, lmax - lmin)
+        dU = (np.abs(qt)[None, :] * width).sum(axis=1)
+    else:
+        dU = np.zeros(P)     # fp32 extrema: within the 1e-5 S_p of the bound's reading
+    return BOUND_RTOL * Sp + dU
+
+
+def check_page_set(gp, o_pages, U_orc, n_keep, tau, where):
+    """The GPU's kept pages gp against the oracle's: a page in the symmetric difference must have
+    an oracle bound within tau_p + max(tau over the difference) of the oracle's cut (a swapped
+    pair p, c satisfies U(c) - U(p) <= tau_p + tau_c)."""
+    cut = np.sort(U_orc)[::-1][n_keep - 1]
+    sym = sorted(set(gp.tolist()) ^ set(o_pages.tolist()))
+    if sym:
+        tmax = max(tau[p] for p in sym)
+        for p in sym:
+            assert abs(U_orc[p] - cut) <= tau[p] + tmax, (where, p, U_orc[p], cut, tau[p])
+    return len(sym) // 2
 
 
 def check_decode(layer: GpuLayer, out, dbg, rho, k, scale=None, heads=None, ref_index=None,
-                 stages="both"):
+                 stages="both", extrema_atol_scale=None):
     """Compare one decode step with the oracle on the listed (b, h) pairs (default: all).
     `stages`: "both", "pages" (coarse stage only) or "codes" (fine stage only)."""
     d, cfg = layer.data, layer.cfg
     S, G = cfg.page_size, cfg.group
     scale = orc.default_scale(128) if not scale else scale
     ref_index = ref_index or oracle_index(layer)
+    if extrema_atol_scale is None:
+        extrema_atol_scale = layer.extrema_scale()
     out_h = out.cpu().numpy()
     qr = dbg.q_rot.cpu().numpy()
     qc = dbg.q_code.cpu().numpy().view(np.uint32)
@@ -139,11 +222,6 @@ def check_decode(layer: GpuLayer, out, dbg, rho, k, scale=None, heads=None, ref_
     dist = dbg.dist.cpu().numpy().view(np.uint16)
     tidx = dbg.token_idx.cpu().numpy()
     tcnt = dbg.token_count.cpu().numpy()
-    gidx = layer.index_host()
-    if layer.summary == "bf16":
-        # bf16 extrema: the bounds and the page set are checked against the GPU's own extrema, which
-        # check_index holds to the oracle's outward rounding (equal or one bf16 step apart)
-        ref_index = dict(ref_index, lo=gidx["lo"], hi=gidx["hi"])
     heads = heads or [(b, h) for b in range(cfg.batch) for h in range(cfg.num_q_heads)]
     stats = dict(max_out_rel=0.0, swaps=0)
     for b, h in heads:
@@ -166,22 +244,15 @@ def check_decode(layer: GpuLayer, out, dbg, rho, k, scale=None, heads=None, ref_
         if stages == "codes":
             np.testing.assert_array_equal(gp, np.arange(P))   # every page is a candidate
         else:
-            # bounds: GPU (own index, own q~) against the oracle
-            qt = o["q_rot"].astype(np.float64)
-            lo = ref_index["lo"][b, g, :P].astype(np.float64)
-            hi = ref_index["hi"][b, g, :P].astype(np.float64)
-            Sp = np.abs(qt)[None, :] * np.maximum(np.abs(lo), np.abs(hi))
-            Sp = Sp.sum(axis=1)
-            assert np.all(np.abs(U[b, h, :P] - o["U"]) <= BOUND_RTOL * Sp), (b, h)
+            # bounds: GPU (own index, own q~) against the oracle's (its own extrema)
+            tol = extrema_tolerance(d["K"][b, g], L) * extrema_atol_scale
+            tau = bound_tolerance(o["q_rot"], ref_index, b, g, P, tol, layer.summary)
+            assert np.all(np.abs(U[b, h, :P] - o["U"]) <= tau), (b, h)
             # page set: exact for the GPU's own bounds; swaps against the oracle only at
             # near-ties
             np.testing.assert_array_equal(gp, orc.select_pages(U[b, h, :P].astype(np.float64),
                                                                n_keep))
-            cut = np.sort(o["U"])[::-1][n_keep - 1]
-            sym = set(gp.tolist()) ^ set(o["pages"].tolist())
-            for p in sym:
-                assert abs(o["U"][p] - cut) <= BOUND_RTOL * Sp[p], (b, h, p, o["U"][p], cut)
-            stats["swaps"] += len(sym) // 2
+            stats["swaps"] += check_page_set(gp, o["pages"], o["U"], n_keep, tau, (b, h))
         # fine stage on the GPU's pages
         cand = orc.candidates(gp, L, S)
         if stages == "pages":
@@ -203,7 +274,7 @@ def check_decode(layer: GpuLayer, out, dbg, rho, k, scale=None, heads=None, ref_
 
 
 def check_decode_shared(layer: GpuLayer, out, dbg, rho, k, scale=None, ref_index=None,
-                        stages="both", groups=None):
+                        stages="both", groups=None, extrema_atol_scale=None):
     """One selection per (b, KV head) (group_shared): per-head bounds and query codes as in
     check_decode; the group's page set on the GPU's own U (the largest head bound) and, against
     the oracle, swaps only at near-ties; distances (smallest over the group) and tokens
@@ -212,9 +283,8 @@ def check_decode_shared(layer: GpuLayer, out, dbg, rho, k, scale=None, ref_index
     S, G, Hkv = cfg.page_size, cfg.group, cfg.num_kv_heads
     scale = orc.default_scale(128) if not scale else scale
     ref_index = ref_index or oracle_index(layer)
-    gidx = layer.index_host()
-    if layer.summary == "bf16":
-        ref_index = dict(ref_index, lo=gidx["lo"], hi=gidx["hi"])
+    if extrema_atol_scale is None:
+        extrema_atol_scale = layer.extrema_scale()
     out_h = out.cpu().numpy()
     qr = dbg.q_rot.cpu().numpy()
     qc = dbg.q_code.cpu().numpy().view(np.uint32)
@@ -247,23 +317,17 @@ def check_decode_shared(layer: GpuLayer, out, dbg, rho, k, scale=None, ref_index
         if stages == "codes":
             np.testing.assert_array_equal(gp, np.arange(P))
         else:
-            lo = ref_index["lo"][b, g, :P].astype(np.float64)
-            hi = ref_index["hi"][b, g, :P].astype(np.float64)
-            Sp = np.zeros(P)
+            tol = extrema_tolerance(d["K"][b, g], L) * extrema_atol_scale
+            tau = np.zeros(P)
             for i, h in enumerate(heads):
-                sp = (np.abs(o["q_rot"][i].astype(np.float64))[None, :]
-                      * np.maximum(np.abs(lo), np.abs(hi))).sum(axis=1)
+                th = bound_tolerance(o["q_rot"][i], ref_index, b, g, P, tol, layer.summary)
                 Uh = orc.page_bounds(o["q_rot"][i], ref_index["lo"][b, g, :P],
                                      ref_index["hi"][b, g, :P])
-                assert np.all(np.abs(U[b, h, :P] - Uh) <= BOUND_RTOL * sp), (b, h)
-                Sp = np.maximum(Sp, sp)
+                assert np.all(np.abs(U[b, h, :P] - Uh) <= th), (b, h)
+                tau = np.maximum(tau, th)
             Ug = U[b, heads, :P].astype(np.float64).max(axis=0)   # the GPU's group bound
             np.testing.assert_array_equal(gp, orc.select_pages(Ug, n_keep))
-            cut = np.sort(o["U"])[::-1][n_keep - 1]
-            sym = set(gp.tolist()) ^ set(o["pages"].tolist())
-            for p in sym:
-                assert abs(o["U"][p] - cut) <= BOUND_RTOL * Sp[p], (b, g, p)
-            stats["swaps"] += len(sym) // 2
+            stats["swaps"] += check_page_set(gp, o["pages"], o["U"], n_keep, tau, (b, g))
         cand = orc.candidates(gp, L, S)
         if stages == "pages":
             sel = cand

@@ -188,6 +188,7 @@ def test_decode_clustered_bounds(mode):
     ext = (c[:, None] * v[None, :]).astype(np.float32)          # [P][128]
     lo = np.broadcast_to(ext, (1, Hkv, P, 128)).copy()
     ref["lo"], ref["hi"] = lo, lo.copy()
+    ref["lo32"], ref["hi32"] = ref["lo"], ref["hi"]
     dev = torch.from_numpy(lo).permute(0, 1, 3, 2).contiguous().cuda()
     lay.cache.page_min.copy_(dev)
     lay.cache.page_max.copy_(dev)
