@@ -1,12 +1,37 @@
 // C ABI of the HHR decode library: argument validation, workspace planning, launch order.
 // Declarations and the full contract are in include/hhr.h.
 #include <math.h>
+#include <stdarg.h>
 #include <stdint.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
 
 #include "hhr.h"
 #include "hhr_launch.h"
 
 using namespace hhr;
+
+namespace hhr {
+
+bool trace_on() {
+  static const bool on = [] {
+    const char* v = getenv("HHR_TRACE");
+    return v && *v && strcmp(v, "0") != 0;
+  }();
+  return on;
+}
+
+void trace_printf(const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  fputs("[hhr] ", stderr);
+  vfprintf(stderr, fmt, ap);
+  fputc('\n', stderr);
+  va_end(ap);
+}
+
+}  // namespace hhr
 
 namespace {
 

@@ -119,7 +119,7 @@ template <int NB, int S>
 static hipError_t launch_build_fp64_t(const Shape& s, const CacheView& c, const float* R,
                                       const float* W, hipStream_t st) {
   dim3 grid((s.Lmax + kBuildTile - 1) / kBuildTile, s.Hkv, s.B);
-  return launch_kernel(build_fp64_kernel<NB, S>, grid, dim3(kD + NB), st,
+  return launch_kernel("build_fp64_kernel", build_fp64_kernel<NB, S>, grid, dim3(kD + NB), st,
                        KernelTimer{nullptr, nullptr}, s, c, R, W);
 }
 
@@ -348,17 +348,22 @@ static hipError_t launch_prep_t(const Shape& s, const CacheView& c, const void* 
   dim3 block(prep_threads<NB>());
   if (mode == PrepMode::kDecode) {
     switch (s.G) {
-      case 1: return launch_kernel(prep_kernel<NB, KB, QB, 1>, grid, block, st, tm, s, c, k_new,
+      case 1: return launch_kernel("prep_kernel",
+                                   prep_kernel<NB, KB, QB, 1>, grid, block, st, tm, s, c, k_new,
                                    v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
-      case 2: return launch_kernel(prep_kernel<NB, KB, QB, 2>, grid, block, st, tm, s, c, k_new,
+      case 2: return launch_kernel("prep_kernel",
+                                   prep_kernel<NB, KB, QB, 2>, grid, block, st, tm, s, c, k_new,
                                    v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
-      case 4: return launch_kernel(prep_kernel<NB, KB, QB, 4>, grid, block, st, tm, s, c, k_new,
+      case 4: return launch_kernel("prep_kernel",
+                                   prep_kernel<NB, KB, QB, 4>, grid, block, st, tm, s, c, k_new,
                                    v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
-      default: return launch_kernel(prep_kernel<NB, KB, QB, 8>, grid, block, st, tm, s, c, k_new,
+      default: return launch_kernel("prep_kernel",
+                                    prep_kernel<NB, KB, QB, 8>, grid, block, st, tm, s, c, k_new,
                                     v_new, q, R, W, qrot, qcode, dbg_qrot, dbg_qcode);
     }
   }
-  return launch_kernel(prep_kernel<NB, KB, QB, 0>, grid, block, st, tm, s, c, k_new, v_new, q, R,
+  return launch_kernel("prep_kernel",
+                       prep_kernel<NB, KB, QB, 0>, grid, block, st, tm, s, c, k_new, v_new, q, R,
                        W, qrot, qcode, dbg_qrot, dbg_qcode);
 }
 

@@ -326,9 +326,11 @@ hipError_t launch_build_mfma(const Shape& s, const CacheView& c, const float* R,
   dim3 grid(nper * nroles, s.Hkv, s.B);
   const KernelTimer none{nullptr, nullptr};
   if (s.S == 16)
-    return launch_kernel(build_mfma_kernel<16>, grid, dim3(kMThreads), st, none, s, c, R, W,
+    return launch_kernel("build_mfma_kernel",
+                         build_mfma_kernel<16>, grid, dim3(kMThreads), st, none, s, c, R, W,
                          ntiles, nper);
-  return launch_kernel(build_mfma_kernel<32>, grid, dim3(kMThreads), st, none, s, c, R, W, ntiles,
+  return launch_kernel("build_mfma_kernel",
+                       build_mfma_kernel<32>, grid, dim3(kMThreads), st, none, s, c, R, W, ntiles,
                        nper);
 }
 

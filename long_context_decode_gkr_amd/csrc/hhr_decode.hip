@@ -445,9 +445,10 @@ static hipError_t launch_bound_t(const Shape& s, const CacheView& c, const Bound
                                  const DebugView& dbg, hipStream_t st) {
   dim3 grid((s.Pmax + kBoundPages - 1) / kBoundPages, s.Hkv, s.B);
   if (s.sum_bf16)
-    return launch_kernel(page_bound_kernel<G, 1>, grid, dim3(kBoundThreads), st,
+    return launch_kernel("page_bound_kernel",
+                         page_bound_kernel<G, 1>, grid, dim3(kBoundThreads), st,
                          kernel_timer(dbg, 1), s, c, a, dbg.bounds);
-  return launch_kernel(page_bound_kernel<G, 0>, grid, dim3(kBoundThreads), st,
+  return launch_kernel("page_bound_kernel", page_bound_kernel<G, 0>, grid, dim3(kBoundThreads), st,
                        kernel_timer(dbg, 1), s, c, a, dbg.bounds);
 }
 
@@ -472,6 +473,22 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
   float* part = reinterpret_cast<float*>(base + p.off_part);
   const int appended = k_new != nullptr ? 1 : 0;
   hipError_t e;
+  if (trace_on()) {
+    // sizes for full sequences (seq_lens is in device memory): what each kernel reads at most
+    const double esz = s.kv_bf16 ? 2.0 : 4.0, xsz = s.sum_bf16 ? 2.0 : 4.0;
+    const double NU = double(s.B) * (p.shared ? s.Hkv : s.Hq);
+    trace_printf("decode B %d Hq %d Hkv %d S %d NB %d Lmax %d stages %d shared %d append %d: "
+                 "kpages %d kcap %d, selection %s (%d slices), %d attention splits, workspace "
+                 "%zu B", s.B, s.Hq, s.Hkv, s.S, s.NB, s.Lmax, int(p.stages), p.shared, appended,
+                 p.kpages, p.kcap, p.unit_select ? "one workgroup per unit" : "sliced", p.nsl,
+                 p.nsplit, p.total);
+    trace_printf("bytes at most: prep %.0f (R, W, q), page_bound %.0f (extrema) + %.0f (U), "
+                 "select %.0f (U, candidate codes), attention %.0f (K, V rows)",
+                 double(s.Hkv) * 128 * (128 + s.NB) * 4 + double(s.B) * s.Hq * 128 * esz,
+                 double(s.B) * s.Hkv * 128 * s.Pmax * 2 * xsz, NU * s.Pmax * 4,
+                 NU * (s.Pmax * 4.0 + double(p.kpages) * s.S * s.NB / 8),
+                 NU * double(p.kcap) * 2 * 128 * esz);
+  }
 
   // seq_lens[b] stays t during the step; every kernel works on t + 1 tokens when a token is
   // appended, and the last kernel stores t + 1.
@@ -505,10 +522,12 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
     e = launch_attn_gather(s, c, q, p.scale, idx, cnt, p.istride, part, p.nsplit,
                            kernel_timer(dbg, 4), st);
   else if (s.kv_bf16)
-    e = launch_kernel(attn_kernel<1>, grid, dim3(256), st, kernel_timer(dbg, 4), s, c.K, c.V, q,
+    e = launch_kernel("attn_kernel",
+                      attn_kernel<1>, grid, dim3(256), st, kernel_timer(dbg, 4), s, c.K, c.V, q,
                       aa);
   else
-    e = launch_kernel(attn_kernel<0>, grid, dim3(256), st, kernel_timer(dbg, 4), s, c.K, c.V, q,
+    e = launch_kernel("attn_kernel",
+                      attn_kernel<0>, grid, dim3(256), st, kernel_timer(dbg, 4), s, c.K, c.V, q,
                       aa);
   if (e != hipSuccess) return e;
   return launch_combine(s, part, p.nsplit, out, c.seq_lens, appended, kernel_timer(dbg, 5), st);
@@ -519,15 +538,19 @@ hipError_t launch_combine(const Shape& s, const float* part, int nsplit, float* 
   // one batch of 16 partials per group of 128 threads, up to 8 groups
   const dim3 grid(s.B * s.Hq);
   if (nsplit <= 16)
-    return launch_kernel(combine_kernel<1>, grid, dim3(kD), st, tm, part, nsplit, out, seq_lens,
+    return launch_kernel("combine_kernel",
+                         combine_kernel<1>, grid, dim3(kD), st, tm, part, nsplit, out, seq_lens,
                          s.Hq, s.Lmax, appended);
   if (nsplit <= 32)
-    return launch_kernel(combine_kernel<2>, grid, dim3(2 * kD), st, tm, part, nsplit, out,
+    return launch_kernel("combine_kernel",
+                         combine_kernel<2>, grid, dim3(2 * kD), st, tm, part, nsplit, out,
                          seq_lens, s.Hq, s.Lmax, appended);
   if (nsplit <= 64)
-    return launch_kernel(combine_kernel<4>, grid, dim3(4 * kD), st, tm, part, nsplit, out,
+    return launch_kernel("combine_kernel",
+                         combine_kernel<4>, grid, dim3(4 * kD), st, tm, part, nsplit, out,
                          seq_lens, s.Hq, s.Lmax, appended);
-  return launch_kernel(combine_kernel<8>, grid, dim3(8 * kD), st, tm, part, nsplit, out,
+  return launch_kernel("combine_kernel",
+                       combine_kernel<8>, grid, dim3(8 * kD), st, tm, part, nsplit, out,
                        seq_lens, s.Hq, s.Lmax, appended);
 }
 

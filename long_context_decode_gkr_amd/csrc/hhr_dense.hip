@@ -454,12 +454,15 @@ static hipError_t launch_dense_t(const Shape& s, const CacheView& c, const void*
   const GatherList none{nullptr, nullptr, 0};
   if constexpr (BF16) {
     if (s.q_bf16)
-      return launch_kernel(dense_attn_mfma_kernel<G, 0, 0>, grid, dim3(256), st, tm, s, c.K, c.V,
+      return launch_kernel("dense_attn_mfma_kernel",
+                           dense_attn_mfma_kernel<G, 0, 0>, grid, dim3(256), st, tm, s, c.K, c.V,
                            q, c.seq_lens, part, nsplit, tpw, scale_log2e, none);
-    return launch_kernel(dense_attn_mfma_kernel<G, 1, 0>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+    return launch_kernel("dense_attn_mfma_kernel",
+                         dense_attn_mfma_kernel<G, 1, 0>, grid, dim3(256), st, tm, s, c.K, c.V, q,
                          c.seq_lens, part, nsplit, tpw, scale_log2e, none);
   } else {
-    return launch_kernel(dense_attn_kernel<BF16, G>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+    return launch_kernel("dense_attn_kernel",
+                         dense_attn_kernel<BF16, G>, grid, dim3(256), st, tm, s, c.K, c.V, q,
                          c.seq_lens, part, nsplit, tpw, scale_log2e);
   }
 }
@@ -492,9 +495,11 @@ static hipError_t launch_gather_t(const Shape& s, const CacheView& c, const void
                             hipStream_t st) {
   const dim3 grid(nsplit, s.Hkv, s.B);
   if (s.q_bf16)
-    return launch_kernel(dense_attn_mfma_kernel<G, 0, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+    return launch_kernel("dense_attn_mfma_kernel",
+                         dense_attn_mfma_kernel<G, 0, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
                          c.seq_lens, part, nsplit, kGatherChunk, scale_log2e, gl);
-  return launch_kernel(dense_attn_mfma_kernel<G, 1, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
+  return launch_kernel("dense_attn_mfma_kernel",
+                       dense_attn_mfma_kernel<G, 1, 1>, grid, dim3(256), st, tm, s, c.K, c.V, q,
                        c.seq_lens, part, nsplit, kGatherChunk, scale_log2e, gl);
 }
 

@@ -46,6 +46,11 @@ constexpr int kStepKernels = 6;
 inline KernelTimer kernel_timer(const DebugView& d, int k) {
   return d.events ? KernelTimer{d.events[2 * k], d.events[2 * k + 1]} : KernelTimer{nullptr, nullptr};
 }
+// HHR_TRACE: when the environment variable is set to anything but "0" (read once per process),
+// every launch and every decode step's plan and byte counts are logged to stderr.
+bool trace_on();
+void trace_printf(const char* fmt, ...) __attribute__((format(printf, 1, 2)));
+
 // Launch on stream st and return this launch's own status (not a sticky error left by an earlier
 // call); with a timer the runtime records its events around the kernel itself.
 template <typename... KArgs>
@@ -56,12 +61,17 @@ inline hipError_t launch_args(const void* f, dim3 grid, dim3 block, hipStream_t 
   return hipLaunchKernel(f, grid, block, argv, 0, st);
 }
 template <typename... KArgs, typename... Args>
-inline hipError_t launch_kernel(void (*kernel)(KArgs...), dim3 grid, dim3 block, hipStream_t st,
-                                KernelTimer tm, Args... args) {
+inline hipError_t launch_kernel(const char* name, void (*kernel)(KArgs...), dim3 grid, dim3 block,
+                                hipStream_t st, KernelTimer tm, Args... args) {
   static_assert(sizeof...(KArgs) == sizeof...(Args), "argument count");
   // each argument converted to the kernel's parameter type before its address is taken
-  return launch_args<KArgs...>(reinterpret_cast<const void*>(kernel), grid, block, st, tm,
-                               args...);
+  const hipError_t e = launch_args<KArgs...>(reinterpret_cast<const void*>(kernel), grid, block,
+                                             st, tm, args...);
+  if (trace_on())
+    trace_printf("launch %s grid (%u, %u, %u) block %u stream %p timed %d: %s", name, grid.x,
+                 grid.y, grid.z, block.x, static_cast<void*>(st), tm.start ? 1 : 0,
+                 hipGetErrorString(e));
+  return e;
 }
 
 // Which stages choose the attended tokens (the stage-wise ablation of the method).

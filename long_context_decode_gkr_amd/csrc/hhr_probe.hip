@@ -54,7 +54,7 @@ hhr_status hhr_read_probe(const void* src, size_t bytes, float* partial, hhr_str
     return HHR_ERR_INVALID_ARG;
   const size_t blocks = hhr_read_probe_blocks(bytes);
   if (blocks > 0x7FFFFFFFull) return HHR_ERR_CAPACITY;
-  const hipError_t e = hhr::launch_kernel(
+  const hipError_t e = hhr::launch_kernel("read_probe_kernel", 
       read_probe_kernel, dim3(unsigned(blocks)), dim3(kProbeThreads),
       reinterpret_cast<hipStream_t>(stream), hhr::KernelTimer{nullptr, nullptr},
       static_cast<const f32x4v*>(src), bytes / 16, partial);

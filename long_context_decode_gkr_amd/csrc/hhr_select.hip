@@ -866,20 +866,25 @@ static hipError_t launch_select_ept(const Shape& s, const CacheView& c, const Se
   if (unit) {
     const dim3 grid(units, s.B);
     const hipError_t e =
-        a.shared ? launch_kernel(select_unit_kernel<NB, EPT, 1>, grid, dim3(kScanThreads), st,
+        a.shared ? launch_kernel("select_unit_kernel",
+                                 select_unit_kernel<NB, EPT, 1>, grid, dim3(kScanThreads), st,
                                  kernel_timer(dbg, 2), s, c, a, dbg)
-                 : launch_kernel(select_unit_kernel<NB, EPT, 0>, grid, dim3(kScanThreads), st,
+                 : launch_kernel("select_unit_kernel",
+                                 select_unit_kernel<NB, EPT, 0>, grid, dim3(kScanThreads), st,
                                  kernel_timer(dbg, 2), s, c, a, dbg);
     return e != hipSuccess ? e : record_empty(kernel_timer(dbg, 3), st);
   }
   const dim3 grid(a.nsl, units, s.B);
   const hipError_t e =
-      a.shared ? launch_kernel(select_scan_kernel<NB, EPT, 1>, grid, dim3(kScanThreads), st,
+      a.shared ? launch_kernel("select_scan_kernel",
+                               select_scan_kernel<NB, EPT, 1>, grid, dim3(kScanThreads), st,
                                kernel_timer(dbg, 2), s, c, a, dbg)
-               : launch_kernel(select_scan_kernel<NB, EPT, 0>, grid, dim3(kScanThreads), st,
+               : launch_kernel("select_scan_kernel",
+                               select_scan_kernel<NB, EPT, 0>, grid, dim3(kScanThreads), st,
                                kernel_timer(dbg, 2), s, c, a, dbg);
   if (e != hipSuccess) return e;
-  return launch_kernel(select_emit_kernel<NB>, grid, dim3(kEmitThreads), st, kernel_timer(dbg, 3),
+  return launch_kernel("select_emit_kernel",
+                       select_emit_kernel<NB>, grid, dim3(kEmitThreads), st, kernel_timer(dbg, 3),
                        s, c, a, dbg);
 }
 

@@ -183,6 +183,20 @@ def make_layer(cfg: Config, max_seq_len: Optional[int] = None, layer: int = 0,
                 planted=planted)
 
 
+def layer_inputs(cfg: Config, layer: int) -> dict:
+    """The per-layer inputs of make_layer alone: q [B][Hq][d] and the rotation and projection
+    stand-ins R, W of layer `layer` (the same draws make_layer(cfg, layer=layer) makes)."""
+    B, Hq, Hkv, d = cfg.batch, cfg.num_q_heads, cfg.num_kv_heads, cfg.head_dim
+    q = np.zeros((B, Hq, d), np.float32)
+    for b in range(B):
+        for h in range(Hq):
+            q[b, h] = _storage(rng(cfg.cfg_id, b, h, "q", layer).standard_normal(d, dtype=np.float32),
+                               cfg.dtype)
+    R = np.stack([rotation(cfg.cfg_id, g, d, layer) for g in range(Hkv)])
+    W = np.stack([projection(cfg.cfg_id, g, d, cfg.hash_bits, layer) for g in range(Hkv)])
+    return dict(q=q, R=R, W=W)
+
+
 def append_tokens(cfg: Config, n: int, layer: int = 0) -> tuple:
     """n fresh (k, v) tokens per (b, kv-head), same background key distribution; [n][B][Hkv][d]."""
     B, Hkv, d = cfg.batch, cfg.num_kv_heads, cfg.head_dim
@@ -203,5 +217,5 @@ def append_tokens(cfg: Config, n: int, layer: int = 0) -> tuple:
     return kn, vn
 
 
-__all__ = ["Config", "CONFIGS", "make_layer", "append_tokens", "rotation", "projection",
-           "round_to_bf16", "rng"]
+__all__ = ["Config", "CONFIGS", "make_layer", "layer_inputs", "append_tokens", "rotation",
+           "projection", "round_to_bf16", "rng"]

@@ -21,9 +21,29 @@ def test_more_than_one_gpu_is_refused():
 
 def test_workloads_name_existing_configs():
     assert bench.DEFAULT_WORKLOAD in bench.WORKLOADS
-    for cfg_id, append, layers, desc in bench.WORKLOADS.values():
+    for name, (cfg_id, append, layers, desc, ctx) in bench.WORKLOADS.items():
         assert cfg_id in synth.CONFIGS and layers >= 8 and desc
+        cfg = bench.workload_config(name)
+        assert cfg.seq_len == (ctx or synth.CONFIGS[cfg_id].seq_len)
+        # enough instances that a revisit is not served from the 256 MB last-level cache
+        kv = cfg.batch * cfg.num_kv_heads * cfg.seq_len * 128 * 2 * 2
+        assert layers * kv >= 4 * 256e6 or layers >= 16, name
     assert [w for w, v in bench.WORKLOADS.items() if v[1]] == [bench.DEFAULT_WORKLOAD]
+    # the batch-1 context sweep: 16K, 32K, 64K, 128K
+    sweep = sorted(bench.workload_config(w).seq_len for w in
+                   ("llama-16k", "llama-32k", "llama-64k", "llama-128k"))
+    assert sweep == [16384, 32768, 65536, 131072]
+
+
+def test_layer_inputs_are_make_layers_draws():
+    cfg = synth.CONFIGS[2].scaled(seq_len=200, n_plant=2)
+    for layer in (0, 3):
+        full = synth.make_layer(cfg, layer=layer)
+        part = synth.layer_inputs(cfg, layer)
+        for k in ("q", "R", "W"):
+            assert (full[k] == part[k]).all(), (layer, k)
+    a, b = synth.layer_inputs(cfg, 1), synth.layer_inputs(cfg, 2)
+    assert not (a["q"] == b["q"]).all() and not (a["R"] == b["R"]).all()
 
 
 def test_byte_model_128k():
