@@ -233,6 +233,25 @@ hhr_status hhr_append_decode(const hhr_dims* dims, const hhr_params* params,
                              size_t ws_bytes, float* out, const hhr_debug* dbg,
                              hhr_stream_t stream);
 
+/* hhr_decode for callers that cannot allocate memory (code under HIP graph capture, tight
+ * serving loops, harnesses that forbid hipMalloc): the same step and results, with the workspace
+ * taken from scratch memory the library holds in a static device array of HHR_SCRATCH_BYTES per
+ * GPU (each GPU the library runs on keeps its copy until the process ends). It allocates and
+ * frees nothing. Arguments as for hhr_decode, without ws / ws_bytes.
+ *   - Shapes and budgets whose hhr_decode_workspace_bytes exceeds HHR_SCRATCH_BYTES return
+ *     HHR_ERR_CAPACITY before anything is enqueued (HHR_TRACE also logs the sizes).
+ *   - Every call on a GPU uses that GPU's one scratch array: calls that may overlap on one GPU
+ *     (concurrent streams, threads) race and must be serialised by the caller. The array keeps
+ *     the last call's contents; the step needs none of them (its workspace needs no
+ *     initialisation).
+ *   - On the first call on a device (that device current) the library looks up the array's
+ *     address there; a failure returns HHR_ERR_HIP. */
+#define HHR_SCRATCH_BYTES (16u * 1024u * 1024u)
+hhr_status hhr_decode_scratch(const hhr_dims* dims, const hhr_params* params,
+                              const hhr_cache* cache, const void* q, const float* R,
+                              const float* W, float* out, const hhr_debug* dbg,
+                              hhr_stream_t stream);
+
 /* Dense decode attention, the baseline of §4.3 / Fig. 7 (HHR against full attention): for
  * every (b, h), o = softmax(scale q K^T) V over ALL seq_lens[b] tokens of the cache, fp32
  * accumulation; no index is read (page_min, page_max, codes may be anything). Split-K over the

@@ -23,8 +23,9 @@ STATUS = {0: "ok", 1: "invalid argument", 2: "unsupported shape or type",
 
 # Every exported symbol of include/hhr.h.
 EXPORTS = ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode_workspace_bytes",
-           "hhr_decode", "hhr_append_decode", "hhr_dense_workspace_bytes", "hhr_dense_decode",
-           "hhr_read_probe_blocks", "hhr_read_probe", "hhr_status_string")
+           "hhr_decode", "hhr_append_decode", "hhr_decode_scratch", "hhr_dense_workspace_bytes",
+           "hhr_dense_decode", "hhr_read_probe_blocks", "hhr_read_probe", "hhr_status_string")
+HHR_SCRATCH_BYTES = 16 * 1024 * 1024
 
 
 class Dims(ctypes.Structure):
@@ -87,6 +88,8 @@ def load() -> ctypes.CDLL:
                                vp, P(DebugStruct), vp]
     lib.hhr_append_decode.argtypes = [P(Dims), P(Params), P(CacheStruct), vp, vp, vp, vp, vp, vp,
                                       ctypes.c_size_t, vp, P(DebugStruct), vp]
+    lib.hhr_decode_scratch.argtypes = [P(Dims), P(Params), P(CacheStruct), vp, vp, vp, vp,
+                                       P(DebugStruct), vp]
     lib.hhr_dense_workspace_bytes.argtypes = [P(Dims)]
     lib.hhr_dense_workspace_bytes.restype = ctypes.c_size_t
     lib.hhr_dense_decode.argtypes = [P(Dims), P(CacheStruct), vp, ctypes.c_float, vp,
@@ -97,7 +100,7 @@ def load() -> ctypes.CDLL:
     lib.hhr_status_string.argtypes = [ctypes.c_int]
     lib.hhr_status_string.restype = ctypes.c_char_p
     for fn in ("hhr_build_pages", "hhr_build_pages_fp64", "hhr_append", "hhr_decode",
-               "hhr_append_decode", "hhr_dense_decode", "hhr_read_probe"):
+               "hhr_append_decode", "hhr_decode_scratch", "hhr_dense_decode", "hhr_read_probe"):
         getattr(lib, fn).restype = ctypes.c_int
     _lib = lib
     return lib
@@ -138,6 +141,13 @@ def hhr_append_decode(dims: Dims, params: Params, cache: CacheStruct, k_new: int
     _check("hhr_append_decode", load().hhr_append_decode(
         ctypes.byref(dims), ctypes.byref(params), ctypes.byref(cache), k_new, v_new, q, R, W, ws,
         ws_bytes, out, ctypes.byref(dbg) if dbg is not None else None, stream))
+
+
+def hhr_decode_scratch(dims: Dims, params: Params, cache: CacheStruct, q: int, R: int, W: int,
+                       out: int, dbg: Optional[DebugStruct] = None, stream: int = 0) -> None:
+    _check("hhr_decode_scratch", load().hhr_decode_scratch(
+        ctypes.byref(dims), ctypes.byref(params), ctypes.byref(cache), q, R, W, out,
+        ctypes.byref(dbg) if dbg is not None else None, stream))
 
 
 def hhr_read_probe_blocks(nbytes: int) -> int:

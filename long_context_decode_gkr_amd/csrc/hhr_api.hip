@@ -2,6 +2,8 @@
 // Declarations and the full contract are in include/hhr.h.
 #include <math.h>
 #include <stdarg.h>
+#include <atomic>
+#include <mutex>
 #include <stdint.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -29,6 +31,35 @@ void trace_printf(const char* fmt, ...) {
   vfprintf(stderr, fmt, ap);
   fputc('\n', stderr);
   va_end(ap);
+}
+
+// Scratch memory of the allocation-free decode entry point: one copy per device, at that
+// device's own address (resolved once per device with hipGetSymbolAddress; the array's name in
+// host code is only a handle, never a device address).
+__device__ __align__(256) unsigned char scratch[HHR_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::atomic<void*> g_scratch_ptr[kMaxDevices];
+std::mutex g_scratch_mu;
+}  // namespace
+
+// The current device's scratch address, resolved on the first call on that device.
+static hhr_status current_scratch(void** out) {
+  int dev = -1;
+  if (hipGetDevice(&dev) != hipSuccess) return HHR_ERR_HIP;
+  if (dev < 0 || dev >= kMaxDevices) return HHR_ERR_UNSUPPORTED;
+  void* p = g_scratch_ptr[dev].load(std::memory_order_acquire);
+  if (!p) {
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    p = g_scratch_ptr[dev].load(std::memory_order_relaxed);
+    if (!p) {
+      if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) return HHR_ERR_HIP;
+      g_scratch_ptr[dev].store(p, std::memory_order_release);
+    }
+  }
+  *out = p;
+  return HHR_OK;
 }
 
 }  // namespace hhr
@@ -160,6 +191,20 @@ size_t hhr_decode_workspace_bytes(const hhr_dims* dims, const hhr_params* params
   return p.total;
 }
 
+// Validation of a decode call (everything but the workspace) and its plan.
+static hhr_status check_decode_call(const hhr_dims* dims, const hhr_params* params,
+                                    const hhr_cache* cache, const void* k_new, const void* v_new,
+                                    bool append, const void* q, const float* R, const float* W,
+                                    const float* out, Shape* s, CacheView* c, DecodePlan* p) {
+  hhr_status st = check_dims(dims, s);
+  if (st != HHR_OK) return st;
+  if ((st = check_cache(cache, append, c)) != HHR_OK) return st;
+  if ((st = check_params(params, *s, p)) != HHR_OK) return st;
+  if (!q || !R || !W || !out) return HHR_ERR_INVALID_ARG;
+  if (append && (!k_new || !v_new)) return HHR_ERR_INVALID_ARG;
+  return HHR_OK;
+}
+
 static hhr_status decode_common(const hhr_dims* dims, const hhr_params* params,
                                 const hhr_cache* cache, const void* k_new, const void* v_new,
                                 bool append, const void* q, const float* R, const float* W,
@@ -168,12 +213,9 @@ static hhr_status decode_common(const hhr_dims* dims, const hhr_params* params,
   Shape s;
   CacheView c;
   DecodePlan p;
-  hhr_status st = check_dims(dims, &s);
+  hhr_status st = check_decode_call(dims, params, cache, k_new, v_new, append, q, R, W, out, &s,
+                                    &c, &p);
   if (st != HHR_OK) return st;
-  if ((st = check_cache(cache, append, &c)) != HHR_OK) return st;
-  if ((st = check_params(params, s, &p)) != HHR_OK) return st;
-  if (!q || !R || !W || !out) return HHR_ERR_INVALID_ARG;
-  if (append && (!k_new || !v_new)) return HHR_ERR_INVALID_ARG;
   if (!ws || (reinterpret_cast<uintptr_t>(ws) & 255u) != 0 || ws_bytes < p.total)
     return HHR_ERR_WORKSPACE;
   return hip_status(launch_decode(s, p, c, append ? k_new : nullptr, append ? v_new : nullptr, q,
@@ -195,6 +237,28 @@ hhr_status hhr_append_decode(const hhr_dims* dims, const hhr_params* params,
                              hhr_stream_t stream) {
   return decode_common(dims, params, cache, k_new, v_new, true, q, R, W, ws, ws_bytes, out, dbg,
                        stream);
+}
+
+hhr_status hhr_decode_scratch(const hhr_dims* dims, const hhr_params* params,
+                              const hhr_cache* cache, const void* q, const float* R,
+                              const float* W, float* out, const hhr_debug* dbg,
+                              hhr_stream_t stream) {
+  Shape s;
+  CacheView c;
+  DecodePlan p;
+  hhr_status st = check_decode_call(dims, params, cache, nullptr, nullptr, false, q, R, W, out,
+                                    &s, &c, &p);
+  if (st != HHR_OK) return st;
+  if (p.total > HHR_SCRATCH_BYTES) {
+    if (trace_on())
+      trace_printf("hhr_decode_scratch: these shapes need %zu B of workspace, more than the "
+                   "%zu B of scratch", p.total, size_t(HHR_SCRATCH_BYTES));
+    return HHR_ERR_CAPACITY;
+  }
+  void* ws = nullptr;
+  if ((st = current_scratch(&ws)) != HHR_OK) return st;
+  return hip_status(launch_decode(s, p, c, nullptr, nullptr, q, R, W, ws, out, debug_view(dbg),
+                                  reinterpret_cast<hipStream_t>(stream)));
 }
 
 size_t hhr_dense_workspace_bytes(const hhr_dims* dims) {

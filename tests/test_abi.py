@@ -213,6 +213,29 @@ def test_sliced_selection_reads_stay_in_its_rows(lmax, S, rho, units, stages):
             assert r1 * S <= dstride
 
 
+def test_scratch_decode_validates_before_touching_the_device():
+    """The allocation-free decode validates like hhr_decode and refuses shapes whose workspace
+    exceeds HHR_SCRATCH_BYTES, all before any device call (fake pointers, no GPU)."""
+    lib = hb.load()
+    p = hb.Params(0.125, 2048, 0.0)
+
+    def call(dims, params=p, cache=None, q=FAKE, out=FAKE):
+        return lib.hhr_decode_scratch(ctypes.byref(dims), ctypes.byref(params),
+                                      ctypes.byref(cache or fake_cache()), q, FAKE, FAKE, out,
+                                      None, None)
+    assert call(good_dims(), q=None) == 1
+    assert call(good_dims(), out=None) == 1
+    assert call(good_dims(), params=hb.Params(0.0, 2048, 0.0)) == 1
+    big = good_dims(batch=64, max_seq_len=131072)
+    assert hb.hhr_decode_workspace_bytes(big, p) > hb.HHR_SCRATCH_BYTES
+    assert call(big) == 3                                   # HHR_ERR_CAPACITY
+    # the bench's workloads fit
+    for B, L, S, nb, rho, k in ((1, 131072, 16, 128, 1 / 16, 4096), (8, 32768, 16, 128, 0.3, 2048),
+                                (4, 65536, 32, 256, 1 / 8, 4096)):
+        d = good_dims(batch=B, max_seq_len=L, page_size=S, hash_bits=nb)
+        assert hb.hhr_decode_workspace_bytes(d, hb.Params(rho, k, 0.0)) <= hb.HHR_SCRATCH_BYTES
+
+
 def test_pages_only_workspace_holds_every_kept_token():
     d = good_dims(max_seq_len=131072)
     both = hb.hhr_decode_workspace_bytes(d, hb.Params(1 / 16, 4096, 0.0, hb.HHR_STAGES_BOTH))
