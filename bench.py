@@ -373,6 +373,57 @@ def cpu_baseline(cfg, data, append, quiet, budget_s=8.0):
                        f"untimed ({setup_s:.1f} s); no extrapolation")}
 
 
+TOPK_FRAC = 0.015   # the exact top-K reference: K = 1.5 % of the context (HHR §4.1 default)
+
+
+def recall_reference(data, lens, group, frac=TOPK_FRAC):
+    """Per (b, h): the exact top-K token set by q.k (K = max(1, round(frac L)), ties to the
+    lower position) over the first L keys of the head's KV head, fp64; and the planted set."""
+    import numpy as np
+    ref, planted = {}, {}
+    B, Hq = data["q"].shape[:2]
+    for b in range(B):
+        L = lens[b]
+        kref = max(1, int(round(frac * L)))
+        for h in range(Hq):
+            lg = data["K"][b, h // group, :L].astype(np.float64) @ data["q"][b, h].astype(np.float64)
+            order = np.lexsort((np.arange(L), -lg))
+            ref[(b, h)] = set(order[:kref].tolist())
+            pl = data["planted"][b, h]
+            planted[(b, h)] = set(pl[pl >= 0].tolist())
+    return ref, planted
+
+
+def recall_row(selected, kept_pages, ref, planted, lens, page_size):
+    """Means over the heads of: the share of the exact top-K that is selected (topk_recall),
+    the share lying in the kept pages (topk_in_kept_pages), the share of the planted keys that
+    is selected, and the share of the context attended. selected / kept_pages: (b, h) -> sets."""
+    import numpy as np
+    rec, prec, plr, att = [], [], [], []
+    for (b, h), T in ref.items():
+        sel, pages = selected[(b, h)], kept_pages[(b, h)]
+        rec.append(len(sel & T) / len(T))
+        prec.append(sum(1 for t in T if t // page_size in pages) / len(T))
+        P = planted[(b, h)]
+        if P:
+            plr.append(len(sel & P) / len(P))
+        att.append(len(sel) / lens[b])
+    return {"attended_frac": round(float(np.mean(att)), 4),
+            "topk_recall": round(float(np.mean(rec)), 4),
+            "topk_in_kept_pages": round(float(np.mean(prec)), 4),
+            "planted_recall": round(float(np.mean(plr)), 4) if plr else None}
+
+
+def gpu_selections(dbg):
+    """(b, h) -> selected token set and kept page set from a decode's side outputs."""
+    tidx, tcnt = dbg.token_idx.cpu().numpy(), dbg.token_count.cpu().numpy()
+    pid, pcnt = dbg.page_ids.cpu().numpy(), dbg.page_count.cpu().numpy()
+    B, H = tcnt.shape
+    sel = {(b, h): set(tidx[b, h, :tcnt[b, h]].tolist()) for b in range(B) for h in range(H)}
+    pages = {(b, h): set(pid[b, h, :pcnt[b, h]].tolist()) for b in range(B) for h in range(H)}
+    return sel, pages
+
+
 def recall_report(args, quiet):
     """Retrieval quality on the synthetic keys (a diagnostic, no parity claim): for every query
     head, the exact top-K tokens by q.k (K = 1.5 % of the context, the paper's default Top-K
@@ -393,16 +444,7 @@ def recall_report(args, quiet):
     tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
     kvt = hb.HHR_BF16 if cfg.dtype == "bf16" else hb.HHR_F32
     log("recall: exact top-K of every head", quiet)
-    ref, planted = {}, {}
-    for b in range(B):
-        L = lens[b]
-        kref = max(1, int(round(0.015 * L)))
-        for h in range(Hq):
-            lg = data["K"][b, h // G, :L].astype(np.float64) @ data["q"][b, h].astype(np.float64)
-            order = np.lexsort((np.arange(L), -lg))
-            ref[(b, h)] = set(order[:kref].tolist())
-            pl = data["planted"][b, h]
-            planted[(b, h)] = set(pl[pl >= 0].tolist())
+    ref, planted = recall_reference(data, lens, G)
     qd = torch.from_numpy(data["q"]).to(dev).to(tdt)
     rows = []
     base_k = cfg.token_budget
@@ -429,24 +471,11 @@ def recall_report(args, quiet):
             dbg = hb.Debug(dims, k, rho, stages)
             dec(cache, qd, Rd, Wd, out, dbg)
             torch.cuda.synchronize()
-            tidx, tcnt = dbg.token_idx.cpu().numpy(), dbg.token_count.cpu().numpy()
-            pid, pcnt = dbg.page_ids.cpu().numpy(), dbg.page_count.cpu().numpy()
-            rec, prec, plr, att = [], [], [], []
-            for (b, h), T in ref.items():
-                sel = set(tidx[b, h, :tcnt[b, h]].tolist())
-                pages = set(pid[b, h, :pcnt[b, h]].tolist())
-                rec.append(len(sel & T) / len(T))
-                prec.append(sum(1 for t in T if t // S in pages) / len(T))
-                P = planted[(b, h)]
-                if P:
-                    plr.append(len(sel & P) / len(P))
-                att.append(tcnt[b, h] / lens[b])
-            rows.append({"stages": stages, "rotation": rot, "hash_bits": nb,
-                         "keep_ratio": round(rho, 4), "token_budget": k if stages != "pages" else None,
-                         "attended_frac": round(float(np.mean(att)), 4),
-                         "topk_recall": round(float(np.mean(rec)), 4),
-                         "topk_in_kept_pages": round(float(np.mean(prec)), 4),
-                         "planted_recall": round(float(np.mean(plr)), 4) if plr else None})
+            sel, pages = gpu_selections(dbg)
+            rows.append(dict({"stages": stages, "rotation": rot, "hash_bits": nb,
+                              "keep_ratio": round(rho, 4),
+                              "token_budget": k if stages != "pages" else None},
+                             **recall_row(sel, pages, ref, planted, lens, S)))
             log(f"  {rows[-1]}", quiet)
     return {"metric": "HHR retrieval recall on synthetic keys (diagnostic)",
             "workload": WORKLOADS[args.workload][3], "name": args.workload,
