@@ -2,24 +2,36 @@
 //
 // Method: "HHR: Hierarchical Hash Retrieval for Efficient LLM Generation", §3.3.1 (page extrema of
 // the rotated keys k~ = k R, Eq. 4) and §3.1 Eq. 1 / §3.3.2 Eq. 10 (key code = sign of z = k W).
-// Both are one GEMM of the key tile against [R_g | W_g], done with v_mfma_f32_32x32x16_bf16.
+// Both are products of the key tile with R_g and W_g, done with v_mfma_f32_32x32x16_bf16.
 //
-// Precision. The keys are bf16, so they are exact MFMA A operands. The fp32 R and W are split
-// into bf16 pieces (R = r1 + r2 + r3 to ~2^-27, W = w1 + w2 to ~2^-18 relative); every
+// Precision. The keys are bf16, so they are exact MFMA operands. The fp32 R and W are split into
+// bf16 pieces by round-to-nearest (8-bit significands, so each piece leaves at most 2^-8 of
+// what it splits): R = r1 + r2 + r3 exactly, W = w1 + w2 to 2^-16 relative; every
 // bf16 x bf16 product is exact in fp32 and the MFMA accumulates in fp32.
 //   * Rotation: k~ carries fp32 accumulation error only (a few ulps of |k|); the page extrema
 //     are taken from it.
-//   * Codes: a bit is accepted when |z| > tau = 2^-13 |k|_2 |w_c|_2. By Cauchy-Schwarz the
-//     accumulated error is at most about 256 * 2^-23 + 2^-18 <= 2^-14.9 times |k|_2 |w_c|_2,
-//     so tau has a margin of ~4x. Bits inside tau (about 1e-3 of them for Gaussian data) are
-//     queued in LDS and recomputed from the stored operands in fp64 (exact products), with
-//     the exact long accumulator behind that: every code equals the sign of the exact z.
+//   * Codes: a code column w_c is first scaled by the power of two that brings |w_c| into
+//     [1, 2) (exact; the sign of k w_c is unchanged). z then differs from the exact k w_c by at
+//     most 256 * 2^-23 + 2^-16 <= 2^-14.4 times |k|_2 |w_c|_2 (256 additions, each rounding at
+//     most 2^-23 of a partial sum bounded by sum |k_i w_i| <= |k|_2 |w_c|_2 by Cauchy-Schwarz,
+//     in any order; plus the dropped third piece of W), so a bit is certain when
+//     |z| > tau = 2^-13 |k|_2 >= 2^-14 |k|_2 |w_c|_2. The other bits (about 8e-4 of them for
+//     Gaussian data) are queued in LDS and recomputed from the stored operands in fp64 (exact
+//     products), with the exact long accumulator behind that: every code equals the sign of
+//     the exact z.
 //
-// Grid (nper x roles, Hkv, B): role 0 = rotation and page extrema, role 1 + s = code words
-// [4 s, 4 s + 4) (128 code columns). A workgroup stages its role's B operand once, then builds
-// every nper-th tile of 512 tokens of its sequence. Per tile, each of its 8 waves walks
-// 32-token sub-tiles: 8 A fragments (one 16-byte load each per lane) are reused against all
-// 4 column tiles x 8 k-steps x pieces, B fragments come from LDS.
+// One workgroup reads each key once for both products. Its waves own output columns and keep
+// their pieces of R_g or W_g in registers for the whole launch; the keys pass through LDS:
+//   * rotation waves 0..3 (with ROT): channels 32 w .. 32 w + 31, the 3 R pieces as MFMA B
+//     fragments, the key sub-tile as A, so a lane holds one channel of 16 tokens and the page
+//     extrema are minima / maxima over its own registers;
+//   * code waves: code columns coff + 32 v .. + 31 (v the code wave's index), the 2 W pieces as
+//     MFMA A fragments, the keys as B, so a lane holds 16 code columns of one token and
+//     assembles its bits without any cross-lane vote.
+// Grid (nper, Hkv, B): workgroup `first` builds chunks first, first + nper, ... of 512 tokens
+// of its sequence; the key rows stream through two LDS buffers of 128 rows (the next tile's
+// global loads in flight while the current one is multiplied), each staged row with its norm.
+// 256-bit codes take a second launch without rotation waves for code columns 128..255.
 #include "hhr_device.h"
 #include "hhr_launch.h"
 
@@ -28,11 +40,14 @@ namespace hhr {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 
-constexpr int kMTok = 512;            // tokens per workgroup
-constexpr int kMThreads = 512;       // 8 waves: two per SIMD, so MFMA and VALU work overlap
-constexpr int kBStride = kD + 8;      // padded k-stride of a transposed B column (bf16 elements)
-constexpr int kFbCap = 2048;          // queued uncertain code bits per workgroup
+constexpr int kChunk = 512;           // tokens per output chunk (page extrema, code words)
+constexpr int kKTile = 128;           // key rows per LDS tile (4 sub-tiles of 32)
+constexpr int kKRow = kD + 8;         // bf16 elements per staged row: 272 B, so that the 16-byte
+                                      // fragment reads of 32 consecutive rows hit distinct banks
+constexpr int kCodeWaves = 4;         // 128 code columns per launch
+constexpr int kFbCap = 4096;          // queued uncertain code bits per workgroup
 constexpr float kCertScale = 1.0f / 8192.0f;   // 2^-13
 
 // One stored bf16 key row, read as fp32 values.
@@ -41,297 +56,382 @@ struct Bf16Row {
   __device__ __forceinline__ float operator[](int j) const { return bf16_bits_to_f32(p[j]); }
 };
 
+template <bool ROT>
+constexpr int build_threads() { return kWave * (kCodeWaves + (ROT ? 4 : 0)); }
 
-template <int S>
-__global__ void __launch_bounds__(kMThreads)
+// Row of the accumulator element r of a 32 x 32 MFMA tile held by a lane of half 0 (half 1:
+// + 4): 8 (r / 4) + r % 4.
+__device__ __forceinline__ constexpr int acc_row(int r) { return 8 * (r / 4) + (r % 4); }
+
+template <int S, bool ROT>
+__global__ void __launch_bounds__(build_threads<ROT>())
 build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float* __restrict__ W,
-                  int ntiles, int nper) {
-  // workgroup (role, first) stages its role's B operand once, then builds tiles first,
-  // first + nper, ... of the sequence
-  const int role = blockIdx.x / nper, first = blockIdx.x % nper;
-  const int g = blockIdx.y, b = blockIdx.z;
+                  int coff, int nper) {
+  constexpr int NT = build_threads<ROT>();
+  constexpr int RW = ROT ? 4 : 0;                 // rotation waves
+  constexpr int KPT = kKTile * (kD / 8) / NT;     // 16-byte key pieces per thread per tile
+  static_assert(KPT * NT == kKTile * (kD / 8), "whole tiles");
+  const int first = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
   const int L = min(max(c.seq_lens[b], 0), s.Lmax);
-  if (first * kMTok >= L) return;
+  if (first * kChunk >= L) return;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-  const int npieces = role == 0 ? 3 : 2;
+  const bool rot = w < RW;
+  const int half = lane >> 5, col = lane & 31;
+  const int cw = w - RW;                          // code wave index (code waves)
 
-  __shared__ __align__(16) uint16_t Bt[3][kD][kBStride];     // Bt[piece][n][k]
-  // page min / max (role 0); rows padded by one word so that the 32 channels a wave writes
-  // at once fall in different LDS banks
-  __shared__ float stage_f[2][kD][kMTok / 16 + 1];
-  __shared__ uint32_t stage_c[kMTok][4];                     // code words (role > 0)
-  __shared__ float wnorm[kD];
-  __shared__ float wpart[kMThreads];
-  __shared__ uint32_t fb_list[kFbCap];
+  __shared__ __align__(16) uint16_t Kt[2][kKTile][kKRow];
+  __shared__ float knorm[2][kKTile];              // 2^-13 |k| of the staged rows (inf if tiny)
+  // page min / max (rotation): rows padded by one word so that the 32 channels a wave writes
+  // at once fall in different banks
+  __shared__ float stage_f[ROT ? 2 : 1][ROT ? kD : 1][kChunk / S + 1];
+  __shared__ uint32_t stage_c[kChunk][kCodeWaves + 1];   // code words, padded rows
+  __shared__ uint32_t fb_list[kFbCap];            // queued uncertain bits: token << 8 | column
   __shared__ int fb_n;
-
-  // ---- B operand: split the fp32 matrix into bf16 pieces (hardware round-to-nearest-even,
-  // two values per conversion), transposed (k contiguous). Thread tid owns column
-  // n = tid % 128 and the row pairs k = 2 (tid / 128 + 4 i), +1: its 32 loads are issued
-  // together, and its quarter of the column's squared norm (code roles) is summed on the way.
-  constexpr int kTPC = kMThreads / kD;                // threads per column
-  constexpr int kPPT = kD * kD / (2 * kMThreads);     // row pairs per thread
-  const float* src = role == 0 ? R + size_t(g) * kD * kD
-                               : W + size_t(g) * kD * s.NB + (role - 1) * kD;
-  const int src_ld = role == 0 ? kD : s.NB;
-  const int bn = tid % kD, bk0 = tid / kD;
-  float bx[kPPT][2];
-#pragma unroll
-  for (int i = 0; i < kPPT; ++i) {
-    const int k = 2 * (bk0 + kTPC * i);
-    bx[i][0] = src[size_t(k) * src_ld + bn];
-    bx[i][1] = src[size_t(k + 1) * src_ld + bn];
-  }
-  float ss = 0.f;
-  auto pack = [](float a, float b) {
-    return __builtin_bit_cast(uint32_t, bf16x2{(__bf16)a, (__bf16)b});
-  };
-  auto lo16 = [](uint32_t v) { return __uint_as_float(v << 16); };
-  auto hi16 = [](uint32_t v) { return __uint_as_float(v & 0xFFFF0000u); };
-#pragma unroll
-  for (int i = 0; i < kPPT; ++i) {
-    const int k = 2 * (bk0 + kTPC * i);
-    const float x0 = bx[i][0], x1 = bx[i][1];
-    const uint32_t p1 = pack(x0, x1);
-    const float r0 = x0 - lo16(p1), r1 = x1 - hi16(p1);
-    const uint32_t p2 = pack(r0, r1);
-    *reinterpret_cast<uint32_t*>(&Bt[0][bn][k]) = p1;
-    *reinterpret_cast<uint32_t*>(&Bt[1][bn][k]) = p2;
-    if (role == 0)
-      *reinterpret_cast<uint32_t*>(&Bt[2][bn][k]) = pack(r0 - lo16(p2), r1 - hi16(p2));
-    ss = fmaf(x0, x0, fmaf(x1, x1, ss));
-  }
-  wpart[tid] = ss;
-  __syncthreads();
-  // |w_c| from fp32 sums of squares (relative error below 2^-16), rounded up by 2^-14
-  if (role != 0 && tid < kD) {
-    float q = 0.f;
-#pragma unroll
-    for (int i = 0; i < kTPC; ++i) q += wpart[tid + i * kD];
-    wnorm[tid] = sqrtf(q) * (1.0f + 0x1p-14f);
-  }
-  __syncthreads();
+  if (tid == 0) fb_n = 0;                         // published by the first staging barrier
 
   const size_t row0 = (size_t(b) * s.Hkv + g) * s.Lmax;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(c.K);
-  const int half = lane >> 5, col = lane & 31;
+  auto tile_tok0 = [&](int T) { return (first + (T >> 2) * nper) * kChunk + (T & 3) * kKTile; };
 
-  for (int tile = first; tile < ntiles; tile += nper) {
-    const int t0 = tile * kMTok;
-    if (t0 >= L) break;
-    const int ntok = min(kMTok, L - t0);
-    if (tid == 0) fb_n = 0;
-    __syncthreads();
-    // A fragments of a sub-tile: row tl0 + col, k = 16 ks + 8 half + 0..7 (rows past the end
-    // read the last valid row).
-    auto load_a = [&](int tl0, bf16x8 (&a)[8]) {
-      const int trc = min(t0 + tl0 + col, L - 1);
-      const uint4* ap = reinterpret_cast<const uint4*>(Kb + (row0 + trc) * kD + 8 * half);
+  // ---- key tile staging: thread piece e = tid + i NT is row e / 16, bytes 16 (e % 16) .. + 15;
+  // rows past the end repeat the last valid row
+  uint4 kv[KPT];
+  auto load_tile = [&](int t0) {
 #pragma unroll
-      for (int ks = 0; ks < 8; ++ks) a[ks] = __builtin_bit_cast(bf16x8, ap[2 * ks]);
-    };
-    constexpr int kStep = kMThreads / kWave;   // sub-tiles between a wave's consecutive ones
-    for (int st = w; st < kMTok / 32; st += kStep) {
-      const int tl0 = st * 32;                 // first token of the sub-tile (block-local)
-      if (tl0 >= ntok) break;
-      bf16x8 a[8];
-      load_a(tl0, a);
-      f32x16 acc[4];
+    for (int i = 0; i < KPT; ++i) {
+      const int e = tid + i * NT;
+      const int t = min(t0 + (e >> 4), L - 1);
+      kv[i] = *reinterpret_cast<const uint4*>(Kb + (row0 + t) * kD + (e & 15) * 8);
+    }
+  };
+  auto store_tile = [&](int buf) {
 #pragma unroll
-      for (int nt = 0; nt < 4; ++nt)
-#pragma unroll
-        for (int r = 0; r < 16; ++r) acc[nt][r] = 0.f;
-      for (int p = 0; p < npieces; ++p) {
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks) {
-#pragma unroll
-          for (int nt = 0; nt < 4; ++nt) {
-            const bf16x8 bv = *reinterpret_cast<const bf16x8*>(&Bt[p][nt * 32 + col][16 * ks + 8 * half]);
-            acc[nt] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ks], bv, acc[nt], 0, 0, 0);
-          }
-        }
-      }
-      // result rows of this lane: i(r) = 8 (r / 4) + 4 half + r % 4
-      if (role == 0) {
-        // ---- page extrema of k~ over the valid rows (pages are 16 or 32 rows of the sub-tile).
-        // Rows past the end repeat the last valid row (load_a clamps), which lies in the same
-        // page, so they leave the partial page's extrema unchanged; pages with no valid row are
-        // not written out.
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int j = nt * 32 + col;
-          constexpr int PPS = 32 / S;            // pages per sub-tile
-#pragma unroll
-          for (int pp = 0; pp < PPS; ++pp) {
-            float lo = INFINITY, hi = -INFINITY;
-#pragma unroll
-            for (int r = pp * (16 / PPS); r < (pp + 1) * (16 / PPS); ++r) {
-              lo = fminf(lo, acc[nt][r]);
-              hi = fmaxf(hi, acc[nt][r]);
-            }
-            lo = fminf(lo, __shfl_xor(lo, 32));
-            hi = fmaxf(hi, __shfl_xor(hi, 32));
-            if (half == 0) {
-              stage_f[0][j][tl0 / S + pp] = lo;
-              stage_f[1][j][tl0 / S + pp] = hi;
-            }
-          }
-        }
-      } else {
-        // ---- code bits: certified sign of z, or queued for the exact path
-        float xn2 = 0.f;
-#pragma unroll
-        for (int ks = 0; ks < 8; ++ks)
-#pragma unroll
-          for (int e = 0; e < 8; ++e) {
-            const float v = float(a[ks][e]);
-            xn2 = fmaf(v, v, xn2);
-          }
-        xn2 += __shfl_xor(xn2, 32);
-        const float xnorm = sqrtf(xn2) * (1.0f + 1e-6f);   // |k_row|, row = tl0 + col
-        float xr[16];                                      // |k| of the rows of acc[.][r]
-#pragma unroll
-        for (int r = 0; r < 16; ++r) xr[r] = __shfl(xnorm, 8 * (r / 4) + 4 * half + (r % 4));
-#pragma unroll
-        for (int nt = 0; nt < 4; ++nt) {
-          const int lc = nt * 32 + col;                    // code column within the slice
-          const float wn = wnorm[lc];
-#pragma unroll
-          for (int r = 0; r < 16; ++r) {
-            const int i = 8 * (r / 4) + 4 * half + (r % 4);
-            const float xi = xr[r];
-            const float tau = kCertScale * xi * wn;
-            const float z = acc[nt][r];
-            const bool valid = tl0 + i < ntok;
-            const bool sure = fabsf(z) > tau && xi * wn > 1e-30f;
-            bool bit = z > 0.f;
-            if (valid && !sure) {
-              // queued for the exact path (past the capacity only counted: see below)
-              const int pos = atomicAdd(&fb_n, 1);
-              if (pos < kFbCap) fb_list[pos] = (uint32_t(tl0 + i) << 8) | uint32_t(lc);
-            }
-            const uint64_t m = __ballot(bit);
-            if (lane == 0) {
-              // bits 0..31 of the ballot are row i(r) of half 0, bits 32..63 row i(r) + 4
-              const int i0 = 8 * (r / 4) + (r % 4);
-              stage_c[tl0 + i0][nt] = uint32_t(m);
-              stage_c[tl0 + i0 + 4][nt] = uint32_t(m >> 32);
-            }
-          }
-        }
+    for (int i = 0; i < KPT; ++i) {
+      const int e = tid + i * NT;
+      *reinterpret_cast<uint4*>(&Kt[buf][e >> 4][(e & 15) * 8]) = kv[i];
+      // the row's squared norm over its 16 pieces (16 consecutive lanes), rounded up
+      float q = 0.f;
+      q = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kv[i].x),
+                                          __builtin_bit_cast(bf16x2, kv[i].x), q, false);
+      q = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kv[i].y),
+                                          __builtin_bit_cast(bf16x2, kv[i].y), q, false);
+      q = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kv[i].z),
+                                          __builtin_bit_cast(bf16x2, kv[i].z), q, false);
+      q = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, kv[i].w),
+                                          __builtin_bit_cast(bf16x2, kv[i].w), q, false);
+      q = row16_sum(q);
+      if ((e & 15) == 0) {
+        const float n = sqrtf(q) * (1.0f + 0x1p-10f);
+        knorm[buf][e >> 4] = n > 1e-15f ? n * kCertScale : INFINITY;
       }
     }
-    __syncthreads();
+  };
+  load_tile(tile_tok0(0));
 
-    if (role == 0) {
-      // ---- write the page extrema: channel-major rows of this tile's pages
-      const int npg = (ntok + S - 1) / S;
-      const int pg0 = t0 / S;
-      const size_t sbase = (size_t(b) * s.Hkv + g) * kD;
-      for (int e = tid; e < kD * npg; e += kMThreads) {
-        const int j = e / npg, pl = e % npg;
-        store_extrema(s, c, (sbase + j) * s.Pmax + pg0 + pl, stage_f[0][j][pl], stage_f[1][j][pl]);
+  // ---- stationary operand pieces (bf16, hardware round-to-nearest-even): lane (half, col)
+  // holds rows 16 ks + 8 half .. + 7 of column `col` of its 32-column block, for ks = 0..7.
+  // A code column is first scaled by the power of two 2^-e that brings its norm into [1, 2)
+  // (exact, and sign(k w_c 2^-e) = sign(k w_c)), so that the certainty test needs no per-column
+  // factor: |z| > 2^-13 |k| >= 2^-14 |k| |w_c 2^-e|. Columns of tiny norm are never certain.
+  bf16x8 frag[3][8];
+  uint32_t tiny_mask = 0;                          // code waves: never-certain bit positions
+  {
+    const float* src = rot ? R + size_t(g) * kD * kD + 32 * w + col
+                           : W + size_t(g) * kD * s.NB + coff + 32 * cw + col;
+    const int ld = rot ? kD : s.NB;
+    float scale = 1.0f;
+    if (!rot) {
+      // |w_c| from fp32 sums of squares (relative error below 2^-16), rounded up by 2^-14
+      float nrm = 0.f;
+#pragma unroll
+      for (int i = 0; i < 64; ++i) {
+        const float x = src[size_t(16 * (i >> 3) + 8 * half + (i & 7)) * ld];
+        nrm = fmaf(x, x, nrm);
+      }
+      nrm += __shfl_xor(nrm, 32);
+      const float wn = sqrtf(nrm) * (1.0f + 0x1p-14f);
+      const uint32_t be = (__float_as_uint(wn) >> 23) & 0xFFu;   // wn in [2^(be-127), 2^(be-126))
+      const bool tiny = !(wn > 1e-15f) || be >= 253u;
+      scale = tiny ? 1.0f : __uint_as_float((254u - be) << 23);   // 2^-(be - 127)
+      const uint64_t tb = __ballot(tiny);                          // lanes 0..31: columns
+#pragma unroll
+      for (int r = 0; r < 16; ++r)
+        tiny_mask |= uint32_t((tb >> (acc_row(r) + 4 * half)) & 1u) << (acc_row(r) + 4 * half);
+    }
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks) {
+      float x[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) x[e] = src[size_t(16 * ks + 8 * half + e) * ld] * scale;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const __bf16 p1 = __bf16(x[e]);
+        const float r1 = x[e] - float(p1);
+        const __bf16 p2 = __bf16(r1);
+        frag[0][ks][e] = p1;
+        frag[1][ks][e] = p2;
+        frag[2][ks][e] = __bf16(r1 - float(p2));
+      }
+    }
+  }
+  store_tile(0);
+  __syncthreads();
+
+  const uint32_t pos_mask = 0x0F0F0F0Fu << (4 * half);   // the code bits a lane's half holds
+  const int NWd = s.NB / 32;
+  const float* wcols = W + size_t(g) * kD * s.NB;       // column c at wcols + c, stride NB
+
+  // Exact path for the queued bits, after every code word written so far has completed (the
+  // corrections are device atomics on those words). The launch's 128 fp32 columns of W are
+  // staged transposed in the key buffers (free at that point), then 4 lanes per queued bit form
+  // the fp64 sum of exact products (32 terms per lane: four 16-byte key loads, all in flight
+  // together), certified as in any summation order; the exact long accumulator decides the
+  // rest. Called by every thread; the caller re-stages a key tile afterwards if one is pending.
+  constexpr int kWTs = kD + 1;                    // staged row stride: conflict-free transposes
+  static_assert(sizeof(Kt) >= sizeof(float) * kD * kWTs, "W^T fits in the key buffers");
+  auto drain_queue = [&](int n) {
+    float* WT = reinterpret_cast<float*>(&Kt[0][0][0]);   // WT[c * kWTs + k] = W[k][coff + c]
+    for (int i = tid; i < kD * kD; i += NT) {
+      const int k = i >> 7, cl = i & (kD - 1);
+      WT[cl * kWTs + k] = wcols[size_t(k) * s.NB + coff + cl];
+    }
+    __syncthreads();
+    const int q = tid & 3;
+    for (int e = tid >> 2; e < n; e += NT / 4) {
+      const uint32_t ent = fb_list[e];
+      const int tok = int(ent >> 8), cc = int(ent & 0xFFu);
+      const uint16_t* kr = Kb + (row0 + tok) * kD;
+      uint4 kq[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) kq[i] = *reinterpret_cast<const uint4*>(kr + 32 * q + 8 * i);
+      const float* wq = WT + (cc - coff) * kWTs + 32 * q;
+      double z = 0.0, sa = 0.0;
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const uint32_t kw = i < 4 ? (&kq[0].x)[i] : i < 8 ? (&kq[1].x)[i - 4]
+                          : i < 12 ? (&kq[2].x)[i - 8] : (&kq[3].x)[i - 12];
+        const double p0 = double(__uint_as_float(kw << 16)) * double(wq[2 * i]);
+        const double p1 = double(__uint_as_float(kw & 0xFFFF0000u)) * double(wq[2 * i + 1]);
+        z += p0;
+        sa += fabs(p0);
+        z += p1;
+        sa += fabs(p1);
+      }
+      z = group_sum_f64<2>(z);
+      sa = group_sum_f64<2>(sa);
+      if (q == 0) {
+        int cb = certain_bit(z, sa);
+        if (cb < 0) cb = int(exact_bit(Bf16Row{kr}, wcols + cc, s.NB));
+        uint32_t* word = c.codes + (row0 + tok) * NWd + (cc >> 5);
+        const uint32_t mask = 1u << (cc & 31);
+        if (cb) atomicOr(word, mask);
+        else atomicAnd(word, ~mask);
+      }
+    }
+  };
+
+  for (int T = 0;; ++T) {
+    const int t0 = tile_tok0(T);                  // < L
+    const int cbase = (first + (T >> 2) * nper) * kChunk;
+    const int tc = t0 - cbase;                    // the tile's first token within its chunk
+    const int t1 = tile_tok0(T + 1);
+    const bool more = t1 < L;
+    if (more) load_tile(t1);                      // in flight during the products
+    const int buf = T & 1;
+
+    // ---- products: sub-tiles (2 sp, 2 sp + 1) of 32 rows, two accumulators in flight; the
+    // role is uniform over the wave, and each role's loop is straight-line code of its own
+    auto load_kf = [&](int sp, int ks, bf16x8 (&kf)[2]) {
+#pragma unroll
+      for (int u = 0; u < 2; ++u)
+        kf[u] = *reinterpret_cast<const bf16x8*>(
+            &Kt[buf][32 * (2 * sp + u) + col][16 * ks + 8 * half]);
+    };
+    if (rot) {
+      if constexpr (ROT) {
+#pragma unroll 1
+        for (int sp = 0; sp < 2; ++sp) {
+          f32x16 acc[2];
+#pragma unroll
+          for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
+#pragma unroll
+          for (int ks = 0; ks < 8; ++ks) {
+            bf16x8 kf[2];
+            load_kf(sp, ks, kf);
+#pragma unroll
+            for (int p = 0; p < 3; ++p)
+#pragma unroll
+              for (int u = 0; u < 2; ++u)
+                acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kf[u], frag[p][ks], acc[u], 0, 0,
+                                                                 0);
+          }
+          // page extrema of channel 32 w + col over each sub-tile's rows (pages of 16 or 32
+          // rows): rows past the end repeat the last valid row, of the same page, and pages
+          // with no valid row are not written out
+          const int j = 32 * w + col;
+          constexpr int PPS = 32 / S;
+#pragma unroll
+          for (int u = 0; u < 2; ++u) {
+            const int tl0 = 32 * (2 * sp + u);
+#pragma unroll
+            for (int pp = 0; pp < PPS; ++pp) {
+              float lo = INFINITY, hi = -INFINITY;
+#pragma unroll
+              for (int r = pp * (16 / PPS); r < (pp + 1) * (16 / PPS); ++r) {
+                lo = fminf(lo, acc[u][r]);
+                hi = fmaxf(hi, acc[u][r]);
+              }
+              lo = fminf(lo, __shfl_xor(lo, 32));
+              hi = fmaxf(hi, __shfl_xor(hi, 32));
+              if (half == 0) {
+                stage_f[0][j][(tc + tl0) / S + pp] = lo;
+                stage_f[1][j][(tc + tl0) / S + pp] = hi;
+              }
+            }
+          }
+        }
       }
     } else {
-      // ---- exact path for the queued bits, then the code words. 8 lanes per queued bit form
-      // the fp64 sum of exact products (16 terms per lane: two 16-byte key loads and 16 W
-      // loads, all in flight together), certified as in any summation order; the exact long
-      // accumulator decides the rest. If more bits were uncertain than the queue holds
-      // (degenerate projections), every word of the tile is recomputed from the stored
-      // operands instead: slow, and only for such inputs.
-      const float* wbase_p = W + size_t(g) * kD * s.NB + (role - 1) * kD;
-      if (fb_n <= kFbCap) {
-        const int gl = tid & 7;
-        for (int e = tid >> 3; e < fb_n; e += kMThreads / 8) {
-          const uint32_t ent = fb_list[e];
-          const int tl = int(ent >> 8), lc = int(ent & 0xFFu);
-          const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
-          const uint4 k0 = *reinterpret_cast<const uint4*>(kr + 16 * gl);
-          const uint4 k1 = *reinterpret_cast<const uint4*>(kr + 16 * gl + 8);
-          const float* wc = wbase_p + lc + size_t(16 * gl) * s.NB;
-          float wv[16];
+#pragma unroll 1
+      for (int sp = 0; sp < 2; ++sp) {
+        f32x16 acc[2];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) wv[i] = wc[size_t(i) * s.NB];
-          const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
-          double z = 0.0, sa = 0.0;
+        for (int u = 0; u < 2; ++u)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float x =
-                __uint_as_float((i & 1) ? (kw[i >> 1] & 0xFFFF0000u) : (kw[i >> 1] << 16));
-            const double pr = double(x) * double(wv[i]);
-            z += pr;
-            sa += fabs(pr);
-          }
+          for (int r = 0; r < 16; ++r) acc[u][r] = 0.f;
 #pragma unroll
-          for (int o = 4; o >= 1; o >>= 1) {
-            z += __shfl_xor(z, o, 8);
-            sa += __shfl_xor(sa, o, 8);
-          }
-          if (gl == 0) {
-            int cb = certain_bit(z, sa);
-            if (cb < 0) cb = int(exact_bit(Bf16Row{kr}, wbase_p + lc, s.NB));
-            const uint32_t mask = 1u << (lc & 31);
-            if (cb) atomicOr(&stage_c[tl][lc >> 5], mask);
-            else atomicAnd(&stage_c[tl][lc >> 5], ~mask);
-          }
+        for (int ks = 0; ks < 8; ++ks) {
+          bf16x8 kf[2];
+          load_kf(sp, ks, kf);
+#pragma unroll
+          for (int p = 0; p < 2; ++p)
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+              acc[u] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(frag[p][ks], kf[u], acc[u], 0, 0, 0);
         }
-      } else {
-        for (int e = tid; e < ntok * 4; e += kMThreads) {
-          const int tl = e >> 2, wd = e & 3;
-          const uint16_t* kr = Kb + (row0 + t0 + tl) * kD;
-          uint32_t word = 0;
-          for (int i = 0; i < 32; ++i)
-            word |= certified_bit(Bf16Row{kr}, wbase_p + 32 * wd + i, s.NB) << i;
-          stage_c[tl][wd] = word;
+#pragma unroll
+        for (int u = 0; u < 2; ++u) {
+          // ---- code bits of token t0 + tl0 + col, columns coff + 32 cw + acc_row(r) + 4 half:
+          // sign bits, and certainty |z| > 2^-13 |k| |w_c|
+          const int tl0 = 32 * (2 * sp + u);
+          const float tau = knorm[buf][tl0 + col];
+          uint32_t neg = 0, sure = 0;
+#pragma unroll
+          for (int r = 0; r < 16; ++r) {
+            const float z = acc[u][r];
+            neg |= (__float_as_uint(z) >> 31) << acc_row(r);
+            sure |= (fabsf(z) > tau) ? (1u << acc_row(r)) : 0u;
+          }
+          neg <<= 4 * half;
+          sure <<= 4 * half;
+          uint32_t word = ~neg & pos_mask;
+          word |= __shfl_xor(word, 32);
+          const int t = t0 + tl0 + col;
+          uint32_t uns = t < L ? (~sure | tiny_mask) & pos_mask : 0u;
+          // queue the uncertain bits: one LDS atomic per wave, each lane writes its entries
+          // at its prefix
+          const int nu = __popc(uns);
+          const int incl = wave_incl_sum(nu);
+          const int total = __builtin_amdgcn_readlane(incl, 63);
+          if (total) {
+            int base = 0;
+            if (lane == 0) base = atomicAdd(&fb_n, total);
+            int pos = __builtin_amdgcn_readfirstlane(base) + incl - nu;
+            while (uns) {
+              const int bi = __builtin_ctz(uns);
+              uns &= uns - 1;
+              if (pos < kFbCap) fb_list[pos] = (uint32_t(t) << 8) | uint32_t(coff + 32 * cw + bi);
+              ++pos;
+            }
+          }
+          if (half == 0) stage_c[tc + tl0 + col][cw] = word;
         }
-      }
-      __syncthreads();
-      const int wbase = (role - 1) * 4;
-      for (int tl = tid; tl < ntok; tl += kMThreads) {
-        const uint4 v = make_uint4(stage_c[tl][0], stage_c[tl][1], stage_c[tl][2], stage_c[tl][3]);
-        *reinterpret_cast<uint4*>(c.codes + (row0 + t0 + tl) * s.NW + wbase) = v;
       }
     }
-    __syncthreads();   // this tile's LDS staging is read out before the next tile reuses it
+    if (more) store_tile(buf ^ 1);
+    __syncthreads();
+
+    if (!more || (T & 3) == 3) {
+      // ---- the chunk is complete: write its page extrema and code words out (certain bits
+      // final; the queued ones are decided by the exact path)
+      const int ntok = min(kChunk, L - cbase);
+      if constexpr (ROT) {
+        constexpr int PPC = kChunk / S;           // pages per chunk
+        const int npg = (ntok + S - 1) / S;
+        const int pg0 = cbase / S;
+        const size_t sbase = (size_t(b) * s.Hkv + g) * kD;
+        for (int e = tid; e < kD * PPC; e += NT) {
+          const int j = e / PPC, pl = e % PPC;
+          if (pl < npg)
+            store_extrema(s, c, (sbase + j) * s.Pmax + pg0 + pl, stage_f[0][j][pl],
+                          stage_f[1][j][pl]);
+        }
+      }
+      for (int tl = tid; tl < ntok; tl += NT) {
+        const uint4 v = make_uint4(stage_c[tl][0], stage_c[tl][1], stage_c[tl][2], stage_c[tl][3]);
+        *reinterpret_cast<uint4*>(c.codes + (row0 + cbase + tl) * NWd + coff / 32) = v;
+      }
+      // ---- drain the queue when 3/4 full, and at the end. Entries past the capacity (more
+      // than it holds uncertain in one chunk: degenerate projections) are lost; then every
+      // word of this chunk is recomputed from the stored operands instead (slow, only for
+      // such inputs).
+      const int nq = fb_n;
+      if (nq >= 3 * kFbCap / 4 || !more) {
+        wait_memory();
+        __syncthreads();
+        drain_queue(min(nq, kFbCap));
+        if (nq > kFbCap) {
+          wait_memory();
+          __syncthreads();
+          for (int e = tid; e < ntok * kCodeWaves; e += NT) {
+            const int tl = e >> 2, wd = e & 3;
+            const uint16_t* kr = Kb + (row0 + cbase + tl) * kD;
+            uint32_t word = 0;
+            for (int i = 0; i < 32; ++i)
+              word |= certified_bit(Bf16Row{kr}, wcols + coff + 32 * wd + i, s.NB) << i;
+            c.codes[(row0 + cbase + tl) * NWd + coff / 32 + wd] = word;
+          }
+        }
+        __syncthreads();
+        if (tid == 0) fb_n = 0;
+        if (more) store_tile((T + 1) & 1);        // the drain used the key buffers
+      }
+      __syncthreads();   // the chunk's LDS staging is read out before the next chunk reuses it
+    }
+    if (!more) break;
   }
 }
 
 hipError_t launch_build_mfma(const Shape& s, const CacheView& c, const float* R, const float* W,
                              hipStream_t st) {
-  const int ntiles = (s.Lmax + kMTok - 1) / kMTok;
-  const int nroles = 1 + s.NB / kD;
-  // The LDS staging (about 156 KB) keeps one workgroup per CU, so the build takes
-  // ceil(workgroups / CUs) rounds of ceil(ntiles / nper) tiles each. nper is the split with the
-  // fewest tiles in sequence, counting one tile for each round's B staging, among the splits
-  // of at least 4 rounds (measured on MI355X at 128K: 4 rounds of 4 tiles 340 us, 1 round of
-  // 16 tiles 372 us; sequences shorter than max_seq_len also leave room to rebalance); among
-  // equals the fewest workgroups (fewest stagings).
+  // about one workgroup per CU (about 120 KB of LDS each): nper workgroups per (b, KV head),
+  // each building every nper-th chunk of 512 tokens
+  const int nch = (s.Lmax + kChunk - 1) / kChunk;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       ncu <= 0)
     ncu = 256;
-  const long long units = (long long)nroles * s.Hkv * s.B;
-  int nper = 1;
-  long long best = -1;
-  for (int n = 1; n <= ntiles; ++n) {
-    const long long rounds = (units * n + ncu - 1) / ncu;
-    const long long cost = rounds * ((ntiles + n - 1) / n + 1);
-    if (rounds < 4 && n < ntiles) continue;
-    if (best < 0 || cost < best) {
-      best = cost;
-      nper = n;
-    }
-  }
-  dim3 grid(nper * nroles, s.Hkv, s.B);
+  const int heads = s.Hkv * s.B;
+  const int nper = std::max(1, std::min(nch, (ncu + heads - 1) / heads));
+  const dim3 grid(nper, s.Hkv, s.B);
   const KernelTimer none{nullptr, nullptr};
+  hipError_t e;
   if (s.S == 16)
-    return launch_kernel("build_mfma_kernel",
-                         build_mfma_kernel<16>, grid, dim3(kMThreads), st, none, s, c, R, W,
-                         ntiles, nper);
-  return launch_kernel("build_mfma_kernel",
-                       build_mfma_kernel<32>, grid, dim3(kMThreads), st, none, s, c, R, W, ntiles,
-                       nper);
+    e = launch_kernel("build_mfma_kernel", build_mfma_kernel<16, true>, grid,
+                      dim3(build_threads<true>()), st, none, s, c, R, W, 0, nper);
+  else
+    e = launch_kernel("build_mfma_kernel", build_mfma_kernel<32, true>, grid,
+                      dim3(build_threads<true>()), st, none, s, c, R, W, 0, nper);
+  if (e != hipSuccess || s.NB == 128) return e;
+  // code columns 128 .. 255
+  if (s.S == 16)
+    return launch_kernel("build_mfma_kernel", build_mfma_kernel<16, false>, grid,
+                         dim3(build_threads<false>()), st, none, s, c, R, W, 128, nper);
+  return launch_kernel("build_mfma_kernel", build_mfma_kernel<32, false>, grid,
+                       dim3(build_threads<false>()), st, none, s, c, R, W, 128, nper);
 }
 
 }  // namespace hhr

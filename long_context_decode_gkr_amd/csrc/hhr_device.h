@@ -304,6 +304,10 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): every global load and store of
+// this wave has completed. A workgroup barrier does not wait for them by itself.
+__device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
 // ---------------------------------------------------------------------------------------------
 // Block-wide scan for up to 1024 threads: DPP wave scans, then the wave totals through LDS,
 // scanned again by DPP in the first row of 16 lanes of every wave (one LDS read per lane).

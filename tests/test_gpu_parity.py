@@ -417,8 +417,8 @@ def test_build_mfma_matches_oracle(cfg_id, L, batch, lens):
 def test_build_mfma_exact_path_for_zero_and_tiny_projections(nzero, ntiny):
     # nzero code columns give z = k0 - k1 = 0 exactly (k0 == k1), ntiny give z = 2^-30 k2: all
     # of them fall inside the certification band. 24 columns x 512 rows overflow the
-    # per-workgroup queue of 2048 (every word of the tile recomputed); 3 x 512 fit (8 lanes
-    # per queued bit, z == 0 decided by the exact accumulator).
+    # per-workgroup queue of 4096 (every word of the 512-token chunk recomputed); 3 x 512 fit
+    # (4 lanes per queued bit, z == 0 decided by the exact accumulator).
     _torch()
     cfg = _cfg(3, 2048, n_plant=0, num_q_heads=4, num_kv_heads=1)
     data = synth.make_layer(cfg)
