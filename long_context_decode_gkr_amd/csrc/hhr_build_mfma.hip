@@ -22,7 +22,8 @@
 //
 // One workgroup reads each key once for both products. Its waves own output columns and keep
 // their pieces of R_g or W_g in registers for the whole launch; the keys pass through LDS:
-//   * rotation waves 0..3 (with ROT): channels 32 w .. 32 w + 31, the 3 R pieces as MFMA B
+//   * rotation waves (with ROT, the even ones): channels 32 (w / 2) .. + 31, the 3 R pieces as
+//     MFMA B
 //     fragments, the key sub-tile as A, so a lane holds one channel of 16 tokens and the page
 //     extrema are minima / maxima over its own registers;
 //   * code waves: code columns coff + 32 v .. + 31 (v the code wave's index), the 2 W pieces as
@@ -75,9 +76,12 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   const int L = min(max(c.seq_lens[b], 0), s.Lmax);
   if (first * kChunk >= L) return;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
-  const bool rot = w < RW;
+  // with rotation waves, even waves rotate (channel block w / 2) and odd waves hash (code
+  // block w / 2): consecutive waves share a SIMD, so each SIMD runs one wave of each kind
+  // (measured 227 -> 209 us at 128K against waves 0..3 rotating)
+  const bool rot = RW > 0 && (w & 1) == 0;
   const int half = lane >> 5, col = lane & 31;
-  const int cw = w - RW;                          // code wave index (code waves)
+  const int cw = RW > 0 ? (w >> 1) : w;          // code block (code waves)
 
   __shared__ __align__(16) uint16_t Kt[2][kKTile][kKRow];
   __shared__ float knorm[2][kKTile];              // 2^-13 |k| of the staged rows (inf if tiny)
@@ -85,9 +89,13 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   // at once fall in different banks
   __shared__ float stage_f[ROT ? 2 : 1][ROT ? kD : 1][kChunk / S + 1];
   __shared__ uint32_t stage_c[kChunk][kCodeWaves + 1];   // code words, padded rows
-  __shared__ uint32_t fb_list[kFbCap];            // queued uncertain bits: token << 8 | column
-  __shared__ int fb_n;
-  if (tid == 0) fb_n = 0;                         // published by the first staging barrier
+  // queued uncertain bits (token << 8 | column), one segment of kSeg per code wave, and each
+  // wave's count (which may pass kSeg: the rest is lost, see the drain)
+  constexpr int kSeg = kFbCap / kCodeWaves;
+  __shared__ uint32_t fb_list[kFbCap];
+  __shared__ int fb_cnt[kCodeWaves];
+  if (tid < kCodeWaves) fb_cnt[tid] = 0;          // published by the first staging barrier
+  int qn = 0;                                     // this code wave's count (uniform)
 
   const size_t row0 = (size_t(b) * s.Hkv + g) * s.Lmax;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(c.K);
@@ -136,7 +144,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   bf16x8 frag[3][8];
   uint32_t tiny_mask = 0;                          // code waves: never-certain bit positions
   {
-    const float* src = rot ? R + size_t(g) * kD * kD + 32 * w + col
+    const float* src = rot ? R + size_t(g) * kD * kD + 32 * (w >> 1) + col
                            : W + size_t(g) * kD * s.NB + coff + 32 * cw + col;
     const int ld = rot ? kD : s.NB;
     float scale = 1.0f;
@@ -189,7 +197,8 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   // rest. Called by every thread; the caller re-stages a key tile afterwards if one is pending.
   constexpr int kWTs = kD + 1;                    // staged row stride: conflict-free transposes
   static_assert(sizeof(Kt) >= sizeof(float) * kD * kWTs, "W^T fits in the key buffers");
-  auto drain_queue = [&](int n) {
+  auto drain_queue = [&](int nseg) {               // nseg entries from each wave's segment
+    const int n = nseg * kCodeWaves;
     float* WT = reinterpret_cast<float*>(&Kt[0][0][0]);   // WT[c * kWTs + k] = W[k][coff + c]
     for (int i = tid; i < kD * kD; i += NT) {
       const int k = i >> 7, cl = i & (kD - 1);
@@ -198,7 +207,9 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
     __syncthreads();
     const int q = tid & 3;
     for (int e = tid >> 2; e < n; e += NT / 4) {
-      const uint32_t ent = fb_list[e];
+      const int sg = e / nseg, se = e % nseg;
+      if (se >= min(fb_cnt[sg], kSeg)) continue;   // a shorter segment
+      const uint32_t ent = fb_list[sg * kSeg + se];
       const int tok = int(ent >> 8), cc = int(ent & 0xFFu);
       const uint16_t* kr = Kb + (row0 + tok) * kD;
       uint4 kq[4];
@@ -270,7 +281,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
           // page extrema of channel 32 w + col over each sub-tile's rows (pages of 16 or 32
           // rows): rows past the end repeat the last valid row, of the same page, and pages
           // with no valid row are not written out
-          const int j = 32 * w + col;
+          const int j = 32 * (w >> 1) + col;
           constexpr int PPS = 32 / S;
 #pragma unroll
           for (int u = 0; u < 2; ++u) {
@@ -330,19 +341,18 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
           word |= __shfl_xor(word, 32);
           const int t = t0 + tl0 + col;
           uint32_t uns = t < L ? (~sure | tiny_mask) & pos_mask : 0u;
-          // queue the uncertain bits: one LDS atomic per wave, each lane writes its entries
-          // at its prefix
-          const int nu = __popc(uns);
-          const int incl = wave_incl_sum(nu);
-          const int total = __builtin_amdgcn_readlane(incl, 63);
-          if (total) {
-            int base = 0;
-            if (lane == 0) base = atomicAdd(&fb_n, total);
-            int pos = __builtin_amdgcn_readfirstlane(base) + incl - nu;
+          // queue the uncertain bits in the wave's own segment, each lane at its prefix (no
+          // atomics; skipped when no lane has one)
+          if (__ballot(uns != 0u)) {
+            const int nu = __popc(uns);
+            const int incl = wave_incl_sum(nu);
+            int pos = qn + incl - nu;
+            qn += __builtin_amdgcn_readlane(incl, 63);
             while (uns) {
               const int bi = __builtin_ctz(uns);
               uns &= uns - 1;
-              if (pos < kFbCap) fb_list[pos] = (uint32_t(t) << 8) | uint32_t(coff + 32 * cw + bi);
+              if (pos < kSeg)
+                fb_list[cw * kSeg + pos] = (uint32_t(t) << 8) | uint32_t(coff + 32 * cw + bi);
               ++pos;
             }
           }
@@ -350,6 +360,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
         }
       }
     }
+    if (!rot && lane == 0) fb_cnt[cw] = qn;
     if (more) store_tile(buf ^ 1);
     __syncthreads();
 
@@ -373,16 +384,18 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
         const uint4 v = make_uint4(stage_c[tl][0], stage_c[tl][1], stage_c[tl][2], stage_c[tl][3]);
         *reinterpret_cast<uint4*>(c.codes + (row0 + cbase + tl) * NWd + coff / 32) = v;
       }
-      // ---- drain the queue when 3/4 full, and at the end. Entries past the capacity (more
-      // than it holds uncertain in one chunk: degenerate projections) are lost; then every
-      // word of this chunk is recomputed from the stored operands instead (slow, only for
-      // such inputs).
-      const int nq = fb_n;
-      if (nq >= 3 * kFbCap / 4 || !more) {
+      // ---- drain the queue when a segment is 3/4 full, and at the end. Entries past a
+      // segment's capacity (more uncertain bits in one chunk than it holds: degenerate
+      // projections) are lost; then every word of this chunk is recomputed from the stored
+      // operands instead (slow, only for such inputs).
+      int nq = 0;
+#pragma unroll
+      for (int i = 0; i < kCodeWaves; ++i) nq = max(nq, fb_cnt[i]);
+      if (nq >= 3 * kSeg / 4 || !more) {
         wait_memory();
         __syncthreads();
-        drain_queue(min(nq, kFbCap));
-        if (nq > kFbCap) {
+        drain_queue(min(nq, kSeg));
+        if (nq > kSeg) {
           wait_memory();
           __syncthreads();
           for (int e = tid; e < ntok * kCodeWaves; e += NT) {
@@ -395,7 +408,8 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
           }
         }
         __syncthreads();
-        if (tid == 0) fb_n = 0;
+        if (tid < kCodeWaves) fb_cnt[tid] = 0;
+        qn = 0;
         if (more) store_tile((T + 1) & 1);        // the drain used the key buffers
       }
       __syncthreads();   // the chunk's LDS staging is read out before the next chunk reuses it

@@ -413,12 +413,13 @@ def test_build_mfma_matches_oracle(cfg_id, L, batch, lens):
     hc.check_index(lay, hc.oracle_index(lay), extrema_atol_scale=MFMA_EXTREMA_SCALE)
 
 
-@pytest.mark.parametrize("nzero,ntiny", [(16, 8), (2, 1)])
+@pytest.mark.parametrize("nzero,ntiny", [(16, 8), (1, 0), (0, 1)])
 def test_build_mfma_exact_path_for_zero_and_tiny_projections(nzero, ntiny):
     # nzero code columns give z = k0 - k1 = 0 exactly (k0 == k1), ntiny give z = 2^-30 k2: all
-    # of them fall inside the certification band. 24 columns x 512 rows overflow the
-    # per-workgroup queue of 4096 (every word of the 512-token chunk recomputed); 3 x 512 fit
-    # (4 lanes per queued bit, z == 0 decided by the exact accumulator).
+    # of them fall inside the certification band. 24 columns x 512 rows overflow the queue
+    # segment (1024 entries) of the code wave owning columns 0..31 (every word of the 512-token
+    # chunk recomputed); one column's 512 fit (4 lanes per queued bit, z == 0 decided by the
+    # exact accumulator).
     _torch()
     cfg = _cfg(3, 2048, n_plant=0, num_q_heads=4, num_kv_heads=1)
     data = synth.make_layer(cfg)
