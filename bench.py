@@ -127,9 +127,9 @@ def unit_select(variant, kpages, page_size):
 
 
 def select_slices(kpages, units, all_kept):
-    """Selection slices per unit (the library's rule): about 256 workgroups in all (1024 when
+    """Selection slices per unit (the library's rule): about 256 workgroups in all (512 when
     every page is kept and no page cut is repeated), between 8 and 512 kept pages per slice."""
-    target = 1024 if all_kept else 256
+    target = 512 if all_kept else 256
     want = -(-target // units)
     lo = -(-kpages // SLICE_PAGES)
     hi = max(lo, -(-kpages // MIN_SLICE_PAGES))

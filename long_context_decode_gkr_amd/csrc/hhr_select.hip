@@ -843,9 +843,12 @@ select_emit_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
 // Host side
 // ---------------------------------------------------------------------------------------------
 int select_slices(int kpages, int units, bool all_kept) {
-  // enough workgroups to spread a batch-1 step over the GPU; fewer per unit when a page cut is
-  // computed (every workgroup repeats it); at most kSlicePages pages per slice
-  const int target = all_kept ? 1024 : 256;
+  // enough workgroups to spread a batch-1 step over the GPU, but no more than are resident at
+  // once (two 1024-thread workgroups per CU: a second round of workgroups repeats the whole
+  // latency chain; 1024 workgroups measured 18.2 us for the fine stage alone at 128K); fewer per
+  // unit when a page cut is computed (every workgroup repeats it); at most kSlicePages pages
+  // per slice
+  const int target = all_kept ? 512 : 256;
   const int want = (target + units - 1) / units;
   const int lo = (kpages + kSlicePages - 1) / kSlicePages;
   const int hi = max(lo, (kpages + kMinSlicePages - 1) / kMinSlicePages);

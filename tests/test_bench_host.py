@@ -88,13 +88,13 @@ def test_byte_model_of_the_variants():
     # coarse stage alone: no codes read, all 512 x 16 candidates attended
     assert pages["select"] == 32 * (8192 * 4 + 16 + 8192 * 4)
     assert pages["sparse_attn"] > 2 * base["sparse_attn"] - 32 * 4096 * 8
-    # fine stage alone: no bound kernel; the sliced selection (8192 pages in 32 slices of 256
+    # fine stage alone: no bound kernel; the sliced selection (8192 pages in 16 slices of 512
     # per query head) reads every token's code once and writes a distance byte per token, the
     # page ids and the histograms, which the emission reads back with the 4096 indices written
     assert "page_bound" not in codes
     assert not bench.unit_select("codes", 8192, 16)
-    assert bench.select_slices(8192, 32, True) == 32
-    inter = 131072 + 8192 * 4 + 32 * 129 * 4
+    assert bench.select_slices(8192, 32, True) == 16
+    inter = 131072 + 8192 * 4 + 16 * 129 * 4
     assert codes["select"] == 32 * (16 + 131072 * 16 + inter)
     assert codes["select_emit"] == 32 * (inter + 4096 * 4)
     assert codes["sparse_attn"] == base["sparse_attn"]
@@ -122,12 +122,13 @@ def test_select_form_rule():
 
 
 def test_select_slice_rule():
-    # about 256 workgroups with a page cut, 1024 without; 8..512 kept pages per slice
+    # about 256 workgroups with a page cut, 512 without; 8..512 kept pages per slice
     assert bench.select_slices(256, 32, False) == 8            # 32K, batch 1: 32 pages each
     assert bench.select_slices(512, 8, False) == 32            # 128K, group-shared
     assert bench.select_slices(615, 256, False) == 2           # 8 sequences: the 512-page cap
     assert bench.select_slices(4, 1, False) == 1               # tiny: at least 8 pages a slice
-    assert bench.select_slices(16384, 1, True) == 1024
+    assert bench.select_slices(16384, 1, True) == 512
+    assert bench.select_slices(8192, 32, True) == 16           # 128K, fine stage alone
 
 
 def test_dense_split_rule():
