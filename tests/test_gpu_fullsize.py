@@ -67,6 +67,19 @@ def test_fullsize_32k_all_heads():
     _check(lay, out, dbg, cfg, heads, [(0, g) for g in range(8)])
 
 
+@pytest.mark.parametrize("cfg_id,ctx", [(2, 16384), (3, 65536)])
+def test_fullsize_context_sweep_points(cfg_id, ctx):
+    """The batch-1 context sweep's other two points: 16K with the 32K layer's budgets (keep 1/8,
+    k = 2048) and 64K with the 128K layer's (keep 1/16, k = 4096); sampled heads."""
+    _torch()
+    cfg = synth.CONFIGS[cfg_id].scaled(seq_len=ctx)
+    lay = hc.GpuLayer(cfg)
+    lay.build()
+    out, dbg = lay.decode(cfg.keep_ratio, cfg.token_budget)
+    heads = [(0, 0), (0, 6), (0, 17), (0, 31)]
+    _check(lay, out, dbg, cfg, heads, sorted({(0, h // 4) for _, h in heads}))
+
+
 def test_fullsize_varlen_batch():
     """8 sequences, lengths U[8K, 32K], keep 0.30, k = 2048."""
     _torch()
