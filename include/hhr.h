@@ -170,8 +170,9 @@ typedef struct {
  *   The selection runs as one workgroup per selection unit when the largest kept page set's
  *   tokens fit its cache (at most 32768 candidates) and the stages include the coarse one, and
  *   otherwise in slices of the kept pages over two kernels; both give identical results. For
- *   testing, the environment variable HHR_SELECT=sliced forces the sliced form and
- *   HHR_SELECT_SLICES=n (1..1024) its slice count. */
+ *   testing, the environment variable HHR_SELECT=sliced forces the sliced form,
+ *   HHR_SELECT_SLICES=n (1..1024) its slice count, and HHR_SELECT_THREADS=512 runs the first
+ *   form with 512-thread workgroups where max_seq_len / page_size <= 4096. */
 typedef struct {
   float* q_rot;
   uint32_t* q_code;

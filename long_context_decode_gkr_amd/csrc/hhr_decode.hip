@@ -414,11 +414,14 @@ DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages st
   const size_t NU = size_t(s.B) * (shared ? s.Hkv : s.Hq);   // selection units
   // The selection form: one workgroup per unit when the candidates fit its LDS cache; the
   // sliced form otherwise (always for the fine stage alone). HHR_SELECT=sliced forces the sliced
-  // form and HHR_SELECT_SLICES=n its slice count (1..1024): a second decomposition of the same
-  // selection, for checking that both give identical results.
+  // form and HHR_SELECT_SLICES=n its slice count (1..1024), HHR_SELECT_THREADS=512 the unit
+  // form's workgroup size (where the unit's pages fit 8 per thread): other decompositions of
+  // the same selection, for checking that all give identical results.
   const char* force = getenv("HHR_SELECT");
   p.unit_select = stages != Stages::kCodesOnly && p.kpages * s.S <= kUnitSlots &&
                   !(force && strcmp(force, "sliced") == 0);
+  const char* nthr = getenv("HHR_SELECT_THREADS");
+  p.unit_threads = nthr && strcmp(nthr, "512") == 0 ? 512 : 1024;
   p.nsl = select_slices(p.kpages, int(NU), stages == Stages::kCodesOnly);
   if (const char* ns = getenv("HHR_SELECT_SLICES")) {
     const int n = atoi(ns);
@@ -513,7 +516,7 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
                 reinterpret_cast<int32_t*>(base + p.off_hist), idx, cnt, p.rho, p.kcap,
                 p.istride, p.nsl, p.kpages, p.dstride, appended,
                 p.stages == Stages::kPagesOnly ? 0 : 1, p.shared};
-  e = launch_select(s, c, sa, dbg, p.unit_select != 0, st);
+  e = launch_select(s, c, sa, dbg, p.unit_select ? p.unit_threads : 0, st);
   if (e != hipSuccess) return e;
   AttnArgs aa{idx, cnt, part, p.kcap, p.istride, p.nsplit, p.shared,
               p.scale * 1.4426950408889634f};

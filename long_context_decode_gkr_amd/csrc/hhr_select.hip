@@ -278,7 +278,8 @@ __device__ __forceinline__ uint32_t code_dist(const uint4 (&x)[NW / 4], const ui
 }
 
 // ---------------------------------------------------------------------------------------------
-// Whole selection of one unit in one workgroup of 1024 threads (pages per thread EPT):
+// Whole selection of one unit in one workgroup of NT threads (1024; 512 as a second
+// decomposition of the same work for the race check; pages per thread EPT):
 //   the bounds and the query code(s) are loaded before the sequence length is known;
 //   page cut; kept pages in ascending order in LDS;
 //   Hamming distance of every candidate slot (ascending token order), cached in LDS as one byte
@@ -293,10 +294,9 @@ __device__ __forceinline__ uint32_t code_dist(const uint4 (&x)[NW / 4], const ui
 constexpr int kEmitSPT = 8;         // cached distances per thread per emission round
 static_assert(16 % kEmitSPT == 0, "an emission round must not cross a page (sizes 16, 32)");
 
-template <int NB, int EPT, int SHARED>
-__global__ void __launch_bounds__(kScanThreads)
+template <int NB, int EPT, int SHARED, int NT>
+__global__ void __launch_bounds__(NT)
 select_unit_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
-  constexpr int NT = kScanThreads;
   constexpr int NWV = NT / kWave;
   constexpr int NW = NB / 32;
   using DT = typename std::conditional<NB == 128, uint8_t, uint16_t>::type;
@@ -862,21 +862,24 @@ static hipError_t record_empty(KernelTimer tm, hipStream_t st) {
   return e != hipSuccess ? e : hipEventRecord(tm.stop, st);
 }
 
+template <int NB, int EPT, int NT>
+static hipError_t launch_unit(const Shape& s, const CacheView& c, const SelectArgs& a,
+                              const DebugView& dbg, hipStream_t st) {
+  const dim3 grid(a.shared ? s.Hkv : s.Hq, s.B);
+  const hipError_t e =
+      a.shared ? launch_kernel("select_unit_kernel",
+                               select_unit_kernel<NB, EPT, 1, NT>, grid, dim3(NT), st,
+                               kernel_timer(dbg, 2), s, c, a, dbg)
+               : launch_kernel("select_unit_kernel",
+                               select_unit_kernel<NB, EPT, 0, NT>, grid, dim3(NT), st,
+                               kernel_timer(dbg, 2), s, c, a, dbg);
+  return e != hipSuccess ? e : record_empty(kernel_timer(dbg, 3), st);
+}
+
 template <int NB, int EPT>
-static hipError_t launch_select_ept(const Shape& s, const CacheView& c, const SelectArgs& a,
-                                    const DebugView& dbg, bool unit, hipStream_t st) {
+static hipError_t launch_sliced(const Shape& s, const CacheView& c, const SelectArgs& a,
+                                const DebugView& dbg, hipStream_t st) {
   const int units = a.shared ? s.Hkv : s.Hq;
-  if (unit) {
-    const dim3 grid(units, s.B);
-    const hipError_t e =
-        a.shared ? launch_kernel("select_unit_kernel",
-                                 select_unit_kernel<NB, EPT, 1>, grid, dim3(kScanThreads), st,
-                                 kernel_timer(dbg, 2), s, c, a, dbg)
-                 : launch_kernel("select_unit_kernel",
-                                 select_unit_kernel<NB, EPT, 0>, grid, dim3(kScanThreads), st,
-                                 kernel_timer(dbg, 2), s, c, a, dbg);
-    return e != hipSuccess ? e : record_empty(kernel_timer(dbg, 3), st);
-  }
   const dim3 grid(a.nsl, units, s.B);
   const hipError_t e =
       a.shared ? launch_kernel("select_scan_kernel",
@@ -893,18 +896,27 @@ static hipError_t launch_select_ept(const Shape& s, const CacheView& c, const Se
 
 template <int NB>
 static hipError_t launch_select_nb(const Shape& s, const CacheView& c, const SelectArgs& a,
-                                   const DebugView& dbg, bool unit, hipStream_t st) {
+                                   const DebugView& dbg, int unit_threads, hipStream_t st) {
   static_assert(kMaxPages <= 16 * kScanThreads, "16 pages per thread cover the page capacity");
+  if (unit_threads == 512 && s.Pmax <= 8 * 512) {
+    if (s.Pmax <= 4 * 512) return launch_unit<NB, 4, 512>(s, c, a, dbg, st);
+    return launch_unit<NB, 8, 512>(s, c, a, dbg, st);
+  }
   const int ept = (s.Pmax + kScanThreads - 1) / kScanThreads;
-  if (ept <= 4) return launch_select_ept<NB, 4>(s, c, a, dbg, unit, st);
-  if (ept <= 8) return launch_select_ept<NB, 8>(s, c, a, dbg, unit, st);
-  return launch_select_ept<NB, 16>(s, c, a, dbg, unit, st);
+  if (unit_threads > 0) {
+    if (ept <= 4) return launch_unit<NB, 4, kScanThreads>(s, c, a, dbg, st);
+    if (ept <= 8) return launch_unit<NB, 8, kScanThreads>(s, c, a, dbg, st);
+    return launch_unit<NB, 16, kScanThreads>(s, c, a, dbg, st);
+  }
+  if (ept <= 4) return launch_sliced<NB, 4>(s, c, a, dbg, st);
+  if (ept <= 8) return launch_sliced<NB, 8>(s, c, a, dbg, st);
+  return launch_sliced<NB, 16>(s, c, a, dbg, st);
 }
 
 hipError_t launch_select(const Shape& s, const CacheView& c, const SelectArgs& a,
-                         const DebugView& dbg, bool unit, hipStream_t st) {
-  if (s.NB == 128) return launch_select_nb<128>(s, c, a, dbg, unit, st);
-  return launch_select_nb<256>(s, c, a, dbg, unit, st);
+                         const DebugView& dbg, int unit_threads, hipStream_t st) {
+  if (s.NB == 128) return launch_select_nb<128>(s, c, a, dbg, unit_threads, st);
+  return launch_select_nb<256>(s, c, a, dbg, unit_threads, st);
 }
 
 }  // namespace hhr
