@@ -171,8 +171,9 @@ typedef struct {
  *   tokens fit its cache (at most 32768 candidates) and the stages include the coarse one, and
  *   otherwise in slices of the kept pages over two kernels; both give identical results. For
  *   testing, the environment variable HHR_SELECT=sliced forces the sliced form,
- *   HHR_SELECT_SLICES=n (1..1024) its slice count, and HHR_SELECT_THREADS=512 runs the first
- *   form with 512-thread workgroups where max_seq_len / page_size <= 4096. */
+ *   HHR_SELECT_SLICES=n (1..1024) its slice count, and HHR_SELECT_THREADS=256, 512 or 1024
+ *   the first form's workgroup size (by default 512 up to 2048 pages of max_seq_len, else
+ *   1024; a smaller size is used only up to 16 pages per thread). */
 typedef struct {
   float* q_rot;
   uint32_t* q_code;

@@ -414,14 +414,21 @@ DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages st
   const size_t NU = size_t(s.B) * (shared ? s.Hkv : s.Hq);   // selection units
   // The selection form: one workgroup per unit when the candidates fit its LDS cache; the
   // sliced form otherwise (always for the fine stage alone). HHR_SELECT=sliced forces the sliced
-  // form and HHR_SELECT_SLICES=n its slice count (1..1024), HHR_SELECT_THREADS=512 the unit
-  // form's workgroup size (where the unit's pages fit 8 per thread): other decompositions of
-  // the same selection, for checking that all give identical results.
+  // form and HHR_SELECT_SLICES=n its slice count (1..1024): another decomposition of the same
+  // selection, for checking that both give identical results.
   const char* force = getenv("HHR_SELECT");
   p.unit_select = stages != Stages::kCodesOnly && p.kpages * s.S <= kUnitSlots &&
                   !(force && strcmp(force, "sliced") == 0);
-  const char* nthr = getenv("HHR_SELECT_THREADS");
-  p.unit_threads = nthr && strcmp(nthr, "512") == 0 ? 512 : 1024;
+  // The one-workgroup form's size: 512 threads while they hold the pages 4 per thread, else
+  // 1024 (fewer waves meet at each of its barriers: 9.2 -> 8.0 us at 32K, 9.1 -> 7.6 us at 16K,
+  // where 256 threads measured no better; at 128K 1024 threads take 11.4 us against 13.2 with
+  // 512 threads of 16 pages each). HHR_SELECT_THREADS=256, 512 or 1024 forces one (the smaller
+  // ones only where the pages fit 16 per thread).
+  p.unit_threads = s.Pmax <= 4 * 512 ? 512 : 1024;
+  if (const char* nthr = getenv("HHR_SELECT_THREADS")) {
+    const int n = atoi(nthr);
+    if (n == 256 || n == 512 || n == 1024) p.unit_threads = n;
+  }
   p.nsl = select_slices(p.kpages, int(NU), stages == Stages::kCodesOnly);
   if (const char* ns = getenv("HHR_SELECT_SLICES")) {
     const int n = atoi(ns);
@@ -481,10 +488,10 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
     const double esz = s.kv_bf16 ? 2.0 : 4.0, xsz = s.sum_bf16 ? 2.0 : 4.0;
     const double NU = double(s.B) * (p.shared ? s.Hkv : s.Hq);
     trace_printf("decode B %d Hq %d Hkv %d S %d NB %d Lmax %d stages %d shared %d append %d: "
-                 "kpages %d kcap %d, selection %s (%d slices), %d attention splits, workspace "
-                 "%zu B", s.B, s.Hq, s.Hkv, s.S, s.NB, s.Lmax, int(p.stages), p.shared, appended,
-                 p.kpages, p.kcap, p.unit_select ? "one workgroup per unit" : "sliced", p.nsl,
-                 p.nsplit, p.total);
+                 "kpages %d kcap %d, selection %s (%d threads; %d slices), %d attention splits, "
+                 "workspace %zu B", s.B, s.Hq, s.Hkv, s.S, s.NB, s.Lmax, int(p.stages), p.shared,
+                 appended, p.kpages, p.kcap, p.unit_select ? "one workgroup per unit" : "sliced",
+                 p.unit_threads, p.nsl, p.nsplit, p.total);
     trace_printf("bytes at most: prep %.0f (R, W, q), page_bound %.0f (extrema) + %.0f (U), "
                  "select %.0f (U, candidate codes), attention %.0f (K, V rows)",
                  double(s.Hkv) * 128 * (128 + s.NB) * 4 + double(s.B) * s.Hq * 128 * esz,

@@ -94,7 +94,7 @@ struct DecodePlan {
   int nsplit;      // attention workgroups per (b, h)
   int kpages;      // most kept pages per selection unit, min(Pmax, max(1, ceil(rho Pmax)))
   int unit_select; // one workgroup per unit selects (else the sliced form)
-  int unit_threads;  // its workgroup size: 1024, or 512 when HHR_SELECT_THREADS=512
+  int unit_threads;  // its workgroup size: 256, 512 or 1024
   int nsl;         // selection slices per unit (sliced form)
   int dstride;     // per-unit stride of the candidate distances (elements, a multiple of 16)
   double rho;
@@ -140,8 +140,8 @@ struct SelectArgs {
 };
 // Slices per unit for kpages kept pages at most over `units` selection units.
 int select_slices(int kpages, int units, bool all_kept);
-// unit_threads: the workgroup size of the one-workgroup-per-unit form (1024, or 512 where the
-// unit's pages fit 8 per thread), or 0 for the sliced form.
+// unit_threads: the workgroup size of the one-workgroup-per-unit form (1024, or 256 / 512 where
+// the pages fit 16 per thread), or 0 for the sliced form.
 hipError_t launch_select(const Shape& s, const CacheView& c, const SelectArgs& a,
                          const DebugView& dbg, int unit_threads, hipStream_t st);
 // Merge of split-K attention partials [B][Hq][nsplit][128 + 2] (o, m, l) into out

@@ -278,8 +278,8 @@ __device__ __forceinline__ uint32_t code_dist(const uint4 (&x)[NW / 4], const ui
 }
 
 // ---------------------------------------------------------------------------------------------
-// Whole selection of one unit in one workgroup of NT threads (1024; 512 as a second
-// decomposition of the same work for the race check; pages per thread EPT):
+// Whole selection of one unit in one workgroup of NT threads (256, 512 or 1024; pages per
+// thread EPT):
 //   the bounds and the query code(s) are loaded before the sequence length is known;
 //   page cut; kept pages in ascending order in LDS;
 //   Hamming distance of every candidate slot (ascending token order), cached in LDS as one byte
@@ -898,9 +898,15 @@ template <int NB>
 static hipError_t launch_select_nb(const Shape& s, const CacheView& c, const SelectArgs& a,
                                    const DebugView& dbg, int unit_threads, hipStream_t st) {
   static_assert(kMaxPages <= 16 * kScanThreads, "16 pages per thread cover the page capacity");
-  if (unit_threads == 512 && s.Pmax <= 8 * 512) {
+  if (unit_threads == 256 && s.Pmax <= 16 * 256) {
+    if (s.Pmax <= 4 * 256) return launch_unit<NB, 4, 256>(s, c, a, dbg, st);
+    if (s.Pmax <= 8 * 256) return launch_unit<NB, 8, 256>(s, c, a, dbg, st);
+    return launch_unit<NB, 16, 256>(s, c, a, dbg, st);
+  }
+  if (unit_threads == 512 && s.Pmax <= 16 * 512) {
     if (s.Pmax <= 4 * 512) return launch_unit<NB, 4, 512>(s, c, a, dbg, st);
-    return launch_unit<NB, 8, 512>(s, c, a, dbg, st);
+    if (s.Pmax <= 8 * 512) return launch_unit<NB, 8, 512>(s, c, a, dbg, st);
+    return launch_unit<NB, 16, 512>(s, c, a, dbg, st);
   }
   const int ept = (s.Pmax + kScanThreads - 1) / kScanThreads;
   if (unit_threads > 0) {

@@ -223,7 +223,7 @@ SELECT_FORM_CASES = [
                          SELECT_FORM_CASES)
 def test_selection_forms_agree_bit_for_bit(cfg_id, L, batch, lens, rho, k, stages,
                                            group_shared, summary, monkeypatch):
-    """The two forms of the selection (one workgroup per unit, of 1024 or of 512 threads; the
+    """The two forms of the selection (one workgroup per unit, of 256, 512 or 1024 threads; the
     sliced pair of a 1024-thread scan and a 256-thread emission, at several slice counts)
     decompose the same work differently over workgroups, LDS and barriers: their kept pages,
     distances, selected tokens and outputs must be identical to the bit (a check for races in
@@ -234,14 +234,14 @@ def test_selection_forms_agree_bit_for_bit(cfg_id, L, batch, lens, rho, k, stage
     lay = hc.GpuLayer(cfg, max_seq_len=-(-L // 128) * 128, lens=lens, summary=summary)
     lay.build()
     runs = []
-    for form, nsl in (("unit", None), ("unit512", None), ("sliced", None), ("sliced", 1),
-                      ("sliced", 3), ("sliced", 7)):
+    for form, nsl in (("unit", None), ("unit256", None), ("unit512", None), ("unit1024", None),
+                      ("sliced", None), ("sliced", 1), ("sliced", 3), ("sliced", 7)):
         for var in ("HHR_SELECT", "HHR_SELECT_SLICES", "HHR_SELECT_THREADS"):
             monkeypatch.delenv(var, raising=False)
         if form == "sliced":
             monkeypatch.setenv("HHR_SELECT", "sliced")
-        if form == "unit512":
-            monkeypatch.setenv("HHR_SELECT_THREADS", "512")
+        if form in ("unit256", "unit512", "unit1024"):
+            monkeypatch.setenv("HHR_SELECT_THREADS", form[4:])
         if nsl is not None:
             monkeypatch.setenv("HHR_SELECT_SLICES", str(nsl))
         out, dbg = lay.decode(rho, k, stages=stages, group_shared=group_shared)
