@@ -443,6 +443,34 @@ def test_build_mfma_exact_path_for_zero_and_tiny_projections(nzero, ntiny):
     assert np.array_equal((bits0 >> nzero) & ((1 << ntiny) - 1), k2pos * ((1 << ntiny) - 1))
 
 
+def test_build_mfma_queue_drained_between_chunks():
+    """One workgroup per (sequence, KV head) building all 8 of its 512-token chunks (32 sequences
+    x 8 KV heads fill the GPU with nper = 1): code column 0 is z = k0 - k1 with k0 == k1 on every
+    other token, so about 270 uncertain bits a chunk reach the first code wave's queue segment;
+    it is drained into the stored words every third chunk (at 3/4 of its 1024 entries) and the
+    key tile staged before the drain is staged again. Codes bit-exact and extrema admissible on
+    sampled heads; bit 0 of the tied tokens is 0."""
+    _torch()
+    cfg = _cfg(3, 4096, batch=32, n_plant=0)
+    data = synth.make_layer(cfg)
+    tied = np.arange(4096) % 2 == 0
+    data["K"][:, :, tied, 1] = data["K"][:, :, tied, 0]
+    W = data["W"]
+    W[:, :, 0] = 0.0
+    W[:, 0, 0] = 1.0
+    W[:, 1, 0] = -1.0
+    lay = hc.GpuLayer(cfg, data=data)
+    lay.build(method="auto")
+    pairs = [(0, 0), (13, 5), (31, 7)]
+    ref = hc.oracle_index(lay, heads_kv=pairs)
+    hc.check_index(lay, ref, pairs=pairs, extrema_atol_scale=MFMA_EXTREMA_SCALE)
+    got = lay.index_host()["codes"]
+    assert np.all(got[:, :, :4096, 0][:, :, tied] & 1 == 0)
+    k0, k1 = data["K"][..., 0], data["K"][..., 1]
+    want = (k0 - k1 > 0)[:, :, :4096][:, :, ~tied].astype(np.uint32)
+    assert np.array_equal(got[:, :, :4096, 0][:, :, ~tied] & 1, want)
+
+
 def test_step_codes_exact_for_zero_and_tiny_projections():
     """Codes computed in the decode step (queries) and by appends (keys) where the projection
     is exactly 0 (16 columns: x0 - x1 with x0 == x1) or tiny (8 columns: 2^-30 x2): the
