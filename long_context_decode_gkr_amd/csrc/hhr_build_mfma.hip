@@ -140,7 +140,8 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   // holds rows 16 ks + 8 half .. + 7 of column `col` of its 32-column block, for ks = 0..7.
   // A code column is first scaled by the power of two 2^-e that brings its norm into [1, 2)
   // (exact, and sign(k w_c 2^-e) = sign(k w_c)), so that the certainty test needs no per-column
-  // factor: |z| > 2^-13 |k| >= 2^-14 |k| |w_c 2^-e|. Columns of tiny norm are never certain.
+  // factor: |z| > 2^-13 |k| >= 2^-14 |k| |w_c 2^-e|. Columns of tiny norm (below 1e-15) or of
+  // norm 2^126 and above are never certain.
   bf16x8 frag[3][8];
   uint32_t tiny_mask = 0;                          // code waves: never-certain bit positions
   {
