@@ -53,7 +53,9 @@ typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 template <int G, int SB>   // SB: extrema stored as bf16
 __global__ void __launch_bounds__(kBoundThreads)
 page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) {
-  const int b = blockIdx.z, g = blockIdx.y, p0 = blockIdx.x * kBoundPages;
+  const int F = xcd_flat(linear_block_id(), grid_blocks());
+  const int x = F % int(gridDim.x), g = (F / int(gridDim.x)) % s.Hkv;
+  const int b = F / (int(gridDim.x) * s.Hkv), p0 = x * kBoundPages;
   const int t = c.seq_lens[b];
   const bool app = a.appended && t >= 0 && t < s.Lmax;
   const int L = min(max(t, 0) + (app ? 1 : 0), s.Lmax);

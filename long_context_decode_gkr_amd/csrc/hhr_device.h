@@ -304,6 +304,19 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// XCD-aware placement. Workgroups are dealt to the 8 XCDs round-robin by linear id, and each
+// XCD has its own L2 and address translation. A grid of T workgroups (T a multiple of 8) handled
+// by flat work index F = (L % 8) (T / 8) + L / 8 gives XCD k the contiguous eighth
+// [k T / 8, (k + 1) T / 8) of the work, e.g. one KV head's page extrema. Other grid sizes keep
+// F = L.
+__device__ __forceinline__ int xcd_flat(int L, int T) {
+  return (T & 7) ? L : (L & 7) * (T >> 3) + (L >> 3);
+}
+__device__ __forceinline__ int linear_block_id() {
+  return int(blockIdx.x + gridDim.x * (blockIdx.y + gridDim.y * blockIdx.z));
+}
+__device__ __forceinline__ int grid_blocks() { return int(gridDim.x * gridDim.y * gridDim.z); }
+
 // s_waitcnt vmcnt(0) (expcnt and lgkmcnt left at their maxima): every global load and store of
 // this wave has completed. A workgroup barrier does not wait for them by itself.
 __device__ __forceinline__ void wait_memory() { __builtin_amdgcn_s_waitcnt(0x0F70); }
