@@ -223,6 +223,24 @@ def algorithmic_bytes(cfg, lens, append=True, variant="hhr", lmax=None):
     return out
 
 
+def hamming_scored(cfg, lens, variant="hhr"):
+    """Hamming distances a step computes: per selection unit, one per candidate (every token of
+    the kept pages; every token for the fine stage alone) and query code (G codes per unit with
+    the group-shared selection); none for the coarse stage alone or the dense baseline."""
+    if variant in ("pages", "dense"):
+        return 0
+    S = cfg.page_size
+    shared = variant == "group-shared"
+    units = cfg.num_kv_heads if shared else cfg.num_q_heads
+    ncodes = cfg.group if shared else 1
+    total = 0
+    for L in lens:
+        P = -(-L // S)
+        n_keep = P if variant == "codes" else min(P, max(1, math.ceil(cfg.keep_ratio * P)))
+        total += units * ncodes * min(n_keep * S, L)
+    return total
+
+
 def kernel_source_digest(kernel):
     """Digest of the sources a kernel is built from (its own file and the shared headers)."""
     h = hashlib.sha256()
@@ -774,6 +792,8 @@ def main():
                    "context_range": [min(lens0), max(lens0) + visits],
                    "total_context": int(sum(lens_avg))},
         "keys_scored_per_s": round(Hq * sum(lens_avg) / (ms_step * 1e-3), 1),
+        "hamming_scored_per_s": round(hamming_scored(cfg, lens_avg, variant) / (ms_step * 1e-3),
+                                      1),
         "step_alg_bytes": step_bytes,
         "step_hbm_frac": round(step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "roofline": {"bound": "hbm", "kernel": dominant, "achieved": round(achieved, 1),

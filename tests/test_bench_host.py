@@ -115,6 +115,21 @@ def test_byte_model_of_the_variants():
         assert {n for n, _ in bench.timed_kernels(v, unit)} == set(alg), v
 
 
+def test_hamming_scored_counts():
+    cfg = synth.CONFIGS[3]
+    # 128K: 32 query heads x 512 kept pages x 16 tokens
+    assert bench.hamming_scored(cfg, [131072]) == 32 * 512 * 16
+    # group-shared: 8 KV heads, each candidate against the group's 4 query codes
+    assert bench.hamming_scored(cfg, [131072], "group-shared") == 8 * 4 * 512 * 16
+    # fine stage alone: every token; coarse stage alone: none
+    assert bench.hamming_scored(cfg, [131072], "codes") == 32 * 131072
+    assert bench.hamming_scored(cfg, [131072], "pages") == 0
+    # 40 tokens in 3 pages of 16, keep 1/4: one kept page of 16 tokens; with every page kept,
+    # the partial last page holds only its 8 valid tokens
+    assert bench.hamming_scored(synth.CONFIGS[1], [40]) == 16
+    assert bench.hamming_scored(synth.CONFIGS[1], [40], "codes") == 40
+
+
 def test_select_form_rule():
     # one workgroup per unit while the largest kept page set's tokens fit 32768 LDS slots
     assert bench.unit_select("hhr", 2048, 16) and not bench.unit_select("hhr", 2049, 16)

@@ -25,12 +25,15 @@ def test_bench_prints_one_contract_line():
     d = json.loads(lines[0])
     for k in ("metric", "value", "unit", "n_gpus", "steps", "warmup", "ms_per_step",
               "higher_is_better", "scaling", "vs_baseline", "dtype", "data", "config",
-              "roofline", "cpu_baseline", "step_spread", "kernels"):
+              "roofline", "cpu_baseline", "step_spread", "kernels", "keys_scored_per_s",
+              "hamming_scored_per_s"):
         assert k in d, k
     assert d["n_gpus"] == 1 and d["steps"] == 20 and d["warmup"] == 4
     assert d["higher_is_better"] is False and d["unit"] == "us/step/layer"
     assert abs(d["ms_per_step"] * 1e3 - d["value"]) < 1e-6 * max(1.0, d["value"]) + 1e-3
     assert d["config"]["workload"] and d["config"]["seq_len"] == 16384
+    # 32 query heads x 128 kept pages (keep 1/8 of 1024) x 16 tokens per step
+    assert abs(d["hamming_scored_per_s"] * d["ms_per_step"] * 1e-3 / (32 * 128 * 16) - 1) < 1e-3
     rf = d["roofline"]
     assert rf["bound"] == "hbm" and rf["unit"] == "GB/s" and rf["peak"] == 8000.0
     assert abs(rf["frac"] - rf["achieved"] / rf["peak"]) < 1e-3
