@@ -173,7 +173,9 @@ typedef struct {
  *   testing, the environment variable HHR_SELECT=sliced forces the sliced form,
  *   HHR_SELECT_SLICES=n (1..1024) its slice count, and HHR_SELECT_THREADS=256, 512 or 1024
  *   the first form's workgroup size (by default 512 up to 2048 pages of max_seq_len, else
- *   1024; a smaller size is used only up to 16 pages per thread). */
+ *   1024; a smaller size is used only up to 16 pages per thread). The page-bound kernel's
+ *   workgroups cover 64, 128 or 256 pages (the largest that still gives every compute unit a
+ *   workgroup); HHR_BOUND_PAGES=64, 128 or 256 forces one, with identical results. */
 typedef struct {
   float* q_rot;
   uint32_t* q_code;

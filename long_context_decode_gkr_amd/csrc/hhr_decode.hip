@@ -10,8 +10,8 @@
 // Kernels of a step, all on the caller's stream (after the preparation kernel of hhr_build.hip,
 // which appends the new token and writes q~ and the query codes; the selection between the
 // bound and the attention is in hhr_select.hip):
-//   page_bound_kernel  grid (ceil(Pmax/256), Hkv, B): streams the page extrema once for the G
-//                      query heads of a KV head (HBM-bound).
+//   page_bound_kernel  grid (ceil(Pmax/PB), Hkv, B), PB = 64, 128 or 256 pages: streams the
+//                      page extrema once for the G query heads of a KV head (HBM-bound).
 //   attn_kernel        grid (nsplit, Hq, B): split-K softmax attention over gathered K/V rows,
 //                      one partial (m, l, o) per workgroup;
 //   combine_kernel     grid (B * Hq): merges the partials of each (b, h) into the output and
@@ -29,14 +29,18 @@
 
 namespace hhr {
 
-constexpr int kBoundPages = 256;       // pages per bound workgroup (4 per lane)
 constexpr int kBoundThreads = 512;     // 8 waves x 16 channels
 
 // ---------------------------------------------------------------------------------------------
 // Coarse stage: page bounds (Eq. 3) for the G query heads of one KV head from ONE read of the
-// page extrema. Lane l of wave w covers pages p0 + 4l .. p0 + 4l + 3 and channels
-// 16w .. 16w + 15: 32 float4 loads per lane are issued at once, q~ (prepared by the preparation
-// kernel) is read with wave-uniform loads, and the 8 waves' partial sums meet in LDS.
+// page extrema. A workgroup covers PB = 64 PPL pages: lane l of wave w covers pages
+// p0 + PPL l .. + PPL - 1 and channels 16w .. 16w + 15, i.e. 32 loads of PPL consecutive extrema
+// per lane, all issued at once; q~ (prepared by the preparation kernel) is read with
+// wave-uniform loads, and the 8 waves' partial sums meet in LDS. PPL (4, 2 or 1) is the largest
+// whose grid still gives every CU a workgroup, so that a short context's extrema are streamed
+// by the whole chip; a page's bound is the same sequence of operations for every PPL (a chain of
+// 16 fused multiply-adds per wave in channel order, then the 8 waves' sums in wave order), so
+// the bounds do not depend on it.
 // Nothing else happens here: while the extrema stream in, any other load waits behind them, so
 // work that depends on one would sit on the kernel's tail.
 // ---------------------------------------------------------------------------------------------
@@ -48,14 +52,46 @@ struct BoundArgs {
 };
 
 typedef float f32x4v __attribute__((ext_vector_type(4)));
+typedef float f32x2v __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
 
-template <int G, int SB>   // SB: extrema stored as bf16
+// PPL consecutive stored extrema (element i of the fp32 or bf16 array) as fp32, with one
+// non-temporal load (the extrema are read once per step: 14.6 -> 13.8 us at 128K).
+template <int PPL, int SB>
+__device__ __forceinline__ void load_pages_nt(const void* base, size_t i, float (&v)[PPL]) {
+  if constexpr (SB) {
+    const uint16_t* p = static_cast<const uint16_t*>(base) + i;
+    if constexpr (PPL == 4) {
+      const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(p));
+      v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xFFFF0000u);
+      v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xFFFF0000u);
+    } else if constexpr (PPL == 2) {
+      const uint32_t x = __builtin_nontemporal_load(reinterpret_cast<const uint32_t*>(p));
+      v[0] = __uint_as_float(x << 16); v[1] = __uint_as_float(x & 0xFFFF0000u);
+    } else {
+      v[0] = __uint_as_float(uint32_t(__builtin_nontemporal_load(p)) << 16);
+    }
+  } else {
+    const float* p = static_cast<const float*>(base) + i;
+    if constexpr (PPL == 4) {
+      const f32x4v x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(p));
+      v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+    } else if constexpr (PPL == 2) {
+      const f32x2v x = __builtin_nontemporal_load(reinterpret_cast<const f32x2v*>(p));
+      v[0] = x.x; v[1] = x.y;
+    } else {
+      v[0] = __builtin_nontemporal_load(p);
+    }
+  }
+}
+
+template <int G, int SB, int PPL>   // SB: extrema stored as bf16; PPL: pages per lane
 __global__ void __launch_bounds__(kBoundThreads)
 page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) {
+  constexpr int PB = kWave * PPL;                  // pages per workgroup
   const int F = xcd_flat(linear_block_id(), grid_blocks());
   const int x = F % int(gridDim.x), g = (F / int(gridDim.x)) % s.Hkv;
-  const int b = F / (int(gridDim.x) * s.Hkv), p0 = x * kBoundPages;
+  const int b = F / (int(gridDim.x) * s.Hkv), p0 = x * PB;
   const int t = c.seq_lens[b];
   const bool app = a.appended && t >= 0 && t < s.Lmax;
   const int L = min(max(t, 0) + (app ? 1 : 0), s.Lmax);
@@ -63,60 +99,51 @@ page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) 
   if (p0 >= P) return;
   const int w = wave_id(), lane = lane_id();
   const int j0 = w * 16;
-  const int pl = p0 + lane * 4;
-  const int plc = min(pl, s.Pmax - 4);             // in bounds for every lane
+  const int plc = min(p0 + lane * PPL, s.Pmax - PPL);   // in bounds for every lane
   const size_t srow = (size_t(b) * s.Hkv + g) * kD + j0;
 
-  float4 lo[16], hi[16];
+  float lo[16][PPL], hi[16][PPL];
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) {
-    // non-temporal loads: the extrema are read once per step (measured 14.6 -> 13.8 us at 128K)
-    if constexpr (SB) {
-      const u32x2 x = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
-          static_cast<const uint16_t*>(c.pmin) + (srow + jj) * s.Pmax + plc));
-      const u32x2 y = __builtin_nontemporal_load(reinterpret_cast<const u32x2*>(
-          static_cast<const uint16_t*>(c.pmax) + (srow + jj) * s.Pmax + plc));
-      lo[jj] = make_float4(__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u),
-                           __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xFFFF0000u));
-      hi[jj] = make_float4(__uint_as_float(y.x << 16), __uint_as_float(y.x & 0xFFFF0000u),
-                           __uint_as_float(y.y << 16), __uint_as_float(y.y & 0xFFFF0000u));
-    } else {
-      const f32x4v x = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(
-          static_cast<const float*>(c.pmin) + (srow + jj) * s.Pmax + plc));
-      const f32x4v y = __builtin_nontemporal_load(reinterpret_cast<const f32x4v*>(
-          static_cast<const float*>(c.pmax) + (srow + jj) * s.Pmax + plc));
-      lo[jj] = make_float4(x.x, x.y, x.z, x.w);
-      hi[jj] = make_float4(y.x, y.y, y.z, y.w);
-    }
+    load_pages_nt<PPL, SB>(c.pmin, (srow + jj) * s.Pmax + plc, lo[jj]);
+    load_pages_nt<PPL, SB>(c.pmax, (srow + jj) * s.Pmax + plc, hi[jj]);
   }
   const float* qb = a.qrot + (size_t(b) * s.Hq + size_t(g) * G) * kD + j0;
 
-  float acc[G][4];
+  float acc[G][PPL];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh) acc[hh][0] = acc[hh][1] = acc[hh][2] = acc[hh][3] = 0.f;
+  for (int hh = 0; hh < G; ++hh)
+#pragma unroll
+    for (int k = 0; k < PPL; ++k) acc[hh][k] = 0.f;
 #pragma unroll
   for (int jj = 0; jj < 16; ++jj) {
 #pragma unroll
     for (int hh = 0; hh < G; ++hh) {
       // max(q l, q u) = q * (q >= 0 ? u : l) since l <= u; q is wave-uniform.
       const float qv = qb[hh * kD + jj];
-      const float4 e = (qv >= 0.f) ? hi[jj] : lo[jj];
-      acc[hh][0] = fmaf(qv, e.x, acc[hh][0]);
-      acc[hh][1] = fmaf(qv, e.y, acc[hh][1]);
-      acc[hh][2] = fmaf(qv, e.z, acc[hh][2]);
-      acc[hh][3] = fmaf(qv, e.w, acc[hh][3]);
+#pragma unroll
+      for (int k = 0; k < PPL; ++k)
+        acc[hh][k] = fmaf(qv, (qv >= 0.f) ? hi[jj][k] : lo[jj][k], acc[hh][k]);
     }
   }
 
-  __shared__ float4 red[kBoundThreads / kWave][G][kBoundPages / 4];
+  __shared__ __align__(16) float red[kBoundThreads / kWave][G][PB];
 #pragma unroll
-  for (int hh = 0; hh < G; ++hh)
-    red[w][hh][lane] = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+  for (int hh = 0; hh < G; ++hh) {
+    float* r = &red[w][hh][lane * PPL];
+    if constexpr (PPL == 4) {
+      *reinterpret_cast<float4*>(r) = make_float4(acc[hh][0], acc[hh][1], acc[hh][2], acc[hh][3]);
+    } else if constexpr (PPL == 2) {
+      *reinterpret_cast<float2*>(r) = make_float2(acc[hh][0], acc[hh][1]);
+    } else {
+      r[0] = acc[hh][0];
+    }
+  }
   __syncthreads();
   if (a.shared) {
     // one bound per page for the whole group: the largest of its heads' bounds (the group's
     // pages are chosen once; each head's own bound goes to the debug output only)
-    for (int pp = threadIdx.x; pp < kBoundPages; pp += kBoundThreads) {
+    for (int pp = threadIdx.x; pp < PB; pp += kBoundThreads) {
       const int p = p0 + pp;
       if (p < P) {
         float um = -INFINITY;
@@ -124,8 +151,7 @@ page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) 
         for (int hh = 0; hh < G; ++hh) {
           float sum = 0.f;
 #pragma unroll
-          for (int w2 = 0; w2 < kBoundThreads / kWave; ++w2)
-            sum += reinterpret_cast<const float*>(&red[w2][hh][0])[pp];
+          for (int w2 = 0; w2 < kBoundThreads / kWave; ++w2) sum += red[w2][hh][pp];
           um = fmaxf(um, sum);
           if (dbg_U) dbg_U[(size_t(b) * s.Hq + g * G + hh) * s.Pmax + p] = sum;
         }
@@ -134,14 +160,13 @@ page_bound_kernel(Shape s, CacheView c, BoundArgs a, float* __restrict__ dbg_U) 
     }
     return;
   }
-  for (int o = threadIdx.x; o < G * kBoundPages; o += kBoundThreads) {
-    const int hh = o / kBoundPages, pp = o % kBoundPages;
+  for (int o = threadIdx.x; o < G * PB; o += kBoundThreads) {
+    const int hh = o / PB, pp = o % PB;
     const int p = p0 + pp;
     if (p < P) {
       float sum = 0.f;
 #pragma unroll
-      for (int w2 = 0; w2 < kBoundThreads / kWave; ++w2)
-        sum += reinterpret_cast<const float*>(&red[w2][hh][0])[pp];
+      for (int w2 = 0; w2 < kBoundThreads / kWave; ++w2) sum += red[w2][hh][pp];
       const size_t oi = (size_t(b) * s.Hq + g * G + hh) * s.Pmax + p;
       a.U[oi] = sum;
       if (dbg_U) dbg_U[oi] = sum;
@@ -452,16 +477,58 @@ DecodePlan plan_decode(const Shape& s, double rho, int k, float scale, Stages st
   return p;
 }
 
+template <int G, int SB, int PPL>
+static hipError_t launch_bound_p(const Shape& s, const CacheView& c, const BoundArgs& a,
+                                 const DebugView& dbg, hipStream_t st) {
+  const dim3 grid((s.Pmax + kWave * PPL - 1) / (kWave * PPL), s.Hkv, s.B);
+  return launch_kernel("page_bound_kernel", page_bound_kernel<G, SB, PPL>, grid,
+                       dim3(kBoundThreads), st, kernel_timer(dbg, 1), s, c, a, dbg.bounds);
+}
+
 template <int G>
 static hipError_t launch_bound_t(const Shape& s, const CacheView& c, const BoundArgs& a,
-                                 const DebugView& dbg, hipStream_t st) {
-  dim3 grid((s.Pmax + kBoundPages - 1) / kBoundPages, s.Hkv, s.B);
-  if (s.sum_bf16)
-    return launch_kernel("page_bound_kernel",
-                         page_bound_kernel<G, 1>, grid, dim3(kBoundThreads), st,
-                         kernel_timer(dbg, 1), s, c, a, dbg.bounds);
-  return launch_kernel("page_bound_kernel", page_bound_kernel<G, 0>, grid, dim3(kBoundThreads), st,
-                       kernel_timer(dbg, 1), s, c, a, dbg.bounds);
+                                 int ppl, const DebugView& dbg, hipStream_t st) {
+  if (s.sum_bf16) {
+    if (ppl == 4) return launch_bound_p<G, 1, 4>(s, c, a, dbg, st);
+    if (ppl == 2) return launch_bound_p<G, 1, 2>(s, c, a, dbg, st);
+    return launch_bound_p<G, 1, 1>(s, c, a, dbg, st);
+  }
+  if (ppl == 4) return launch_bound_p<G, 0, 4>(s, c, a, dbg, st);
+  if (ppl == 2) return launch_bound_p<G, 0, 2>(s, c, a, dbg, st);
+  return launch_bound_p<G, 0, 1>(s, c, a, dbg, st);
+}
+
+// Compute units of the current device (queried once per device; 256 if the query fails).
+static int device_cus() {
+  static int cached[64] = {0};
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+  if (cached[dev] == 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        n <= 0)
+      n = 256;
+    cached[dev] = n;
+  }
+  return cached[dev];
+}
+
+// Pages per lane of the bound kernel: the largest of 4, 2, 1 whose grid still gives every
+// compute unit a workgroup (at batch 1: 4 from 128K, 2 at 64K, 1 at 32K and below).
+// HHR_BOUND_PAGES=256, 128 or 64 forces the workgroup's page count (the bounds are identical
+// for every choice).
+static int bound_pages_per_lane(const Shape& s) {
+  if (const char* e = getenv("HHR_BOUND_PAGES")) {
+    const int n = atoi(e);
+    if (n == 256 || n == 128 || n == 64) return n / kWave;
+  }
+  const int cus = device_cus();
+  for (int ppl = 4; ppl > 1; ppl >>= 1) {
+    const long long blocks =
+        (long long)((s.Pmax + kWave * ppl - 1) / (kWave * ppl)) * s.Hkv * s.B;
+    if (blocks >= cus) return ppl;
+  }
+  return 1;
 }
 
 // Both events of a kernel slot that has no launch of its own in this step, back to back.
@@ -490,10 +557,12 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
     const double esz = s.kv_bf16 ? 2.0 : 4.0, xsz = s.sum_bf16 ? 2.0 : 4.0;
     const double NU = double(s.B) * (p.shared ? s.Hkv : s.Hq);
     trace_printf("decode B %d Hq %d Hkv %d S %d NB %d Lmax %d stages %d shared %d append %d: "
-                 "kpages %d kcap %d, selection %s (%d threads; %d slices), %d attention splits, "
-                 "workspace %zu B", s.B, s.Hq, s.Hkv, s.S, s.NB, s.Lmax, int(p.stages), p.shared,
-                 appended, p.kpages, p.kcap, p.unit_select ? "one workgroup per unit" : "sliced",
-                 p.unit_threads, p.nsl, p.nsplit, p.total);
+                 "kpages %d kcap %d, %d pages per bound workgroup, selection %s (%d threads; "
+                 "%d slices), %d attention splits, workspace %zu B", s.B, s.Hq, s.Hkv, s.S, s.NB,
+                 s.Lmax, int(p.stages), p.shared, appended, p.kpages, p.kcap,
+                 kWave * bound_pages_per_lane(s),
+                 p.unit_select ? "one workgroup per unit" : "sliced", p.unit_threads, p.nsl,
+                 p.nsplit, p.total);
     trace_printf("bytes at most: prep %.0f (R, W, q), page_bound %.0f (extrema) + %.0f (U), "
                  "select %.0f (U, candidate codes), attention %.0f (K, V rows)",
                  double(s.Hkv) * 128 * (128 + s.NB) * 4 + double(s.B) * s.Hq * 128 * esz,
@@ -512,11 +581,12 @@ hipError_t launch_decode(const Shape& s, const DecodePlan& p, const CacheView& c
     if ((e = record_empty_slot(dbg, 1, st)) != hipSuccess) return e;
   } else {
     BoundArgs ba{qrot, U, appended, p.shared};
+    const int ppl = bound_pages_per_lane(s);
     switch (s.G) {
-      case 1: e = launch_bound_t<1>(s, c, ba, dbg, st); break;
-      case 2: e = launch_bound_t<2>(s, c, ba, dbg, st); break;
-      case 4: e = launch_bound_t<4>(s, c, ba, dbg, st); break;
-      default: e = launch_bound_t<8>(s, c, ba, dbg, st); break;
+      case 1: e = launch_bound_t<1>(s, c, ba, ppl, dbg, st); break;
+      case 2: e = launch_bound_t<2>(s, c, ba, ppl, dbg, st); break;
+      case 4: e = launch_bound_t<4>(s, c, ba, ppl, dbg, st); break;
+      default: e = launch_bound_t<8>(s, c, ba, ppl, dbg, st); break;
     }
     if (e != hipSuccess) return e;
   }

@@ -258,6 +258,47 @@ def test_selection_forms_agree_bit_for_bit(cfg_id, L, batch, lens, rho, k, stage
         hc.check_decode(lay, out0, d0, rho, k, stages=stages)
 
 
+BOUND_PAGE_CASES = [
+    # cfg, L, batch, lens, rho, k, group_shared, summary
+    (2, 9000, None, None, 0.125, 700, False, "f32"),
+    (5, 4200, 2, [4200, 1777], 0.3, 600, False, "f32"),               # page 32, 256-bit codes
+    (4, 6000, 3, [6000, 1, 2500], 0.3, 400, False, "f32"),            # ragged, one-token sequence
+    (2, 7000, None, None, 0.2, 900, True, "f32"),
+    (2, 5000, None, None, 0.125, 300, False, "bf16"),
+]
+
+
+@pytest.mark.parametrize("cfg_id,L,batch,lens,rho,k,group_shared,summary", BOUND_PAGE_CASES)
+def test_bound_workgroup_sizes_agree_bit_for_bit(cfg_id, L, batch, lens, rho, k, group_shared,
+                                                 summary, monkeypatch):
+    """The page-bound kernel covers 64, 128 or 256 pages per workgroup (1, 2 or 4 per lane, the
+    largest that still fills the chip unless HHR_BOUND_PAGES forces one): every choice runs the
+    same sequence of operations per page, so bounds, kept pages, selected tokens and outputs
+    must be identical to the bit (also a check of the partial-workgroup and early-exit paths,
+    with lengths that end inside a workgroup's range)."""
+    torch = _torch()
+    kw = dict(n_plant=8) if batch is None else dict(batch=batch, n_plant=8)
+    cfg = _cfg(cfg_id, L, **kw)
+    lay = hc.GpuLayer(cfg, max_seq_len=-(-L // 128) * 128, lens=lens, summary=summary)
+    lay.build()
+    runs = []
+    for pages in (None, "64", "128", "256"):
+        monkeypatch.delenv("HHR_BOUND_PAGES", raising=False)
+        if pages is not None:
+            monkeypatch.setenv("HHR_BOUND_PAGES", pages)
+        out, dbg = lay.decode(rho, k, group_shared=group_shared)
+        runs.append((pages, out, dbg))
+    _, out0, d0 = runs[0]
+    for pages, out, dbg in runs[1:]:
+        for name in ("bounds", "page_ids", "page_count", "token_idx", "token_count"):
+            assert torch.equal(getattr(d0, name), getattr(dbg, name)), (pages, name)
+        assert torch.equal(out0, out), pages
+    if group_shared:
+        hc.check_decode_shared(lay, out0, d0, rho, k)
+    else:
+        hc.check_decode(lay, out0, d0, rho, k)
+
+
 @pytest.mark.parametrize("stages,group_shared", [("both", False), ("codes", False),
                                                  ("both", True)])
 def test_decode_on_a_side_stream_and_in_a_replayed_graph(stages, group_shared):
