@@ -241,16 +241,21 @@ __device__ __forceinline__ void page_cut(const uint32_t (&key)[EPT], const bool 
 }
 
 // A unit's bound row as keys, from whole float4 loads at clamped addresses (rows are Pmax long,
-// Pmax a multiple of 4). The loads are issued by every lane before anything depends on them.
+// Pmax a multiple of 4). The loads are issued by every lane before anything depends on them:
+// all of them first, then each value is pinned (materialize) so that the compiler cannot sink
+// a load into the code that needs the sequence length (pinning each load's value before the
+// next load is issued would wait for it: one memory round trip per load).
 template <int EPT>
 __device__ __forceinline__ void load_bounds(const float* Urow, int Pmax, float (&uv)[EPT]) {
   const float4* U4 = reinterpret_cast<const float4*>(Urow);
   const int last4 = Pmax / 4 - 1;
+  float4 x[EPT / 4];
+#pragma unroll
+  for (int e = 0; e < EPT; e += 4) x[e / 4] = U4[min(int(threadIdx.x) * (EPT / 4) + e / 4, last4)];
 #pragma unroll
   for (int e = 0; e < EPT; e += 4) {
-    const float4 x = U4[min(int(threadIdx.x) * (EPT / 4) + e / 4, last4)];
-    uv[e] = materialize(x.x); uv[e + 1] = materialize(x.y);
-    uv[e + 2] = materialize(x.z); uv[e + 3] = materialize(x.w);
+    uv[e] = materialize(x[e / 4].x); uv[e + 1] = materialize(x[e / 4].y);
+    uv[e + 2] = materialize(x[e / 4].z); uv[e + 3] = materialize(x[e / 4].w);
   }
 }
 
@@ -380,9 +385,11 @@ select_unit_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   const uint32_t* cbase = c.codes + (size_t(b) * s.Hkv + g) * s.Lmax * NW;
   auto slot_token = [&](int slot) { return (s_pages[slot >> lgS] << lgS) + (slot & (s.S - 1)); };
   uint32_t* whist = cl.hist;   // bins 0..NB (cleared by the cut's last pass or above)
-  // batches of BAT slots per thread: all code loads of a batch are issued before any is used
+  // batches of BAT slots per thread: all code loads of a batch are issued before any is used.
+  // The first batch is a copy of its own (outside the loop), so that its loads are not held
+  // back by waits that a loop's reuse of its load registers would require
   constexpr int BAT = 8 / (NW / 4);
-  for (int base = 0; base < nslots; base += BAT * NT) {
+  auto batch = [&](int base) {
     int tt[BAT];
     uint4 cw[BAT][NW / 4];
 #pragma unroll
@@ -408,7 +415,9 @@ select_unit_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
       atomicAdd(live ? &whist[dd] : &whist[kRadixBins + lane], 1u);
       s_dist[slot < nslots ? slot : kUnitSlots + lane] = DT(live ? dd : kNone);
     }
-  }
+  };
+  batch(0);
+  for (int base = BAT * NT; base < nslots; base += BAT * NT) batch(base);
   __syncthreads();
   if (dbg.dist) {
     for (int i = tid; i < nslots; i += NT) {
