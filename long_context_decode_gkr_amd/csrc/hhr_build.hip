@@ -219,8 +219,10 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
   const bool app = has_k && t >= 0 && t < s.Lmax;
   const int p = app ? t / s.S : 0;
   const size_t si = ((size_t(b) * s.Hkv + g) * kD + (rot ? j : sl * 32)) * s.Pmax + p;
-  const float omin = load_pmin(s, c, si);
-  const float omax = load_pmax(s, c, si);
+  // raw bits, converted where they are used (a conversion inside the load's branch would make
+  // the compiler wait for every load issued before it)
+  const uint32_t omin_raw = load_raw(c.pmin, si, s.sum_bf16);
+  const uint32_t omax_raw = load_raw(c.pmax, si, s.sum_bf16);
 
   const size_t row = (size_t(b) * s.Hkv + g) * s.Lmax + (app ? t : 0);
   if (tid < kD && has_k) {
@@ -264,6 +266,8 @@ prep_kernel(Shape s, CacheView c, const void* __restrict__ kn, const void* __res
         const bool first = t % s.S == 0;        // the key opens page p
         // (a stored bf16 extremum is already rounded outward, so rounding the fp32 min / max
         // of it and k~ outward equals folding the rounded k~ into it)
+        const float omin = raw_to_f32(omin_raw, s.sum_bf16);
+        const float omax = raw_to_f32(omax_raw, s.sum_bf16);
         store_extrema(s, c, si, first ? kt : fminf(omin, kt), first ? kt : fmaxf(omax, kt));
       }
 #pragma unroll

@@ -237,29 +237,23 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
   for (int e = 0; e < EPL; ++e) o[e] = 0.f;
 
   if (live) {
-    // query slice (scaled into the log2 domain)
-    float qv[EPL];
+    // query slice: raw bits now (16 bytes per lane), unpacked and scaled into the log2 domain
+    // only after the row loads are issued, so that nothing waits for it before them
     const size_t qo = size_t(bh) * kD + sub * EPL;
+    uint4 qraw[2] = {make_uint4(0u, 0u, 0u, 0u), make_uint4(0u, 0u, 0u, 0u)};
     if (s.q_bf16) {
+      const uint16_t* qb = static_cast<const uint16_t*>(q) + qo;
       if constexpr (EPL == 8) {
-        float f[8];
-        unpack(*reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(q) + qo), f);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) qv[e] = f[e];
+        qraw[0] = *reinterpret_cast<const uint4*>(qb);
       } else {
-        const uint2 x = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(q) + qo);
-        qv[0] = __uint_as_float(x.x << 16); qv[1] = __uint_as_float(x.x & 0xFFFF0000u);
-        qv[2] = __uint_as_float(x.y << 16); qv[3] = __uint_as_float(x.y & 0xFFFF0000u);
+        const uint2 x = *reinterpret_cast<const uint2*>(qb);
+        qraw[0].x = x.x; qraw[0].y = x.y;
       }
     } else {
+      const float* qf = static_cast<const float*>(q) + qo;
 #pragma unroll
-      for (int e = 0; e < EPL; e += 4) {
-        const float4 x = *reinterpret_cast<const float4*>(static_cast<const float*>(q) + qo + e);
-        qv[e] = x.x; qv[e + 1] = x.y; qv[e + 2] = x.z; qv[e + 3] = x.w;
-      }
+      for (int e = 0; e < EPL; e += 4) qraw[e / 4] = *reinterpret_cast<const uint4*>(qf + e);
     }
-#pragma unroll
-    for (int e = 0; e < EPL; ++e) qv[e] *= a.scale_log2e;
 
     // selected rows: indices first (no branches, so all loads stay in flight together)
     const size_t kvrow0 = (size_t(b) * s.Hkv + g) * s.Lmax;
@@ -281,6 +275,28 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
     }
     // keep all 2 x ITER row loads in flight before the first use
     __builtin_amdgcn_sched_barrier(0);
+
+    float qv[EPL];
+    if (s.q_bf16) {
+      if constexpr (EPL == 8) {
+        float f[8];
+        unpack(qraw[0], f);
+#pragma unroll
+        for (int e = 0; e < 8; ++e) qv[e] = f[e];
+      } else {
+        qv[0] = __uint_as_float(qraw[0].x << 16); qv[1] = __uint_as_float(qraw[0].x & 0xFFFF0000u);
+        qv[2] = __uint_as_float(qraw[0].y << 16); qv[3] = __uint_as_float(qraw[0].y & 0xFFFF0000u);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < EPL; e += 4) {
+        float f[4];
+        unpack(qraw[e / 4], f);
+        qv[e] = f[0]; qv[e + 1] = f[1]; qv[e + 2] = f[2]; qv[e + 3] = f[3];
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < EPL; ++e) qv[e] *= a.scale_log2e;
 
     // logits (log2 domain)
     float sc[ITER];
