@@ -240,18 +240,21 @@ __device__ __forceinline__ void page_cut(const uint32_t (&key)[EPT], const bool 
   }
 }
 
-// A unit's bound row as keys, from whole float4 loads at clamped addresses (rows are Pmax long,
-// Pmax a multiple of 4). The loads are issued by every lane before anything depends on them:
-// all of them first, then each value is pinned (materialize) so that the compiler cannot sink
-// a load into the code that needs the sequence length (pinning each load's value before the
-// next load is issued would wait for it: one memory round trip per load).
+// A unit's bound row, from whole float4 loads at clamped addresses (rows are Pmax long, Pmax a
+// multiple of 4), in two steps: issue_bounds issues every load, and pin_bounds, called after
+// the caller has issued its other early loads, pins each value (materialize) so that the
+// compiler cannot sink a load into the code that needs the sequence length. (Pinning a value
+// right after its load would wait for it before the next load is issued: one memory round trip
+// per load.)
 template <int EPT>
-__device__ __forceinline__ void load_bounds(const float* Urow, int Pmax, float (&uv)[EPT]) {
+__device__ __forceinline__ void issue_bounds(const float* Urow, int Pmax, float4 (&x)[EPT / 4]) {
   const float4* U4 = reinterpret_cast<const float4*>(Urow);
   const int last4 = Pmax / 4 - 1;
-  float4 x[EPT / 4];
 #pragma unroll
   for (int e = 0; e < EPT; e += 4) x[e / 4] = U4[min(int(threadIdx.x) * (EPT / 4) + e / 4, last4)];
+}
+template <int EPT>
+__device__ __forceinline__ void pin_bounds(const float4 (&x)[EPT / 4], float (&uv)[EPT]) {
 #pragma unroll
   for (int e = 0; e < EPT; e += 4) {
     uv[e] = materialize(x[e / 4].x); uv[e + 1] = materialize(x[e / 4].y);
@@ -320,13 +323,15 @@ select_unit_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   __shared__ int s_pick[3];
   BlockScan<NWV> scan{s_wt, 0};
 
-  // bounds and query code(s) first: their addresses do not depend on the sequence length
-  float uv[EPT];
-  load_bounds<EPT>(a.U + size_t(bu) * s.Pmax, s.Pmax, uv);
-  uint32_t qraw = 0;
-  if (tid < ncodes * NW)
-    qraw = a.qcode[(size_t(b) * s.Hq + (SHARED ? g * s.G : u)) * NW + tid];
+  // bounds, query code(s) and sequence length loaded together (the first two do not depend on
+  // the length); every lane loads a code word (clamped), so that no branch holds a load back
+  float4 ux[EPT / 4];
+  issue_bounds<EPT>(a.U + size_t(bu) * s.Pmax, s.Pmax, ux);
+  const uint32_t qraw =
+      a.qcode[(size_t(b) * s.Hq + (SHARED ? g * s.G : u)) * NW + min(tid, ncodes * NW - 1)];
   const int t = c.seq_lens[b];                   // position of the appended token, if any
+  float uv[EPT];
+  pin_bounds<EPT>(ux, uv);
   const bool app = a.appended && t >= 0 && t < s.Lmax;
   const int L = min(max(t, 0) + (app ? 1 : 0), s.Lmax);
   const int P = (L + s.S - 1) / s.S;
@@ -559,12 +564,13 @@ select_scan_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   BlockScan<NWV> scan{s_wt, 0};
 
   const bool cutting = a.U != nullptr;           // else every page is kept (no bounds)
-  float uv[EPT];
-  if (cutting) load_bounds<EPT>(a.U + size_t(bu) * s.Pmax, s.Pmax, uv);
-  uint32_t qraw = 0;
-  if (tid < ncodes * NW)
-    qraw = a.qcode[(size_t(b) * s.Hq + (SHARED ? g * s.G : u)) * NW + tid];
+  float4 ux[EPT / 4];
+  if (cutting) issue_bounds<EPT>(a.U + size_t(bu) * s.Pmax, s.Pmax, ux);
+  const uint32_t qraw =
+      a.qcode[(size_t(b) * s.Hq + (SHARED ? g * s.G : u)) * NW + min(tid, ncodes * NW - 1)];
   const int t = c.seq_lens[b];
+  float uv[EPT];
+  if (cutting) pin_bounds<EPT>(ux, uv);
   const bool app = a.appended && t >= 0 && t < s.Lmax;
   const int L = min(max(t, 0) + (app ? 1 : 0), s.Lmax);
   const int P = (L + s.S - 1) / s.S;
