@@ -148,15 +148,18 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
     const float* src = rot ? R + size_t(g) * kD * kD + 32 * (w >> 1) + col
                            : W + size_t(g) * kD * s.NB + coff + 32 * cw + col;
     const int ld = rot ? kD : s.NB;
+    // the lane's 64 values (rows 16 ks + 8 half + e), loaded once for the norm and the pieces
+    float xv[8][8];
+#pragma unroll
+    for (int ks = 0; ks < 8; ++ks)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) xv[ks][e] = src[size_t(16 * ks + 8 * half + e) * ld];
     float scale = 1.0f;
     if (!rot) {
       // |w_c| from fp32 sums of squares (relative error below 2^-16), rounded up by 2^-14
       float nrm = 0.f;
 #pragma unroll
-      for (int i = 0; i < 64; ++i) {
-        const float x = src[size_t(16 * (i >> 3) + 8 * half + (i & 7)) * ld];
-        nrm = fmaf(x, x, nrm);
-      }
+      for (int i = 0; i < 64; ++i) nrm = fmaf(xv[i >> 3][i & 7], xv[i >> 3][i & 7], nrm);
       nrm += __shfl_xor(nrm, 32);
       const float wn = sqrtf(nrm) * (1.0f + 0x1p-14f);
       const uint32_t be = (__float_as_uint(wn) >> 23) & 0xFFu;   // wn in [2^(be-127), 2^(be-126))
@@ -171,7 +174,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
     for (int ks = 0; ks < 8; ++ks) {
       float x[8];
 #pragma unroll
-      for (int e = 0; e < 8; ++e) x[e] = src[size_t(16 * ks + 8 * half + e) * ld] * scale;
+      for (int e = 0; e < 8; ++e) x[e] = xv[ks][e] * scale;
 #pragma unroll
       for (int e = 0; e < 8; ++e) {
         const __bf16 p1 = __bf16(x[e]);
