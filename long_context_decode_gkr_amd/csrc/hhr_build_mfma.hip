@@ -201,46 +201,77 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   // rest. Called by every thread; the caller re-stages a key tile afterwards if one is pending.
   constexpr int kWTs = kD + 1;                    // staged row stride: conflict-free transposes
   static_assert(sizeof(Kt) >= sizeof(float) * kD * kWTs, "W^T fits in the key buffers");
+  // Every load of a thread's share of W, and of a pass's two entries, is issued before any of
+  // them is used (a loop that stored each value as it arrived took one memory round trip per
+  // value).
+  constexpr int kWPer = kD * kD / NT;              // staged W values per thread
+  constexpr int kWBatch = kWPer < 32 ? kWPer : 32;
+  static_assert(kWPer % kWBatch == 0, "whole batches");
+  constexpr int kEnt = 2;                          // queued entries per 4 lanes per pass
   auto drain_queue = [&](int nseg) {               // nseg entries from each wave's segment
     const int n = nseg * kCodeWaves;
     float* WT = reinterpret_cast<float*>(&Kt[0][0][0]);   // WT[c * kWTs + k] = W[k][coff + c]
-    for (int i = tid; i < kD * kD; i += NT) {
-      const int k = i >> 7, cl = i & (kD - 1);
-      WT[cl * kWTs + k] = wcols[size_t(k) * s.NB + coff + cl];
+    {
+      // value tid + j NT is W[(tid >> 7) + j NT / 128][coff + tid % 128]; the thread's offsets
+      // are formed here (materialized), not hoisted into the setup where they would stay live
+      // through the whole launch
+      const int gofs = materialize(int((tid >> 7) * s.NB + coff + (tid & (kD - 1))));
+      const int lofs = materialize(int((tid & (kD - 1)) * kWTs + (tid >> 7)));
+#pragma unroll 1
+      for (int j0 = 0; j0 < kWPer; j0 += kWBatch) {
+        float wv[kWBatch];
+#pragma unroll
+        for (int j = 0; j < kWBatch; ++j)
+          wv[j] = wcols[gofs + size_t(j0 + j) * (NT / kD) * s.NB];
+#pragma unroll
+        for (int j = 0; j < kWBatch; ++j) WT[lofs + (j0 + j) * (NT / kD)] = wv[j];
+      }
     }
     __syncthreads();
     const int q = tid & 3;
-    for (int e = tid >> 2; e < n; e += NT / 4) {
-      const int sg = e / nseg, se = e % nseg;
-      if (se >= min(fb_cnt[sg], kSeg)) continue;   // a shorter segment
-      const uint32_t ent = fb_list[sg * kSeg + se];
-      const int tok = int(ent >> 8), cc = int(ent & 0xFFu);
-      const uint16_t* kr = Kb + (row0 + tok) * kD;
-      uint4 kq[4];
+    for (int e0 = tid >> 2; e0 < n; e0 += kEnt * (NT / 4)) {   // the 4 lanes of an entry agree
+      bool ok[kEnt];
+      uint32_t ent[kEnt];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) kq[i] = *reinterpret_cast<const uint4*>(kr + 32 * q + 8 * i);
-      const float* wq = WT + (cc - coff) * kWTs + 32 * q;
-      double z = 0.0, sa = 0.0;
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const uint32_t kw = i < 4 ? (&kq[0].x)[i] : i < 8 ? (&kq[1].x)[i - 4]
-                          : i < 12 ? (&kq[2].x)[i - 8] : (&kq[3].x)[i - 12];
-        const double p0 = double(__uint_as_float(kw << 16)) * double(wq[2 * i]);
-        const double p1 = double(__uint_as_float(kw & 0xFFFF0000u)) * double(wq[2 * i + 1]);
-        z += p0;
-        sa += fabs(p0);
-        z += p1;
-        sa += fabs(p1);
+      for (int j = 0; j < kEnt; ++j) {
+        const int e = min(e0 + j * (NT / 4), n - 1);
+        const int sg = e / nseg, se = e % nseg;
+        ok[j] = e0 + j * (NT / 4) < n && se < min(fb_cnt[sg], kSeg);   // else a shorter segment
+        ent[j] = ok[j] ? fb_list[sg * kSeg + se] : uint32_t(coff);       // else token 0: a dummy
       }
-      z = group_sum_f64<2>(z);
-      sa = group_sum_f64<2>(sa);
-      if (q == 0) {
-        int cb = certain_bit(z, sa);
-        if (cb < 0) cb = int(exact_bit(Bf16Row{kr}, wcols + cc, s.NB));
-        uint32_t* word = c.codes + (row0 + tok) * NWd + (cc >> 5);
-        const uint32_t mask = 1u << (cc & 31);
-        if (cb) atomicOr(word, mask);
-        else atomicAnd(word, ~mask);
+      uint4 kq[kEnt][4];
+#pragma unroll
+      for (int j = 0; j < kEnt; ++j) {
+        const uint16_t* kr = Kb + (row0 + int(ent[j] >> 8)) * kD;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) kq[j][i] = *reinterpret_cast<const uint4*>(kr + 32 * q + 8 * i);
+      }
+#pragma unroll
+      for (int j = 0; j < kEnt; ++j) {
+        const int tok = int(ent[j] >> 8), cc = int(ent[j] & 0xFFu);
+        const float* wq = WT + (cc - coff) * kWTs + 32 * q;
+        double z = 0.0, sa = 0.0;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const uint32_t kw = (&kq[j][i >> 2].x)[i & 3];
+          const double p0 = double(__uint_as_float(kw << 16)) * double(wq[2 * i]);
+          const double p1 = double(__uint_as_float(kw & 0xFFFF0000u)) * double(wq[2 * i + 1]);
+          z += p0;
+          sa += fabs(p0);
+          z += p1;
+          sa += fabs(p1);
+        }
+        z = group_sum_f64<2>(z);
+        sa = group_sum_f64<2>(sa);
+        if (q == 0 && ok[j]) {
+          const uint16_t* kr = Kb + (row0 + tok) * kD;
+          int cb = certain_bit(z, sa);
+          if (cb < 0) cb = int(exact_bit(Bf16Row{kr}, wcols + cc, s.NB));
+          uint32_t* word = c.codes + (row0 + tok) * NWd + (cc >> 5);
+          const uint32_t mask = 1u << (cc & 31);
+          if (cb) atomicOr(word, mask);
+          else atomicAnd(word, ~mask);
+        }
       }
     }
   };
