@@ -160,7 +160,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
       float nrm = 0.f;
 #pragma unroll
       for (int i = 0; i < 64; ++i) nrm = fmaf(xv[i >> 3][i & 7], xv[i >> 3][i & 7], nrm);
-      nrm += __shfl_xor(nrm, 32);
+      nrm += lane_xor(nrm, 32);
       const float wn = sqrtf(nrm) * (1.0f + 0x1p-14f);
       const uint32_t be = (__float_as_uint(wn) >> 23) & 0xFFu;   // wn in [2^(be-127), 2^(be-126))
       const bool tiny = !(wn > 1e-15f) || be >= 253u;
@@ -329,8 +329,8 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
                 lo = fminf(lo, acc[u][r]);
                 hi = fmaxf(hi, acc[u][r]);
               }
-              lo = fminf(lo, __shfl_xor(lo, 32));
-              hi = fmaxf(hi, __shfl_xor(hi, 32));
+              lo = fminf(lo, lane_from_above(lo, 32));   // lanes 0-31 store
+              hi = fmaxf(hi, lane_from_above(hi, 32));
               if (half == 0) {
                 stage_f[0][j][(tc + tl0) / S + pp] = lo;
                 stage_f[1][j][(tc + tl0) / S + pp] = hi;
@@ -373,7 +373,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
           neg <<= 4 * half;
           sure <<= 4 * half;
           uint32_t word = ~neg & pos_mask;
-          word |= __shfl_xor(word, 32);
+          word |= lane_from_above_u(word, 32);   // lanes 0-31 store
           const int t = t0 + tl0 + col;
           uint32_t uns = t < L ? (~sure | tiny_mask) & pos_mask : 0u;
           // queue the uncertain bits in the wave's own segment, each lane at its prefix (no

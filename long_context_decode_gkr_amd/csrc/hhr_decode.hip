@@ -308,8 +308,8 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
       float d = 0.f;
 #pragma unroll
       for (int e = 0; e < EPL; ++e) d = fmaf(qv[e], f[e], d);
-#pragma unroll
-      for (int off = LPR / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+      d = row16_sum(d);                         // the row's LPR lanes: 16, or 32 for fp32
+      if constexpr (LPR == 32) d += lane_xor(d, 16);
       sc[it] = (row0 + it * RPI + rg < count) ? d : -INFINITY;
       mx = fmaxf(mx, sc[it]);
     }
@@ -326,12 +326,13 @@ attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ V,
 #pragma unroll
       for (int e = 0; e < EPL; ++e) o[e] = fmaf(p, f[e], o[e]);
     }
-    // reduce across the row groups of the wave (lanes that share `sub`)
+    // reduce across the row groups of the wave (lanes that share `sub`) into row group 0, the
+    // lanes that store the result
 #pragma unroll
     for (int off = LPR; off < kWave; off <<= 1) {
-      l += __shfl_xor(l, off);
+      l += lane_from_above(l, off);
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[e] += __shfl_xor(o[e], off);
+      for (int e = 0; e < EPL; ++e) o[e] += lane_from_above(o[e], off);
     }
     if (rg == 0) {
 #pragma unroll

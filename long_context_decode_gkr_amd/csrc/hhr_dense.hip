@@ -99,8 +99,8 @@ dense_attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ 
         float d = 0.f;
 #pragma unroll
         for (int e = 0; e < EPL; ++e) d = fmaf(qv[hh][e], f[e], d);
-#pragma unroll
-        for (int off = LPR / 2; off >= 1; off >>= 1) d += __shfl_xor(d, off);
+        d = row16_sum(d);                       // the row's LPR lanes: 16, or 32 for fp32
+        if constexpr (LPR == 32) d += lane_xor(d, 16);
         sc[hh][it] = ok ? d : -INFINITY;
       }
     }
@@ -148,9 +148,9 @@ dense_attn_kernel(Shape s, const void* __restrict__ K, const void* __restrict__ 
   for (int hh = 0; hh < G; ++hh) {
 #pragma unroll
     for (int off = LPR; off < kWave; off <<= 1) {
-      l[hh] += __shfl_xor(l[hh], off);
+      l[hh] += lane_from_above(l[hh], off);   // into row group 0, which stores
 #pragma unroll
-      for (int e = 0; e < EPL; ++e) o[hh][e] += __shfl_xor(o[hh][e], off);
+      for (int e = 0; e < EPL; ++e) o[hh][e] += lane_from_above(o[hh][e], off);
     }
     if (rg == 0) {
 #pragma unroll
@@ -313,10 +313,7 @@ dense_attn_mfma_kernel(Shape s, const void* __restrict__ K, const void* __restri
     float mx[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      float m = fmaxf(sc[0][i], sc[1][i]);
-#pragma unroll
-      for (int off = 8; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-      mx[i] = m;
+      mx[i] = row16_max(fmaxf(sc[0][i], sc[1][i]));
     }
     float f0[G];
 #pragma unroll
@@ -383,9 +380,7 @@ dense_attn_mfma_kernel(Shape s, const void* __restrict__ K, const void* __restri
   __shared__ float s_o[4][G][kD];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    float v = lp[i];
-#pragma unroll
-    for (int off = 8; off >= 1; off >>= 1) v += __shfl_xor(v, off);
+    const float v = row16_sum(lp[i]);
     const int hh = 4 * quad + i;
     if (col == 0 && hh < G) s_l[w][hh] = v;
   }
@@ -394,7 +389,7 @@ dense_attn_mfma_kernel(Shape s, const void* __restrict__ K, const void* __restri
 #pragma unroll
     for (int off = 16; off < kWave; off <<= 1)
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[hh][e] += __shfl_xor(o[hh][e], off);
+      for (int e = 0; e < 8; ++e) o[hh][e] += lane_from_above(o[hh][e], off);   // row group 0 stores
     if (rg == 0) {
 #pragma unroll
       for (int e = 0; e < 8; ++e) s_o[w][hh][sub * 8 + e] = o[hh][e];

@@ -293,15 +293,46 @@ __device__ __forceinline__ double group_sum_f64(double v) {
   return v;
 }
 
-__device__ __forceinline__ float wave_max(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+// Maximum over each row of 16 lanes, returned in every lane of the row (the same butterfly).
+__device__ __forceinline__ float row16_max(float v) {
+  v = fmaxf(v, dpp_f<0xB1>(v));   // quad_perm [1,0,3,2]
+  v = fmaxf(v, dpp_f<0x4E>(v));   // quad_perm [2,3,0,1]
+  v = fmaxf(v, dpp_f<0x141>(v));  // row_half_mirror
+  v = fmaxf(v, dpp_f<0x140>(v));  // row_mirror
   return v;
 }
-__device__ __forceinline__ float wave_sum(float v) {
-#pragma unroll
-  for (int o = 32; o >= 1; o >>= 1) v += __shfl_xor(v, o);
-  return v;
+
+// The value of lane l ^ 32 (l ^ 16) in lane l, from one v_permlane32_swap (v_permlane16_swap)
+// and a select: VALU only, no LDS round trip (a __shfl_xor becomes ds_bpermute). With both
+// operands x, the swap returns {x of lanes 0-31 in both halves, x of lanes 32-63 in both
+// halves}; the 16-lane form does the same per pair of rows (rows 0 and 1, rows 2 and 3).
+__device__ __forceinline__ uint32_t lane_xor32_u(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+  return (lane_id() & 32) ? r[0] : r[1];
+}
+__device__ __forceinline__ uint32_t lane_xor16_u(uint32_t x) {
+  const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+  return (lane_id() & 16) ? r[0] : r[1];
+}
+// x of lane l ^ off for off = 16 or 32 (a compile-time value once the caller's loop is unrolled)
+__device__ __forceinline__ float lane_xor(float x, int off) {
+  const uint32_t u = __float_as_uint(x);
+  return __uint_as_float(off == 16 ? lane_xor16_u(u) : lane_xor32_u(u));
+}
+// The same exchange where only the lower lane of each pair uses the result (lanes with bit
+// log2(off) clear get lane l + off's value; the others keep their own): the swap alone, no select.
+__device__ __forceinline__ uint32_t lane_from_above_u(uint32_t x, int off) {
+  return off == 16 ? __builtin_amdgcn_permlane16_swap(x, x, false, false)[1]
+                   : __builtin_amdgcn_permlane32_swap(x, x, false, false)[1];
+}
+__device__ __forceinline__ float lane_from_above(float x, int off) {
+  return __uint_as_float(lane_from_above_u(__float_as_uint(x), off));
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+  v = row16_max(v);
+  v = fmaxf(v, lane_xor(v, 16));
+  return fmaxf(v, lane_xor(v, 32));
 }
 
 // XCD-aware placement. Workgroups are dealt to the 8 XCDs round-robin by linear id, and each
