@@ -49,6 +49,7 @@ Prints ONE JSON line. Options: --gpus (must be 1), --steps, --warmup, --workload
 from __future__ import annotations
 
 import argparse
+import gc
 import hashlib
 import json
 import math
@@ -655,6 +656,11 @@ def main():
         torch.cuda.synchronize()
         return (time.perf_counter() - t_start) * 1e3 / K
 
+    # the timed passes run with Python's cycle collector paused (collected once before), so that a
+    # collection cannot stall the host loop that keeps the GPU queue filled
+    gc.collect()
+    gc.disable()
+
     # ---- pass 1 (launches with events): per-kernel durations from HIP events that the runtime
     # records around each kernel's own execution on the decode stream (hipExtLaunchKernel)
     stream = hb.current_stream()
@@ -741,6 +747,7 @@ def main():
             dense_step(i, None, stream)
         torch.cuda.synchronize()
         dense_ms = (time.perf_counter() - t_start) * 1e3 / K
+    gc.enable()
 
     ms_step = stream_ms
     avg_ms = {n: float(np.mean(v)) for n, v in per.items()}
