@@ -29,8 +29,11 @@
 //   * code waves: code columns coff + 32 v .. + 31 (v the code wave's index), the 2 W pieces as
 //     MFMA A fragments, the keys as B, so a lane holds 16 code columns of one token and
 //     assembles its bits without any cross-lane vote.
-// Grid (nper, Hkv, B): workgroup `first` builds chunks first, first + nper, ... of 512 tokens
-// of its sequence; the key rows stream through two LDS buffers of 128 rows (the next tile's
+// Grid (nper, Hkv, ceil(B / 64)): the 512-token chunks of KV head g of a group of at most 64
+// sequences form one list (sequence by sequence, in order), and workgroup `first` builds its
+// entries first, first + nper, ..., so the workgroups of a batch of unequal lengths get equal
+// shares (one workgroup per sequence and KV head had left the longest sequence's workgroups
+// with 14 chunks against 10 at 8 sequences of 8K-32K tokens); the key rows stream through two LDS buffers of 128 rows (the next tile's
 // global loads in flight while the current one is multiplied), each staged row with its norm.
 // 256-bit codes take a second launch without rotation waves for code columns 128..255.
 #include "hhr_device.h"
@@ -49,6 +52,7 @@ constexpr int kKRow = kD + 8;         // bf16 elements per staged row: 272 B, so
                                       // fragment reads of 32 consecutive rows hit distinct banks
 constexpr int kCodeWaves = 4;         // 128 code columns per launch
 constexpr int kFbCap = 4096;          // queued uncertain code bits per workgroup
+constexpr int kSeqGroup = 64;         // sequences whose chunks one list covers (one per lane)
 constexpr float kCertScale = 1.0f / 8192.0f;   // 2^-13
 
 // One stored bf16 key row, read as fp32 values.
@@ -72,10 +76,17 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   constexpr int RW = ROT ? 4 : 0;                 // rotation waves
   constexpr int KPT = kKTile * (kD / 8) / NT;     // 16-byte key pieces per thread per tile
   static_assert(KPT * NT == kKTile * (kD / 8), "whole tiles");
-  const int first = blockIdx.x, g = blockIdx.y, b = blockIdx.z;
-  const int L = min(max(c.seq_lens[b], 0), s.Lmax);
-  if (first * kChunk >= L) return;
+  const int first = blockIdx.x, g = blockIdx.y, grp = blockIdx.z;
   const int tid = threadIdx.x, lane = lane_id(), w = wave_id();
+  // lane l of every wave: the length of sequence 64 grp + l (0 past the batch), its chunk count
+  // and the number of chunks up to and including it, so that the sequence of list entry f is
+  // the number of lanes whose inclusive count is at most f (one ballot)
+  const int bl = kSeqGroup * grp + lane;
+  const int lenl = bl < s.B ? min(max(c.seq_lens[bl], 0), s.Lmax) : 0;
+  const int nchl = (lenl + kChunk - 1) / kChunk;
+  const int cincl = wave_incl_sum(nchl);
+  const int ntot = __builtin_amdgcn_readlane(cincl, kWave - 1);
+  if (first >= ntot) return;
   // with rotation waves, even waves rotate (channel block w / 2) and odd waves hash (code
   // block w / 2): consecutive waves share a SIMD, so each SIMD runs one wave of each kind
   // (measured 227 -> 209 us at 128K against waves 0..3 rotating)
@@ -89,22 +100,36 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   // at once fall in different banks
   __shared__ float stage_f[ROT ? 2 : 1][ROT ? kD : 1][kChunk / S + 1];
   __shared__ uint32_t stage_c[kChunk][kCodeWaves + 1];   // code words, padded rows
-  // queued uncertain bits (token << 8 | column), one segment of kSeg per code wave, and each
-  // wave's count (which may pass kSeg: the rest is lost, see the drain)
+  // queued uncertain bits (row of K, column), one segment of kSeg per code wave, and each
+  // wave's count (which may pass kSeg: the rest is lost, see the drain). A row index is below
+  // 2^32 for any K cache under 1 TiB.
   constexpr int kSeg = kFbCap / kCodeWaves;
-  __shared__ uint32_t fb_list[kFbCap];
+  __shared__ uint2 fb_list[kFbCap];
   __shared__ int fb_cnt[kCodeWaves];
   if (tid < kCodeWaves) fb_cnt[tid] = 0;          // published by the first staging barrier
   int qn = 0;                                     // this code wave's count (uniform)
 
-  const size_t row0 = (size_t(b) * s.Hkv + g) * s.Lmax;
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(c.K);
-  auto tile_tok0 = [&](int T) { return (first + (T >> 2) * nper) * kChunk + (T & 3) * kKTile; };
+  // list entry f: its sequence, the chunk's index in it and the sequence's length (uniform)
+  struct ChunkPos { int f, b, ch, L; };
+  auto locate = [&](int f) {
+    const int l = int(__popcll(__ballot(cincl <= f)));   // < 64 since f < ntot
+    ChunkPos p;
+    p.f = f;
+    p.b = kSeqGroup * grp + l;
+    p.ch = f - (__builtin_amdgcn_readlane(cincl, l) - __builtin_amdgcn_readlane(nchl, l));
+    p.L = __builtin_amdgcn_readlane(lenl, l);
+    return p;
+  };
+  auto kv_row0 = [&](const ChunkPos& p) { return (size_t(p.b) * s.Hkv + g) * s.Lmax; };
+  auto chunk_tiles = [&](const ChunkPos& p) {
+    return min(kChunk / kKTile, (p.L - p.ch * kChunk + kKTile - 1) / kKTile);
+  };
 
   // ---- key tile staging: thread piece e = tid + i NT is row e / 16, bytes 16 (e % 16) .. + 15;
   // rows past the end repeat the last valid row
   uint4 kv[KPT];
-  auto load_tile = [&](int t0) {
+  auto load_tile = [&](size_t row0, int L, int t0) {
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int e = tid + i * NT;
@@ -134,7 +159,9 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
       }
     }
   };
-  load_tile(tile_tok0(0));
+  ChunkPos cp = locate(first);                    // the chunk being built
+  int tq = 0;                                     // its tile
+  load_tile(kv_row0(cp), cp.L, cp.ch * kChunk);
 
   // ---- stationary operand pieces (bf16, hardware round-to-nearest-even): lane (half, col)
   // holds rows 16 ks + 8 half .. + 7 of column `col` of its 32-column block, for ks = 0..7.
@@ -208,7 +235,8 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   constexpr int kWBatch = kWPer < 32 ? kWPer : 32;
   static_assert(kWPer % kWBatch == 0, "whole batches");
   constexpr int kEnt = 2;                          // queued entries per 4 lanes per pass
-  auto drain_queue = [&](int nseg) {               // nseg entries from each wave's segment
+  auto drain_queue = [&](int nseg, size_t row_any) {   // nseg entries from each wave's segment;
+                                                         // row_any: a valid row of K
     const int n = nseg * kCodeWaves;
     float* WT = reinterpret_cast<float*>(&Kt[0][0][0]);   // WT[c * kWTs + k] = W[k][coff + c]
     {
@@ -231,24 +259,26 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
     const int q = tid & 3;
     for (int e0 = tid >> 2; e0 < n; e0 += kEnt * (NT / 4)) {   // the 4 lanes of an entry agree
       bool ok[kEnt];
-      uint32_t ent[kEnt];
+      uint2 ent[kEnt];
 #pragma unroll
       for (int j = 0; j < kEnt; ++j) {
         const int e = min(e0 + j * (NT / 4), n - 1);
         const int sg = e / nseg, se = e % nseg;
         ok[j] = e0 + j * (NT / 4) < n && se < min(fb_cnt[sg], kSeg);   // else a shorter segment
-        ent[j] = ok[j] ? fb_list[sg * kSeg + se] : uint32_t(coff);       // else token 0: a dummy
+        ent[j] = ok[j] ? fb_list[sg * kSeg + se]
+                       : make_uint2(uint32_t(row_any), uint32_t(coff));   // else a dummy
       }
       uint4 kq[kEnt][4];
 #pragma unroll
       for (int j = 0; j < kEnt; ++j) {
-        const uint16_t* kr = Kb + (row0 + int(ent[j] >> 8)) * kD;
+        const uint16_t* kr = Kb + size_t(ent[j].x) * kD;
 #pragma unroll
         for (int i = 0; i < 4; ++i) kq[j][i] = *reinterpret_cast<const uint4*>(kr + 32 * q + 8 * i);
       }
 #pragma unroll
       for (int j = 0; j < kEnt; ++j) {
-        const int tok = int(ent[j] >> 8), cc = int(ent[j] & 0xFFu);
+        const size_t row = ent[j].x;
+        const int cc = int(ent[j].y);
         const float* wq = WT + (cc - coff) * kWTs + 32 * q;
         double z = 0.0, sa = 0.0;
 #pragma unroll
@@ -264,10 +294,10 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
         z = group_sum_f64<2>(z);
         sa = group_sum_f64<2>(sa);
         if (q == 0 && ok[j]) {
-          const uint16_t* kr = Kb + (row0 + tok) * kD;
+          const uint16_t* kr = Kb + row * kD;
           int cb = certain_bit(z, sa);
           if (cb < 0) cb = int(exact_bit(Bf16Row{kr}, wcols + cc, s.NB));
-          uint32_t* word = c.codes + (row0 + tok) * NWd + (cc >> 5);
+          uint32_t* word = c.codes + row * NWd + (cc >> 5);
           const uint32_t mask = 1u << (cc & 31);
           if (cb) atomicOr(word, mask);
           else atomicAnd(word, ~mask);
@@ -277,12 +307,18 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   };
 
   for (int T = 0;; ++T) {
-    const int t0 = tile_tok0(T);                  // < L
-    const int cbase = (first + (T >> 2) * nper) * kChunk;
+    const size_t row0 = kv_row0(cp);              // row of token 0 of the chunk's (b, g)
+    const int L = cp.L;
+    const int cbase = cp.ch * kChunk;
+    const int t0 = cbase + tq * kKTile;           // < L
     const int tc = t0 - cbase;                    // the tile's first token within its chunk
-    const int t1 = tile_tok0(T + 1);
-    const bool more = t1 < L;
-    if (more) load_tile(t1);                      // in flight during the products
+    // the next tile: this chunk's next one, else the first of the workgroup's next chunk
+    const bool chunk_done = tq + 1 >= chunk_tiles(cp);
+    const bool more = !chunk_done || cp.f + nper < ntot;
+    const ChunkPos np = chunk_done && more ? locate(cp.f + nper) : cp;
+    const int nq = chunk_done ? 0 : tq + 1;
+    if (more) load_tile(kv_row0(np), np.L, np.ch * kChunk + nq * kKTile);   // in flight during
+                                                                             // the products
     const int buf = T & 1;
 
     // ---- products: sub-tiles (2 sp, 2 sp + 1) of 32 rows, two accumulators in flight; the
@@ -387,7 +423,8 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
               const int bi = __builtin_ctz(uns);
               uns &= uns - 1;
               if (pos < kSeg)
-                fb_list[cw * kSeg + pos] = (uint32_t(t) << 8) | uint32_t(coff + 32 * cw + bi);
+                fb_list[cw * kSeg + pos] =
+                    make_uint2(uint32_t(row0 + t), uint32_t(coff + 32 * cw + bi));
               ++pos;
             }
           }
@@ -399,7 +436,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
     if (more) store_tile(buf ^ 1);
     __syncthreads();
 
-    if (!more || (T & 3) == 3) {
+    if (chunk_done) {
       // ---- the chunk is complete: write its page extrema and code words out (certain bits
       // final; the queued ones are decided by the exact path)
       const int ntok = min(kChunk, L - cbase);
@@ -407,7 +444,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
         constexpr int PPC = kChunk / S;           // pages per chunk
         const int npg = (ntok + S - 1) / S;
         const int pg0 = cbase / S;
-        const size_t sbase = (size_t(b) * s.Hkv + g) * kD;
+        const size_t sbase = (size_t(cp.b) * s.Hkv + g) * kD;
         for (int e = tid; e < kD * PPC; e += NT) {
           const int j = e / PPC, pl = e % PPC;
           if (pl < npg)
@@ -423,14 +460,14 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
       // segment's capacity (more uncertain bits in one chunk than it holds: degenerate
       // projections) are lost; then every word of this chunk is recomputed from the stored
       // operands instead (slow, only for such inputs).
-      int nq = 0;
+      int nfb = 0;
 #pragma unroll
-      for (int i = 0; i < kCodeWaves; ++i) nq = max(nq, fb_cnt[i]);
-      if (nq >= 3 * kSeg / 4 || !more) {
+      for (int i = 0; i < kCodeWaves; ++i) nfb = max(nfb, fb_cnt[i]);
+      if (nfb >= 3 * kSeg / 4 || !more) {
         wait_memory();
         __syncthreads();
-        drain_queue(min(nq, kSeg));
-        if (nq > kSeg) {
+        drain_queue(min(nfb, kSeg), row0);
+        if (nfb > kSeg) {
           wait_memory();
           __syncthreads();
           for (int e = tid; e < ntok * kCodeWaves; e += NT) {
@@ -450,22 +487,25 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
       __syncthreads();   // the chunk's LDS staging is read out before the next chunk reuses it
     }
     if (!more) break;
+    cp = np;
+    tq = nq;
   }
 }
 
 hipError_t launch_build_mfma(const Shape& s, const CacheView& c, const float* R, const float* W,
                              hipStream_t st) {
-  // about one workgroup per CU (about 120 KB of LDS each): nper workgroups per (b, KV head),
-  // each building every nper-th chunk of 512 tokens
+  // about one workgroup per CU (about 144 KB of LDS each): nper workgroups per (KV head, group
+  // of 64 sequences), each building every nper-th entry of the group's list of chunks
   const int nch = (s.Lmax + kChunk - 1) / kChunk;
   int dev = 0, ncu = 0;
   if (hipGetDevice(&dev) != hipSuccess ||
       hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
       ncu <= 0)
     ncu = 256;
-  const int heads = s.Hkv * s.B;
-  const int nper = std::max(1, std::min(nch, (ncu + heads - 1) / heads));
-  const dim3 grid(nper, s.Hkv, s.B);
+  const int ngrp = (s.B + kSeqGroup - 1) / kSeqGroup;
+  const int units = s.Hkv * ngrp;
+  const int nper = std::max(1, std::min(std::min(s.B, kSeqGroup) * nch, (ncu + units - 1) / units));
+  const dim3 grid(nper, s.Hkv, ngrp);
   const KernelTimer none{nullptr, nullptr};
   hipError_t e;
   if (s.S == 16)

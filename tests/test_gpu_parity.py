@@ -457,6 +457,34 @@ def test_build_mfma_matches_oracle(cfg_id, L, batch, lens):
     hc.check_index(lay, hc.oracle_index(lay), extrema_atol_scale=MFMA_EXTREMA_SCALE)
 
 
+def test_build_mfma_balanced_chunk_list_across_sequence_groups():
+    """70 sequences of ragged lengths (empty, one token, chunk and tile boundaries, the full
+    capacity) in two groups of at most 64: each KV head's workgroups share out the group's
+    list of 512-token chunks, so one workgroup builds chunks of several sequences in turn and
+    its queued uncertain bits carry their own rows. Codes bit-exact and extrema admissible
+    against the oracle on sampled (sequence, KV head) pairs of both groups; codes equal to the
+    fp64 builder's on every pair."""
+    _torch()
+    r = np.random.default_rng(7)
+    lens = [int(x) for x in r.integers(0, 1281, size=70)]
+    lens[:6] = [0, 1, 512, 513, 1280, 127]
+    lens[64:68] = [0, 1280, 640, 1]
+    cfg = _cfg(3, 1280, batch=70, lens=lens, n_plant=0, num_q_heads=4, num_kv_heads=2)
+    lay = hc.GpuLayer(cfg, max_seq_len=1280)
+    lay.build(method="fp64")
+    codes64 = lay.cache.codes.cpu().numpy().view(np.uint32).copy()
+    lay.cache.codes.zero_()
+    lay.cache.page_min.zero_()
+    lay.cache.page_max.zero_()
+    lay.build(method="auto")
+    got = lay.cache.codes.cpu().numpy().view(np.uint32)
+    for b, L in enumerate(lens):
+        np.testing.assert_array_equal(got[b, :, :L], codes64[b, :, :L], err_msg=f"b={b}")
+    pairs = [(b, g) for b in (1, 2, 3, 4, 5, 17, 63, 65, 66, 69) for g in (0, 1)]
+    hc.check_index(lay, hc.oracle_index(lay, heads_kv=pairs), pairs=pairs,
+                   extrema_atol_scale=MFMA_EXTREMA_SCALE)
+
+
 @pytest.mark.parametrize("nzero,ntiny", [(16, 8), (1, 0), (0, 1)])
 def test_build_mfma_exact_path_for_zero_and_tiny_projections(nzero, ntiny):
     # nzero code columns give z = k0 - k1 = 0 exactly (k0 == k1), ntiny give z = 2^-30 k2: all
