@@ -327,10 +327,11 @@ def read_ceiling(hb, nbytes, quiet, reps=48):
 
 def cpu_baseline(cfg, data, append, quiet, budget_s=8.0):
     """The oracle, as it stands, on the whole layer: for every sequence and KV head (index built
-    untimed beforehand), with `append` one append, then the decode of its query heads; repeated
-    for ~budget_s, once with the BLAS/OpenMP thread pools limited to one thread and once to all
-    the cores this process may run on (len(os.sched_getaffinity(0))). The whole layer is timed,
-    so nothing is extrapolated."""
+    beforehand), with `append` one append, then the decode of its query heads; repeated for
+    ~budget_s, once with the BLAS/OpenMP thread pools limited to one thread and once to all the
+    cores this process may run on (len(os.sched_getaffinity(0))). The index build over every key
+    of the layer is timed on its own, once at each thread setting. The whole layer is timed, so
+    nothing is extrapolated."""
     import numpy as np
     import threadpoolctl
     from oracle import hhr_oracle as orc
@@ -341,20 +342,28 @@ def cpu_baseline(cfg, data, append, quiet, budget_s=8.0):
     B, Hkv = len(lens), cfg.num_kv_heads
     Lmax = data["K"].shape[2]
     Pmax = Lmax // S
-    t0 = time.perf_counter()
-    log(f"cpu baseline: oracle index of {B} x {Hkv} (sequence, KV head) pairs (untimed setup)",
-        quiet)
-    base = {}
-    for b in range(B):
-        for g in range(Hkv):
-            lo, hi, kc = orc.build_head(data["K"][b, g], lens[b], data["R"][g], data["W"][g], S)
-            st = dict(lo=np.zeros((Pmax, d), np.float32), hi=np.zeros((Pmax, d), np.float32),
-                      codes=np.zeros((Lmax, cfg.hash_bits // 32), np.uint32),
-                      K=data["K"][b, g].copy() if append else data["K"][b, g],
-                      V=data["V"][b, g].copy() if append else data["V"][b, g])
-            st["lo"][:len(lo)], st["hi"][:len(hi)], st["codes"][:lens[b]] = lo, hi, kc
-            base[(b, g)] = st
-    setup_s = time.perf_counter() - t0
+    log(f"cpu baseline: oracle index of {B} x {Hkv} (sequence, KV head) pairs, "
+        f"{ncores} threads, then 1", quiet)
+
+    def build_all(threads):
+        base = {}
+        with threadpoolctl.threadpool_limits(limits=threads):
+            t0 = time.perf_counter()
+            for b in range(B):
+                for g in range(Hkv):
+                    lo, hi, kc = orc.build_head(data["K"][b, g], lens[b], data["R"][g],
+                                                data["W"][g], S)
+                    st = dict(lo=np.zeros((Pmax, d), np.float32),
+                              hi=np.zeros((Pmax, d), np.float32),
+                              codes=np.zeros((Lmax, cfg.hash_bits // 32), np.uint32),
+                              K=data["K"][b, g].copy() if append else data["K"][b, g],
+                              V=data["V"][b, g].copy() if append else data["V"][b, g])
+                    st["lo"][:len(lo)], st["hi"][:len(hi)], st["codes"][:lens[b]] = lo, hi, kc
+                    base[(b, g)] = st
+            return base, time.perf_counter() - t0
+
+    base, build_n = build_all(ncores)
+    _, build_1 = build_all(1)
     kn, vn = synth.append_tokens(cfg, 1)
     scale = orc.default_scale(d)
 
@@ -385,11 +394,14 @@ def cpu_baseline(cfg, data, append, quiet, budget_s=8.0):
     what = "append + decode" if append else "decode"
     return {"value": round(usn, 1), "unit": "us/step/layer", "cores": ncores, "kind": "oracle",
             "single_thread_value": round(us1, 1),
+            "builder_value": round(build_n * 1e6, 1), "builder_single_thread_value":
+                round(build_1 * 1e6, 1), "builder_unit": "us per index build of the layer",
             "sample": (f"the whole layer ({B} sequence(s) x {Hkv} KV heads x {G} query heads, "
                        f"{sum(lens)} tokens, {what}): {repsn} steps in {spentn:.1f} s with the "
                        f"thread pools at {ncores} threads (all cores of the process's affinity "
-                       f"mask), {reps1} steps in {spent1:.1f} s at 1 thread; index build "
-                       f"untimed ({setup_s:.1f} s); no extrapolation")}
+                       f"mask), {reps1} steps in {spent1:.1f} s at 1 thread; the index build "
+                       f"over every key of the layer once at each setting ({build_n:.2f} s, "
+                       f"{build_1:.2f} s); no extrapolation")}
 
 
 TOPK_FRAC = 0.015   # the exact top-K reference: K = 1.5 % of the context (HHR §4.1 default)

@@ -41,6 +41,7 @@ def test_bench_prints_one_contract_line():
     cb = d["cpu_baseline"]
     assert cb["kind"] == "oracle" and cb["cores"] == len(os.sched_getaffinity(0))
     assert cb["value"] > 0 and cb["single_thread_value"] > 0 and cb["sample"]
+    assert cb["builder_value"] > 0 and cb["builder_single_thread_value"] > 0
     sp = d["step_spread"]
     assert sp["p10_us"] <= sp["p50_us"] <= sp["p90_us"]
     # the kernels a batch-1 step launches, each timed
