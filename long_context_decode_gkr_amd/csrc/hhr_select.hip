@@ -417,7 +417,14 @@ select_unit_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
       // (without the fine stage every live candidate has distance 0: all are taken)
       const uint32_t dd = a.fine ? code_dist<NW, SHARED>(cw[k], qw, s_qw, ncodes) : 0u;
       const bool live = tt[k] < L;               // implies slot < nslots
-      atomicAdd(live ? &whist[dd] : &whist[kRadixBins + lane], 1u);
+      if (a.fine) {   // uniform
+        atomicAdd(live ? &whist[dd] : &whist[kRadixBins + lane], 1u);
+      } else {
+        // every live slot has distance 0: one count per wave (per-lane atomics on one LDS word
+        // would queue behind each other)
+        const uint32_t nl = uint32_t(__popcll(__ballot(live)));
+        if (lane == 0) atomicAdd(&whist[0], nl);
+      }
       s_dist[slot < nslots ? slot : kUnitSlots + lane] = DT(live ? dd : kNone);
     }
   };
@@ -659,7 +666,12 @@ select_scan_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
         // (without the fine stage every live candidate has distance 0: all are taken)
         const uint32_t d = a.fine ? code_dist<NW, SHARED>(cw[k][i], qw, s_qw, ncodes) : 0u;
         const bool live = in && tok0[k] + i < L;
-        atomicAdd(live ? &cl.hist[d] : &cl.hist[kRadixBins + lane], 1u);
+        if (a.fine) {   // uniform
+          atomicAdd(live ? &cl.hist[d] : &cl.hist[kRadixBins + lane], 1u);
+        } else {        // every live slot has distance 0: one count per wave
+          const uint32_t nl = uint32_t(__popcll(__ballot(live)));
+          if (lane == 0) atomicAdd(&cl.hist[0], nl);
+        }
         dd[i] = live ? d : kNone;
       }
       if (in) {
