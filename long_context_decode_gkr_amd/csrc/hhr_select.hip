@@ -302,7 +302,9 @@ __device__ __forceinline__ uint32_t code_dist(const uint4 (&x)[NW / 4], const ui
 constexpr int kEmitSPT = 8;         // cached distances per thread per emission round
 static_assert(16 % kEmitSPT == 0, "an emission round must not cross a page (sizes 16, 32)");
 
-template <int NB, int EPT, int SHARED, int NT>
+// FINE: the instantiation for a.fine = 1 (the Hamming ranking runs) or 0 (the coarse stage
+// alone: every live candidate is taken, and the histogram counts them once per wave)
+template <int NB, int EPT, int SHARED, int NT, int FINE>
 __global__ void __launch_bounds__(NT)
 select_unit_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   constexpr int NWV = NT / kWave;
@@ -417,11 +419,10 @@ select_unit_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
       // (without the fine stage every live candidate has distance 0: all are taken)
       const uint32_t dd = a.fine ? code_dist<NW, SHARED>(cw[k], qw, s_qw, ncodes) : 0u;
       const bool live = tt[k] < L;               // implies slot < nslots
-      if (a.fine) {   // uniform
+      if constexpr (FINE) {
         atomicAdd(live ? &whist[dd] : &whist[kRadixBins + lane], 1u);
       } else {
-        // every live slot has distance 0: one count per wave (per-lane atomics on one LDS word
-        // would queue behind each other)
+        // one count per wave: per-lane atomics on the one bin would queue behind each other
         const uint32_t nl = uint32_t(__popcll(__ballot(live)));
         if (lane == 0) atomicAdd(&whist[0], nl);
       }
@@ -549,7 +550,7 @@ select_unit_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
 // (one page) per thread and unit of work, the code loads of up to 16 slots issued before any
 // use.
 // ---------------------------------------------------------------------------------------------
-template <int NB, int EPT, int SHARED>
+template <int NB, int EPT, int SHARED, int FINE>
 __global__ void __launch_bounds__(kScanThreads)
 select_scan_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
   constexpr int NT = kScanThreads;
@@ -666,9 +667,9 @@ select_scan_kernel(Shape s, CacheView c, SelectArgs a, DebugView dbg) {
         // (without the fine stage every live candidate has distance 0: all are taken)
         const uint32_t d = a.fine ? code_dist<NW, SHARED>(cw[k][i], qw, s_qw, ncodes) : 0u;
         const bool live = in && tok0[k] + i < L;
-        if (a.fine) {   // uniform
+        if constexpr (FINE) {
           atomicAdd(live ? &cl.hist[d] : &cl.hist[kRadixBins + lane], 1u);
-        } else {        // every live slot has distance 0: one count per wave
+        } else {   // one count per wave (per-lane atomics on the one bin would queue)
           const uint32_t nl = uint32_t(__popcll(__ballot(live)));
           if (lane == 0) atomicAdd(&cl.hist[0], nl);
         }
@@ -893,13 +894,17 @@ template <int NB, int EPT, int NT>
 static hipError_t launch_unit(const Shape& s, const CacheView& c, const SelectArgs& a,
                               const DebugView& dbg, hipStream_t st) {
   const dim3 grid(a.shared ? s.Hkv : s.Hq, s.B);
+  const KernelTimer tm = kernel_timer(dbg, 2);
+  const char* nm = "select_unit_kernel";
   const hipError_t e =
-      a.shared ? launch_kernel("select_unit_kernel",
-                               select_unit_kernel<NB, EPT, 1, NT>, grid, dim3(NT), st,
-                               kernel_timer(dbg, 2), s, c, a, dbg)
-               : launch_kernel("select_unit_kernel",
-                               select_unit_kernel<NB, EPT, 0, NT>, grid, dim3(NT), st,
-                               kernel_timer(dbg, 2), s, c, a, dbg);
+      a.fine ? (a.shared ? launch_kernel(nm, select_unit_kernel<NB, EPT, 1, NT, 1>, grid, dim3(NT),
+                                         st, tm, s, c, a, dbg)
+                         : launch_kernel(nm, select_unit_kernel<NB, EPT, 0, NT, 1>, grid, dim3(NT),
+                                         st, tm, s, c, a, dbg))
+             : (a.shared ? launch_kernel(nm, select_unit_kernel<NB, EPT, 1, NT, 0>, grid, dim3(NT),
+                                         st, tm, s, c, a, dbg)
+                         : launch_kernel(nm, select_unit_kernel<NB, EPT, 0, NT, 0>, grid, dim3(NT),
+                                         st, tm, s, c, a, dbg));
   return e != hipSuccess ? e : record_empty(kernel_timer(dbg, 3), st);
 }
 
@@ -908,13 +913,18 @@ static hipError_t launch_sliced(const Shape& s, const CacheView& c, const Select
                                 const DebugView& dbg, hipStream_t st) {
   const int units = a.shared ? s.Hkv : s.Hq;
   const dim3 grid(a.nsl, units, s.B);
+  const KernelTimer tm = kernel_timer(dbg, 2);
+  const dim3 blk(kScanThreads);
+  const char* nm = "select_scan_kernel";
   const hipError_t e =
-      a.shared ? launch_kernel("select_scan_kernel",
-                               select_scan_kernel<NB, EPT, 1>, grid, dim3(kScanThreads), st,
-                               kernel_timer(dbg, 2), s, c, a, dbg)
-               : launch_kernel("select_scan_kernel",
-                               select_scan_kernel<NB, EPT, 0>, grid, dim3(kScanThreads), st,
-                               kernel_timer(dbg, 2), s, c, a, dbg);
+      a.fine ? (a.shared ? launch_kernel(nm, select_scan_kernel<NB, EPT, 1, 1>, grid, blk, st, tm,
+                                         s, c, a, dbg)
+                         : launch_kernel(nm, select_scan_kernel<NB, EPT, 0, 1>, grid, blk, st, tm,
+                                         s, c, a, dbg))
+             : (a.shared ? launch_kernel(nm, select_scan_kernel<NB, EPT, 1, 0>, grid, blk, st, tm,
+                                         s, c, a, dbg)
+                         : launch_kernel(nm, select_scan_kernel<NB, EPT, 0, 0>, grid, blk, st, tm,
+                                         s, c, a, dbg));
   if (e != hipSuccess) return e;
   return launch_kernel("select_emit_kernel",
                        select_emit_kernel<NB>, grid, dim3(kEmitThreads), st, kernel_timer(dbg, 3),
