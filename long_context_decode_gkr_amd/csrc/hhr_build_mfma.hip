@@ -35,7 +35,9 @@
 // shares (one workgroup per sequence and KV head had left the longest sequence's workgroups
 // with 14 chunks against 10 at 8 sequences of 8K-32K tokens); the key rows stream through two LDS buffers of 128 rows (the next tile's
 // global loads in flight while the current one is multiplied), each staged row with its norm.
-// 256-bit codes take a second launch without rotation waves for code columns 128..255.
+// 256-bit codes take a second launch for code columns 128..255 without rotation waves: 8 code
+// waves, two per 32-column block, each taking half of every tile's rows (4 waves over all the
+// rows had left one wave per SIMD: 667 -> 582 us for the Qwen3-8B-shaped layer's build).
 #include "hhr_device.h"
 #include "hhr_launch.h"
 
@@ -62,7 +64,11 @@ struct Bf16Row {
 };
 
 template <bool ROT>
-constexpr int build_threads() { return kWave * (kCodeWaves + (ROT ? 4 : 0)); }
+constexpr int build_threads() { return kWave * 8; }   // 4 rotation + 4 code waves, or 8 code
+// Code waves of a launch: 4 (with rotation), else 8, two per code block, each taking half of a
+// tile's rows (so that every SIMD runs two waves)
+template <bool ROT>
+constexpr int code_waves() { return ROT ? kCodeWaves : 2 * kCodeWaves; }
 
 // Row of the accumulator element r of a 32 x 32 MFMA tile held by a lane of half 0 (half 1:
 // + 4): 8 (r / 4) + r % 4.
@@ -92,7 +98,10 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   // (measured 227 -> 209 us at 128K against waves 0..3 rotating)
   const bool rot = RW > 0 && (w & 1) == 0;
   const int half = lane >> 5, col = lane & 31;
-  const int cw = RW > 0 ? (w >> 1) : w;          // code block (code waves)
+  const int cw = RW > 0 ? (w >> 1) : (w & 3);    // code block (code waves)
+  const int rh = RW > 0 ? 0 : (w >> 2);          // without rotation: the half of the rows
+  constexpr int NCW = code_waves<ROT>();
+  const int seg = RW > 0 ? cw : w;               // the code wave's queue segment
 
   __shared__ __align__(16) uint16_t Kt[2][kKTile][kKRow];
   __shared__ float knorm[2][kKTile];              // 2^-13 |k| of the staged rows (inf if tiny)
@@ -103,10 +112,10 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   // queued uncertain bits (row of K, column), one segment of kSeg per code wave, and each
   // wave's count (which may pass kSeg: the rest is lost, see the drain). A row index is below
   // 2^32 for any K cache under 1 TiB.
-  constexpr int kSeg = kFbCap / kCodeWaves;
+  constexpr int kSeg = kFbCap / NCW;
   __shared__ uint2 fb_list[kFbCap];
-  __shared__ int fb_cnt[kCodeWaves];
-  if (tid < kCodeWaves) fb_cnt[tid] = 0;          // published by the first staging barrier
+  __shared__ int fb_cnt[NCW];
+  if (tid < NCW) fb_cnt[tid] = 0;                 // published by the first staging barrier
   int qn = 0;                                     // this code wave's count (uniform)
 
   const uint16_t* Kb = reinterpret_cast<const uint16_t*>(c.K);
@@ -237,7 +246,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
   constexpr int kEnt = 2;                          // queued entries per 4 lanes per pass
   auto drain_queue = [&](int nseg, size_t row_any) {   // nseg entries from each wave's segment;
                                                          // row_any: a valid row of K
-    const int n = nseg * kCodeWaves;
+    const int n = nseg * NCW;
     float* WT = reinterpret_cast<float*>(&Kt[0][0][0]);   // WT[c * kWTs + k] = W[k][coff + c]
     {
       // value tid + j NT is W[(tid >> 7) + j NT / 128][coff + tid % 128]; the thread's offsets
@@ -377,7 +386,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
       }
     } else {
 #pragma unroll 1
-      for (int sp = 0; sp < 2; ++sp) {
+      for (int sp = ROT ? 0 : rh; sp < (ROT ? 2 : rh + 1); ++sp) {
         f32x16 acc[2];
 #pragma unroll
         for (int u = 0; u < 2; ++u)
@@ -423,7 +432,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
               const int bi = __builtin_ctz(uns);
               uns &= uns - 1;
               if (pos < kSeg)
-                fb_list[cw * kSeg + pos] =
+                fb_list[seg * kSeg + pos] =
                     make_uint2(uint32_t(row0 + t), uint32_t(coff + 32 * cw + bi));
               ++pos;
             }
@@ -432,7 +441,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
         }
       }
     }
-    if (!rot && lane == 0) fb_cnt[cw] = qn;
+    if (!rot && lane == 0) fb_cnt[seg] = qn;
     if (more) store_tile(buf ^ 1);
     __syncthreads();
 
@@ -462,7 +471,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
       // operands instead (slow, only for such inputs).
       int nfb = 0;
 #pragma unroll
-      for (int i = 0; i < kCodeWaves; ++i) nfb = max(nfb, fb_cnt[i]);
+      for (int i = 0; i < NCW; ++i) nfb = max(nfb, fb_cnt[i]);
       if (nfb >= 3 * kSeg / 4 || !more) {
         wait_memory();
         __syncthreads();
@@ -480,7 +489,7 @@ build_mfma_kernel(Shape s, CacheView c, const float* __restrict__ R, const float
           }
         }
         __syncthreads();
-        if (tid < kCodeWaves) fb_cnt[tid] = 0;
+        if (tid < NCW) fb_cnt[tid] = 0;
         qn = 0;
         if (more) store_tile((T + 1) & 1);        // the drain used the key buffers
       }
