@@ -513,8 +513,8 @@ def test_build_mfma_exact_path_for_zero_and_tiny_projections(nzero, ntiny):
 
 
 def test_build_mfma_queue_drained_between_chunks():
-    """One workgroup per (sequence, KV head) building all 8 of its 512-token chunks (32 sequences
-    x 8 KV heads fill the GPU with nper = 1): code column 0 is z = k0 - k1 with k0 == k1 on every
+    """Every workgroup builds 8 chunks of 512 tokens in turn (32 sequences x 8 KV heads: each KV
+    head's 32 workgroups share out its 256 chunks): code column 0 is z = k0 - k1 with k0 == k1 on every
     other token, so about 270 uncertain bits a chunk reach the first code wave's queue segment;
     it is drained into the stored words every third chunk (at 3/4 of its 1024 entries) and the
     key tile staged before the drain is staged again. Codes bit-exact and extrema admissible on
