@@ -485,28 +485,31 @@ def test_build_mfma_balanced_chunk_list_across_sequence_groups():
                    extrema_atol_scale=MFMA_EXTREMA_SCALE)
 
 
-@pytest.mark.parametrize("nzero,ntiny", [(16, 8), (1, 0), (0, 1)])
-def test_build_mfma_exact_path_for_zero_and_tiny_projections(nzero, ntiny):
-    # nzero code columns give z = k0 - k1 = 0 exactly (k0 == k1), ntiny give z = 2^-30 k2: all
-    # of them fall inside the certification band. 24 columns x 512 rows overflow the queue
-    # segment (1024 entries) of the code wave owning columns 0..31 (every word of the 512-token
-    # chunk recomputed); one column's 512 fit (4 lanes per queued bit, z == 0 decided by the
-    # exact accumulator).
+@pytest.mark.parametrize("cfg_id,col0,nzero,ntiny", [(3, 0, 16, 8), (3, 0, 1, 0), (3, 0, 0, 1),
+                                                    (5, 128, 16, 8), (5, 128, 1, 0)])
+def test_build_mfma_exact_path_for_zero_and_tiny_projections(cfg_id, col0, nzero, ntiny):
+    # code columns col0 + [0, nzero) give z = k0 - k1 = 0 exactly (k0 == k1), the next ntiny give
+    # z = 2^-30 k2: all of them fall inside the certification band. 24 columns x 512 rows
+    # overflow the queue segment of the code wave owning those columns (every word of the
+    # 512-token chunk recomputed); one column's 512 fit (4 lanes per queued bit, z == 0 decided
+    # by the exact accumulator). cfg 5 (256-bit codes, page 32) puts them in columns 128.., which
+    # the second, code-only launch builds with two waves per code block.
     _torch()
-    cfg = _cfg(3, 2048, n_plant=0, num_q_heads=4, num_kv_heads=1)
+    cfg = _cfg(cfg_id, 2048, n_plant=0, num_q_heads=4, num_kv_heads=1)
     data = synth.make_layer(cfg)
     data["K"][:, :, :, 1] = data["K"][:, :, :, 0]
     W = data["W"]
     nc = nzero + ntiny
-    W[:, :, :nc] = 0.0
-    W[:, 0, :nc] = 1.0
-    W[:, 1, :nc] = -1.0
-    W[:, 2, nzero:nc] = np.float32(2.0 ** -30)
+    cols = slice(col0, col0 + nc)
+    W[:, :, cols] = 0.0
+    W[:, 0, cols] = 1.0
+    W[:, 1, cols] = -1.0
+    W[:, 2, col0 + nzero:col0 + nc] = np.float32(2.0 ** -30)
     lay = hc.GpuLayer(cfg, data=data)
     lay.build(method="auto")
     ref = hc.oracle_index(lay)
     hc.check_index(lay, ref, extrema_atol_scale=MFMA_EXTREMA_SCALE)
-    bits0 = ref["codes"][0, :, :2048, 0]
+    bits0 = ref["codes"][0, :, :2048, col0 // 32]
     assert np.all(bits0 & ((1 << nzero) - 1) == 0)                         # z == 0 gives 0
     k2pos = (data["K"][0, :, :2048, 2] > 0).astype(np.uint32)
     assert np.array_equal((bits0 >> nzero) & ((1 << ntiny) - 1), k2pos * ((1 << ntiny) - 1))
